@@ -1,0 +1,107 @@
+"""Seeded synthetic inputs for the fp16 GEMM workloads.
+
+This module only draws random numbers and rounds them to fp16; it holds none of
+the GEMM's arithmetic.  Both the GPU library's tests/benchmark and the CPU
+oracle take their inputs from here, so both sides see the same bits.
+
+Recipe (the pages fix only the shapes and the 4096^3 fp16 headline, see the
+TileLang blog post, sections "performance" and "Step 4"; the distributions
+below are this project's workload definitions):
+  * ``rng = numpy.random.default_rng(seed)`` (PCG64);
+  * draw A, then B, then bias, each as float64, in that order;
+  * ``N(0, v)`` means variance v (std = sqrt(v)); ``U[-1,1)`` is
+    ``rng.uniform(-1, 1)``;
+  * cast each array once to fp16 with numpy's round-to-nearest-even.
+Numpy's Generator streams are not promised stable across numpy versions, so
+``input_digest`` records a sha256 of the bits actually used.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+import math
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    seed: int
+    epilogue: str          # "none" | "bias" | "bias_gelu"
+    a_dist: tuple          # ("uniform", lo, hi) or ("normal", variance)
+    b_dist: tuple
+    bias_dist: tuple | None
+    note: str = ""
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """A, B, bias (if used) and C, each moved once, fp16."""
+        b = 2 * (self.M * self.K + self.K * self.N + self.M * self.N)
+        if self.epilogue != "none":
+            b += 2 * self.N
+        return b
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("gemm_256", 256, 256, 256, 0, "none", ("uniform", -1.0, 1.0), ("uniform", -1.0, 1.0), None,
+                 "small square GEMM, no epilogue"),
+        Workload("gemm_4096", 4096, 4096, 4096, 1, "none", ("uniform", -1.0, 1.0), ("uniform", -1.0, 1.0), None,
+                 "the pages' 4096^3 fp16 headline shape"),
+        Workload("mlp_up_8192x16384x4096", 8192, 16384, 4096, 2, "bias_gelu", ("normal", 1.0),
+                 ("normal", 1.0 / 4096), ("normal", 0.1), "fused MLP up-projection, GELU(A.B + bias)"),
+        Workload("ragged_4095x3001x1000", 4095, 3001, 1000, 3, "bias", ("uniform", -1.0, 1.0),
+                 ("uniform", -1.0, 1.0), ("normal", 0.1), "no dimension a multiple of any tile size"),
+        Workload("skinny_16x16384x8192", 16, 16384, 8192, 4, "bias_gelu", ("normal", 1.0),
+                 ("normal", 1.0 / 8192), ("normal", 0.1), "skinny M, HBM-bound"),
+    ]
+}
+ORDER = list(WORKLOADS)
+
+
+def _draw(rng: np.random.Generator, dist: tuple, shape) -> np.ndarray:
+    if dist[0] == "uniform":
+        return rng.uniform(dist[1], dist[2], size=shape)
+    if dist[0] == "normal":
+        return rng.standard_normal(size=shape) * math.sqrt(dist[1])
+    raise ValueError(dist)
+
+
+def make_inputs(w: Workload | str, M: int | None = None, N: int | None = None, K: int | None = None):
+    """Return (A, B, bias) as float16 numpy arrays (bias None without epilogue).
+
+    M/N/K override the workload's shape (same distributions and seed), which
+    lets tests draw small instances with the same value statistics.
+    """
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    M = w.M if M is None else M
+    N = w.N if N is None else N
+    K = w.K if K is None else K
+    rng = np.random.default_rng(w.seed)
+    A = _draw(rng, w.a_dist, (M, K)).astype(np.float16)
+    B = _draw(rng, w.b_dist, (K, N)).astype(np.float16)
+    bias = _draw(rng, w.bias_dist, (N,)).astype(np.float16) if w.bias_dist is not None else None
+    return A, B, bias
+
+
+def random_f16(seed: int, shape, lo: float = -1.0, hi: float = 1.0) -> np.ndarray:
+    """Plain uniform fp16 draws for ad-hoc test shapes."""
+    rng = np.random.default_rng(seed)
+    return rng.uniform(lo, hi, size=shape).astype(np.float16)
+
+
+def input_digest(*arrays) -> str:
+    h = hashlib.sha256()
+    for a in arrays:
+        if a is not None:
+            h.update(np.ascontiguousarray(a).view(np.uint8).tobytes())
+    return h.hexdigest()
