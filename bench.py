@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X fp16 GEMM (+ fused bias / GELU) library.
+
+One "step" is one call of the library's C entry point gemm_f16 on one batch of
+synthetic, seeded input already resident in HBM: the whole hot path (tile
+scheduling, LDS staging, MFMA main loop, fused epilogue, single write of C).
+The default workload is the 4096^3 fp16 GEMM (the headline shape of the
+TileLang tutorial's blog post, sections "performance" and "Step 4").
+
+Prints ONE JSON line:
+  value     = TFLOP/s = 2*M*N*K / (time per step)
+  roofline  = the dominant kernel against MI355X's published peak (dense fp16
+              MFMA 2.5 PFLOP/s, or HBM 8 TB/s for the skinny workload), its
+              duration measured here with HIP events on the launch stream;
+              traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE
+              counters (profiles/), null if the kernel sources changed since.
+  cpu_baseline = the CPU oracle (fp64, all host threads) on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_tiled_gemm_04_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".h", ".hip")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch recorded from rocprofv3 counters, if still valid."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(workload)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_sha256") != kernel_source_digest() or rec.get("kernel") != kernel:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, A, B, bias, target_s: float = 10.0):
+    """Time the CPU oracle on the first R rows of the workload (full K, all N)."""
+    import numpy as np
+    import oracle
+
+    threads = oracle.max_threads()
+    # calibrate on a few rows, then size the sample for ~target_s of CPU work
+    r0 = min(w.M, 16)
+    t = time.perf_counter()
+    oracle.gemm(A[:r0], B, bias, w.epilogue, threads=threads)
+    dt = max(time.perf_counter() - t, 1e-6)
+    rows = int(min(w.M, max(r0, r0 * target_s / dt)))
+    t = time.perf_counter()
+    oracle.gemm(np.ascontiguousarray(A[:rows]), B, bias, w.epilogue, threads=threads)
+    dt = time.perf_counter() - t
+    flops = 2.0 * rows * w.N * w.K
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "rows 0..%d of C (%d x %d outputs, full K=%d, epilogue %s), fp64 oracle, %.2f s wall"
+                  % (rows - 1, rows, w.N, w.K, w.epilogue, dt),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gemm_4096")
+    ap.add_argument("--config", type=int, default=None, help="force a kernel config index")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", type=int, default=None,
+                    help="copies of B to rotate through (default: 3 for HBM-bound workloads, else 1)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the GEMM runs on a single MI355X and this build has no "
+              "multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import dense_tiled_gemm_04_amd as g
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    g.load()
+    w = workloads.WORKLOADS[args.workload]
+    A, B, bias = workloads.make_inputs(w)
+    hbm_bound = w.flops / w.algorithmic_bytes < 100.0
+    rotate = args.rotate if args.rotate is not None else (3 if hbm_bound else 1)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dA = torch.from_numpy(A).to(dev)
+    dBs = [torch.from_numpy(B).to(dev) for _ in range(rotate)]
+    db = torch.from_numpy(bias).to(dev) if bias is not None else None
+    dC = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    epi = g.EPILOGUES[w.epilogue]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    pA, pC = dA.data_ptr(), dC.data_ptr()
+    pBs = [b.data_ptr() for b in dBs]
+    pb = db.data_ptr() if db is not None else None
+    cfg_idx = args.config if args.config is not None else g.select_config_raw(w.M, w.N, w.K, pA, pBs[0], pb, pC, epi)
+    cfg = g.config_info(cfg_idx)
+    lib = g.load()
+
+    def step(i):
+        st = lib.gemm_f16_with_config(cfg_idx, w.M, w.N, w.K, pA, pBs[i % rotate], pb, pC, epi, sh) \
+            if args.config is not None else lib.gemm_f16(w.M, w.N, w.K, pA, pBs[i % rotate], pb, pC, epi, sh)
+        if st != 0:
+            raise g.GemmError(st)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: synchronised on both sides, HIP events on the launch stream
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    gbs = w.algorithmic_bytes / (ms * 1e-3) / 1e9
+
+    # context: the vendor BLAS on the same tensors (torch.matmul; + bias + gelu eagerly if fused)
+    def torch_step(i):
+        c = torch.matmul(dA, dBs[i % rotate])
+        if w.epilogue == "bias":
+            c = c + db
+        elif w.epilogue == "bias_gelu":
+            c = torch.nn.functional.gelu(c + db)
+        return c
+    for i in range(5):
+        torch_step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    n_t = max(10, min(args.steps, 100))
+    t0.record(stream)
+    for i in range(n_t):
+        torch_step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    torch_ms = t0.elapsed_time(t1) / n_t
+
+    traffic = load_traffic(w.name, cfg["name"])
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS, "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / PEAK_FP16_TFLOPS, "traffic": traffic}
+    roof["kernel"] = cfg["name"]
+    roof["algorithmic_flops_per_launch"] = w.flops
+    roof["algorithmic_bytes_per_launch"] = w.algorithmic_bytes
+    roof["avg_launch_us"] = ms * 1e3
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, A, B, bias)
+
+    out = {
+        "metric": "fp16 GEMM TFLOPS (4096^3; fused bias+GELU MLP) + % of MI355X MFMA peak",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "epilogue": w.epilogue,
+                   "inputs": "seeded numpy draws (%s), B copies rotated: %d" % (w.note, rotate)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "context": {"torch_matmul_ms": round(torch_ms, 6),
+                    "torch_tflops": round(w.flops / (torch_ms * 1e-3) / 1e12, 3),
+                    "algorithmic_GBps": round(gbs, 1)},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

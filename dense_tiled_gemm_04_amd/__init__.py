@@ -1,0 +1,188 @@
+"""Python binding of the MI355X (gfx950) fp16 GEMM library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libgemm_f16.so`` (built from ``csrc/`` by ``build.py``), reached
+through the C ABI in ``include/gemm_f16.h``.  PyTorch supplies device memory and
+the current stream.  If the shared library is missing, every entry point
+raises: there is no CPU or PyTorch fallback.
+
+Computes C = fp16(epi(A @ B)), epi in {none, bias, bias_gelu} with GELU in its
+exact erf form, fp32 accumulation (TileLang tutorial: blog post "Designing
+High-Performance GPU Kernels with TileLang", section "Step 4"; news article on
+TileLang kernel design, paragraphs on the tiled GEMM and the fused epilogue).
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libgemm_f16.so")
+
+EPILOGUES = {"none": 0, "bias": 1, "bias_gelu": 2}
+STATUS = {
+    0: "GEMM_OK", 1: "GEMM_ERR_INVALID_DIM", 2: "GEMM_ERR_NULL_POINTER", 3: "GEMM_ERR_BAD_EPILOGUE",
+    4: "GEMM_ERR_LAUNCH", 5: "GEMM_ERR_NO_CONFIG", 6: "GEMM_ERR_UNSUPPORTED", 7: "GEMM_ERR_MISALIGNED",
+}
+# every symbol include/gemm_f16.h declares
+EXPORTS = [
+    "gemm_f16", "gemm_f16_status_string", "gemm_f16_num_configs", "gemm_f16_config_info",
+    "gemm_f16_select_config", "gemm_f16_with_config", "vector_add_f32",
+]
+
+_lib = None
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(status_string(status))
+
+
+def load():
+    """Load libgemm_f16.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libgemm_f16.so is not built; run `python -m dense_tiled_gemm_04_amd.build` "
+                           "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.gemm_f16.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32, vp]
+    lib.gemm_f16.restype = i32
+    lib.gemm_f16_with_config.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, i32, vp]
+    lib.gemm_f16_with_config.restype = i32
+    lib.gemm_f16_select_config.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32]
+    lib.gemm_f16_select_config.restype = i32
+    lib.gemm_f16_status_string.argtypes = [i32]
+    lib.gemm_f16_status_string.restype = ctypes.c_char_p
+    lib.gemm_f16_num_configs.argtypes = []
+    lib.gemm_f16_num_configs.restype = i32
+    lib.gemm_f16_config_info.argtypes = [i32, ctypes.c_char_p, i32]
+    lib.gemm_f16_config_info.restype = i32
+    lib.vector_add_f32.argtypes = [i64, vp, vp, vp, vp]
+    lib.vector_add_f32.restype = i32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().gemm_f16_status_string(int(status)).decode()
+
+
+def num_configs() -> int:
+    return int(load().gemm_f16_num_configs())
+
+
+def config_info(idx: int) -> dict:
+    buf = ctypes.create_string_buffer(1024)
+    n = load().gemm_f16_config_info(int(idx), buf, 1024)
+    if n < 0:
+        raise GemmError(-n)
+    return json.loads(buf.value.decode())
+
+
+def configs() -> list[dict]:
+    return [config_info(i) for i in range(num_configs())]
+
+
+# ---------------------------------------------------------------------------
+# raw-pointer entry points (ints are device addresses; stream is a hipStream_t)
+# ---------------------------------------------------------------------------
+def gemm_f16_raw(M, N, K, A, B, bias, C, epilogue: int, stream=0, config: int | None = None) -> int:
+    lib = load()
+    if config is None:
+        return int(lib.gemm_f16(M, N, K, A, B, bias, C, epilogue, stream))
+    return int(lib.gemm_f16_with_config(config, M, N, K, A, B, bias, C, epilogue, stream))
+
+
+def select_config_raw(M, N, K, A, B, bias, C, epilogue: int) -> int:
+    return int(load().gemm_f16_select_config(M, N, K, A, B, bias, C, epilogue))
+
+
+# ---------------------------------------------------------------------------
+# torch front end
+# ---------------------------------------------------------------------------
+def _check(t, name, ndim):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != torch.float16:
+        raise TypeError("%s must be float16, got %s" % (name, t.dtype))
+    if t.dim() != ndim:
+        raise ValueError("%s must be %d-D" % (name, ndim))
+    if not t.is_cuda:
+        raise ValueError("%s must be on the GPU" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous (row-major)" % name)
+
+
+def _stream_handle():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def gemm_f16(A, B, bias=None, epilogue: str = "none", out=None, config: int | None = None):
+    """C = fp16(epi(A @ B [+ bias])) on the current stream; returns C (torch.float16 [M, N])."""
+    import torch
+    if epilogue not in EPILOGUES:
+        raise ValueError("epilogue must be one of %s" % list(EPILOGUES))
+    _check(A, "A", 2)
+    _check(B, "B", 2)
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ: A is %s, B is %s" % (tuple(A.shape), tuple(B.shape)))
+    if A.device != B.device:
+        raise ValueError("A and B on different devices")
+    epi = EPILOGUES[epilogue]
+    if epi != 0:
+        if bias is None:
+            raise ValueError("epilogue %r needs a bias" % epilogue)
+        _check(bias, "bias", 1)
+        if bias.shape[0] != N:
+            raise ValueError("bias must have N=%d elements" % N)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    else:
+        _check(out, "out", 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be [%d, %d]" % (M, N))
+    with torch.cuda.device(A.device):
+        st = gemm_f16_raw(M, N, K, A.data_ptr(), B.data_ptr(), bias.data_ptr() if epi != 0 else None,
+                          out.data_ptr(), epi, _stream_handle(), config)
+    if st != 0:
+        raise GemmError(st)
+    return out
+
+
+def select_config(A, B, bias=None, epilogue: str = "none", out=None) -> int:
+    """Index of the configuration gemm_f16 would launch (-1 for an empty output)."""
+    M, K = A.shape
+    N = B.shape[1]
+    epi = EPILOGUES[epilogue]
+    optr = out.data_ptr() if out is not None else 256  # a 256-byte-aligned stand-in address
+    r = select_config_raw(M, N, K, A.data_ptr(), B.data_ptr(), bias.data_ptr() if bias is not None else None,
+                          optr, epi)
+    if r < -1:
+        raise GemmError(-r)
+    return r
+
+
+def vector_add(a, b, out=None):
+    """out = a + b for contiguous float32 GPU tensors (the HBM calibration kernel)."""
+    import torch
+    for t, n in ((a, "a"), (b, "b")):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError("%s must be a contiguous float32 GPU tensor" % n)
+    if a.numel() != b.numel():
+        raise ValueError("size mismatch")
+    if out is None:
+        out = torch.empty_like(a)
+    with torch.cuda.device(a.device):
+        st = int(load().vector_add_f32(a.numel(), a.data_ptr(), b.data_ptr(), out.data_ptr(), _stream_handle()))
+    if st != 0:
+        raise GemmError(st)
+    return out

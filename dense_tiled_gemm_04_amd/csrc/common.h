@@ -1,0 +1,111 @@
+// Shared device-side definitions for the gfx950 fp16 GEMM kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gk {
+
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define GK_LDS __attribute__((address_space(3)))
+#define GK_GLB __attribute__((address_space(1)))
+
+enum Epilogue { EPI_NONE = 0, EPI_BIAS = 1, EPI_BIAS_GELU = 2 };
+
+struct GemmArgs {
+    const f16* A;     // [M][K]
+    const f16* B;     // [K][N]
+    const f16* bias;  // [N] or null
+    f16* C;           // [M][N]
+    int M, N, K;
+    int tiles_m, tiles_n;
+    int k_split;      // skinny path: number of K slices (1 = none)
+    float* partial;   // skinny path: [k_split][M][N] fp32 partial sums (k_split > 1)
+};
+
+// Exact-erf GELU on an fp32 value: 0.5 x (1 + erf(x/sqrt2)) = 0.5 x erfc(-x/sqrt2).
+// The erfc form has no cancellation for x << 0 (where 1 + erf(.) -> 0 and the
+// erf form loses most of its significant bits); erfc from the device math library.
+__device__ __forceinline__ float gelu_erf(float x) {
+    return 0.5f * x * erfcf(x * -0.70710678118654752f);
+}
+
+template <int EPI>
+__device__ __forceinline__ float apply_epilogue(float s, float b) {
+    if constexpr (EPI == EPI_NONE) {
+        return s;
+    } else if constexpr (EPI == EPI_BIAS) {
+        return s + b;
+    } else {
+        return gelu_erf(s + b);
+    }
+}
+
+// Workgroup id -> linear tile id.  The dispatcher deals consecutive workgroup
+// ids round-robin over the 8 XCDs; this regroups them so that each XCD (each
+// with its own L2) receives one contiguous run of tile ids.  A bijection on
+// [0, nwg) for any nwg.
+__device__ __forceinline__ int xcd_contiguous_id(int wg, int nwg) {
+    const int xcd = wg & 7, slot = wg >> 3;
+    const int q = nwg >> 3, r = nwg & 7;
+    return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + slot;
+}
+
+// Linear tile id -> (tile_m, tile_n), walking GROUP_M tile-rows column by
+// column so neighbouring ids share B column panels and A row panels in L2.
+template <int GROUP_M>
+__device__ __forceinline__ void grouped_tile(int lid, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int per_group = GROUP_M * tiles_n;
+    const int group = lid / per_group;
+    const int first_m = group * GROUP_M;
+    const int rows = min(tiles_m - first_m, GROUP_M);
+    const int in_g = lid - group * per_group;
+    tm = first_m + in_g % rows;
+    tn = in_g / rows;
+}
+
+__device__ __forceinline__ f16x4 lds_read_tr16_b64(const GK_LDS char* p) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GK_LDS s16x4*)p);
+    return __builtin_bit_cast(f16x4, v);
+}
+
+// ---- asynchronous HBM/L2 -> LDS copies (LDS-DMA) ----
+// Issued through inline assembly on purpose: when the compiler sees an
+// LDS-DMA builtin it must assume any later LDS read may alias the copy and
+// places "s_waitcnt vmcnt(0)" before it, which serialises the prefetch of
+// stage s+1 behind the compute of stage s.  Here the kernels order the copies
+// themselves (wait_vmcnt<> + barrier before a stage is read).  The LDS
+// destination of lane l is m0 + size*l; m0 is written right before each copy
+// (the compiler never keeps a value of its own in m0 in these kernels).
+__device__ __forceinline__ uint32_t lds_addr(const GK_LDS void* p) { return (uint32_t)(uintptr_t)p; }
+
+// 16 bytes per lane from sbase + voff (global, 64-bit scalar base + 32-bit lane offset).
+__device__ __forceinline__ void dma_global_16(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+                 : "memory");
+}
+// 16 / 4 bytes per lane through a buffer resource: offsets past num_records read as 0.
+__device__ __forceinline__ void dma_buffer_16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "s"(lds)
+                 : "memory");
+}
+__device__ __forceinline__ void dma_buffer_4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "s"(lds)
+                 : "memory");
+}
+
+__device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wait until at most CNT vector-memory operations of this wave are outstanding.
+template <int CNT>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(CNT >= 0 && CNT <= 63, "vmcnt field");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CNT) : "memory");
+}
+
+}  // namespace gk

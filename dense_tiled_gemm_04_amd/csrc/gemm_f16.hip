@@ -1,0 +1,272 @@
+// C-ABI entry points, configuration table and host dispatch of the gfx950
+// fp16 GEMM library.  Declarations and the contract are in include/gemm_f16.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gemm_f16.h"
+#include "skinny_kernel.h"
+#include "tile_kernel.h"
+
+using namespace gk;
+
+namespace {
+
+enum Kind { KIND_TILE = 0, KIND_SKINNY = 1 };
+
+typedef hipError_t (*launch_fn)(const GemmArgs&, hipStream_t);
+
+struct Config {
+    const char* name;
+    int kind;
+    int bm, bn, bk, wm, wn;  // tile: block tile and wave grid; skinny: bm = 16*MB rows
+    int loader;              // tile loaders; -1 for skinny
+    int group_m;
+    int stages;
+    int lds_bytes;
+    int threads;
+    launch_fn launch[3];     // indexed by epilogue
+};
+
+template <int BM, int BN, int BK, int WM, int WN, int LOADER, int GROUP_M, int EPI>
+hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
+    dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(WM * WN * 64);
+    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, BK, WM, WN, LOADER, EPI, GROUP_M>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+template <int MB, int STAGES, int EPI>
+hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
+    dim3 grid((unsigned)a.tiles_n), block(SK_WAVES * 64);
+    hipLaunchKernelGGL((gemm_skinny_kernel<MB, STAGES, EPI>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+#define TILE_CFG(BM, BN, BK, WM, WN, LOADER, G, NAME)                                              \
+    Config {                                                                                       \
+        NAME, KIND_TILE, BM, BN, BK, WM, WN, LOADER, G, 2,                                         \
+            TileCfg<BM, BN, BK, WM, WN, LOADER, 0, G>::LDS_BYTES, WM * WN * 64,                    \
+        {                                                                                          \
+            launch_tile<BM, BN, BK, WM, WN, LOADER, G, 0>, launch_tile<BM, BN, BK, WM, WN, LOADER, G, 1>, \
+                launch_tile<BM, BN, BK, WM, WN, LOADER, G, 2>                                      \
+        }                                                                                          \
+    }
+
+#define SKINNY_CFG(MB, ST, NAME)                                                                    \
+    Config {                                                                                       \
+        NAME, KIND_SKINNY, 16 * MB, SK_BN, SK_BK, 1, SK_WAVES, -1, 1, ST,                          \
+            ST * (16 * MB * SK_BK * 2 + SK_BK * SK_BN * 2), SK_WAVES * 64,                         \
+        {                                                                                          \
+            launch_skinny<MB, ST, 0>, launch_skinny<MB, ST, 1>, launch_skinny<MB, ST, 2>           \
+        }                                                                                          \
+    }
+
+const Config kConfigs[] = {
+    TILE_CFG(256, 256, 64, 2, 2, LOAD_DIRECT, 4, "tile_256x256x64_w2x2_direct_g4"),   // 0
+    TILE_CFG(256, 256, 64, 2, 2, LOAD_VEC, 4, "tile_256x256x64_w2x2_vec_g4"),         // 1
+    TILE_CFG(128, 128, 64, 2, 2, LOAD_DIRECT, 4, "tile_128x128x64_w2x2_direct_g4"),   // 2
+    TILE_CFG(128, 128, 64, 2, 2, LOAD_VEC, 4, "tile_128x128x64_w2x2_vec_g4"),         // 3
+    TILE_CFG(128, 128, 64, 2, 2, LOAD_ELEM, 4, "tile_128x128x64_w2x2_elem_g4"),       // 4
+    TILE_CFG(256, 128, 64, 2, 2, LOAD_DIRECT, 4, "tile_256x128x64_w2x2_direct_g4"),   // 5
+    SKINNY_CFG(1, 6, "skinny_m16_s6"),                                                // 6
+    SKINNY_CFG(2, 5, "skinny_m32_s5"),                                                // 7
+    SKINNY_CFG(4, 4, "skinny_m64_s4"),                                                // 8
+};
+constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
+
+enum DefaultIdx {
+    CFG_T256_DIRECT = 0,
+    CFG_T256_VEC = 1,
+    CFG_T128_DIRECT = 2,
+    CFG_T128_VEC = 3,
+    CFG_T128_ELEM = 4,
+    CFG_SKINNY16 = 6,
+    CFG_SKINNY32 = 7,
+    CFG_SKINNY64 = 8,
+};
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Call {
+    int64_t M, N, K;
+    const void *A, *B, *bias;
+    void* C;
+    int epi;
+};
+
+int validate(const Call& c) {
+    if (c.M < 0 || c.N < 0 || c.K < 0 || c.M > INT32_MAX || c.N > INT32_MAX || c.K > INT32_MAX)
+        return GEMM_ERR_INVALID_DIM;
+    if (c.epi < GEMM_EPI_NONE || c.epi > GEMM_EPI_BIAS_GELU) return GEMM_ERR_BAD_EPILOGUE;
+    if (c.M == 0 || c.N == 0) return GEMM_OK;
+    if (!c.C) return GEMM_ERR_NULL_POINTER;
+    if (c.K > 0 && (!c.A || !c.B)) return GEMM_ERR_NULL_POINTER;
+    if (c.epi != GEMM_EPI_NONE && !c.bias) return GEMM_ERR_NULL_POINTER;
+    if (!aligned(c.C, 2) || (c.K > 0 && (!aligned(c.A, 2) || !aligned(c.B, 2))) ||
+        (c.epi != GEMM_EPI_NONE && !aligned(c.bias, 2)))
+        return GEMM_ERR_MISALIGNED;
+    return GEMM_OK;
+}
+
+// Whether config `cfg` can run call `c` (validated, M, N > 0).
+bool supports(const Config& cfg, const Call& c) {
+    const bool epi_bias_ok = (c.epi == GEMM_EPI_NONE) || aligned(c.bias, 8);
+    const bool vec_ok = aligned(c.A, 16) && aligned(c.B, 16) && aligned(c.C, 16) && c.K % 8 == 0 &&
+                        c.N % 8 == 0 && epi_bias_ok;
+    if (cfg.kind == KIND_SKINNY) {
+        return vec_ok && c.M <= cfg.bm && c.K * c.N * 2 < (int64_t)INT32_MAX &&
+               c.M * c.K * 2 < (int64_t)INT32_MAX;
+    }
+    switch (cfg.loader) {
+        case LOAD_DIRECT:
+            return vec_ok && c.K % cfg.bk == 0 && (int64_t)cfg.bm * c.K * 2 < (int64_t)INT32_MAX &&
+                   (int64_t)cfg.bk * c.N * 2 < (int64_t)INT32_MAX;
+        case LOAD_VEC:
+            return vec_ok;
+        default:
+            return true;
+    }
+}
+
+int pick_default(const Call& c) {
+    // skinny M: bandwidth path streaming B once
+    if (c.M <= 64) {
+        const int idx = c.M <= 16 ? CFG_SKINNY16 : (c.M <= 32 ? CFG_SKINNY32 : CFG_SKINNY64);
+        if (supports(kConfigs[idx], c)) return idx;
+    }
+    const int64_t tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256);
+    const bool big = tiles256 >= 256;  // at least one workgroup per CU with 256x256 tiles
+    const int cand[] = {big ? CFG_T256_DIRECT : CFG_T128_DIRECT, big ? CFG_T256_VEC : CFG_T128_VEC};
+    for (int idx : cand)
+        if (supports(kConfigs[idx], c)) return idx;
+    return CFG_T128_ELEM;
+}
+
+int run(const Config& cfg, const Call& c, hipStream_t stream) {
+    GemmArgs a;
+    a.A = (const f16*)c.A;
+    a.B = (const f16*)c.B;
+    a.bias = (const f16*)c.bias;
+    a.C = (f16*)c.C;
+    a.M = (int)c.M;
+    a.N = (int)c.N;
+    a.K = (int)c.K;
+    a.k_split = 1;
+    a.partial = nullptr;
+    if (cfg.kind == KIND_SKINNY) {
+        a.tiles_m = 1;
+        a.tiles_n = (int)((c.N + SK_BN - 1) / SK_BN);
+    } else {
+        a.tiles_m = (int)((c.M + cfg.bm - 1) / cfg.bm);
+        a.tiles_n = (int)((c.N + cfg.bn - 1) / cfg.bn);
+    }
+    hipError_t e = cfg.launch[c.epi](a, stream);
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+__global__ void vector_add_f32_kernel(const float* __restrict__ A, const float* __restrict__ B,
+                                      float* __restrict__ C, int64_t n) {
+    // 16-byte vector body (bases are 16-byte aligned, checked on the host) plus a scalar tail.
+    const int64_t n4 = n / 4;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const float4* A4 = (const float4*)A;
+    const float4* B4 = (const float4*)B;
+    float4* C4 = (float4*)C;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        const float4 a = A4[i], b = B4[i];
+        C4[i] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+    }
+    for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) C[i] = A[i] + B[i];
+}
+
+__global__ void vector_add_f32_scalar_kernel(const float* __restrict__ A, const float* __restrict__ B,
+                                             float* __restrict__ C, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) C[i] = A[i] + B[i];
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gemm_f16_status_string(int status) {
+    switch (status) {
+        case GEMM_OK: return "GEMM_OK";
+        case GEMM_ERR_INVALID_DIM: return "GEMM_ERR_INVALID_DIM";
+        case GEMM_ERR_NULL_POINTER: return "GEMM_ERR_NULL_POINTER";
+        case GEMM_ERR_BAD_EPILOGUE: return "GEMM_ERR_BAD_EPILOGUE";
+        case GEMM_ERR_LAUNCH: return "GEMM_ERR_LAUNCH";
+        case GEMM_ERR_NO_CONFIG: return "GEMM_ERR_NO_CONFIG";
+        case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED";
+        case GEMM_ERR_MISALIGNED: return "GEMM_ERR_MISALIGNED";
+        default: return "GEMM_ERR_UNKNOWN";
+    }
+}
+
+int gemm_f16_num_configs(void) { return kNumConfigs; }
+
+int gemm_f16_config_info(int idx, char* buf, int buflen) {
+    if (idx < 0 || idx >= kNumConfigs) return -GEMM_ERR_NO_CONFIG;
+    const Config& c = kConfigs[idx];
+    static const char* loaders[] = {"direct", "vec", "elem"};
+    char tmp[512];
+    int n = snprintf(tmp, sizeof(tmp),
+                     "{\"idx\": %d, \"name\": \"%s\", \"kind\": \"%s\", \"bm\": %d, \"bn\": %d, \"bk\": %d, "
+                     "\"waves_m\": %d, \"waves_n\": %d, \"loader\": \"%s\", \"group_m\": %d, \"stages\": %d, "
+                     "\"lds_bytes\": %d, \"threads\": %d}",
+                     idx, c.name, c.kind == KIND_TILE ? "tile" : "skinny", c.bm, c.bn, c.bk, c.wm, c.wn,
+                     c.kind == KIND_TILE ? loaders[c.loader] : "lds_dma", c.group_m, c.stages, c.lds_bytes,
+                     c.threads);
+    if (buf && buflen > 0) {
+        strncpy(buf, tmp, (size_t)buflen - 1);
+        buf[buflen - 1] = '\0';
+    }
+    return n;
+}
+
+int gemm_f16_select_config(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias, void* C,
+                           int epilogue) {
+    Call c{M, N, K, A, B, bias, C, epilogue};
+    int st = validate(c);
+    if (st != GEMM_OK) return -st;
+    if (M == 0 || N == 0) return -1;
+    return pick_default(c);
+}
+
+int gemm_f16_with_config(int idx, int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias,
+                         void* C, int epilogue, void* stream) {
+    Call c{M, N, K, A, B, bias, C, epilogue};
+    int st = validate(c);
+    if (st != GEMM_OK) return st;
+    if (idx < 0 || idx >= kNumConfigs) return GEMM_ERR_NO_CONFIG;
+    if (M == 0 || N == 0) return GEMM_OK;
+    if (!supports(kConfigs[idx], c)) return GEMM_ERR_UNSUPPORTED;
+    return run(kConfigs[idx], c, (hipStream_t)stream);
+}
+
+int gemm_f16(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias, void* C, int epilogue,
+             void* stream) {
+    Call c{M, N, K, A, B, bias, C, epilogue};
+    int st = validate(c);
+    if (st != GEMM_OK) return st;
+    if (M == 0 || N == 0) return GEMM_OK;
+    return run(kConfigs[pick_default(c)], c, (hipStream_t)stream);
+}
+
+int vector_add_f32(int64_t n, const float* A, const float* B, float* C, void* stream) {
+    if (n < 0) return GEMM_ERR_INVALID_DIM;
+    if (n == 0) return GEMM_OK;
+    if (!A || !B || !C) return GEMM_ERR_NULL_POINTER;
+    if (!aligned(A, 4) || !aligned(B, 4) || !aligned(C, 4)) return GEMM_ERR_MISALIGNED;
+    const int threads = 256;
+    const int64_t blocks_needed = (n / 4 + threads - 1) / threads;
+    const unsigned blocks = (unsigned)(blocks_needed < 1 ? 1 : (blocks_needed > 256 * 64 ? 256 * 64 : blocks_needed));
+    if (aligned(A, 16) && aligned(B, 16) && aligned(C, 16))
+        hipLaunchKernelGGL(vector_add_f32_kernel, dim3(blocks), dim3(threads), 0, (hipStream_t)stream, A, B, C, n);
+    else
+        hipLaunchKernelGGL(vector_add_f32_scalar_kernel, dim3(blocks), dim3(threads), 0, (hipStream_t)stream, A, B, C, n);
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,177 @@
+// Skinny-M fp16 GEMM for gfx950 (M <= 16 * MB): the HBM-bound shape, where B
+// is streamed exactly once and A (M x K, a few hundred KiB) stays in L2.
+//
+// The tutorial notes that bandwidth-bound kernels are limited by memory
+// traffic rather than math (TileLang blog post, section on pitfalls; news
+// article, paragraph on the fused epilogue and memory-bandwidth bottlenecks).
+// Here the design goal is to keep enough bytes of B in flight per CU:
+//  * one workgroup = 4 wave64s owns a 64-column panel of B/C and all of K;
+//    the grid has ceil(N / 64) workgroups (256 for N = 16384: one per CU);
+//  * B and A reach LDS by asynchronous LDS-DMA (buffer_load ... lds), STAGES
+//    deep, so the bytes in flight do not occupy VGPRs;
+//  * B rows past K fall outside the buffer range and read as zero, which
+//    zeroes a ragged K tail without per-lane masks; A rows are range-masked
+//    at the same granularity (see below);
+//  * wave w computes the 16-column block w of the panel with
+//    v_mfma_f32_16x16x32_f16, B fragments via the LDS transpose read;
+//  * the fused epilogue runs on the accumulators; C is written once.
+#pragma once
+#include "common.h"
+
+namespace gk {
+
+constexpr int SK_BN = 64;       // panel width (columns of B / C per workgroup)
+constexpr int SK_BK = 128;      // K rows per stage
+constexpr int SK_WAVES = 4;
+
+// B stage: [SK_BK][SK_BN] fp16, 8 chunks of 16 bytes per row.  Logical chunk
+// c of row kr lives at c ^ sk_swz_b(kr); a half-wave transpose read touches
+// 8 rows x 2 chunks, which this spreads over 16 distinct bank groups.
+__device__ __forceinline__ int sk_swz_b(int kr) {
+    return 2 * (((kr >> 1) & 1) | (((kr >> 3) & 1) << 1));
+}
+
+template <int MB, int STAGES, int EPI>
+__global__ void __launch_bounds__(SK_WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
+gemm_skinny_kernel(GemmArgs p) {
+    constexpr int NT = SK_WAVES * 64;
+    constexpr int MR = 16 * MB;                      // A rows held per stage
+    constexpr int B_STAGE = SK_BK * SK_BN * 2;       // 16 KiB
+    constexpr int A_STAGE = MR * SK_BK * 2;          // 4 KiB per 16 rows
+    constexpr int B_INS = B_STAGE / 16 / NT;         // 16-byte DMA per lane
+    constexpr int A_INS = A_STAGE / 4 / NT;          // 4-byte DMA per lane
+    static_assert(B_INS * 16 * NT == B_STAGE && A_INS * 4 * NT == A_STAGE, "stage split");
+    __shared__ __attribute__((aligned(1024))) char smem_raw[STAGES * (A_STAGE + B_STAGE)];
+    GK_LDS char* smem = (GK_LDS char*)smem_raw;
+    GK_LDS char* const b_lds = smem;
+    GK_LDS char* const a_lds = smem + STAGES * B_STAGE;
+
+    const int M = p.M, N = p.N, K = p.K;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = blockIdx.x * SK_BN;
+    const int KT = (K + SK_BK - 1) / SK_BK;
+
+    // Buffer resources: B covers exactly K*N elements, so k-rows >= K read 0.
+    const __amdgpu_buffer_rsrc_t b_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.B, (short)0, (int)min((int64_t)K * N * 2, (int64_t)0x7fffffff), 0x00020000);
+    const __amdgpu_buffer_rsrc_t a_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, (int)min((int64_t)M * K * 2, (int64_t)0x7fffffff), 0x00020000);
+
+    // Per-lane DMA source offsets within one stage.
+    uint32_t b_off[B_INS];
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) {
+        const int P = (i * SK_WAVES + wave) * 64 + lane;  // destination chunk in the stage
+        const int kr = P >> 3, pc = P & 7;
+        const int c = pc ^ sk_swz_b(kr);
+        const int n = min(n0 + 8 * c, N - 8);              // past-N columns re-read the last chunk
+        b_off[i] = (uint32_t)((kr * N + n) * 2);
+    }
+    // A stage: [MR][SK_BK] fp16 = 16 chunks per row, chunk c of row m at c ^ (m & 15).
+    // Rows >= M are clamped to M-1 (results never stored); a dword past K in a
+    // row reads the next row's data, multiplied by B rows that read as zero.
+    // That product is 0 for finite A; to keep it exact even for non-finite A,
+    // dwords past K are redirected out of range (read as 0) below.
+    uint32_t a_off[A_INS];
+    int a_kcol[A_INS];
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) {
+        const int D = (i * SK_WAVES + wave) * 64 + lane;   // destination dword in the stage
+        const int m = D >> 6, pc = (D >> 2) & 15, w = D & 3;
+        const int c = pc ^ (m & 15);
+        const int mm = min(m, M - 1);
+        a_kcol[i] = 8 * c + 2 * w;                         // k offset within the stage
+        a_off[i] = (uint32_t)((mm * K + a_kcol[i]) * 2);
+    }
+
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t b_lds0 = lds_addr(b_lds) + wave_s * 64 * 16;
+    const uint32_t a_lds0 = lds_addr(a_lds) + wave_s * 64 * 4;
+    auto issue = [&](int kt, int s) {
+        const int kbase = kt * SK_BK;
+        const uint32_t b_so = (uint32_t)kbase * N * 2;
+#pragma unroll
+        for (int i = 0; i < B_INS; ++i)
+            dma_buffer_16(b_rsrc, b_off[i] + b_so, b_lds0 + s * B_STAGE + i * SK_WAVES * 64 * 16);
+#pragma unroll
+        for (int i = 0; i < A_INS; ++i) {
+            const uint32_t off = (kbase + a_kcol[i] < K) ? a_off[i] + (uint32_t)kbase * 2 : 0x80000000u;
+            dma_buffer_4(a_rsrc, off, a_lds0 + s * A_STAGE + i * SK_WAVES * 64 * 4);
+        }
+    };
+
+    f32x4 acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // MFMA 16x16x32 as D[n][m] = B^T . A^T:
+    //  operand a (B^T): lane l holds B[k = 8*(l/16) + 0..7][n = l%16], built from
+    //   two transpose reads; lane L = 16g + 4j + q addresses B[8g + 4h + j][4q..4q+3];
+    //  operand b (A^T): lane l holds A[m = l%16][k = 8*(l/16) + 0..7].
+    auto compute_stage = [&](int s) {
+        const GK_LDS char* Bs = b_lds + s * B_STAGE;
+        const GK_LDS char* As = a_lds + s * A_STAGE;
+        const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+        const int nl = wave * 16 + 4 * q;                  // column within the panel
+#pragma unroll
+        for (int ks = 0; ks < SK_BK / 32; ++ks) {
+            f16x4 half_[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int kr = 32 * ks + 8 * g + 4 * h + j;
+                const int c = (nl >> 3) ^ sk_swz_b(kr);
+                half_[h] = lds_read_tr16_b64(Bs + kr * SK_BN * 2 + (c << 4) + ((nl & 7) << 1));
+            }
+            const f16x8 bf = __builtin_shufflevector(half_[0], half_[1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int m = 16 * mb + (lane & 15);
+                const int c = (4 * ks + g) ^ (m & 15);
+                const f16x8 af = *(const GK_LDS f16x8*)(As + m * SK_BK * 2 + (c << 4));
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf, af, acc[mb], 0, 0, 0);
+            }
+        }
+    };
+    // Pipeline: STAGES-1 stages in flight.  Every wave issues B_INS + A_INS
+    // DMA instructions per stage, and vector-memory loads complete in order,
+    // so "stage kt has landed" is vmcnt <= (stages issued after it) * per-stage.
+    constexpr int PER_STAGE = B_INS + A_INS;
+    static_assert((STAGES - 2) * PER_STAGE <= 63, "vmcnt range");
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < KT) issue(s, s);
+    for (int kt = 0; kt < KT; ++kt) {
+        const int after = min(KT - 1 - kt, STAGES - 2);    // stages issued after kt
+        if (after >= STAGES - 2) {
+            wait_vmcnt<(STAGES - 2) * PER_STAGE>();
+        } else {
+            wait_vmcnt0();
+        }
+        __syncthreads();
+        if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+        compute_stage(kt % STAGES);
+    }
+
+    // Epilogue.  Lane l, register r of block mb holds C[16*mb + l%16][n0 + 16*wave + 4*(l/16) + r].
+    const int n = n0 + wave * 16 + 4 * (lane >> 4);
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (EPI != EPI_NONE) {
+        if (n + 4 <= N) {
+            f16x4 b4 = *(const f16x4*)(p.bias + n);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bv[e] = (float)b4[e];
+        }
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int m = 16 * mb + (lane & 15);
+        if (m < M && n + 4 <= N) {
+            f16x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = (f16)apply_epilogue<EPI>(acc[mb][e], bv[e]);
+            *(f16x4*)(p.C + (size_t)m * N + n) = o;
+        }
+    }
+}
+
+}  // namespace gk

@@ -1,0 +1,129 @@
+/*
+ * gemm_f16.h -- C ABI of the MI355X (gfx950) half-precision GEMM library.
+ *
+ * The operation is the tiled half-precision matrix multiply of the TileLang
+ * GEMM tutorial (blog post "Designing High-Performance GPU Kernels with
+ * TileLang", section "Step 4": fp16 tiles of A [block_M x block_K] and
+ * B [block_K x block_N], i.e. B held K x N, multiplied into a float32
+ * accumulator fragment), extended as in the tutorial's fused-epilogue
+ * chapter (TileLang news article, paragraph on fusing the bias add and the
+ * GELU activation into the register-resident accumulator before the output
+ * tensor is written):
+ *
+ *     C[i][j] = fp16( epi( sum_k A[i][k] * B[k][j] ) ),   0 <= i < M, 0 <= j < N
+ *     epi(s)  = s                                  GEMM_EPI_NONE
+ *             = s + bias[j]                        GEMM_EPI_BIAS
+ *             = gelu(s + bias[j])                  GEMM_EPI_BIAS_GELU
+ *     gelu(x) = 0.5 * x * (1 + erf(x / sqrt(2)))   (exact erf form)
+ *
+ * The sum is accumulated in fp32 (products of fp16 values are exact in
+ * fp32); bias add and GELU run in fp32 on the accumulator; C is rounded to
+ * fp16 once, round-to-nearest-even, and written once.
+ *
+ * Layout: every matrix is dense row-major with no padding:
+ *   A: fp16 [M][K] (leading dimension K), B: fp16 [K][N] (leading dimension N),
+ *   C: fp16 [M][N] (leading dimension N), bias: fp16 [N].
+ * fp16 means IEEE binary16, passed as raw 16-bit storage.
+ *
+ * Pointers: A, B, bias and C are DEVICE pointers (memory the caller allocated
+ * on the current HIP device).  Any 2-byte-aligned pointer is accepted;
+ * 16-byte alignment of A, B and C together with K % 8 == 0 and N % 8 == 0
+ * enables the vectorised paths, otherwise a slower element-wise path runs.
+ * Misalignment is never an error.
+ *
+ * Ownership: the caller owns every buffer.  The library never allocates,
+ * frees or retains caller memory.  C must not overlap A, B or bias.
+ *
+ * Streams: `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ * asynchronous, like a kernel launch: C is complete once the stream has been
+ * synchronised.  No call synchronises the device.
+ *
+ * Errors: arguments are validated before any HIP call; on a validation error
+ * nothing is launched and C is left untouched.  Status codes are listed below;
+ * gemm_f16_status_string() names them.  GEMM_ERR_LAUNCH carries no detail
+ * beyond the fact that hipGetLastError() reported a failure after the launch.
+ *
+ * Degenerate sizes: M == 0 or N == 0 is a successful no-op (pointers may be
+ * NULL).  K == 0 writes C = epi(0), i.e. zeros, bias, or gelu(bias).
+ *
+ * Thread safety: the library holds no mutable state; calls from several host
+ * threads on different streams are safe.
+ */
+#ifndef GEMM_F16_H
+#define GEMM_F16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GEMM_EPI_NONE = 0,
+    GEMM_EPI_BIAS = 1,
+    GEMM_EPI_BIAS_GELU = 2
+} gemm_epilogue_t;
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_DIM = 1,   /* M, N or K negative, or above 2^31 - 1     */
+    GEMM_ERR_NULL_POINTER = 2,  /* A/B/C NULL with M*N > 0 (A/B only if K > 0),
+                                   or bias NULL with a bias epilogue          */
+    GEMM_ERR_BAD_EPILOGUE = 3,  /* epilogue not one of gemm_epilogue_t        */
+    GEMM_ERR_LAUNCH = 4,        /* the HIP runtime reported a launch failure  */
+    GEMM_ERR_NO_CONFIG = 5,     /* config index out of range                  */
+    GEMM_ERR_UNSUPPORTED = 6,   /* the forced config cannot run this call
+                                   (alignment / divisibility it requires)     */
+    GEMM_ERR_MISALIGNED = 7     /* a pointer is not 2-byte aligned            */
+} gemm_status_t;
+
+/*
+ * C = epi(A.B) as described above, on `stream`.  The library picks the kernel
+ * configuration from the call's shape class (skinny M, tiled aligned, tiled
+ * general).  Returns a gemm_status_t.
+ */
+int gemm_f16(int64_t M, int64_t N, int64_t K,
+             const void* A, const void* B, const void* bias, void* C,
+             int epilogue, void* stream);
+
+/* Static, NUL-terminated name of a status code ("GEMM_OK", ...). */
+const char* gemm_f16_status_string(int status);
+
+/*
+ * Kernel configurations compiled into the library (the offline sweep space;
+ * the tutorial's autotuner picks among tile sizes, K-block, pipeline depth
+ * and thread count under a shared-memory budget, TileLang news article,
+ * paragraph on autotuning).
+ */
+int gemm_f16_num_configs(void);
+
+/* JSON description of config `idx` written into buf (NUL-terminated, truncated
+ * to buflen).  Returns the full length, or -GEMM_ERR_NO_CONFIG. */
+int gemm_f16_config_info(int idx, char* buf, int buflen);
+
+/* Index of the configuration gemm_f16() would launch for these arguments
+ * (no launch; -1 for a no-op call); negative gemm_status_t on bad arguments. */
+int gemm_f16_select_config(int64_t M, int64_t N, int64_t K,
+                           const void* A, const void* B, const void* bias, void* C,
+                           int epilogue);
+
+/* Same as gemm_f16 but with a forced configuration (used by the sweep and the
+ * tests).  GEMM_ERR_UNSUPPORTED if that config cannot handle the call. */
+int gemm_f16_with_config(int idx, int64_t M, int64_t N, int64_t K,
+                         const void* A, const void* B, const void* bias, void* C,
+                         int epilogue, void* stream);
+
+/*
+ * Element-wise fp32 vector add C[i] = A[i] + B[i], 0 <= i < n (the tutorial's
+ * first kernel: TileLang blog post, section "Step 3"; news article, paragraph
+ * on the vector-add kernel).  Device pointers, asynchronous on `stream`.  It is
+ * HBM-bound and doubles as the bandwidth calibration kernel.  Returns a
+ * gemm_status_t (GEMM_ERR_INVALID_DIM for n < 0).
+ */
+int vector_add_f32(int64_t n, const float* A, const float* B, float* C, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_F16_H */

@@ -1,0 +1,298 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Every comparison uses the same seeded inputs on both sides.  Sizes here span
+several tiles with ragged tails; the full workload shapes are checked either
+completely (where the oracle finishes in seconds) or at sampled positions the
+oracle computes one dot product at a time, in the launch configuration the
+benchmark uses (the default dispatch).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import assert_parity, metrics, ulp_distance
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def run(lib, A, B, bias, epi, config=None):
+    out = lib.gemm_f16(dev(A), dev(B), dev(bias) if bias is not None else None, epi, config=config)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def configs_for(lib, M, N, K, epi):
+    """All compiled configs able to run this (aligned, contiguous) call."""
+    out = []
+    for c in lib.configs():
+        if c["kind"] == "skinny" and M > c["bm"]:
+            continue
+        if c["loader"] == "direct" and K % c["bk"] != 0:
+            continue
+        if c["kind"] == "skinny" or c["loader"] in ("direct", "vec"):
+            if K % 8 or N % 8:
+                continue
+        out.append(c["idx"])
+    return out
+
+
+# ---------------------------------------------------------------------------
+# every config x every epilogue on small ragged shapes
+# ---------------------------------------------------------------------------
+SHAPES = [
+    (300, 520, 256),     # several 128/256 tiles, ragged M and N, K multiple of 64
+    (257, 136, 192),     # one row past a 256 tile
+    (130, 264, 200),     # K tail (200 = 3*64 + 8)
+    (16, 1032, 384),     # skinny
+    (45, 200, 136),      # skinny, 3 m-blocks, ragged N panel, K tail
+    (64, 64, 64),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu"])
+def test_all_configs_small(lib, shape, epi):
+    M, N, K = shape
+    A, B, bias = workloads.make_inputs("mlp_up_8192x16384x4096", M=M, N=N, K=K)
+    if epi == "none":
+        bias = None
+    ref = oracle.gemm(A, B, bias, epi)
+    cfgs = configs_for(lib, M, N, K, epi)
+    assert cfgs
+    for idx in cfgs:
+        got = run(lib, A, B, bias, epi, config=idx)
+        m = assert_parity(got, ref, (shape, epi, lib.config_info(idx)["name"]))
+        assert m["frac_exact"] > 0.97, m
+    got = run(lib, A, B, bias, epi)  # default dispatch
+    assert_parity(got, ref, (shape, epi, "default"))
+
+
+@pytest.mark.parametrize("shape", [(333, 277, 100), (17, 33, 9), (1, 1, 1), (5, 3001, 7), (259, 129, 1000)])
+@pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu"])
+def test_unaligned_shapes(lib, shape, epi):
+    M, N, K = shape
+    A, B, bias = workloads.make_inputs("ragged_4095x3001x1000", M=M, N=N, K=K)
+    if epi == "none":
+        bias = None
+    ref = oracle.gemm(A, B, bias, epi)
+    got = run(lib, A, B, bias, epi)
+    assert_parity(got, ref, (shape, epi))
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+# ---------------------------------------------------------------------------
+def test_workload_gemm_256_full(lib):
+    A, B, bias = workloads.make_inputs("gemm_256")
+    ref = oracle.gemm(A, B)
+    got = run(lib, A, B, None, "none")
+    m = assert_parity(got, ref, "gemm_256")
+    assert m["frac_exact"] > 0.99
+
+
+def test_workload_ragged_full(lib):
+    w = workloads.WORKLOADS["ragged_4095x3001x1000"]
+    A, B, bias = workloads.make_inputs(w)
+    ref = oracle.gemm(A, B, bias, w.epilogue)
+    got = run(lib, A, B, bias, w.epilogue)
+    m = assert_parity(got, ref, w.name)
+    assert m["frac_exact"] > 0.99
+
+
+def test_workload_skinny_full(lib):
+    w = workloads.WORKLOADS["skinny_16x16384x8192"]
+    A, B, bias = workloads.make_inputs(w)
+    ref = oracle.gemm(A, B, bias, w.epilogue)
+    got = run(lib, A, B, bias, w.epilogue)
+    m = assert_parity(got, ref, w.name)
+    assert m["frac_exact"] > 0.97
+
+
+def _sample_points(M, N, seed, n_random=20000):
+    rng = np.random.default_rng(seed)
+    r = [rng.integers(0, M, n_random)]
+    c = [rng.integers(0, N, n_random)]
+    # whole rows at the top, bottom and a tile boundary; whole corner blocks
+    for row in (0, M - 1, min(M - 1, 255), min(M - 1, 256)):
+        r.append(np.full(N, row))
+        c.append(np.arange(N))
+    for (i0, j0) in ((0, 0), (M - 40, N - 40), (0, N - 40), (M - 40, 0)):
+        ii, jj = np.meshgrid(np.arange(i0, i0 + 40), np.arange(j0, j0 + 40), indexing="ij")
+        r.append(ii.ravel())
+        c.append(jj.ravel())
+    return np.concatenate(r), np.concatenate(c)
+
+
+@pytest.mark.parametrize("name", ["gemm_4096", "mlp_up_8192x16384x4096"])
+def test_workload_large_sampled(lib, name):
+    w = workloads.WORKLOADS[name]
+    A, B, bias = workloads.make_inputs(w)
+    got = run(lib, A, B, bias, w.epilogue)
+    r, c = _sample_points(w.M, w.N, 99)
+    ref = oracle.gemm_points(A, B, bias, w.epilogue, r, c)
+    m = assert_parity(got[r, c], ref, name)
+    assert m["frac_exact"] > 0.97, m
+    assert not np.isnan(got.astype(np.float32)).any()
+
+
+# ---------------------------------------------------------------------------
+# bit-exact closed forms
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("K", [1, 64, 1000, 4096, 8192])
+def test_all_ones_exact(lib, K):
+    for M, N in ((256, 256), (16, 512), (100, 72)):
+        A = np.ones((M, K), np.float16)
+        B = np.ones((K, N), np.float16)
+        got = run(lib, A, B, None, "none")
+        assert np.all(got.astype(np.float64) == float(np.float16(K)))
+
+
+def test_identity_passes_every_finite_fp16(lib):
+    # A = I, B = every finite binary16 pattern (non-finite ones replaced by 0):
+    # C must reproduce B bit for bit (up to the sign of zero) -> no subnormal
+    # flushing in the MFMA path, exact decode, exact store.
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = (bits & 0x7C00) != 0x7C00
+    bits = np.where(finite, bits, 0).astype(np.uint16)
+    B = bits.view(np.float16).reshape(256, 256)
+    A = np.eye(256, dtype=np.float16)
+    for idx in configs_for(lib, 256, 256, 256, "none"):
+        got = run(lib, A, B, None, "none", config=idx)
+        assert np.array_equal(got.view(np.uint16) & 0x7FFF, B.view(np.uint16) & 0x7FFF), lib.config_info(idx)
+        nz = (B.view(np.uint16) & 0x7FFF) != 0
+        assert np.array_equal(got.view(np.uint16)[nz], B.view(np.uint16)[nz])
+
+
+def test_rank1_round_to_nearest_even(lib):
+    # C = fp16(u_i * v_j) (exact products), including exact ties that separate
+    # round-to-nearest-even from truncation.
+    rng = np.random.default_rng(5)
+    M, N, K = 64, 64, 64
+    u = rng.uniform(-2, 2, M).astype(np.float16)
+    v = rng.uniform(-2, 2, N).astype(np.float16)
+    u[0], v[0] = np.float16(1 + 2 ** -10), np.float16(1.5)
+    A = np.zeros((M, K), np.float16)
+    A[:, 7] = u
+    B = workloads.random_f16(6, (K, N))
+    B[7, :] = v
+    ref = np.outer(u.astype(np.float64), v.astype(np.float64)).astype(np.float16)
+    for idx in configs_for(lib, M, N, K, "none"):
+        got = run(lib, A, B, None, "none", config=idx)
+        assert np.array_equal(got.view(np.uint16), ref.view(np.uint16)), lib.config_info(idx)
+    assert float(got[0, 0]) == 1.5 + 2 * 2 ** -10
+
+
+def test_bias_only_exact(lib):
+    # A = 0: C = bias broadcast, and gelu(bias) within one fp16 ulp of the oracle
+    M, N, K = 100, 264, 64
+    A = np.zeros((M, K), np.float16)
+    B = workloads.random_f16(7, (K, N))
+    bias = workloads.random_f16(8, (N,), -6, 6)
+    got = run(lib, A, B, bias, "bias")
+    assert np.array_equal(got.astype(np.float64), np.broadcast_to(bias.astype(np.float64), (M, N)))
+    got = run(lib, A, B, bias, "bias_gelu")
+    ref = oracle.gemm(A, B, bias, "bias_gelu")
+    assert ulp_distance(got, ref).max() <= 1
+
+
+# ---------------------------------------------------------------------------
+# edges: canaries, misaligned views, degenerate sizes, determinism
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(300, 520, 256), (16, 1032, 384), (333, 277, 100)])
+def test_canaries_untouched(lib, shape):
+    M, N, K = shape
+    A, B, bias = workloads.make_inputs("ragged_4095x3001x1000", M=M, N=N, K=K)
+    ref = oracle.gemm(A, B, bias, "bias")
+    pad = 4096
+    buf = torch.full((M * N + 2 * pad,), -7.0, dtype=torch.float16, device="cuda")
+    out = buf[pad:pad + M * N].view(M, N)
+    import dense_tiled_gemm_04_amd as g
+    g.gemm_f16(dev(A), dev(B), dev(bias), "bias", out=out)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    assert np.all(host[:pad] == np.float16(-7.0)) and np.all(host[pad + M * N:] == np.float16(-7.0))
+    assert_parity(host[pad:pad + M * N].reshape(M, N), ref, shape)
+
+
+def test_misaligned_views(lib):
+    M, N, K = 130, 136, 72
+    A, B, bias = workloads.make_inputs("ragged_4095x3001x1000", M=M, N=N, K=K)
+    ref = oracle.gemm(A, B, bias, "bias_gelu")
+    ab = torch.zeros(M * K + 1, dtype=torch.float16, device="cuda")
+    bb = torch.zeros(K * N + 1, dtype=torch.float16, device="cuda")
+    cb = torch.zeros(M * N + 1, dtype=torch.float16, device="cuda")
+    ab[1:] = dev(A).reshape(-1)
+    bb[1:] = dev(B).reshape(-1)
+    import dense_tiled_gemm_04_amd as g
+    Av, Bv, Cv = ab[1:].view(M, K), bb[1:].view(K, N), cb[1:].view(M, N)
+    cfg = g.config_info(g.select_config(Av, Bv, dev(bias), "bias_gelu", out=Cv))
+    assert cfg["loader"] == "elem"
+    g.gemm_f16(Av, Bv, dev(bias), "bias_gelu", out=Cv)
+    torch.cuda.synchronize()
+    assert_parity(Cv.cpu().numpy(), ref, "misaligned")
+
+
+def test_degenerate_sizes(lib):
+    import dense_tiled_gemm_04_amd as g
+    bias = workloads.random_f16(9, (40,), -3, 3)
+    for epi in ("none", "bias", "bias_gelu"):
+        A = torch.zeros((30, 0), dtype=torch.float16, device="cuda")
+        B = torch.zeros((0, 40), dtype=torch.float16, device="cuda")
+        out = torch.full((30, 40), 5.0, dtype=torch.float16, device="cuda")
+        g.gemm_f16(A, B, dev(bias) if epi != "none" else None, epi, out=out)
+        torch.cuda.synchronize()
+        ref = oracle.gemm(np.zeros((30, 0), np.float16), np.zeros((0, 40), np.float16),
+                          bias if epi != "none" else None, epi)
+        assert np.array_equal(out.cpu().numpy().view(np.uint16), ref.view(np.uint16))
+    e = g.gemm_f16(torch.zeros((0, 8), dtype=torch.float16, device="cuda"),
+                   torch.zeros((8, 8), dtype=torch.float16, device="cuda"))
+    assert tuple(e.shape) == (0, 8)
+
+
+@pytest.mark.parametrize("name", ["gemm_4096", "skinny_16x16384x8192", "ragged_4095x3001x1000"])
+def test_determinism(lib, name):
+    w = workloads.WORKLOADS[name]
+    A, B, bias = workloads.make_inputs(w)
+    a, b = dev(A), dev(B)
+    bb = dev(bias) if bias is not None else None
+    import dense_tiled_gemm_04_amd as g
+    c1 = g.gemm_f16(a, b, bb, w.epilogue)
+    c2 = g.gemm_f16(a, b, bb, w.epilogue)
+    torch.cuda.synchronize()
+    assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
+
+
+def test_torch_front_end_errors(lib):
+    import dense_tiled_gemm_04_amd as g
+    a = torch.zeros((4, 8), dtype=torch.float16, device="cuda")
+    b = torch.zeros((8, 4), dtype=torch.float16, device="cuda")
+    with pytest.raises(TypeError):
+        g.gemm_f16(a.float(), b)
+    with pytest.raises(ValueError):
+        g.gemm_f16(a, torch.zeros((7, 4), dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError):
+        g.gemm_f16(a, b, None, "bias")
+    with pytest.raises(ValueError):
+        g.gemm_f16(a.t(), b.t())
+
+
+def test_vector_add(lib):
+    import dense_tiled_gemm_04_amd as g
+    for n in (1, 7, 1024, 1000003):
+        x = torch.randn(n, device="cuda")
+        y = torch.randn(n, device="cuda")
+        z = g.vector_add(x, y)
+        torch.cuda.synchronize()
+        assert torch.equal(z, x + y)
+    # unaligned views take the scalar kernel
+    x = torch.randn(1001, device="cuda")
+    z = g.vector_add(x[1:], x[:-1])
+    torch.cuda.synchronize()
+    assert torch.equal(z, x[1:] + x[:-1])
