@@ -57,21 +57,30 @@ def load_traffic(workload: str, kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, A, B, bias, target_s: float = 10.0):
-    """Time the CPU oracle on the first R rows of the workload (full K, all N)."""
+def cpu_baseline(w, A, B, bias, target_s: float = 15.0):
+    """Time the CPU oracle on the first R rows of the workload (full K, all N).
+
+    R grows geometrically until one run takes at least a second, then is sized
+    from that rate for about ``target_s`` seconds of CPU work (capped at M).
+    """
     import numpy as np
     import oracle
 
     threads = oracle.max_threads()
-    # calibrate on a few rows, then size the sample for ~target_s of CPU work
-    r0 = min(w.M, 16)
-    t = time.perf_counter()
-    oracle.gemm(A[:r0], B, bias, w.epilogue, threads=threads)
-    dt = max(time.perf_counter() - t, 1e-6)
-    rows = int(min(w.M, max(r0, r0 * target_s / dt)))
-    t = time.perf_counter()
-    oracle.gemm(np.ascontiguousarray(A[:rows]), B, bias, w.epilogue, threads=threads)
-    dt = time.perf_counter() - t
+    rows, dt = 0, 0.0
+    r = min(w.M, 16)
+    while True:
+        t = time.perf_counter()
+        oracle.gemm(np.ascontiguousarray(A[:r]), B, bias, w.epilogue, threads=threads)
+        rows, dt = r, time.perf_counter() - t
+        if dt >= 1.0 or r >= w.M:
+            break
+        r = min(w.M, r * 4)
+    if dt < target_s and rows < w.M:
+        r = int(min(w.M, max(rows, rows * target_s / max(dt, 1e-6))))
+        t = time.perf_counter()
+        oracle.gemm(np.ascontiguousarray(A[:r]), B, bias, w.epilogue, threads=threads)
+        rows, dt = r, time.perf_counter() - t
     flops = 2.0 * rows * w.N * w.K
     return {
         "value": flops / dt / 1e12,
@@ -81,6 +90,25 @@ def cpu_baseline(w, A, B, bias, target_s: float = 10.0):
         "sample": "rows 0..%d of C (%d x %d outputs, full K=%d, epilogue %s), fp64 oracle, %.2f s wall"
                   % (rows - 1, rows, w.N, w.K, w.epilogue, dt),
     }
+
+
+CALIB_ELEMS = 64 * 1024 * 1024  # fp32 elements per vector: 256 MiB each for a, b and c
+
+
+def hbm_calibration(g, torch) -> int:
+    """c = a + b over 3 x 256 MiB fp32 buffers: each launch reads exactly 512 MiB and writes 256 MiB."""
+    dev = torch.device("cuda:0")
+    a = torch.ones(CALIB_ELEMS, dtype=torch.float32, device=dev)
+    b = torch.ones(CALIB_ELEMS, dtype=torch.float32, device=dev)
+    c = torch.empty_like(a)
+    for _ in range(3):
+        g.vector_add(a, b, out=c)
+    torch.cuda.synchronize()
+    assert bool((c == 2.0).all())
+    print(json.dumps({"calibration": "vector_add_f32", "elems": CALIB_ELEMS, "launches": 3,
+                      "read_bytes_per_launch": 8 * CALIB_ELEMS, "write_bytes_per_launch": 4 * CALIB_ELEMS}),
+          flush=True)
+    return 0
 
 
 def main() -> int:
@@ -93,6 +121,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=None,
                     help="copies of B to rotate through (default: 3 for HBM-bound workloads, else 1)")
+    ap.add_argument("--hbm-calibration", action="store_true",
+                    help="run only the fp32 vector-add kernel on buffers of known size (the reference "
+                         "point that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -110,6 +141,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     g.load()
+    if args.hbm_calibration:
+        return hbm_calibration(g, torch)
     w = workloads.WORKLOADS[args.workload]
     A, B, bias = workloads.make_inputs(w)
     hbm_bound = w.flops / w.algorithmic_bytes < 100.0
@@ -190,7 +223,7 @@ def main() -> int:
         cpu = cpu_baseline(w, A, B, bias)
 
     out = {
-        "metric": "fp16 GEMM TFLOPS (4096^3; fused bias+GELU MLP) + % of MI355X MFMA peak",
+        "metric": "fp16 GEMM TFLOPS (4096\u00b3; fused bias+GELU MLP) + % of MI355X MFMA peak",
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
