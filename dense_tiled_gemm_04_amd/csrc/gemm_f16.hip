@@ -7,6 +7,7 @@
 
 #include "gemm_f16.h"
 #include "skinny_kernel.h"
+#include "tile_dma_kernel.h"
 #include "tile_kernel.h"
 
 using namespace gk;
@@ -36,6 +37,13 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int GROUP_M, int BSLOT, int DSTRIDE, int EPI>
+hipError_t launch_tile_dma(const GemmArgs& a, hipStream_t s) {
+    dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(WM * WN * 64);
+    hipLaunchKernelGGL((gemm_tile_dma_kernel<BM, BN, BK, WM, WN, STAGES, GROUP_M, EPI, BSLOT, DSTRIDE>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
 template <int MB, int STAGES, int EPI>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.tiles_n), block(SK_WAVES * 64);
@@ -53,6 +61,17 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
         }                                                                                          \
     }
 
+#define DMA_CFG(BM, BN, BK, WM, WN, ST, G, BS, DS, NAME)                                          \
+    Config {                                                                                       \
+        NAME, KIND_TILE, BM, BN, BK, WM, WN, LOAD_DMA, G, ST,                                      \
+            TileDmaCfg<BM, BN, BK, WM, WN, ST>::LDS_BYTES, WM * WN * 64,                           \
+        {                                                                                          \
+            launch_tile_dma<BM, BN, BK, WM, WN, ST, G, BS, DS, 0>,                                 \
+                launch_tile_dma<BM, BN, BK, WM, WN, ST, G, BS, DS, 1>,                             \
+                launch_tile_dma<BM, BN, BK, WM, WN, ST, G, BS, DS, 2>                              \
+        }                                                                                          \
+    }
+
 #define SKINNY_CFG(MB, ST, NAME)                                                                    \
     Config {                                                                                       \
         NAME, KIND_SKINNY, 16 * MB, SK_BN, SK_BK, 1, SK_WAVES, -1, 1, ST,                          \
@@ -63,12 +82,12 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
     }
 
 const Config kConfigs[] = {
-    TILE_CFG(256, 256, 64, 2, 2, LOAD_DIRECT, 4, "tile_256x256x64_w2x2_direct_g4"),   // 0
+    DMA_CFG(256, 256, 64, 2, 2, 2, 4, 3, 2, "dma_256x256x64_w2x2_s2_g4"),              // 0
     TILE_CFG(256, 256, 64, 2, 2, LOAD_VEC, 4, "tile_256x256x64_w2x2_vec_g4"),         // 1
-    TILE_CFG(128, 128, 64, 2, 2, LOAD_DIRECT, 4, "tile_128x128x64_w2x2_direct_g4"),   // 2
+    DMA_CFG(128, 128, 64, 2, 2, 2, 4, 1, 1, "dma_128x128x64_w2x2_s2_g4"),              // 2
     TILE_CFG(128, 128, 64, 2, 2, LOAD_VEC, 4, "tile_128x128x64_w2x2_vec_g4"),         // 3
     TILE_CFG(128, 128, 64, 2, 2, LOAD_ELEM, 4, "tile_128x128x64_w2x2_elem_g4"),       // 4
-    TILE_CFG(256, 128, 64, 2, 2, LOAD_DIRECT, 4, "tile_256x128x64_w2x2_direct_g4"),   // 5
+    DMA_CFG(256, 128, 64, 2, 2, 2, 4, 3, 2, "dma_256x128x64_w2x2_s2_g4"),              // 5
     SKINNY_CFG(1, 6, "skinny_m16_s6"),                                                // 6
     SKINNY_CFG(2, 5, "skinny_m32_s5"),                                                // 7
     SKINNY_CFG(4, 4, "skinny_m64_s4"),                                                // 8
@@ -76,9 +95,9 @@ const Config kConfigs[] = {
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 
 enum DefaultIdx {
-    CFG_T256_DIRECT = 0,
+    CFG_T256_DMA = 0,
     CFG_T256_VEC = 1,
-    CFG_T128_DIRECT = 2,
+    CFG_T128_DMA = 2,
     CFG_T128_VEC = 3,
     CFG_T128_ELEM = 4,
     CFG_SKINNY16 = 6,
@@ -119,7 +138,7 @@ bool supports(const Config& cfg, const Call& c) {
                c.M * c.K * 2 < (int64_t)INT32_MAX;
     }
     switch (cfg.loader) {
-        case LOAD_DIRECT:
+        case LOAD_DMA:
             return vec_ok && c.K % cfg.bk == 0 && (int64_t)cfg.bm * c.K * 2 < (int64_t)INT32_MAX &&
                    (int64_t)cfg.bk * c.N * 2 < (int64_t)INT32_MAX;
         case LOAD_VEC:
@@ -137,7 +156,7 @@ int pick_default(const Call& c) {
     }
     const int64_t tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256);
     const bool big = tiles256 >= 256;  // at least one workgroup per CU with 256x256 tiles
-    const int cand[] = {big ? CFG_T256_DIRECT : CFG_T128_DIRECT, big ? CFG_T256_VEC : CFG_T128_VEC};
+    const int cand[] = {big ? CFG_T256_DMA : CFG_T128_DMA, big ? CFG_T256_VEC : CFG_T128_VEC};
     for (int idx : cand)
         if (supports(kConfigs[idx], c)) return idx;
     return CFG_T128_ELEM;
@@ -209,7 +228,7 @@ int gemm_f16_num_configs(void) { return kNumConfigs; }
 int gemm_f16_config_info(int idx, char* buf, int buflen) {
     if (idx < 0 || idx >= kNumConfigs) return -GEMM_ERR_NO_CONFIG;
     const Config& c = kConfigs[idx];
-    static const char* loaders[] = {"direct", "vec", "elem"};
+    static const char* loaders[] = {"dma", "vec", "elem"};
     char tmp[512];
     int n = snprintf(tmp, sizeof(tmp),
                      "{\"idx\": %d, \"name\": \"%s\", \"kind\": \"%s\", \"bm\": %d, \"bn\": %d, \"bk\": %d, "

@@ -1,0 +1,273 @@
+// Aligned fast path of the tiled fp16 GEMM on gfx950.
+//
+// It computes the tutorial's tiled GEMM: fp16 tiles A[block_M][block_K] and
+// B[block_K][block_N] staged in shared memory, a float32 register accumulator,
+// a pipelined K loop and the fused bias/GELU epilogue. The sources are the
+// blog post "Designing High-Performance GPU Kernels with TileLang", section
+// "Step 4", and the news article on TileLang kernel design, paragraphs on the
+// tiled GEMM and on the fused epilogue.
+//
+// What is specific to CDNA4:
+//  * Copies. HBM/L2 -> LDS goes by LDS-DMA (global_load_lds_dwordx4), so no
+//    VGPR is spent on staging. STAGES ring buffers. The copies of stage
+//    kt+STAGES-1 are spread over the MFMA slots of stage kt (every DSTRIDE-th
+//    slot).
+//  * Schedule. Every MFMA slot is fenced with sched_barrier, so the issue
+//    order is exactly the one written here:
+//      slot i of a k-step: MFMA i, the LDS reads scheduled for slot i (the
+//      next k-step's fragments), and the copies scheduled for slot i.
+//    At slot BSLOT of a stage's last k-step, the wave waits for its copies of
+//    stage kt+1, and one barrier publishes them. All LDS reads of stage kt
+//    have landed by then, so the same barrier also frees stage kt's buffer.
+//    The next stage's first fragments are then read in the remaining slots.
+//    The result is that LDS reads and copies always overlap MFMAs, and no
+//    wave idles between stages.
+//  * MFMA. v_mfma_f32_32x32x16_f16, issued as C^T = B^T . A^T, so each lane
+//    holds 4 consecutive columns of one output row. A fragments come from
+//    ds_read_b128. B fragments come from row-major [k][n] LDS by the
+//    transpose read ds_read_b64_tr_b16. Both tiles are XOR-swizzled in
+//    16-byte chunks so that the reads are free of bank conflicts.
+//
+// Requirements (checked on the host): K % BK == 0, N % 8 == 0, A/B/C 16-byte
+// aligned, bias 8-byte aligned. Rows past M re-read row M-1, and columns past
+// N re-read the last chunk; neither is stored.
+#pragma once
+#include "common.h"
+#include "tile_kernel.h"
+
+namespace gk {
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES>
+struct TileDmaCfg {
+    static constexpr int NW = WM * WN;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave sub-tile
+    static constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA blocks per wave
+    static constexpr int CA = BK / 8, CB = BN / 8;      // 16-byte chunks per A / B row
+    static constexpr int A_STAGE = BM * BK * 2, B_STAGE = BK * BN * 2;
+    static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE);
+    static constexpr int KSTEPS = BK / 16;              // k16 steps per stage
+    static constexpr int A_INS = BM * CA / 64 / NW;     // LDS-DMA instructions per wave and stage
+    static constexpr int B_INS = BK * CB / 64 / NW;
+    static constexpr int PER_STAGE = A_INS + B_INS;
+    static constexpr int NMMA = TM * TN;                // MFMAs (slots) per k-step
+    static constexpr int NRD = TM + 2 * TN;             // LDS reads per k-step
+    static_assert(KSTEPS % 2 == 0, "even k16-steps per stage (fragment ping-pong)");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile of whole 32x32 blocks");
+    static_assert((CA & (CA - 1)) == 0 && (CB & (CB - 1)) == 0 && CB >= 4, "chunk counts");
+    static_assert((BM * CA) % (64 * NW) == 0 && (BK * CB) % (64 * NW) == 0, "copy split over waves");
+    static_assert(STAGES >= 2 && PER_STAGE * (STAGES - 1) <= 63, "vmcnt range");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
+};
+
+// Slot of LDS read j (0 <= j < NRD) among `avail` slots starting at `first`:
+// one per slot while they fit, otherwise spread evenly.
+template <int NRD>
+__device__ constexpr int read_slot(int j, int first, int avail) {
+    return first + (NRD <= avail ? j : j * avail / NRD);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int GROUP_M, int EPI, int BSLOT, int DSTRIDE>
+__global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_tile_dma_kernel(GemmArgs p) {
+    using Cfg = TileDmaCfg<BM, BN, BK, WM, WN, STAGES>;
+    constexpr int NW = Cfg::NW, WTM = Cfg::WTM, WTN = Cfg::WTN, TM = Cfg::TM, TN = Cfg::TN;
+    constexpr int CA = Cfg::CA, CB = Cfg::CB, A_STAGE = Cfg::A_STAGE, B_STAGE = Cfg::B_STAGE;
+    constexpr int KSTEPS = Cfg::KSTEPS, A_INS = Cfg::A_INS, B_INS = Cfg::B_INS, PER_STAGE = Cfg::PER_STAGE;
+    constexpr int NMMA = Cfg::NMMA, NRD = Cfg::NRD;
+    static_assert(BSLOT >= 0 && BSLOT + 1 < NMMA, "barrier slot inside the last k-step, reads after it");
+    static_assert(DSTRIDE >= 1 && (PER_STAGE - 1) * DSTRIDE < (KSTEPS - 1) * NMMA + BSLOT,
+                  "every copy of a stage is issued before that stage's barrier");
+
+    __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::LDS_BYTES];
+    GK_LDS char* const a_lds = (GK_LDS char*)smem_raw;           // [STAGES][BM][BK]
+    GK_LDS char* const b_lds = a_lds + STAGES * A_STAGE;         // [STAGES][BK][BN]
+
+    const int M = p.M, N = p.N, K = p.K;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    int tm, tn;
+    {
+        const int nwg = p.tiles_m * p.tiles_n;
+        grouped_tile<GROUP_M>(xcd_contiguous_id((int)blockIdx.x, nwg), p.tiles_m, p.tiles_n, tm, tn);
+    }
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int KT = K / BK;
+
+    // Fragment read offsets (bytes within a stage).
+    // A (MFMA operand b): lane holds A[m = row(lane)][k = 16 kk + 8 (lane / 32) .. +7].
+    int a_rd[KSTEPS];
+    {
+        const int row = wm * WTM + (lane & 31);
+        const int s = swz_a<BK>(row);
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) a_rd[kk] = row * BK * 2 + (((2 * kk + (lane >> 5)) ^ s) << 4);
+    }
+    // B (MFMA operand a) by transpose reads: lane L = 16g + 4j + q gives the
+    // address of B[kb + j][nb + 4q .. 4q+3] and receives B[kb + 0..3][nb + L%16].
+    int b_rd[TN];
+    {
+        const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+        const int kr = 8 * (g >> 1) + j;
+#pragma unroll
+        for (int ni = 0; ni < TN; ++ni) {
+            const int nl = wn * WTN + ni * 32 + 16 * (g & 1) + 4 * q;
+            b_rd[ni] = kr * BN * 2 + (((nl >> 3) ^ swz_b<BN>(kr)) << 4) + ((nl & 7) << 1);
+        }
+    }
+    // LDS-DMA sources. Destination chunk P of a stage is lane-contiguous; its
+    // source is the logical chunk that the swizzle puts at P.
+    uint32_t a_off[A_INS], b_off[B_INS];
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) {
+        const int P = (i * NW + wave) * 64 + lane;
+        const int r = P / CA, c = (P % CA) ^ swz_a<BK>(r);
+        const int m = min(m0 + r, M - 1) - m0;
+        a_off[i] = (uint32_t)((m * K + 8 * c) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) {
+        const int P = (i * NW + wave) * 64 + lane;
+        const int kr = P / CB, c = (P % CB) ^ swz_b<BN>(kr);
+        const int n = min(n0 + 8 * c, N - 8) - n0;
+        b_off[i] = (uint32_t)((kr * N + n) * 2);
+    }
+    const char* const a_row0 = (const char*)(p.A + (size_t)m0 * K);
+    const char* const b_col0 = (const char*)(p.B + n0);
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t a_lds0 = lds_addr(a_lds) + wave_s * 64 * 16;
+    const uint32_t b_lds0 = lds_addr(b_lds) + wave_s * 64 * 16;
+
+    // Copy j (0 <= j < PER_STAGE) of stage kt into ring buffer sb.
+    auto dma_op = [&](int j, int kt, int sb) {
+        if (j < A_INS) {
+            dma_global_16(a_row0 + (size_t)kt * BK * 2, a_off[j], a_lds0 + sb * A_STAGE + j * NW * 64 * 16);
+        } else {
+            const int i = j - A_INS;
+            dma_global_16(b_col0 + (size_t)kt * BK * N * 2, b_off[i], b_lds0 + sb * B_STAGE + i * NW * 64 * 16);
+        }
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+
+    // Two fragment sets: the reads of k-step kk+1 land in one while the MFMAs
+    // of k-step kk consume the other.  Read j: 0 -> A[0]; 1..2TN -> halves of
+    // B[(j-1)/2]; then A[1..TM-1] -- the order in which MFMA row 0 needs them.
+    f16x8 fa[2][TM];
+    f16x4 fb[2][TN][2];
+    auto read_op = [&](int set, int j, int sb, int kk) {
+        const GK_LDS char* As = a_lds + sb * A_STAGE;
+        const GK_LDS char* Bs = b_lds + sb * B_STAGE;
+        if (j == 0) {
+            fa[set][0] = *(const GK_LDS f16x8*)(As + a_rd[kk]);
+        } else if (j <= 2 * TN) {
+            const int ni = (j - 1) / 2, h = (j - 1) % 2;
+            fb[set][ni][h] = lds_read_tr16_b64(Bs + b_rd[ni] + (16 * kk + 4 * h) * BN * 2);
+        } else {
+            const int mi = j - 2 * TN;
+            fa[set][mi] = *(const GK_LDS f16x8*)(As + a_rd[kk] + mi * 32 * BK * 2);
+        }
+    };
+    auto mma_op = [&](int set, int i) {
+        const int mi = i / TN, ni = i % TN;
+        const f16x8 b = __builtin_shufflevector(fb[set][ni][0], fb[set][ni][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, fa[set][mi], acc[mi][ni], 0, 0, 0);
+    };
+
+    // Prologue: stages 0 .. STAGES-2 in flight, then stage 0's first fragments.
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+        if (st < KT)
+#pragma unroll
+            for (int j = 0; j < PER_STAGE; ++j) dma_op(j, st, st);
+    if (KT >= STAGES - 1) {
+        wait_vmcnt<(STAGES - 2) * PER_STAGE>();
+    } else {
+        wait_vmcnt0();
+    }
+    __syncthreads();
+    if (KT > 0) {
+#pragma unroll
+        for (int j = 0; j < NRD; ++j) read_op(0, j, 0, 0);
+    }
+
+    int s = 0;  // ring buffer of the stage being computed
+    // MAIN: every stage up to kt+STAGES-1 exists, so the copies are issued
+    // unconditionally and the wait count is exact.  Tail stages issue none
+    // and wait for everything.
+    auto stage = [&]<bool MAIN>(int kt) {
+        const bool has_next = MAIN || kt + 1 < KT;
+        const int sn = (s + 1 == STAGES) ? 0 : s + 1;
+        const int sd = (s == 0) ? STAGES - 1 : s - 1;  // buffer of stage kt+STAGES-1 (freed last stage)
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+            const int cur = kk & 1, nxt = cur ^ 1;
+#pragma unroll
+            for (int i = 0; i < NMMA; ++i) {
+                mma_op(cur, i);
+                const int slot = kk * NMMA + i;
+                if constexpr (MAIN) {
+                    if (slot % DSTRIDE == 0 && slot / DSTRIDE < PER_STAGE) dma_op(slot / DSTRIDE, kt + STAGES - 1, sd);
+                }
+                if (kk + 1 < KSTEPS) {
+#pragma unroll
+                    for (int j = 0; j < NRD; ++j)
+                        if (read_slot<NRD>(j, 0, NMMA) == i) read_op(nxt, j, s, kk + 1);
+                } else if (has_next) {
+                    if (i == BSLOT) {
+                        if constexpr (MAIN) {
+                            wait_vmcnt<(STAGES - 2) * PER_STAGE>();
+                        } else {
+                            wait_vmcnt0();
+                        }
+                        __syncthreads();
+                    }
+#pragma unroll
+                    for (int j = 0; j < NRD; ++j)
+                        if (read_slot<NRD>(j, BSLOT + 1, NMMA - BSLOT - 1) == i) read_op(nxt, j, sn, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        s = sn;
+    };
+    const int kt_main = KT - (STAGES - 1);
+    int kt = 0;
+    for (; kt < kt_main; ++kt) stage.template operator()<true>(kt);
+    for (; kt < KT; ++kt) stage.template operator()<false>(kt);
+
+    // Epilogue on the accumulators, one write of C.  Lane l, register
+    // 4*r4 + e of block (mi, ni) holds
+    //   C[m0 + wm*WTM + mi*32 + l%32][n0 + wn*WTN + ni*32 + 8*r4 + 4*(l/32) + e].
+#pragma unroll
+    for (int ni = 0; ni < TN; ++ni) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int n = n0 + wn * WTN + ni * 32 + 8 * r4 + 4 * (lane >> 5);
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (EPI != EPI_NONE) {
+                if (n + 4 <= N) {
+                    const f16x4 b4 = *(const f16x4*)(p.bias + n);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) bv[e] = (float)b4[e];
+                }
+            }
+#pragma unroll
+            for (int mi = 0; mi < TM; ++mi) {
+                const int m = m0 + wm * WTM + mi * 32 + (lane & 31);
+                if (m >= M || n + 4 > N) continue;  // N % 8 == 0: a column quad is all in or all out
+                f16x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = (f16)apply_epilogue<EPI>(acc[mi][ni][4 * r4 + e], bv[e]);
+                *(f16x4*)(p.C + (size_t)m * N + n) = o;
+            }
+        }
+    }
+}
+
+}  // namespace gk

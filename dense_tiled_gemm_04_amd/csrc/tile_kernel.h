@@ -15,18 +15,16 @@
 //    that fragment reads hit 64 distinct banks.  A rows are K-contiguous and
 //    read with ds_read_b128; B stays row-major [k][n] and is read K-contiguous
 //    per lane with the gfx950 transpose read ds_read_b64_tr_b16.
-//  * loaders: LOAD_DIRECT issues global_load_lds_dwordx4 (HBM/L2 -> LDS with
-//    no VGPR round trip; the swizzle is applied to the *source* address since
-//    the LDS destination of lane l is fixed at base + 16*l); LOAD_VEC and
-//    LOAD_ELEM stage through registers with per-element masking for ragged
-//    K / M / N edges and unaligned rows.
+//  * loaders: LOAD_VEC and LOAD_ELEM stage through registers with
+//    per-element masking for ragged K / M / N edges and unaligned rows (the
+//    aligned fast path with LDS-DMA copies is gemm_tile_dma_kernel).
 //  * tile order: XCD-contiguous remap + GROUP_M grouped raster.
 #pragma once
 #include "common.h"
 
 namespace gk {
 
-enum Loader { LOAD_DIRECT = 0, LOAD_VEC = 1, LOAD_ELEM = 2 };
+enum Loader { LOAD_DMA = 0, LOAD_VEC = 1, LOAD_ELEM = 2 };
 
 template <int BM, int BN, int BK, int WM, int WN, int LOADER, int EPI, int GROUP_M>
 struct TileCfg {
@@ -47,6 +45,7 @@ struct TileCfg {
     static_assert(CB >= 4, "BN >= 32");
     static_assert((BM * CA) % NT == 0 && (BK * CB) % NT == 0, "tile chunks divisible by threads");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
+    static_assert(LOADER == LOAD_VEC || LOADER == LOAD_ELEM, "register-staged loaders only");
 };
 
 // A-tile swizzle: logical chunk c of row r lives at chunk c ^ swz_a(r).  Over
@@ -157,150 +156,77 @@ gemm_tile_kernel(GemmArgs p) {
     constexpr int KSTEPS = BK / 16;
     static_assert(KSTEPS % 2 == 0, "k-steps per stage must be even for the fragment ping-pong");
 
-    if constexpr (LOADER == LOAD_DIRECT) {
-        // Requires: K % BK == 0, N % 8 == 0, A and B 16-byte aligned (host-checked).
-        constexpr int A_INS = BM * CA / 64 / NW;
-        constexpr int B_INS = BK * CB / 64 / NW;
-        constexpr int PER_STAGE = A_INS + B_INS;
-        static_assert(PER_STAGE <= 63, "vmcnt range");
-        uint32_t a_off[A_INS], b_off[B_INS];
+    // Register-staged loads with full masking: any M, N, K; LOAD_VEC also
+    // needs 16-byte aligned A/B rows (K % 8 == 0, N % 8 == 0, aligned bases).
+    constexpr int A_CH = BM * CA / NT;
+    constexpr int B_CH = BK * CB / NT;
+    f16x8 ra[A_CH], rb[B_CH];
+    auto load_regs = [&](int kt) {
+        const int k0 = kt * BK;
 #pragma unroll
-        for (int i = 0; i < A_INS; ++i) {
-            const int P = (i * NW + wave) * 64 + lane;
-            const int r = P / CA, pc = P % CA;
-            const int c = pc ^ swz_a<BK>(r);
-            const int m = min(m0 + r, M - 1) - m0;  // rows past M re-read row M-1 (never stored)
-            a_off[i] = (uint32_t)((m * K + 8 * c) * 2);
-        }
-#pragma unroll
-        for (int i = 0; i < B_INS; ++i) {
-            const int P = (i * NW + wave) * 64 + lane;
-            const int kr = P / CB, pc = P % CB;
-            const int c = pc ^ swz_b<BN>(kr);
-            const int n = min(n0 + 8 * c, N - 8) - n0;  // columns past N re-read the last chunk
-            b_off[i] = (uint32_t)((kr * N + n) * 2);
-        }
-        const char* a_row0 = (const char*)(p.A + (size_t)m0 * K);
-        const char* b_col0 = (const char*)(p.B + n0);
-        const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-        const uint32_t a_lds0 = lds_addr(a_lds) + wave_s * 64 * 16;
-        const uint32_t b_lds0 = lds_addr(b_lds) + wave_s * 64 * 16;
-        auto issue = [&](int kt, int s) {
-            const char* ab = a_row0 + (size_t)kt * BK * 2;
-            const char* bb = b_col0 + (size_t)kt * BK * N * 2;
-#pragma unroll
-            for (int i = 0; i < A_INS; ++i) dma_global_16(ab, a_off[i], a_lds0 + s * A_STAGE + i * NW * 64 * 16);
-#pragma unroll
-            for (int i = 0; i < B_INS; ++i) dma_global_16(bb, b_off[i], b_lds0 + s * B_STAGE + i * NW * 64 * 16);
-        };
-        // Pipeline (2 LDS stages).  At the last k-step of stage kt the wave
-        // waits for its copies of stage kt+1, then one barrier publishes them
-        // and releases stage kt for the copies of kt+2, issued right away;
-        // those have a whole stage of MFMAs to land.
-        Frags f0, f1;
-        if (KT > 0) {
-            issue(0, 0);
-            if (KT > 1) {
-                issue(1, 1);
-                wait_vmcnt<PER_STAGE>();
+        for (int i = 0; i < A_CH; ++i) {
+            const int t = i * NT + tid;
+            const int r = t / CA, c = t % CA;
+            const int m = m0 + r, k = k0 + 8 * c;
+            const f16* src = p.A + (size_t)m * K + k;
+            if (LOADER == LOAD_VEC && m < M && k + 8 <= K) {
+                ra[i] = *(const f16x8*)src;
             } else {
-                wait_vmcnt0();
-            }
-            __syncthreads();
-            load_frags(f0, 0, 0);
-        }
-        for (int kt = 0; kt < KT; ++kt) {
-            const int s = kt & 1;
 #pragma unroll
-            for (int kk = 0; kk + 2 < KSTEPS; kk += 2) {
-                load_frags(f1, s, kk + 1);
-                mma(f0);
-                load_frags(f0, s, kk + 2);
-                mma(f1);
+                for (int e = 0; e < 8; ++e) ra[i][e] = (m < M && k + e < K) ? src[e] : (f16)0.0f;
             }
-            load_frags(f1, s, KSTEPS - 1);
+        }
+#pragma unroll
+        for (int i = 0; i < B_CH; ++i) {
+            const int t = i * NT + tid;
+            const int kr = t / CB, c = t % CB;
+            const int k = k0 + kr, n = n0 + 8 * c;
+            const f16* src = p.B + (size_t)k * N + n;
+            if (LOADER == LOAD_VEC && k < K && n + 8 <= N) {
+                rb[i] = *(const f16x8*)src;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) rb[i][e] = (k < K && n + e < N) ? src[e] : (f16)0.0f;
+            }
+        }
+    };
+    auto store_regs = [&](int s) {
+        GK_LDS char* As = a_lds + s * A_STAGE;
+        GK_LDS char* Bs = b_lds + s * B_STAGE;
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i) {
+            const int t = i * NT + tid;
+            const int r = t / CA, c = t % CA;
+            *(GK_LDS f16x8*)(As + r * BK * 2 + ((c ^ swz_a<BK>(r)) << 4)) = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < B_CH; ++i) {
+            const int t = i * NT + tid;
+            const int kr = t / CB, c = t % CB;
+            *(GK_LDS f16x8*)(Bs + kr * BN * 2 + ((c ^ swz_b<BN>(kr)) << 4)) = rb[i];
+        }
+    };
+    if (KT > 0) {
+        load_regs(0);
+        store_regs(0);
+    }
+    Frags f0, f1;
+    for (int kt = 0; kt < KT; ++kt) {
+        const int s = kt & 1;
+        __syncthreads();
+        if (kt + 1 < KT) load_regs(kt + 1);
+        load_frags(f0, s, 0);
+#pragma unroll
+        for (int kk = 0; kk + 2 < KSTEPS; kk += 2) {
+            load_frags(f1, s, kk + 1);
             mma(f0);
-            if (kt + 1 < KT) {
-                wait_vmcnt0();
-                __syncthreads();
-                if (kt + 2 < KT) issue(kt + 2, s);
-                load_frags(f0, s ^ 1, 0);
-            }
+            load_frags(f0, s, kk + 2);
             mma(f1);
         }
-    } else {
-        // Register-staged loads with full masking: any M, N, K; LOAD_VEC also
-        // needs 16-byte aligned A/B rows (K % 8 == 0, N % 8 == 0, aligned bases).
-        constexpr int A_CH = BM * CA / NT;
-        constexpr int B_CH = BK * CB / NT;
-        f16x8 ra[A_CH], rb[B_CH];
-        auto load_regs = [&](int kt) {
-            const int k0 = kt * BK;
-#pragma unroll
-            for (int i = 0; i < A_CH; ++i) {
-                const int t = i * NT + tid;
-                const int r = t / CA, c = t % CA;
-                const int m = m0 + r, k = k0 + 8 * c;
-                const f16* src = p.A + (size_t)m * K + k;
-                if (LOADER == LOAD_VEC && m < M && k + 8 <= K) {
-                    ra[i] = *(const f16x8*)src;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) ra[i][e] = (m < M && k + e < K) ? src[e] : (f16)0.0f;
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < B_CH; ++i) {
-                const int t = i * NT + tid;
-                const int kr = t / CB, c = t % CB;
-                const int k = k0 + kr, n = n0 + 8 * c;
-                const f16* src = p.B + (size_t)k * N + n;
-                if (LOADER == LOAD_VEC && k < K && n + 8 <= N) {
-                    rb[i] = *(const f16x8*)src;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) rb[i][e] = (k < K && n + e < N) ? src[e] : (f16)0.0f;
-                }
-            }
-        };
-        auto store_regs = [&](int s) {
-            GK_LDS char* As = a_lds + s * A_STAGE;
-            GK_LDS char* Bs = b_lds + s * B_STAGE;
-#pragma unroll
-            for (int i = 0; i < A_CH; ++i) {
-                const int t = i * NT + tid;
-                const int r = t / CA, c = t % CA;
-                *(GK_LDS f16x8*)(As + r * BK * 2 + ((c ^ swz_a<BK>(r)) << 4)) = ra[i];
-            }
-#pragma unroll
-            for (int i = 0; i < B_CH; ++i) {
-                const int t = i * NT + tid;
-                const int kr = t / CB, c = t % CB;
-                *(GK_LDS f16x8*)(Bs + kr * BN * 2 + ((c ^ swz_b<BN>(kr)) << 4)) = rb[i];
-            }
-        };
-        if (KT > 0) {
-            load_regs(0);
-            store_regs(0);
-        }
-        Frags f0, f1;
-        for (int kt = 0; kt < KT; ++kt) {
-            const int s = kt & 1;
-            __syncthreads();
-            if (kt + 1 < KT) load_regs(kt + 1);
-            load_frags(f0, s, 0);
-#pragma unroll
-            for (int kk = 0; kk + 2 < KSTEPS; kk += 2) {
-                load_frags(f1, s, kk + 1);
-                mma(f0);
-                load_frags(f0, s, kk + 2);
-                mma(f1);
-            }
-            load_frags(f1, s, KSTEPS - 1);
-            mma(f0);
-            mma(f1);
-            if (kt + 1 < KT) store_regs(s ^ 1);
-        }
+        load_frags(f1, s, KSTEPS - 1);
+        mma(f0);
+        mma(f1);
+        if (kt + 1 < KT) store_regs(s ^ 1);
     }
 
     // ---------------- epilogue: bias / GELU on the accumulators, one write of C ----------------

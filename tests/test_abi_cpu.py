@@ -99,12 +99,12 @@ def _kind(idx):
 
 def test_dispatch_shape_classes():
     sel = g.select_config_raw
-    # 4096^3 aligned: large tile, direct LDS-DMA loader
+    # 4096^3 aligned: large tile, LDS-DMA loader
     c = _kind(sel(4096, 4096, 4096, FAKE, FAKE, None, FAKE, 0))
-    assert c["kind"] == "tile" and c["loader"] == "direct" and c["bm"] == 256
+    assert c["kind"] == "tile" and c["loader"] == "dma" and c["bm"] == 256
     # fused MLP up-projection
     c = _kind(sel(8192, 16384, 4096, FAKE, FAKE, FAKE, FAKE, 2))
-    assert c["kind"] == "tile" and c["loader"] == "direct"
+    assert c["kind"] == "tile" and c["loader"] == "dma"
     # ragged N = 3001: element-wise loader
     c = _kind(sel(4095, 3001, 1000, FAKE, FAKE, FAKE, FAKE, 1))
     assert c["kind"] == "tile" and c["loader"] == "elem"

@@ -34,9 +34,9 @@ def configs_for(lib, M, N, K, epi):
     for c in lib.configs():
         if c["kind"] == "skinny" and M > c["bm"]:
             continue
-        if c["loader"] == "direct" and K % c["bk"] != 0:
+        if c["loader"] == "dma" and K % c["bk"] != 0:
             continue
-        if c["kind"] == "skinny" or c["loader"] in ("direct", "vec"):
+        if c["kind"] == "skinny" or c["loader"] in ("dma", "vec"):
             if K % 8 or N % 8:
                 continue
         out.append(c["idx"])
