@@ -28,11 +28,35 @@ struct GemmArgs {
     float* partial;   // skinny path: [k_split][M][N] fp32 partial sums (k_split > 1)
 };
 
-// Exact-erf GELU on an fp32 value: 0.5 x (1 + erf(x/sqrt2)) = 0.5 x erfc(-x/sqrt2).
-// The erfc form has no cancellation for x << 0 (where 1 + erf(.) -> 0 and the
-// erf form loses most of its significant bits); erfc from the device math library.
+// GELU in its erf form on an fp32 value:
+//   gelu(x) = x * Phi(x),  Phi(x) = 0.5 * erfc(-x / sqrt 2)
+//           = 1 - 0.5 erfc(z)  (x >= 0)   or   0.5 erfc(z)  (x < 0),   z = |x| / sqrt 2.
+// erfc(z) for z >= 0 uses the Chebyshev-fitted form published in Numerical
+// Recipes (Press, Teukolsky, Vetterling, Flannery, 2nd ed., section 6.2,
+// "erfcc"):  erfc(z) = t exp(-z^2 + P(t)),  t = 1 / (1 + z/2),  with P a
+// degree-9 polynomial.  Its fractional error is below 1.2e-7 for every
+// z >= 0.  In fp32 the error stays below 1e-5 relative, far below the fp16
+// output's half-ulp of 2.4e-4.
+// The evaluation is branch-free: one reciprocal, one exp2 and ~12 FMAs.
+// Computing erfc(|z|) and reflecting avoids the cancellation of 1 + erf(.)
+// for x << 0.
 __device__ __forceinline__ float gelu_erf(float x) {
-    return 0.5f * x * erfcf(x * -0.70710678118654752f);
+    const float z = __builtin_fabsf(x) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, z, 1.0f));
+    float q = 0.17087277f;
+    q = __builtin_fmaf(q, t, -0.82215223f);
+    q = __builtin_fmaf(q, t, 1.48851587f);
+    q = __builtin_fmaf(q, t, -1.13520398f);
+    q = __builtin_fmaf(q, t, 0.27886807f);
+    q = __builtin_fmaf(q, t, -0.18628806f);
+    q = __builtin_fmaf(q, t, 0.09678418f);
+    q = __builtin_fmaf(q, t, 0.37409196f);
+    q = __builtin_fmaf(q, t, 1.00002368f);
+    q = __builtin_fmaf(q, t, -1.26551223f);
+    const float arg = __builtin_fmaf(-z, z, q);                          // <= 0
+    const float half_erfc = 0.5f * t * __builtin_amdgcn_exp2f(arg * 1.44269504088896341f);
+    const float phi = x >= 0.0f ? 1.0f - half_erfc : half_erfc;
+    return x * phi;
 }
 
 template <int EPI>

@@ -202,6 +202,28 @@ def test_bias_only_exact(lib):
     assert ulp_distance(got, ref).max() <= 1
 
 
+@pytest.mark.parametrize("M", [16, 256, 72])
+def test_gelu_epilogue_every_finite_fp16(lib, M):
+    # A = 0, so C[i][j] = gelu(bias[j]) with bias = every finite binary16 value:
+    # the fused GELU of each path (skinny M = 16, DMA tile M = 256, register
+    # tile M = 72 with K = 8) against the oracle, within one fp16 ulp, and
+    # bit-identical on at least 99.5% of the values.
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    bits = bits[(bits & 0x7C00) != 0x7C00]                       # 63488 finite patterns
+    bias = bits.view(np.float16)
+    N = bias.shape[0]
+    K = 8 if M == 72 else 64
+    A = np.zeros((M, K), np.float16)
+    B = workloads.random_f16(11, (K, N))
+    ref = oracle.gemm(A[:1], B, bias, "bias_gelu")[0]
+    got = run(lib, A, B, bias, "bias_gelu")
+    for i in (0, M - 1):
+        u = ulp_distance(got[i], ref)
+        assert u.max() <= 1, (M, i, int(u.argmax()), float(bias[u.argmax()]))
+        assert np.mean(u == 0) >= 0.995, (M, i, float(np.mean(u == 0)))
+    assert np.array_equal(got[0].view(np.uint16), got[M - 1].view(np.uint16))
+
+
 # ---------------------------------------------------------------------------
 # edges: canaries, misaligned views, degenerate sizes, determinism
 # ---------------------------------------------------------------------------
