@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libgemm_f16.so")
 SOURCES = [os.path.join(CSRC, "gemm_f16.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("common.h", "tile_kernel.h", "tile_dma_kernel.h", "skinny_kernel.h")] + [
+HEADERS = [os.path.join(CSRC, f) for f in ("common.h", "tile_pipe_kernel.h", "skinny_kernel.h")] + [
     os.path.join(INCLUDE, "gemm_f16.h")
 ]
 

@@ -7,8 +7,7 @@
 
 #include "gemm_f16.h"
 #include "skinny_kernel.h"
-#include "tile_dma_kernel.h"
-#include "tile_kernel.h"
+#include "tile_pipe_kernel.h"
 
 using namespace gk;
 
@@ -30,17 +29,11 @@ struct Config {
     launch_fn launch[3];     // indexed by epilogue
 };
 
-template <int BM, int BN, int BK, int WM, int WN, int LOADER, int GROUP_M, int EPI>
+template <int BM, int BN, int BK, int WM, int WN, int ST, int G, int BS, int DS, int LOADER, int CS, int WPE, int EPI>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(WM * WN * 64);
-    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, BK, WM, WN, LOADER, EPI, GROUP_M>), grid, block, 0, s, a);
-    return hipGetLastError();
-}
-
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int GROUP_M, int BSLOT, int DSTRIDE, int EPI>
-hipError_t launch_tile_dma(const GemmArgs& a, hipStream_t s) {
-    dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(WM * WN * 64);
-    hipLaunchKernelGGL((gemm_tile_dma_kernel<BM, BN, BK, WM, WN, STAGES, GROUP_M, EPI, BSLOT, DSTRIDE>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_tile_pipe_kernel<BM, BN, BK, WM, WN, ST, G, EPI, BS, DS, LOADER, CS, WPE>), grid, block, 0, s,
+                       a);
     return hipGetLastError();
 }
 
@@ -51,24 +44,17 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-#define TILE_CFG(BM, BN, BK, WM, WN, LOADER, G, NAME)                                              \
+// Tile config: block tile BM x BN x BK, WM x WN waves, ST LDS stages, tile
+// order group G, barrier slot BS, copy stride DS, loader, LDS-write slot CS
+// (register loader), waves per SIMD WPE.
+#define TILE_CFG(BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, NAME)                         \
     Config {                                                                                       \
-        NAME, KIND_TILE, BM, BN, BK, WM, WN, LOADER, G, 2,                                         \
-            TileCfg<BM, BN, BK, WM, WN, LOADER, 0, G>::LDS_BYTES, WM * WN * 64,                    \
+        NAME, KIND_TILE, BM, BN, BK, WM, WN, LOADER, G, ST,                                        \
+            TilePipeCfg<BM, BN, BK, WM, WN, ST>::LDS_BYTES, WM * WN * 64,                          \
         {                                                                                          \
-            launch_tile<BM, BN, BK, WM, WN, LOADER, G, 0>, launch_tile<BM, BN, BK, WM, WN, LOADER, G, 1>, \
-                launch_tile<BM, BN, BK, WM, WN, LOADER, G, 2>                                      \
-        }                                                                                          \
-    }
-
-#define DMA_CFG(BM, BN, BK, WM, WN, ST, G, BS, DS, NAME)                                          \
-    Config {                                                                                       \
-        NAME, KIND_TILE, BM, BN, BK, WM, WN, LOAD_DMA, G, ST,                                      \
-            TileDmaCfg<BM, BN, BK, WM, WN, ST>::LDS_BYTES, WM * WN * 64,                           \
-        {                                                                                          \
-            launch_tile_dma<BM, BN, BK, WM, WN, ST, G, BS, DS, 0>,                                 \
-                launch_tile_dma<BM, BN, BK, WM, WN, ST, G, BS, DS, 1>,                             \
-                launch_tile_dma<BM, BN, BK, WM, WN, ST, G, BS, DS, 2>                              \
+            launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, 0>,                    \
+                launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, 1>,                \
+                launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, 2>                 \
         }                                                                                          \
     }
 
@@ -82,27 +68,28 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
     }
 
 const Config kConfigs[] = {
-    DMA_CFG(256, 256, 64, 2, 2, 2, 4, 3, 2, "dma_256x256x64_w2x2_s2_g4"),              // 0
-    TILE_CFG(256, 256, 64, 2, 2, LOAD_VEC, 4, "tile_256x256x64_w2x2_vec_g4"),         // 1
-    DMA_CFG(128, 128, 64, 2, 2, 2, 4, 1, 1, "dma_128x128x64_w2x2_s2_g4"),              // 2
-    TILE_CFG(128, 128, 64, 2, 2, LOAD_VEC, 4, "tile_128x128x64_w2x2_vec_g4"),         // 3
-    TILE_CFG(128, 128, 64, 2, 2, LOAD_ELEM, 4, "tile_128x128x64_w2x2_elem_g4"),       // 4
-    DMA_CFG(256, 128, 64, 2, 2, 2, 4, 3, 2, "dma_256x128x64_w2x2_s2_g4"),              // 5
-    SKINNY_CFG(1, 6, "skinny_m16_s6"),                                                // 6
-    SKINNY_CFG(2, 5, "skinny_m32_s5"),                                                // 7
-    SKINNY_CFG(4, 4, "skinny_m64_s4"),                                                // 8
+    TILE_CFG(256, 256, 64, 2, 2, 2, 4, 3, 2, LOAD_DMA, 0, 1, "dma_256x256x64_w2x2_s2_g4"),   // 0
+    TILE_CFG(256, 256, 64, 2, 2, 2, 4, 3, 2, LOAD_REG, 0, 1, "reg_256x256x64_w2x2_g4"),     // 1
+    TILE_CFG(128, 128, 64, 2, 2, 2, 4, 1, 1, LOAD_DMA, 0, 1, "dma_128x128x64_w2x2_s2_g4"),   // 2
+    TILE_CFG(128, 128, 64, 2, 2, 2, 4, 1, 1, LOAD_REG, 0, 1, "reg_128x128x64_w2x2_g4"),     // 3
+    TILE_CFG(128, 128, 64, 2, 2, 2, 4, 1, 1, LOAD_REG, 0, 2, "reg_128x128x64_w2x2_g4_o2"),  // 4
+    TILE_CFG(256, 128, 64, 2, 2, 2, 4, 3, 2, LOAD_DMA, 0, 1, "dma_256x128x64_w2x2_s2_g4"),   // 5
+    TILE_CFG(256, 128, 64, 2, 2, 2, 4, 3, 2, LOAD_REG, 0, 1, "reg_256x128x64_w2x2_g4"),     // 6
+    SKINNY_CFG(1, 6, "skinny_m16_s6"),                                                       // 7
+    SKINNY_CFG(2, 5, "skinny_m32_s5"),                                                       // 8
+    SKINNY_CFG(4, 4, "skinny_m64_s4"),                                                       // 9
 };
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 
 enum DefaultIdx {
     CFG_T256_DMA = 0,
-    CFG_T256_VEC = 1,
+    CFG_T256_REG = 1,
     CFG_T128_DMA = 2,
-    CFG_T128_VEC = 3,
-    CFG_T128_ELEM = 4,
-    CFG_SKINNY16 = 6,
-    CFG_SKINNY32 = 7,
-    CFG_SKINNY64 = 8,
+    CFG_T128_REG = 3,
+    CFG_T128_REG_O2 = 4,
+    CFG_SKINNY16 = 7,
+    CFG_SKINNY32 = 8,
+    CFG_SKINNY64 = 9,
 };
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -137,15 +124,10 @@ bool supports(const Config& cfg, const Call& c) {
         return vec_ok && c.M <= cfg.bm && c.K * c.N * 2 < (int64_t)INT32_MAX &&
                c.M * c.K * 2 < (int64_t)INT32_MAX;
     }
-    switch (cfg.loader) {
-        case LOAD_DMA:
-            return vec_ok && c.K % cfg.bk == 0 && (int64_t)cfg.bm * c.K * 2 < (int64_t)INT32_MAX &&
-                   (int64_t)cfg.bk * c.N * 2 < (int64_t)INT32_MAX;
-        case LOAD_VEC:
-            return vec_ok;
-        default:
-            return true;
-    }
+    if (cfg.loader == LOAD_DMA)
+        return vec_ok && c.K % cfg.bk == 0 && (int64_t)cfg.bm * c.K * 2 < (int64_t)INT32_MAX &&
+               (int64_t)cfg.bk * c.N * 2 < (int64_t)INT32_MAX;
+    return true;  // register loader: any shape, any 2-byte alignment
 }
 
 int pick_default(const Call& c) {
@@ -156,10 +138,9 @@ int pick_default(const Call& c) {
     }
     const int64_t tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256);
     const bool big = tiles256 >= 256;  // at least one workgroup per CU with 256x256 tiles
-    const int cand[] = {big ? CFG_T256_DMA : CFG_T128_DMA, big ? CFG_T256_VEC : CFG_T128_VEC};
-    for (int idx : cand)
-        if (supports(kConfigs[idx], c)) return idx;
-    return CFG_T128_ELEM;
+    const int dma = big ? CFG_T256_DMA : CFG_T128_DMA;
+    if (supports(kConfigs[dma], c)) return dma;
+    return big ? CFG_T256_REG : CFG_T128_REG_O2;
 }
 
 int run(const Config& cfg, const Call& c, hipStream_t stream) {
@@ -228,7 +209,7 @@ int gemm_f16_num_configs(void) { return kNumConfigs; }
 int gemm_f16_config_info(int idx, char* buf, int buflen) {
     if (idx < 0 || idx >= kNumConfigs) return -GEMM_ERR_NO_CONFIG;
     const Config& c = kConfigs[idx];
-    static const char* loaders[] = {"dma", "vec", "elem"};
+    static const char* loaders[] = {"dma", "reg"};
     char tmp[512];
     int n = snprintf(tmp, sizeof(tmp),
                      "{\"idx\": %d, \"name\": \"%s\", \"kind\": \"%s\", \"bm\": %d, \"bn\": %d, \"bk\": %d, "

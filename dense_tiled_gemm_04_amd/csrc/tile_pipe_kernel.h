@@ -1,4 +1,4 @@
-// Aligned fast path of the tiled fp16 GEMM on gfx950.
+// Pipelined tile kernel of the fp16 GEMM on gfx950.
 //
 // It computes the tutorial's tiled GEMM: fp16 tiles A[block_M][block_K] and
 // B[block_K][block_N] staged in shared memory, a float32 register accumulator,
@@ -8,37 +8,62 @@
 // tiled GEMM and on the fused epilogue.
 //
 // What is specific to CDNA4:
-//  * Copies. HBM/L2 -> LDS goes by LDS-DMA (global_load_lds_dwordx4), so no
-//    VGPR is spent on staging. STAGES ring buffers. The copies of stage
-//    kt+STAGES-1 are spread over the MFMA slots of stage kt (every DSTRIDE-th
-//    slot).
-//  * Schedule. Every MFMA slot is fenced with sched_barrier, so the issue
-//    order is exactly the one written here:
-//      slot i of a k-step: MFMA i, the LDS reads scheduled for slot i (the
-//      next k-step's fragments), and the copies scheduled for slot i.
-//    At slot BSLOT of a stage's last k-step, the wave waits for its copies of
-//    stage kt+1, and one barrier publishes them. All LDS reads of stage kt
-//    have landed by then, so the same barrier also frees stage kt's buffer.
-//    The next stage's first fragments are then read in the remaining slots.
-//    The result is that LDS reads and copies always overlap MFMAs, and no
-//    wave idles between stages.
 //  * MFMA. v_mfma_f32_32x32x16_f16, issued as C^T = B^T . A^T, so each lane
 //    holds 4 consecutive columns of one output row. A fragments come from
 //    ds_read_b128. B fragments come from row-major [k][n] LDS by the
 //    transpose read ds_read_b64_tr_b16. Both tiles are XOR-swizzled in
 //    16-byte chunks so that the reads are free of bank conflicts.
-//
-// Requirements (checked on the host): K % BK == 0, N % 8 == 0, A/B/C 16-byte
-// aligned, bias 8-byte aligned. Rows past M re-read row M-1, and columns past
-// N re-read the last chunk; neither is stored.
+//  * Schedule. Every MFMA slot is fenced with sched_barrier, so the issue
+//    order is exactly the one written here:
+//      slot i of a k-step: MFMA i, the LDS reads scheduled for slot i (the
+//      next k-step's fragments), and the copy work scheduled for slot i.
+//    At slot BSLOT of a stage's last k-step, the wave waits for its part of
+//    stage kt+1, and one barrier publishes it. All LDS reads of stage kt have
+//    landed by then, so the same barrier also frees stage kt's buffer. The
+//    next stage's first fragments are then read in the remaining slots.
+//  * Copies, two loaders:
+//    - LOAD_DMA: HBM/L2 -> LDS by LDS-DMA (global_load_lds_dwordx4), so no
+//      VGPR is spent on staging. STAGES ring buffers. The copies of stage
+//      kt+STAGES-1 are issued at every DSTRIDE-th slot of stage kt.
+//      Requires K % BK == 0, N % 8 == 0, A/B/C 16-byte aligned and bias
+//      8-byte aligned. Rows past M re-read row M-1, and columns past N
+//      re-read the last chunk; neither is stored.
+//    - LOAD_REG: any M, N, K and any 2-byte alignment. Two LDS stages and one
+//      set of staging registers. In stage kt, slot CSLOT+j writes register j
+//      (stage kt+1, loaded one stage earlier) to LDS with ds_write_b128, and
+//      slot CSLOT+j*DSTRIDE then reloads it with stage kt+2. So every load
+//      has about a stage to land. The loads are 16-byte loads; the hardware
+//      accepts unaligned addresses. Element-wise loads are used only for a
+//      chunk that straddles the end of a row (N) or of K. Zeros are written
+//      past K (in both A and B) and past N, and rows past M are clamped.
+//  * Tile order. XCD-contiguous remap of the workgroup id, then a grouped
+//    raster of GROUP_M tile-rows.
 #pragma once
 #include "common.h"
-#include "tile_kernel.h"
 
 namespace gk {
 
+enum Loader { LOAD_DMA = 0, LOAD_REG = 1 };
+
+// A-tile swizzle: logical chunk c of row r lives at chunk c ^ swz_a(r).  Over
+// any 16 consecutive rows (one ds_read_b128 quarter-wave), the 16 physical
+// positions fall in 16 distinct 16-byte bank groups of the 256-byte window.
+template <int BK>
+__device__ __forceinline__ int swz_a(int r) {
+    constexpr int CA = BK / 8, RPW = 128 / BK;
+    return (r / RPW) & (CA - 1);
+}
+// B-tile swizzle: logical chunk c of k-row kr lives at c ^ swz_b(kr).  A
+// transpose read touches 4 consecutive k-rows x 64 bytes per half-wave; XOR
+// by 4*(kr mod 4) chunks puts those 16 chunks in distinct bank groups.
+template <int BN>
+__device__ __forceinline__ int swz_b(int kr) {
+    constexpr int CB = BN / 8;
+    return (4 * (kr & 3)) & (CB - 1);
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int STAGES>
-struct TileDmaCfg {
+struct TilePipeCfg {
     static constexpr int NW = WM * WN;
     static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave sub-tile
     static constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA blocks per wave
@@ -46,7 +71,7 @@ struct TileDmaCfg {
     static constexpr int A_STAGE = BM * BK * 2, B_STAGE = BK * BN * 2;
     static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE);
     static constexpr int KSTEPS = BK / 16;              // k16 steps per stage
-    static constexpr int A_INS = BM * CA / 64 / NW;     // LDS-DMA instructions per wave and stage
+    static constexpr int A_INS = BM * CA / 64 / NW;     // 16-byte copies per lane and stage
     static constexpr int B_INS = BK * CB / 64 / NW;
     static constexpr int PER_STAGE = A_INS + B_INS;
     static constexpr int NMMA = TM * TN;                // MFMAs (slots) per k-step
@@ -66,17 +91,25 @@ __device__ constexpr int read_slot(int j, int first, int avail) {
     return first + (NRD <= avail ? j : j * avail / NRD);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int GROUP_M, int EPI, int BSLOT, int DSTRIDE>
-__global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-gemm_tile_dma_kernel(GemmArgs p) {
-    using Cfg = TileDmaCfg<BM, BN, BK, WM, WN, STAGES>;
+typedef f16x8 f16x8_u __attribute__((aligned(2)));
+typedef f16x4 f16x4_u __attribute__((aligned(2)));
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int GROUP_M, int EPI, int BSLOT, int DSTRIDE,
+          int LOADER, int CSLOT, int WPE>
+__global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+gemm_tile_pipe_kernel(GemmArgs p) {
+    using Cfg = TilePipeCfg<BM, BN, BK, WM, WN, STAGES>;
     constexpr int NW = Cfg::NW, WTM = Cfg::WTM, WTN = Cfg::WTN, TM = Cfg::TM, TN = Cfg::TN;
     constexpr int CA = Cfg::CA, CB = Cfg::CB, A_STAGE = Cfg::A_STAGE, B_STAGE = Cfg::B_STAGE;
     constexpr int KSTEPS = Cfg::KSTEPS, A_INS = Cfg::A_INS, B_INS = Cfg::B_INS, PER_STAGE = Cfg::PER_STAGE;
     constexpr int NMMA = Cfg::NMMA, NRD = Cfg::NRD;
+    constexpr int LAST = (KSTEPS - 1) * NMMA + BSLOT;  // stage slot of the barrier
     static_assert(BSLOT >= 0 && BSLOT + 1 < NMMA, "barrier slot inside the last k-step, reads after it");
-    static_assert(DSTRIDE >= 1 && (PER_STAGE - 1) * DSTRIDE < (KSTEPS - 1) * NMMA + BSLOT,
-                  "every copy of a stage is issued before that stage's barrier");
+    static_assert(DSTRIDE >= 1 && (PER_STAGE - 1) * DSTRIDE < LAST, "every copy is issued before the barrier");
+    static_assert(LOADER == LOAD_DMA || (STAGES == 2 && CSLOT >= 0 && CSLOT + PER_STAGE <= LAST + 1 &&
+                                         CSLOT + (PER_STAGE - 1) * DSTRIDE < KSTEPS * NMMA),
+                  "register loader: 2 stages; every LDS write precedes the barrier; every reload fits "
+                  "in the stage");
 
     __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::LDS_BYTES];
     GK_LDS char* const a_lds = (GK_LDS char*)smem_raw;           // [STAGES][BM][BK]
@@ -91,7 +124,7 @@ gemm_tile_dma_kernel(GemmArgs p) {
         grouped_tile<GROUP_M>(xcd_contiguous_id((int)blockIdx.x, nwg), p.tiles_m, p.tiles_n, tm, tn);
     }
     const int m0 = tm * BM, n0 = tn * BN;
-    const int KT = K / BK;
+    const int KT = (K + BK - 1) / BK;
 
     // Fragment read offsets (bytes within a stage).
     // A (MFMA operand b): lane holds A[m = row(lane)][k = 16 kk + 8 (lane / 32) .. +7].
@@ -114,22 +147,37 @@ gemm_tile_dma_kernel(GemmArgs p) {
             b_rd[ni] = kr * BN * 2 + (((nl >> 3) ^ swz_b<BN>(kr)) << 4) + ((nl & 7) << 1);
         }
     }
-    // LDS-DMA sources. Destination chunk P of a stage is lane-contiguous; its
-    // source is the logical chunk that the swizzle puts at P.
-    uint32_t a_off[A_INS], b_off[B_INS];
+
+    // Copy j (0 <= j < PER_STAGE) of a stage: destination chunk
+    // P = (i * NW + wave) * 64 + lane of the A (j < A_INS, i = j) or the B
+    // (i = j - A_INS) tile, which is lane-contiguous; its source is the
+    // logical chunk that the swizzle puts at P.
+    uint32_t a_off[A_INS], b_off[B_INS];  // LOAD_DMA: byte offsets from the tile origin
+    int a_ck[A_INS], b_kr[B_INS], b_cn[B_INS];  // LOAD_REG: k offset in stage / k-row / column
+    const f16* a_row[A_INS];                   // LOAD_REG: row pointer (rows clamped to M-1)
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
         const int P = (i * NW + wave) * 64 + lane;
         const int r = P / CA, c = (P % CA) ^ swz_a<BK>(r);
-        const int m = min(m0 + r, M - 1) - m0;
-        a_off[i] = (uint32_t)((m * K + 8 * c) * 2);
+        const int m = min(m0 + r, M - 1);
+        if constexpr (LOADER == LOAD_DMA) {
+            a_off[i] = (uint32_t)(((m - m0) * K + 8 * c) * 2);
+        } else {
+            a_ck[i] = 8 * c;
+            a_row[i] = p.A + (size_t)m * K;
+        }
     }
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
         const int P = (i * NW + wave) * 64 + lane;
         const int kr = P / CB, c = (P % CB) ^ swz_b<BN>(kr);
-        const int n = min(n0 + 8 * c, N - 8) - n0;
-        b_off[i] = (uint32_t)((kr * N + n) * 2);
+        if constexpr (LOADER == LOAD_DMA) {
+            const int n = min(n0 + 8 * c, N - 8) - n0;
+            b_off[i] = (uint32_t)((kr * N + n) * 2);
+        } else {
+            b_kr[i] = kr;
+            b_cn[i] = n0 + 8 * c;
+        }
     }
     const char* const a_row0 = (const char*)(p.A + (size_t)m0 * K);
     const char* const b_col0 = (const char*)(p.B + n0);
@@ -137,7 +185,7 @@ gemm_tile_dma_kernel(GemmArgs p) {
     const uint32_t a_lds0 = lds_addr(a_lds) + wave_s * 64 * 16;
     const uint32_t b_lds0 = lds_addr(b_lds) + wave_s * 64 * 16;
 
-    // Copy j (0 <= j < PER_STAGE) of stage kt into ring buffer sb.
+    // LOAD_DMA: copy j of stage kt into ring buffer sb.
     auto dma_op = [&](int j, int kt, int sb) {
         if (j < A_INS) {
             dma_global_16(a_row0 + (size_t)kt * BK * 2, a_off[j], a_lds0 + sb * A_STAGE + j * NW * 64 * 16);
@@ -145,6 +193,41 @@ gemm_tile_dma_kernel(GemmArgs p) {
             const int i = j - A_INS;
             dma_global_16(b_col0 + (size_t)kt * BK * N * 2, b_off[i], b_lds0 + sb * B_STAGE + i * NW * 64 * 16);
         }
+    };
+    // LOAD_REG: load copy j of stage kt into a register, then write it to LDS.
+    f16x8 stg[LOADER == LOAD_REG ? PER_STAGE : 1];
+    auto gload_op = [&](int j, int kt) {
+        f16x8 v = {};
+        if (j < A_INS) {
+            const int k = kt * BK + a_ck[j];
+            const f16* src = a_row[j] + k;
+            if (k + 8 <= K) {
+                v = *(const f16x8_u*)src;
+            } else if (k < K) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (k + e < K) v[e] = src[e];
+            }
+        } else {
+            const int i = j - A_INS;
+            const int k = kt * BK + b_kr[i], n = b_cn[i];
+            const f16* src = p.B + (size_t)k * N + n;
+            if (k < K) {
+                if (n + 8 <= N) {
+                    v = *(const f16x8_u*)src;
+                } else if (n < N) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < N) v[e] = src[e];
+                }
+            }
+        }
+        stg[LOADER == LOAD_REG ? j : 0] = v;
+    };
+    auto lwrite_op = [&](int j, int sb) {
+        GK_LDS char* dst = (j < A_INS) ? a_lds + sb * A_STAGE + ((j * NW + wave) * 64 + lane) * 16
+                                       : b_lds + sb * B_STAGE + (((j - A_INS) * NW + wave) * 64 + lane) * 16;
+        *(GK_LDS f16x8*)dst = stg[LOADER == LOAD_REG ? j : 0];
     };
 
     f32x16 acc[TM][TN];
@@ -179,16 +262,30 @@ gemm_tile_dma_kernel(GemmArgs p) {
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, fa[set][mi], acc[mi][ni], 0, 0, 0);
     };
 
-    // Prologue: stages 0 .. STAGES-2 in flight, then stage 0's first fragments.
+    // Prologue: stages 0 .. STAGES-2 in LDS (or in flight), then stage 0's
+    // first fragments.
+    if constexpr (LOADER == LOAD_DMA) {
 #pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st)
-        if (st < KT)
+        for (int st = 0; st < STAGES - 1; ++st)
+            if (st < KT)
 #pragma unroll
-            for (int j = 0; j < PER_STAGE; ++j) dma_op(j, st, st);
-    if (KT >= STAGES - 1) {
-        wait_vmcnt<(STAGES - 2) * PER_STAGE>();
+                for (int j = 0; j < PER_STAGE; ++j) dma_op(j, st, st);
+        if (KT >= STAGES - 1) {
+            wait_vmcnt<(STAGES - 2) * PER_STAGE>();
+        } else {
+            wait_vmcnt0();
+        }
     } else {
-        wait_vmcnt0();
+        if (KT > 0) {
+#pragma unroll
+            for (int j = 0; j < PER_STAGE; ++j) gload_op(j, 0);
+#pragma unroll
+            for (int j = 0; j < PER_STAGE; ++j) lwrite_op(j, 0);
+        }
+        if (KT > 1) {
+#pragma unroll
+            for (int j = 0; j < PER_STAGE; ++j) gload_op(j, 1);
+        }
     }
     __syncthreads();
     if (KT > 0) {
@@ -197,11 +294,13 @@ gemm_tile_dma_kernel(GemmArgs p) {
     }
 
     int s = 0;  // ring buffer of the stage being computed
-    // MAIN: every stage up to kt+STAGES-1 exists, so the copies are issued
-    // unconditionally and the wait count is exact.  Tail stages issue none
-    // and wait for everything.
-    auto stage = [&]<bool MAIN>(int kt) {
-        const bool has_next = MAIN || kt + 1 < KT;
+    // PHASE 2: every stage the copies of this stage refer to exists (LOAD_DMA:
+    // kt+STAGES-1; LOAD_REG: kt+1 written and kt+2 loaded), so they are issued
+    // unconditionally and the DMA wait count is exact.  PHASE 1 (LOAD_REG
+    // only): the last write, no reload.  PHASE 0: no copy work; the DMA
+    // loader waits for everything.
+    auto stage = [&]<int PHASE>(int kt) {
+        const bool has_next = PHASE > 0 || kt + 1 < KT;
         const int sn = (s + 1 == STAGES) ? 0 : s + 1;
         const int sd = (s == 0) ? STAGES - 1 : s - 1;  // buffer of stage kt+STAGES-1 (freed last stage)
 #pragma unroll
@@ -211,8 +310,15 @@ gemm_tile_dma_kernel(GemmArgs p) {
             for (int i = 0; i < NMMA; ++i) {
                 mma_op(cur, i);
                 const int slot = kk * NMMA + i;
-                if constexpr (MAIN) {
+                if constexpr (LOADER == LOAD_DMA && PHASE == 2) {
                     if (slot % DSTRIDE == 0 && slot / DSTRIDE < PER_STAGE) dma_op(slot / DSTRIDE, kt + STAGES - 1, sd);
+                }
+                if constexpr (LOADER == LOAD_REG && PHASE >= 1) {
+                    if (slot >= CSLOT && slot < CSLOT + PER_STAGE) lwrite_op(slot - CSLOT, sn);
+                }
+                if constexpr (LOADER == LOAD_REG && PHASE == 2) {
+                    if (slot >= CSLOT && (slot - CSLOT) % DSTRIDE == 0 && (slot - CSLOT) / DSTRIDE < PER_STAGE)
+                        gload_op((slot - CSLOT) / DSTRIDE, kt + 2);
                 }
                 if (kk + 1 < KSTEPS) {
 #pragma unroll
@@ -220,10 +326,12 @@ gemm_tile_dma_kernel(GemmArgs p) {
                         if (read_slot<NRD>(j, 0, NMMA) == i) read_op(nxt, j, s, kk + 1);
                 } else if (has_next) {
                     if (i == BSLOT) {
-                        if constexpr (MAIN) {
-                            wait_vmcnt<(STAGES - 2) * PER_STAGE>();
-                        } else {
-                            wait_vmcnt0();
+                        if constexpr (LOADER == LOAD_DMA) {
+                            if constexpr (PHASE == 2) {
+                                wait_vmcnt<(STAGES - 2) * PER_STAGE>();
+                            } else {
+                                wait_vmcnt0();
+                            }
                         }
                         __syncthreads();
                     }
@@ -236,35 +344,52 @@ gemm_tile_dma_kernel(GemmArgs p) {
         }
         s = sn;
     };
-    const int kt_main = KT - (STAGES - 1);
     int kt = 0;
-    for (; kt < kt_main; ++kt) stage.template operator()<true>(kt);
-    for (; kt < KT; ++kt) stage.template operator()<false>(kt);
+    if constexpr (LOADER == LOAD_DMA) {
+        for (; kt < KT - (STAGES - 1); ++kt) stage.template operator()<2>(kt);
+    } else {
+        for (; kt < KT - 2; ++kt) stage.template operator()<2>(kt);
+        if (kt < KT - 1) stage.template operator()<1>(kt++);
+    }
+    for (; kt < KT; ++kt) stage.template operator()<0>(kt);
 
     // Epilogue on the accumulators, one write of C.  Lane l, register
     // 4*r4 + e of block (mi, ni) holds
     //   C[m0 + wm*WTM + mi*32 + l%32][n0 + wn*WTN + ni*32 + 8*r4 + 4*(l/32) + e].
+    // With LOAD_DMA, N % 8 == 0, so a column quad is all in or all out.
 #pragma unroll
     for (int ni = 0; ni < TN; ++ni) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             const int n = n0 + wn * WTN + ni * 32 + 8 * r4 + 4 * (lane >> 5);
+            const bool quad = n + 4 <= N;
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (EPI != EPI_NONE) {
-                if (n + 4 <= N) {
-                    const f16x4 b4 = *(const f16x4*)(p.bias + n);
+                if (quad) {
+                    const f16x4 b4 = *(const f16x4_u*)(p.bias + n);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) bv[e] = (float)b4[e];
+                } else if (LOADER == LOAD_REG) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) bv[e] = (float)p.bias[n + e];
                 }
             }
 #pragma unroll
             for (int mi = 0; mi < TM; ++mi) {
                 const int m = m0 + wm * WTM + mi * 32 + (lane & 31);
-                if (m >= M || n + 4 > N) continue;  // N % 8 == 0: a column quad is all in or all out
+                if (m >= M || n >= N) continue;
                 f16x4 o;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[e] = (f16)apply_epilogue<EPI>(acc[mi][ni][4 * r4 + e], bv[e]);
-                *(f16x4*)(p.C + (size_t)m * N + n) = o;
+                f16* dst = p.C + (size_t)m * N + n;
+                if (quad) {
+                    *(f16x4_u*)dst = o;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) dst[e] = o[e];
+                }
             }
         }
     }

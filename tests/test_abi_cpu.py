@@ -84,9 +84,9 @@ def test_empty_outputs_are_noops():
 def test_forced_config_rejections():
     n = g.num_configs()
     assert g.gemm_f16_raw(4, 4, 4, FAKE, FAKE, None, FAKE, 0, 0, config=n) == 5
-    # a skinny config cannot take M = 65; a vectorised config cannot take N = 3001
+    # a skinny config cannot take M = 129; an LDS-DMA config cannot take N = 3001
     skinny = [c["idx"] for c in g.configs() if c["kind"] == "skinny"]
-    vec = [c["idx"] for c in g.configs() if c["kind"] == "tile" and c["loader"] != "elem"]
+    vec = [c["idx"] for c in g.configs() if c["kind"] == "tile" and c["loader"] == "dma"]
     for idx in skinny:
         assert g.gemm_f16_raw(65 + 64, 64, 64, FAKE, FAKE, None, FAKE, 0, 0, config=idx) == 6
     for idx in vec:
@@ -105,15 +105,15 @@ def test_dispatch_shape_classes():
     # fused MLP up-projection
     c = _kind(sel(8192, 16384, 4096, FAKE, FAKE, FAKE, FAKE, 2))
     assert c["kind"] == "tile" and c["loader"] == "dma"
-    # ragged N = 3001: element-wise loader
+    # ragged N = 3001: register loader (unaligned rows)
     c = _kind(sel(4095, 3001, 1000, FAKE, FAKE, FAKE, FAKE, 1))
-    assert c["kind"] == "tile" and c["loader"] == "elem"
+    assert c["kind"] == "tile" and c["loader"] == "reg"
     # skinny M = 16
     c = _kind(sel(16, 16384, 8192, FAKE, FAKE, FAKE, FAKE, 2))
     assert c["kind"] == "skinny" and c["bm"] >= 16
-    # K not a multiple of the K-block: vectorised register loader
+    # K not a multiple of the K-block: register loader
     c = _kind(sel(1024, 1024, 1000, FAKE, FAKE, None, FAKE, 0))
-    assert c["kind"] == "tile" and c["loader"] == "vec"
-    # misaligned base (2-byte aligned only): element-wise loader
+    assert c["kind"] == "tile" and c["loader"] == "reg"
+    # misaligned base (2-byte aligned only): register loader
     c = _kind(sel(1024, 1024, 1024, FAKE + 2, FAKE, None, FAKE, 0))
-    assert c["loader"] == "elem"
+    assert c["loader"] == "reg"

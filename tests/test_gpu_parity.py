@@ -36,7 +36,7 @@ def configs_for(lib, M, N, K, epi):
             continue
         if c["loader"] == "dma" and K % c["bk"] != 0:
             continue
-        if c["kind"] == "skinny" or c["loader"] in ("dma", "vec"):
+        if c["kind"] == "skinny" or c["loader"] == "dma":
             if K % 8 or N % 8:
                 continue
         out.append(c["idx"])
@@ -255,7 +255,7 @@ def test_misaligned_views(lib):
     import dense_tiled_gemm_04_amd as g
     Av, Bv, Cv = ab[1:].view(M, K), bb[1:].view(K, N), cb[1:].view(M, N)
     cfg = g.config_info(g.select_config(Av, Bv, dev(bias), "bias_gelu", out=Cv))
-    assert cfg["loader"] == "elem"
+    assert cfg["loader"] == "reg"
     g.gemm_f16(Av, Bv, dev(bias), "bias_gelu", out=Cv)
     torch.cuda.synchronize()
     assert_parity(Cv.cpu().numpy(), ref, "misaligned")
