@@ -105,8 +105,17 @@ def hbm_calibration(g, torch) -> int:
         g.vector_add(a, b, out=c)
     torch.cuda.synchronize()
     assert bool((c == 2.0).all())
-    print(json.dumps({"calibration": "vector_add_f32", "elems": CALIB_ELEMS, "launches": 3,
-                      "read_bytes_per_launch": 8 * CALIB_ELEMS, "write_bytes_per_launch": 4 * CALIB_ELEMS}),
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(20):
+        g.vector_add(a, b, out=c)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / 20 * 1e3
+    print(json.dumps({"calibration": "vector_add_f32", "elems": CALIB_ELEMS, "launches": 23,
+                      "read_bytes_per_launch": 8 * CALIB_ELEMS, "write_bytes_per_launch": 4 * CALIB_ELEMS,
+                      "avg_launch_us": round(us, 2), "GBps": round(12 * CALIB_ELEMS / us / 1e3, 1)}),
           flush=True)
     return 0
 

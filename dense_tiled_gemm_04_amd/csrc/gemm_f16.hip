@@ -24,6 +24,7 @@ struct Config {
     int loader;              // tile loaders; -1 for skinny
     int group_m;
     int stages;
+    int bslot, dstride, cslot, wpe;  // tile schedule: barrier slot, copy stride, LDS-write slot, waves/SIMD
     int lds_bytes;
     int threads;
     launch_fn launch[3];     // indexed by epilogue
@@ -49,7 +50,7 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
 // (register loader), waves per SIMD WPE.
 #define TILE_CFG(BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, NAME)                         \
     Config {                                                                                       \
-        NAME, KIND_TILE, BM, BN, BK, WM, WN, LOADER, G, ST,                                        \
+        NAME, KIND_TILE, BM, BN, BK, WM, WN, LOADER, G, ST, BS, DS, CS, WPE,                       \
             TilePipeCfg<BM, BN, BK, WM, WN, ST>::LDS_BYTES, WM * WN * 64,                          \
         {                                                                                          \
             launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, 0>,                    \
@@ -60,37 +61,27 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
 
 #define SKINNY_CFG(MB, ST, NAME)                                                                    \
     Config {                                                                                       \
-        NAME, KIND_SKINNY, 16 * MB, SK_BN, SK_BK, 1, SK_WAVES, -1, 1, ST,                          \
+        NAME, KIND_SKINNY, 16 * MB, SK_BN, SK_BK, 1, SK_WAVES, -1, 1, ST, 0, 0, 0, 1,              \
             ST * (16 * MB * SK_BK * 2 + SK_BK * SK_BN * 2), SK_WAVES * 64,                         \
         {                                                                                          \
             launch_skinny<MB, ST, 0>, launch_skinny<MB, ST, 1>, launch_skinny<MB, ST, 2>           \
         }                                                                                          \
     }
 
-const Config kConfigs[] = {
-    TILE_CFG(256, 256, 64, 2, 2, 2, 4, 3, 2, LOAD_DMA, 0, 1, "dma_256x256x64_w2x2_s2_g4"),   // 0
-    TILE_CFG(256, 256, 64, 2, 2, 2, 4, 3, 2, LOAD_REG, 0, 1, "reg_256x256x64_w2x2_g4"),     // 1
-    TILE_CFG(128, 128, 64, 2, 2, 2, 4, 1, 1, LOAD_DMA, 0, 1, "dma_128x128x64_w2x2_s2_g4"),   // 2
-    TILE_CFG(128, 128, 64, 2, 2, 2, 4, 1, 1, LOAD_REG, 0, 1, "reg_128x128x64_w2x2_g4"),     // 3
-    TILE_CFG(128, 128, 64, 2, 2, 2, 4, 1, 1, LOAD_REG, 0, 2, "reg_128x128x64_w2x2_g4_o2"),  // 4
-    TILE_CFG(256, 128, 64, 2, 2, 2, 4, 3, 2, LOAD_DMA, 0, 1, "dma_256x128x64_w2x2_s2_g4"),   // 5
-    TILE_CFG(256, 128, 64, 2, 2, 2, 4, 3, 2, LOAD_REG, 0, 1, "reg_256x128x64_w2x2_g4"),     // 6
-    SKINNY_CFG(1, 6, "skinny_m16_s6"),                                                       // 7
-    SKINNY_CFG(2, 5, "skinny_m32_s5"),                                                       // 8
-    SKINNY_CFG(4, 4, "skinny_m64_s4"),                                                       // 9
-};
-constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
+// The configuration table and the per-shape-class defaults (SEL_*) come from
+// a generated include: the offline sweep (sweep.py) writes config_table.inc.
+// A different table can be compiled in with -DGEMM_F16_CONFIG_TABLE="file".
+#ifndef GEMM_F16_CONFIG_TABLE
+#define GEMM_F16_CONFIG_TABLE "config_table.inc"
+#endif
+#include GEMM_F16_CONFIG_TABLE
 
-enum DefaultIdx {
-    CFG_T256_DMA = 0,
-    CFG_T256_REG = 1,
-    CFG_T128_DMA = 2,
-    CFG_T128_REG = 3,
-    CFG_T128_REG_O2 = 4,
-    CFG_SKINNY16 = 7,
-    CFG_SKINNY32 = 8,
-    CFG_SKINNY64 = 9,
-};
+const Config kConfigs[] = {GEMM_F16_CONFIGS};
+constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
+static_assert(SEL_SKINNY16 < kNumConfigs && SEL_SKINNY32 < kNumConfigs && SEL_SKINNY64 < kNumConfigs &&
+                  SEL_DMA_BIG < kNumConfigs && SEL_DMA_SMALL < kNumConfigs && SEL_REG_BIG < kNumConfigs &&
+                  SEL_REG_SMALL < kNumConfigs,
+              "shape-class defaults index the table");
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -121,7 +112,8 @@ bool supports(const Config& cfg, const Call& c) {
     const bool vec_ok = aligned(c.A, 16) && aligned(c.B, 16) && aligned(c.C, 16) && c.K % 8 == 0 &&
                         c.N % 8 == 0 && epi_bias_ok;
     if (cfg.kind == KIND_SKINNY) {
-        return vec_ok && c.M <= cfg.bm && c.K * c.N * 2 < (int64_t)INT32_MAX &&
+        // 32-bit buffer offsets: B rows up to K + SK_BK (the last stage's tail) and all of A
+        return vec_ok && c.M <= cfg.bm && (c.K + SK_BK) * c.N * 2 < (int64_t)INT32_MAX &&
                c.M * c.K * 2 < (int64_t)INT32_MAX;
     }
     if (cfg.loader == LOAD_DMA)
@@ -133,14 +125,14 @@ bool supports(const Config& cfg, const Call& c) {
 int pick_default(const Call& c) {
     // skinny M: bandwidth path streaming B once
     if (c.M <= 64) {
-        const int idx = c.M <= 16 ? CFG_SKINNY16 : (c.M <= 32 ? CFG_SKINNY32 : CFG_SKINNY64);
+        const int idx = c.M <= 16 ? SEL_SKINNY16 : (c.M <= 32 ? SEL_SKINNY32 : SEL_SKINNY64);
         if (supports(kConfigs[idx], c)) return idx;
     }
     const int64_t tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256);
-    const bool big = tiles256 >= 256;  // at least one workgroup per CU with 256x256 tiles
-    const int dma = big ? CFG_T256_DMA : CFG_T128_DMA;
+    const bool big = tiles256 >= 256;  // at least one 256x256 tile per CU
+    const int dma = big ? SEL_DMA_BIG : SEL_DMA_SMALL;
     if (supports(kConfigs[dma], c)) return dma;
-    return big ? CFG_T256_REG : CFG_T128_REG_O2;
+    return big ? SEL_REG_BIG : SEL_REG_SMALL;
 }
 
 int run(const Config& cfg, const Call& c, hipStream_t stream) {
@@ -214,10 +206,11 @@ int gemm_f16_config_info(int idx, char* buf, int buflen) {
     int n = snprintf(tmp, sizeof(tmp),
                      "{\"idx\": %d, \"name\": \"%s\", \"kind\": \"%s\", \"bm\": %d, \"bn\": %d, \"bk\": %d, "
                      "\"waves_m\": %d, \"waves_n\": %d, \"loader\": \"%s\", \"group_m\": %d, \"stages\": %d, "
+                     "\"bslot\": %d, \"dstride\": %d, \"cslot\": %d, \"waves_per_simd\": %d, "
                      "\"lds_bytes\": %d, \"threads\": %d}",
                      idx, c.name, c.kind == KIND_TILE ? "tile" : "skinny", c.bm, c.bn, c.bk, c.wm, c.wn,
-                     c.kind == KIND_TILE ? loaders[c.loader] : "lds_dma", c.group_m, c.stages, c.lds_bytes,
-                     c.threads);
+                     c.kind == KIND_TILE ? loaders[c.loader] : "lds_dma", c.group_m, c.stages, c.bslot,
+                     c.dstride, c.cslot, c.wpe, c.lds_bytes, c.threads);
     if (buf && buflen > 0) {
         strncpy(buf, tmp, (size_t)buflen - 1);
         buf[buflen - 1] = '\0';

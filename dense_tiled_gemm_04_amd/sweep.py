@@ -1,0 +1,439 @@
+"""Offline configuration sweep of the gfx950 fp16 GEMM library.
+
+This plays the part of the tutorial's autotuner. That autotuner has a search
+space over tile sizes, K-block, pipeline depth and thread count, drops the
+configurations that exceed the shared-memory budget, then compiles, benches,
+validates and caches each one (news article on TileLang kernel design,
+paragraph on autotuning; blog post "Designing High-Performance GPU Kernels
+with TileLang", section "Step 5"). Here the search happens once, offline, on
+the target GPU, and its outcome is compiled into the library. There is no JIT.
+
+Steps:
+
+1. ``space()`` enumerates kernel configurations. The tile kernel's knobs are
+   block tile, K-block, waves, LDS stages, tile-order group, barrier slot,
+   copy stride, loader and waves per SIMD; the skinny kernel's are rows per
+   workgroup and stages. ``valid()`` mirrors the kernels' static_asserts and
+   applies the budgets: at most 160 KiB of LDS per workgroup (per CU when two
+   workgroups share one), and the 512 registers per lane (VGPR + AGPR) shared
+   by the waves of a SIMD.
+2. ``--build`` writes the whole space into a config-table include and
+   compiles ``libgemm_f16_sweep.so`` from the library's own sources, with
+   -DGEMM_F16_CONFIG_TABLE pointing at that include.
+3. ``--run`` (on the GPU) times every configuration on each sweep workload
+   through the C ABI entry ``gemm_f16_with_config``, as the median of
+   HIP-event-timed launches. It checks each output against a float32
+   PyTorch reference on sampled rows; that check is a screen only, and the
+   library's parity tests compare with the CPU oracle. One JSON record per
+   (config, workload) is appended to the results file, and a restarted run
+   skips the records already there.
+4. ``--select`` picks, for each shape class the dispatcher knows (skinny
+   M <= 16/32/64, LDS-DMA big/small, register loader big/small), the
+   configuration with the lowest geometric-mean time over that class's
+   workloads. It writes csrc/config_table.inc with just those configurations
+   and a Markdown summary of the measurements.
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import json
+import math
+import os
+import subprocess
+import sys
+import time
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+TABLE = os.path.join(CSRC, "config_table.inc")
+SWEEP_LIB = os.path.join(PKG_DIR, "libgemm_f16_sweep.so")
+SWEEP_TABLE = os.path.join(PKG_DIR, "_build", "sweep_space.inc")
+
+LDS_PER_CU = 160 * 1024
+REGS_PER_LANE = 512      # VGPR + AGPR per SIMD lane, shared by the waves resident on the SIMD
+SK_BN, SK_BK, SK_WAVES = 64, 128, 4   # skinny kernel constants (csrc/skinny_kernel.h)
+
+
+@dataclasses.dataclass(frozen=True)
+class Tile:
+    bm: int
+    bn: int
+    bk: int
+    wm: int
+    wn: int
+    stages: int
+    group: int
+    bslot: int
+    dstride: int
+    loader: str          # "dma" | "reg"
+    cslot: int = 0
+    wpe: int = 1         # waves per SIMD (= workgroups per CU, 4-wave workgroups)
+
+    kind = "tile"
+
+    @property
+    def name(self) -> str:
+        n = "%s_%dx%dx%d_w%dx%d_s%d_g%d_b%d_d%d" % (self.loader, self.bm, self.bn, self.bk, self.wm, self.wn,
+                                                   self.stages, self.group, self.bslot, self.dstride)
+        if self.loader == "reg":
+            n += "_c%d" % self.cslot
+        return n + ("_o%d" % self.wpe if self.wpe != 1 else "")
+
+    # derived quantities, as in TilePipeCfg (csrc/tile_pipe_kernel.h)
+    @property
+    def lds_bytes(self) -> int:
+        return self.stages * (self.bm * self.bk * 2 + self.bk * self.bn * 2)
+
+    def derived(self):
+        nw = self.wm * self.wn
+        wtm, wtn = self.bm // self.wm, self.bn // self.wn
+        tm, tn = wtm // 32, wtn // 32
+        ca, cb = self.bk // 8, self.bn // 8
+        ksteps = self.bk // 16
+        a_ins = self.bm * ca // 64 // nw
+        b_ins = self.bk * cb // 64 // nw
+        return dict(nw=nw, wtm=wtm, wtn=wtn, tm=tm, tn=tn, ca=ca, cb=cb, ksteps=ksteps, a_ins=a_ins, b_ins=b_ins,
+                    per_stage=a_ins + b_ins, nmma=tm * tn, nrd=tm + 2 * tn)
+
+    def macro(self) -> str:
+        return "TILE_CFG(%d, %d, %d, %d, %d, %d, %d, %d, %d, %s, %d, %d, \"%s\")" % (
+            self.bm, self.bn, self.bk, self.wm, self.wn, self.stages, self.group, self.bslot, self.dstride,
+            "LOAD_DMA" if self.loader == "dma" else "LOAD_REG", self.cslot, self.wpe, self.name)
+
+
+@dataclasses.dataclass(frozen=True)
+class Skinny:
+    mb: int
+    stages: int
+
+    kind = "skinny"
+    loader = "lds_dma"
+
+    @property
+    def name(self) -> str:
+        return "skinny_m%d_s%d" % (16 * self.mb, self.stages)
+
+    @property
+    def lds_bytes(self) -> int:
+        return self.stages * (16 * self.mb * SK_BK * 2 + SK_BK * SK_BN * 2)
+
+    def macro(self) -> str:
+        return "SKINNY_CFG(%d, %d, \"%s\")" % (self.mb, self.stages, self.name)
+
+
+def pow2(x: int) -> bool:
+    return x > 0 and (x & (x - 1)) == 0
+
+
+def valid(c) -> bool:
+    """The kernels' static_asserts plus the LDS and register budgets."""
+    if isinstance(c, Skinny):
+        b_ins = SK_BK * SK_BN * 2 // 16 // (SK_WAVES * 64)
+        a_ins = 16 * c.mb * SK_BK * 2 // 4 // (SK_WAVES * 64)
+        return c.stages >= 2 and (c.stages - 2) * (a_ins + b_ins) <= 63 and c.lds_bytes <= LDS_PER_CU
+    d = c.derived()
+    if d["ksteps"] % 2 or d["wtm"] % 32 or d["wtn"] % 32 or d["tm"] < 1 or d["tn"] < 1:
+        return False
+    if not (pow2(d["ca"]) and pow2(d["cb"]) and d["cb"] >= 4):
+        return False
+    if (c.bm * d["ca"]) % (64 * d["nw"]) or (c.bk * d["cb"]) % (64 * d["nw"]):
+        return False
+    ps = d["per_stage"]
+    if c.stages < 2 or ps * (c.stages - 1) > 63:
+        return False
+    if c.lds_bytes * c.wpe > LDS_PER_CU:
+        return False
+    last = (d["ksteps"] - 1) * d["nmma"] + c.bslot
+    if not (0 <= c.bslot and c.bslot + 1 < d["nmma"]):
+        return False
+    if not (c.dstride >= 1 and (ps - 1) * c.dstride < last):
+        return False
+    if c.loader == "reg":
+        if c.stages != 2 or c.cslot < 0 or c.cslot + ps > last + 1:
+            return False
+        if c.cslot + (ps - 1) * c.dstride >= d["ksteps"] * d["nmma"]:
+            return False
+    # registers per lane: accumulators + two fragment sets + staging (reg loader) + ~40 of addressing
+    acc = d["tm"] * d["tn"] * 16
+    frags = 2 * (d["tm"] * 4 + d["tn"] * 4)
+    stg = 4 * ps if c.loader == "reg" else 0
+    return acc + frags + stg + 40 <= REGS_PER_LANE // c.wpe
+
+
+def space() -> list:
+    out = []
+    for g in (4, 8):
+        for bs in (1, 3):
+            for ds in (1, 2):
+                out.append(Tile(256, 256, 64, 2, 2, 2, g, bs, ds, "dma"))
+    for st in (2, 3):
+        out.append(Tile(256, 128, 64, 2, 2, st, 4, 3, 2, "dma"))
+        out.append(Tile(128, 256, 64, 2, 2, st, 4, 3, 2, "dma"))
+    for st in (2, 3, 4):
+        out.append(Tile(128, 128, 64, 2, 2, st, 4, 1, 1, "dma"))
+    out.append(Tile(128, 128, 64, 2, 2, 2, 4, 1, 1, "dma", wpe=2))
+    out.append(Tile(128, 128, 128, 2, 2, 2, 4, 1, 1, "dma"))
+    for ds in (1, 2):
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, 3, ds, "reg"))
+    out.append(Tile(256, 128, 64, 2, 2, 2, 4, 3, 2, "reg"))
+    out.append(Tile(128, 256, 64, 2, 2, 2, 4, 3, 2, "reg"))
+    for wpe in (1, 2):
+        out.append(Tile(128, 128, 64, 2, 2, 2, 4, 1, 1, "reg", wpe=wpe))
+    out.append(Tile(128, 128, 128, 2, 2, 2, 4, 1, 1, "reg", wpe=2))
+    for mb, sts in ((1, (4, 6, 8)), (2, (4, 6)), (4, (3, 5))):
+        for st in sts:
+            out.append(Skinny(mb, st))
+    return [c for c in out if valid(c)]
+
+
+CLASSES = ["SEL_SKINNY16", "SEL_SKINNY32", "SEL_SKINNY64", "SEL_DMA_BIG", "SEL_DMA_SMALL", "SEL_REG_BIG",
+           "SEL_REG_SMALL"]
+
+
+def class_of(c, cls: str) -> bool:
+    """Whether configuration c may serve shape class cls.  The skinny classes
+    (M <= 16/32/64, aligned) accept any skinny kernel with enough rows and any
+    LDS-DMA tile configuration; the dispatcher falls back if it cannot run."""
+    if cls.startswith("SEL_SKINNY"):
+        if c.kind == "skinny":
+            return 16 * c.mb >= int(cls[len("SEL_SKINNY"):])
+        return c.loader == "dma"
+    return c.kind == "tile" and c.loader == ("dma" if "_DMA_" in cls else "reg")
+
+
+def emit_table(configs: list, sel: dict, path: str, header: str) -> None:
+    lines = ["// " + l for l in header.splitlines()]
+    lines += ["#define GEMM_F16_CONFIGS \\"]
+    for i, c in enumerate(configs):
+        lines.append("    %s%s  /* %d */" % (c.macro(), "," if i + 1 < len(configs) else "", i)
+                     + (" \\" if i + 1 < len(configs) else ""))
+    for cls in CLASSES:
+        lines.append("#define %s %d" % (cls, sel[cls]))
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def build_sweep_lib(verbose: bool = True) -> str:
+    from dense_tiled_gemm_04_amd import build as libbuild
+
+    configs = space()
+    sel = {}
+    for cls in CLASSES:
+        sel[cls] = next(i for i, c in enumerate(configs) if class_of(c, cls))
+    emit_table(configs, sel, SWEEP_TABLE, "Sweep space (generated by sweep.py --build); not the product table.")
+    cmd = libbuild.compile_cmd(SWEEP_LIB + ".tmp")
+    cmd.insert(1, "-DGEMM_F16_CONFIG_TABLE=\"%s\"" % SWEEP_TABLE)
+    if verbose:
+        print("%d configurations; compiling %s" % (len(configs), SWEEP_LIB), flush=True)
+    t = time.time()
+    r = subprocess.run(cmd, cwd=PKG_DIR, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + r.stderr[-4000:])
+    os.replace(SWEEP_LIB + ".tmp", SWEEP_LIB)
+    if verbose:
+        print("built in %.0f s" % (time.time() - t), flush=True)
+    return SWEEP_LIB
+
+
+# ---------------------------------------------------------------------------
+# workloads of the sweep: name -> (workload id or shape spec, classes it scores)
+# ---------------------------------------------------------------------------
+def sweep_workloads():
+    import workloads as wl
+
+    W = wl.WORKLOADS
+    out = []
+    out.append(("gemm_4096", W["gemm_4096"], {}, ["SEL_DMA_BIG"]))
+    out.append(("mlp_up_8192x16384x4096", W["mlp_up_8192x16384x4096"], {}, ["SEL_DMA_BIG"]))
+    out.append(("gemm_256", W["gemm_256"], {}, ["SEL_DMA_SMALL"]))
+    out.append(("gemm_2048", dataclasses.replace(W["gemm_4096"], name="gemm_2048", M=2048, N=2048, K=2048, seed=5),
+                {}, ["SEL_DMA_SMALL"]))
+    out.append(("ragged_4095x3001x1000", W["ragged_4095x3001x1000"], {}, ["SEL_REG_SMALL"]))
+    out.append(("gemm_4096_offset1", W["gemm_4096"], {"offset": 1}, ["SEL_REG_BIG"]))
+    out.append(("skinny_16x16384x8192", W["skinny_16x16384x8192"], {}, ["SEL_SKINNY16"]))
+    out.append(("skinny_32x16384x8192", dataclasses.replace(W["skinny_16x16384x8192"], name="skinny_32", M=32), {},
+                ["SEL_SKINNY32"]))
+    out.append(("skinny_64x16384x8192", dataclasses.replace(W["skinny_16x16384x8192"], name="skinny_64", M=64), {},
+                ["SEL_SKINNY64"]))
+    return out
+
+
+def _reference_rows(A, B, bias, epilogue, rows):
+    """float32 PyTorch reference of the sampled output rows (a screen, not the oracle)."""
+    import torch
+
+    r = A[rows].float() @ B.float()
+    if epilogue != "none":
+        r = r + bias.float()
+    if epilogue == "bias_gelu":
+        r = torch.nn.functional.gelu(r)
+    return r
+
+
+def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str | None = None) -> None:
+    import ctypes
+    import numpy as np
+    import torch
+    import workloads as wl
+
+    lib = ctypes.CDLL(lib_path)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.gemm_f16_with_config.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, i32, vp]
+    lib.gemm_f16_with_config.restype = i32
+    lib.gemm_f16_config_info.argtypes = [i32, ctypes.c_char_p, i32]
+    n_cfg = lib.gemm_f16_num_configs()
+    infos = []
+    for i in range(n_cfg):
+        buf = ctypes.create_string_buffer(1024)
+        lib.gemm_f16_config_info(i, buf, 1024)
+        infos.append(json.loads(buf.value.decode()))
+    done = set()
+    if os.path.exists(results_path):
+        for line in open(results_path):
+            try:
+                rec = json.loads(line)
+                done.add((rec["config"], rec["workload"]))
+            except ValueError:
+                pass
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    epi_ids = {"none": 0, "bias": 1, "bias_gelu": 2}
+    out = open(results_path, "a")
+    for name, w, opts, classes in sweep_workloads():
+        if only and name not in only.split(","):
+            continue
+        A, B, bias = wl.make_inputs(w)
+        off = opts.get("offset", 0)
+
+        def place(x):
+            t = torch.empty(x.size + off, dtype=torch.float16, device=dev)
+            t[off:] = torch.from_numpy(np.ascontiguousarray(x).reshape(-1)).to(dev)
+            return t[off:].view(*x.shape)
+
+        dA, dB = place(A), place(B)
+        db = place(bias) if bias is not None else None
+        cbuf = torch.empty(w.M * w.N + off, dtype=torch.float16, device=dev)
+        dC = cbuf[off:].view(w.M, w.N)
+        rng = np.random.default_rng(0)
+        rows = sorted(set(list(range(min(w.M, 16))) + list(range(max(0, w.M - 16), w.M)) +
+                      list(rng.integers(0, w.M, 32))))
+        ref = _reference_rows(dA, dB, db, w.epilogue, rows)
+        refh = ref.half().float()
+        epi = epi_ids[w.epilogue]
+        for i, info in enumerate(infos):
+            if (info["name"], name) in done:
+                continue
+            args = (i, w.M, w.N, w.K, dA.data_ptr(), dB.data_ptr(), db.data_ptr() if db is not None else None,
+                    dC.data_ptr(), epi, stream.cuda_stream)
+            st = lib.gemm_f16_with_config(*args)
+            if st == 6:  # GEMM_ERR_UNSUPPORTED: this config cannot run this call
+                continue
+            if st != 0:
+                raise RuntimeError("config %s on %s: status %d" % (info["name"], name, st))
+            for _ in range(3):
+                lib.gemm_f16_with_config(*args)
+            torch.cuda.synchronize()
+            evs = []
+            for _ in range(iters):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                lib.gemm_f16_with_config(*args)
+                e1.record(stream)
+                evs.append((e0, e1))
+            torch.cuda.synchronize()
+            us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+            med = us[len(us) // 2]
+            got = dC[rows].float()
+            diff = (got - refh)
+            rel = float(diff.norm() / refh.norm()) if float(refh.norm()) > 0 else float(diff.norm())
+            mx = float((diff.abs() / (1 + refh.abs())).max())
+            ok = bool(rel <= 2e-3 and mx <= 1e-2 and not torch.isnan(got).any())
+            rec = {"config": info["name"], "idx": i, "workload": name, "classes": classes, "median_us": med,
+                   "min_us": us[0], "tflops": 2.0 * w.M * w.N * w.K / med / 1e6, "rel_fro_vs_fp32": rel,
+                   "max_elem_vs_fp32": mx, "ok": ok, "info": info}
+            out.write(json.dumps(rec) + "\n")
+            out.flush()
+            print("%-28s %-48s %9.1f us %7.1f TF %s" % (name, info["name"], med, rec["tflops"],
+                                                        "ok" if ok else "FAIL rel=%.2e" % rel), flush=True)
+        del dA, dB, db, cbuf, dC
+        torch.cuda.empty_cache()
+    out.close()
+
+
+def select(results_path: str, table_path: str = TABLE, summary_path: str | None = None) -> dict:
+    recs = [json.loads(l) for l in open(results_path) if l.strip()]
+    by_name = {c.name: c for c in space()}
+    chosen, scores = {}, {}
+    for cls in CLASSES:
+        wls = sorted({r["workload"] for r in recs if cls in r["classes"]})
+        best = None
+        for name, c in by_name.items():
+            if not class_of(c, cls):
+                continue
+            ts = [r["median_us"] for r in recs if r["config"] == name and r["workload"] in wls]
+            oks = [r["ok"] for r in recs if r["config"] == name and r["workload"] in wls]
+            if len(ts) != len(wls) or not all(oks) or not ts:
+                continue
+            g = math.exp(sum(math.log(t) for t in ts) / len(ts))
+            if best is None or g < best[0]:
+                best = (g, name)
+        if best is None:
+            raise RuntimeError("no valid configuration measured for %s" % cls)
+        chosen[cls] = best[1]
+        scores[cls] = best[0]
+    names = []
+    for cls in CLASSES:
+        if chosen[cls] not in names:
+            names.append(chosen[cls])
+    configs = [by_name[n] for n in names]
+    sel = {cls: names.index(chosen[cls]) for cls in CLASSES}
+    emit_table(configs, sel, table_path,
+               "Generated by dense_tiled_gemm_04_amd/sweep.py --select from the sweep results\n"
+               "(%s). Do not edit by hand; rerun the sweep." % os.path.basename(results_path))
+    if summary_path:
+        lines = ["# Offline sweep of the tile and skinny kernels", "",
+                 "Median of %s HIP-event-timed launches per (configuration, workload) on one MI355X;" % "20",
+                 "outputs screened against a float32 PyTorch reference on sampled rows (parity proper is the",
+                 "oracle tests). Command: `python -m dense_tiled_gemm_04_amd.sweep --run RESULTS` on the GPU, then",
+                 "`--select RESULTS` here.", "", "## Chosen per shape class", "",
+                 "| class | configuration | geo-mean us |", "|---|---|---|"]
+        for cls in CLASSES:
+            lines.append("| %s | %s | %.1f |" % (cls, chosen[cls], scores[cls]))
+        lines += ["", "## All measurements", "", "| workload | configuration | median us | TFLOP/s | screen |",
+                  "|---|---|---|---|---|"]
+        for r in sorted(recs, key=lambda r: (r["workload"], r["median_us"])):
+            lines.append("| %s | %s | %.1f | %.1f | %s |" % (r["workload"], r["config"], r["median_us"], r["tflops"],
+                                                             "ok" if r["ok"] else "FAIL"))
+        with open(summary_path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+    return chosen
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--list", action="store_true", help="print the sweep space")
+    ap.add_argument("--build", action="store_true", help="compile libgemm_f16_sweep.so with the whole space")
+    ap.add_argument("--run", metavar="RESULTS", help="time every configuration (GPU); JSONL, resumable")
+    ap.add_argument("--only", default=None, help="comma-separated sweep workload names for --run")
+    ap.add_argument("--select", metavar="RESULTS", help="pick per-class defaults, write csrc/config_table.inc")
+    ap.add_argument("--summary", default=None, help="Markdown summary path for --select")
+    a = ap.parse_args()
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    if a.list:
+        for c in space():
+            print("%-50s lds=%6d" % (c.name, c.lds_bytes))
+    if a.build:
+        build_sweep_lib()
+    if a.run:
+        run(a.run, only=a.only)
+    if a.select:
+        print(json.dumps(select(a.select, summary_path=a.summary), indent=1))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
