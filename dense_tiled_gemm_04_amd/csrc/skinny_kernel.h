@@ -8,7 +8,8 @@
 //  * one workgroup = 4 wave64s owns a 64-column panel of B/C and all of K;
 //    the grid has ceil(N / 64) workgroups (256 for N = 16384: one per CU);
 //  * B and A reach LDS by asynchronous LDS-DMA (buffer_load ... lds), STAGES
-//    deep, so the bytes in flight do not occupy VGPRs;
+//    deep, so the bytes in flight do not occupy VGPRs; B, read exactly once,
+//    is loaded non-temporal;
 //  * B rows past K fall outside the buffer range and read as zero, which
 //    zeroes a ragged K tail without per-lane masks; A rows are range-masked
 //    at the same granularity (see below);
@@ -92,7 +93,7 @@ gemm_skinny_kernel(GemmArgs p) {
         const uint32_t b_so = (uint32_t)kbase * N * 2;
 #pragma unroll
         for (int i = 0; i < B_INS; ++i)
-            dma_buffer_16(b_rsrc, b_off[i] + b_so, b_lds0 + s * B_STAGE + i * SK_WAVES * 64 * 16);
+            dma_buffer_16_nt(b_rsrc, b_off[i] + b_so, b_lds0 + s * B_STAGE + i * SK_WAVES * 64 * 16);
 #pragma unroll
         for (int i = 0; i < A_INS; ++i) {
             const uint32_t off = (kbase + a_kcol[i] < K) ? a_off[i] + (uint32_t)kbase * 2 : 0x80000000u;

@@ -1,0 +1,100 @@
+"""The offline sweep's host logic: search space, budget filter, table emission
+and per-class selection (no GPU; synthetic timing records)."""
+import json
+import os
+import re
+
+import pytest
+
+from dense_tiled_gemm_04_amd import sweep
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_budget_filter():
+    # 256x256x64 double-buffered: 128 KiB of LDS, fits; three stages: 192 KiB, rejected
+    assert sweep.valid(sweep.Tile(256, 256, 64, 2, 2, 2, 4, 3, 2, "dma"))
+    assert not sweep.valid(sweep.Tile(256, 256, 64, 2, 2, 3, 4, 3, 2, "dma"))
+    # two 128x128x64 double-buffered workgroups per CU: 2 x 64 KiB fits; 2 x 96 KiB does not
+    assert sweep.valid(sweep.Tile(128, 128, 64, 2, 2, 2, 4, 1, 1, "dma", wpe=2))
+    assert not sweep.valid(sweep.Tile(128, 128, 64, 2, 2, 3, 4, 1, 1, "dma", wpe=2))
+    # 256 accumulators per lane cannot share a SIMD with a second wave
+    assert not sweep.valid(sweep.Tile(256, 256, 64, 2, 2, 2, 4, 3, 2, "dma", wpe=2))
+    # skinny: M <= 16 with 8 stages uses the whole 160 KiB; 9 would not fit
+    assert sweep.valid(sweep.Skinny(1, 8)) and not sweep.valid(sweep.Skinny(1, 9))
+
+
+def test_schedule_constraints_mirror_kernel():
+    # barrier slot must leave room in the last k-step for the next stage's reads
+    assert not sweep.valid(sweep.Tile(128, 128, 64, 2, 2, 2, 4, 3, 1, "dma"))   # 4 MFMAs per k-step
+    # every copy must be issued before the stage's barrier
+    assert not sweep.valid(sweep.Tile(128, 128, 64, 2, 2, 2, 4, 1, 4, "dma"))
+    # register loader is double-buffered only
+    assert not sweep.valid(sweep.Tile(128, 128, 64, 2, 2, 3, 4, 1, 1, "reg"))
+    # odd number of k16-steps per stage breaks the fragment ping-pong
+    assert not sweep.valid(sweep.Tile(128, 128, 16, 2, 2, 2, 4, 1, 1, "dma"))
+
+
+def test_space_is_valid_and_unique():
+    sp = sweep.space()
+    assert len(sp) >= 20
+    names = [c.name for c in sp]
+    assert len(set(names)) == len(names)
+    assert all(sweep.valid(c) for c in sp)
+    assert all(c.lds_bytes <= 160 * 1024 for c in sp)
+    for cls in sweep.CLASSES:
+        assert any(sweep.class_of(c, cls) for c in sp), cls
+
+
+def _table_entries(path):
+    src = open(path).read()
+    tiles = re.findall(r'TILE_CFG\(([^)]*)\)', src)
+    skinny = re.findall(r'SKINNY_CFG\(([^)]*)\)', src)
+    sel = dict(re.findall(r'#define (SEL_\w+) (\d+)', src))
+    return tiles, skinny, {k: int(v) for k, v in sel.items()}
+
+
+def test_product_table_entries_are_in_budget():
+    tiles, skinny, sel = _table_entries(os.path.join(ROOT, "dense_tiled_gemm_04_amd", "csrc", "config_table.inc"))
+    n = len(tiles) + len(skinny)
+    assert set(sel) == set(sweep.CLASSES) and all(0 <= v < n for v in sel.values())
+    for t in tiles:
+        f = [x.strip() for x in t.split(",")]
+        c = sweep.Tile(*map(int, f[:9]), "dma" if f[9] == "LOAD_DMA" else "reg", int(f[10]), int(f[11]))
+        assert sweep.valid(c), c
+        assert f[12].strip('"') == c.name
+    for s in skinny:
+        f = [x.strip() for x in s.split(",")]
+        assert sweep.valid(sweep.Skinny(int(f[0]), int(f[1])))
+
+
+def test_select_picks_fastest_valid_per_class(tmp_path):
+    sp = sweep.space()
+    recs = []
+    # synthetic timings: time grows with the config's position, except one clear winner per class
+    winners = {}
+    for cls in sweep.CLASSES:
+        winners[cls] = [c for c in sp if sweep.class_of(c, cls)][-1].name
+    for name, w, opts, classes in sweep.sweep_workloads():
+        for i, c in enumerate(sp):
+            if not any(sweep.class_of(c, cls) for cls in classes):
+                continue
+            t = 100.0 + i
+            if any(winners[cls] == c.name for cls in classes):
+                t = 10.0
+            recs.append({"config": c.name, "workload": name, "classes": classes, "median_us": t, "ok": True,
+                         "tflops": 1.0})
+    # a faster configuration whose output failed the screen must never be chosen
+    bad = [c for c in sp if sweep.class_of(c, "SEL_DMA_BIG")][0].name
+    for r in recs:
+        if r["config"] == bad and "SEL_DMA_BIG" in r["classes"]:
+            r["median_us"], r["ok"] = 1.0, False
+    res = tmp_path / "res.jsonl"
+    res.write_text("\n".join(json.dumps(r) for r in recs) + "\n")
+    table = tmp_path / "table.inc"
+    chosen = sweep.select(str(res), table_path=str(table), summary_path=str(tmp_path / "s.md"))
+    for cls in sweep.CLASSES:
+        assert chosen[cls] == winners[cls], cls
+    tiles, skinny, sel = _table_entries(str(table))
+    assert len(tiles) + len(skinny) == len(set(chosen.values()))
+    assert (tmp_path / "s.md").read_text().count("|") > 10
