@@ -25,16 +25,18 @@ struct Config {
     int group_m;
     int stages;
     int bslot, dstride, cslot, wpe;  // tile schedule: barrier slot, copy stride, LDS-write slot, waves/SIMD
+    int mfma, spread;                // tile MFMA shape (32: 32x32x16, 16: 16x16x32), spread LDS reads
     int lds_bytes;
     int threads;
     launch_fn launch[3];     // indexed by epilogue
 };
 
-template <int BM, int BN, int BK, int WM, int WN, int ST, int G, int BS, int DS, int LOADER, int CS, int WPE, int EPI>
+template <int BM, int BN, int BK, int WM, int WN, int ST, int G, int BS, int DS, int LOADER, int CS, int WPE, int MF,
+          int SP, int EPI>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(WM * WN * 64);
-    hipLaunchKernelGGL((gemm_tile_pipe_kernel<BM, BN, BK, WM, WN, ST, G, EPI, BS, DS, LOADER, CS, WPE>), grid, block, 0, s,
-                       a);
+    hipLaunchKernelGGL((gemm_tile_pipe_kernel<BM, BN, BK, WM, WN, ST, G, EPI, BS, DS, LOADER, CS, WPE, MF, SP>), grid,
+                       block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -47,21 +49,22 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
 
 // Tile config: block tile BM x BN x BK, WM x WN waves, ST LDS stages, tile
 // order group G, barrier slot BS, copy stride DS, loader, LDS-write slot CS
-// (register loader), waves per SIMD WPE.
-#define TILE_CFG(BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, NAME)                         \
+// (register loader), waves per SIMD WPE, MFMA shape MF (32 or 16), spread
+// LDS reads SP.
+#define TILE_CFG(BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, NAME)                 \
     Config {                                                                                       \
-        NAME, KIND_TILE, BM, BN, BK, WM, WN, LOADER, G, ST, BS, DS, CS, WPE,                       \
-            TilePipeCfg<BM, BN, BK, WM, WN, ST>::LDS_BYTES, WM * WN * 64,                          \
+        NAME, KIND_TILE, BM, BN, BK, WM, WN, LOADER, G, ST, BS, DS, CS, WPE, MF, SP,               \
+            TilePipeCfg<BM, BN, BK, WM, WN, ST, MF>::LDS_BYTES, WM * WN * 64,                      \
         {                                                                                          \
-            launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, 0>,                    \
-                launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, 1>,                \
-                launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, 2>                 \
+            launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, 0>,            \
+                launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, 1>,        \
+                launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, 2>         \
         }                                                                                          \
     }
 
 #define SKINNY_CFG(MB, ST, NAME)                                                                    \
     Config {                                                                                       \
-        NAME, KIND_SKINNY, 16 * MB, SK_BN, SK_BK, 1, SK_WAVES, -1, 1, ST, 0, 0, 0, 1,              \
+        NAME, KIND_SKINNY, 16 * MB, SK_BN, SK_BK, 1, SK_WAVES, -1, 1, ST, 0, 0, 0, 1, 16, 0,       \
             ST * (16 * MB * SK_BK * 2 + SK_BK * SK_BN * 2), SK_WAVES * 64,                         \
         {                                                                                          \
             launch_skinny<MB, ST, 0>, launch_skinny<MB, ST, 1>, launch_skinny<MB, ST, 2>           \
@@ -207,10 +210,10 @@ int gemm_f16_config_info(int idx, char* buf, int buflen) {
                      "{\"idx\": %d, \"name\": \"%s\", \"kind\": \"%s\", \"bm\": %d, \"bn\": %d, \"bk\": %d, "
                      "\"waves_m\": %d, \"waves_n\": %d, \"loader\": \"%s\", \"group_m\": %d, \"stages\": %d, "
                      "\"bslot\": %d, \"dstride\": %d, \"cslot\": %d, \"waves_per_simd\": %d, "
-                     "\"lds_bytes\": %d, \"threads\": %d}",
+                     "\"mfma\": %d, \"spread\": %d, \"lds_bytes\": %d, \"threads\": %d}",
                      idx, c.name, c.kind == KIND_TILE ? "tile" : "skinny", c.bm, c.bn, c.bk, c.wm, c.wn,
                      c.kind == KIND_TILE ? loaders[c.loader] : "lds_dma", c.group_m, c.stages, c.bslot,
-                     c.dstride, c.cslot, c.wpe, c.lds_bytes, c.threads);
+                     c.dstride, c.cslot, c.wpe, c.mfma, c.spread, c.lds_bytes, c.threads);
     if (buf && buflen > 0) {
         strncpy(buf, tmp, (size_t)buflen - 1);
         buf[buflen - 1] = '\0';

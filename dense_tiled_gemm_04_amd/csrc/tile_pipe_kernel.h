@@ -8,15 +8,21 @@
 // tiled GEMM and on the fused epilogue.
 //
 // What is specific to CDNA4:
-//  * MFMA. v_mfma_f32_32x32x16_f16, issued as C^T = B^T . A^T, so each lane
-//    holds 4 consecutive columns of one output row. A fragments come from
-//    ds_read_b128. B fragments come from row-major [k][n] LDS by the
-//    transpose read ds_read_b64_tr_b16. Both tiles are XOR-swizzled in
-//    16-byte chunks so that the reads are free of bank conflicts.
+//  * MFMA. v_mfma_f32_32x32x16_f16 (MF = 32) or v_mfma_f32_16x16x32_f16
+//    (MF = 16). The 16x16 form moves about a fifth less register data per
+//    FLOP (a quarter of the accumulator per MFMA), which lets the chip hold a
+//    higher clock under its power limit. Either is issued as
+//    C^T = B^T . A^T, so each lane holds 4 consecutive columns of one output
+//    row. A fragments come from ds_read_b128. B fragments come from row-major
+//    [k][n] LDS by the transpose read ds_read_b64_tr_b16. Both tiles are
+//    XOR-swizzled in 16-byte chunks so that the reads are free of bank
+//    conflicts.
 //  * Schedule. Every MFMA slot is fenced with sched_barrier, so the issue
 //    order is exactly the one written here:
 //      slot i of a k-step: MFMA i, the LDS reads scheduled for slot i (the
-//      next k-step's fragments), and the copy work scheduled for slot i.
+//      next k-step's fragments, either one per slot from slot 0 or, with
+//      SPREAD, spread evenly over the k-step), and the copy work scheduled
+//      for slot i.
 //    At slot BSLOT of a stage's last k-step, the wave waits for its part of
 //    stage kt+1, and one barrier publishes it. All LDS reads of stage kt have
 //    landed by then, so the same barrier also frees stage kt's buffer. The
@@ -53,31 +59,41 @@ __device__ __forceinline__ int swz_a(int r) {
     constexpr int CA = BK / 8, RPW = 128 / BK;
     return (r / RPW) & (CA - 1);
 }
-// B-tile swizzle: logical chunk c of k-row kr lives at c ^ swz_b(kr).  A
-// transpose read touches 4 consecutive k-rows x 64 bytes per half-wave; XOR
-// by 4*(kr mod 4) chunks puts those 16 chunks in distinct bank groups.
-template <int BN>
+// B-tile swizzle: logical chunk c of k-row kr lives at c ^ swz_b(kr).
+//  MF = 32: a transpose read touches 4 consecutive k-rows x 64 bytes per
+//  half-wave; XOR by 4*(kr mod 4) chunks puts those 16 chunks in distinct
+//  bank groups.
+//  MF = 16: a half-wave touches rows {8g + 4h + j : j < 4} for two
+//  consecutive g, two chunks per row; XOR by an even value made of (kr mod 4)
+//  and bit 3 of kr spreads those 16 chunks over distinct bank groups.
+template <int BN, int MF>
 __device__ __forceinline__ int swz_b(int kr) {
     constexpr int CB = BN / 8;
-    return (4 * (kr & 3)) & (CB - 1);
+    if constexpr (MF == 32) {
+        return (4 * (kr & 3)) & (CB - 1);
+    } else {
+        return (2 * ((kr & 3) | (((kr >> 3) & 1) << 2))) & (CB - 1);
+    }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int MF = 32>
 struct TilePipeCfg {
     static constexpr int NW = WM * WN;
     static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave sub-tile
-    static constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA blocks per wave
+    static constexpr int TM = WTM / MF, TN = WTN / MF;  // MFxMF MFMA blocks per wave
+    static constexpr int KS = MF == 32 ? 16 : 32;       // k per MFMA
     static constexpr int CA = BK / 8, CB = BN / 8;      // 16-byte chunks per A / B row
     static constexpr int A_STAGE = BM * BK * 2, B_STAGE = BK * BN * 2;
     static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE);
-    static constexpr int KSTEPS = BK / 16;              // k16 steps per stage
+    static constexpr int KSTEPS = BK / KS;              // k-steps per stage
     static constexpr int A_INS = BM * CA / 64 / NW;     // 16-byte copies per lane and stage
     static constexpr int B_INS = BK * CB / 64 / NW;
     static constexpr int PER_STAGE = A_INS + B_INS;
     static constexpr int NMMA = TM * TN;                // MFMAs (slots) per k-step
     static constexpr int NRD = TM + 2 * TN;             // LDS reads per k-step
-    static_assert(KSTEPS % 2 == 0, "even k16-steps per stage (fragment ping-pong)");
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile of whole 32x32 blocks");
+    static_assert(MF == 32 || MF == 16, "MFMA shape");
+    static_assert(KSTEPS % 2 == 0, "even k-steps per stage (fragment ping-pong)");
+    static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile of whole MFMA blocks");
     static_assert((CA & (CA - 1)) == 0 && (CB & (CB - 1)) == 0 && CB >= 4, "chunk counts");
     static_assert((BM * CA) % (64 * NW) == 0 && (BK * CB) % (64 * NW) == 0, "copy split over waves");
     static_assert(STAGES >= 2 && PER_STAGE * (STAGES - 1) <= 63, "vmcnt range");
@@ -85,20 +101,21 @@ struct TilePipeCfg {
 };
 
 // Slot of LDS read j (0 <= j < NRD) among `avail` slots starting at `first`:
-// one per slot while they fit, otherwise spread evenly.
-template <int NRD>
+// one per slot while they fit (unless SPREAD), otherwise spread evenly.
+template <int NRD, int SPREAD>
 __device__ constexpr int read_slot(int j, int first, int avail) {
-    return first + (NRD <= avail ? j : j * avail / NRD);
+    return first + (NRD <= avail && !SPREAD ? j : j * avail / NRD);
 }
 
 typedef f16x8 f16x8_u __attribute__((aligned(2)));
 typedef f16x4 f16x4_u __attribute__((aligned(2)));
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int GROUP_M, int EPI, int BSLOT, int DSTRIDE,
-          int LOADER, int CSLOT, int WPE>
+          int LOADER, int CSLOT, int WPE, int MF, int SPREAD>
 __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 gemm_tile_pipe_kernel(GemmArgs p) {
-    using Cfg = TilePipeCfg<BM, BN, BK, WM, WN, STAGES>;
+    using Cfg = TilePipeCfg<BM, BN, BK, WM, WN, STAGES, MF>;
+    constexpr int KS = Cfg::KS;
     constexpr int NW = Cfg::NW, WTM = Cfg::WTM, WTN = Cfg::WTN, TM = Cfg::TM, TN = Cfg::TN;
     constexpr int CA = Cfg::CA, CB = Cfg::CB, A_STAGE = Cfg::A_STAGE, B_STAGE = Cfg::B_STAGE;
     constexpr int KSTEPS = Cfg::KSTEPS, A_INS = Cfg::A_INS, B_INS = Cfg::B_INS, PER_STAGE = Cfg::PER_STAGE;
@@ -127,24 +144,29 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     const int KT = (K + BK - 1) / BK;
 
     // Fragment read offsets (bytes within a stage).
-    // A (MFMA operand b): lane holds A[m = row(lane)][k = 16 kk + 8 (lane / 32) .. +7].
+    // A (MFMA operand b): lane holds A[m = row(lane)][k = KS kk + 8 (lane / MF) .. +7],
+    // row(lane) = lane % MF within the block.
     int a_rd[KSTEPS];
     {
-        const int row = wm * WTM + (lane & 31);
+        const int row = wm * WTM + (lane % MF);
         const int s = swz_a<BK>(row);
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) a_rd[kk] = row * BK * 2 + (((2 * kk + (lane >> 5)) ^ s) << 4);
+        for (int kk = 0; kk < KSTEPS; ++kk)
+            a_rd[kk] = row * BK * 2 + ((((KS / 8) * kk + lane / MF) ^ s) << 4);
     }
     // B (MFMA operand a) by transpose reads: lane L = 16g + 4j + q gives the
     // address of B[kb + j][nb + 4q .. 4q+3] and receives B[kb + 0..3][nb + L%16].
+    // MF = 32: kb = 8 (g / 2) (+ 16 kk + 4 h), nb = 16 (g % 2) within a 32-column block;
+    // MF = 16: kb = 8 g (+ 32 kk + 4 h), nb = 0 within a 16-column block.
+    // Neither the k-step nor the half h changes the swizzle of the row.
     int b_rd[TN];
     {
         const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
-        const int kr = 8 * (g >> 1) + j;
+        const int kr = (MF == 32 ? 8 * (g >> 1) : 8 * g) + j;
 #pragma unroll
         for (int ni = 0; ni < TN; ++ni) {
-            const int nl = wn * WTN + ni * 32 + 16 * (g & 1) + 4 * q;
-            b_rd[ni] = kr * BN * 2 + (((nl >> 3) ^ swz_b<BN>(kr)) << 4) + ((nl & 7) << 1);
+            const int nl = wn * WTN + ni * MF + (MF == 32 ? 16 * (g & 1) : 0) + 4 * q;
+            b_rd[ni] = kr * BN * 2 + (((nl >> 3) ^ swz_b<BN, MF>(kr)) << 4) + ((nl & 7) << 1);
         }
     }
 
@@ -170,7 +192,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
         const int P = (i * NW + wave) * 64 + lane;
-        const int kr = P / CB, c = (P % CB) ^ swz_b<BN>(kr);
+        const int kr = P / CB, c = (P % CB) ^ swz_b<BN, MF>(kr);
         if constexpr (LOADER == LOAD_DMA) {
             const int n = min(n0 + 8 * c, N - 8) - n0;
             b_off[i] = (uint32_t)((kr * N + n) * 2);
@@ -230,13 +252,15 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         *(GK_LDS f16x8*)dst = stg[LOADER == LOAD_REG ? j : 0];
     };
 
-    f32x16 acc[TM][TN];
+    constexpr int NACC = MF * MF / 64;  // fp32 accumulators per lane and block
+    typedef float accv __attribute__((ext_vector_type(NACC)));
+    accv acc[TM][TN];
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
         for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+            for (int r = 0; r < NACC; ++r) acc[mi][ni][r] = 0.0f;
 
     // Two fragment sets: the reads of k-step kk+1 land in one while the MFMAs
     // of k-step kk consume the other.  Read j: 0 -> A[0]; 1..2TN -> halves of
@@ -250,16 +274,20 @@ gemm_tile_pipe_kernel(GemmArgs p) {
             fa[set][0] = *(const GK_LDS f16x8*)(As + a_rd[kk]);
         } else if (j <= 2 * TN) {
             const int ni = (j - 1) / 2, h = (j - 1) % 2;
-            fb[set][ni][h] = lds_read_tr16_b64(Bs + b_rd[ni] + (16 * kk + 4 * h) * BN * 2);
+            fb[set][ni][h] = lds_read_tr16_b64(Bs + b_rd[ni] + (KS * kk + 4 * h) * BN * 2);
         } else {
             const int mi = j - 2 * TN;
-            fa[set][mi] = *(const GK_LDS f16x8*)(As + a_rd[kk] + mi * 32 * BK * 2);
+            fa[set][mi] = *(const GK_LDS f16x8*)(As + a_rd[kk] + mi * MF * BK * 2);
         }
     };
     auto mma_op = [&](int set, int i) {
         const int mi = i / TN, ni = i % TN;
         const f16x8 b = __builtin_shufflevector(fb[set][ni][0], fb[set][ni][1], 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, fa[set][mi], acc[mi][ni], 0, 0, 0);
+        if constexpr (MF == 32) {
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, fa[set][mi], acc[mi][ni], 0, 0, 0);
+        } else {
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, fa[set][mi], acc[mi][ni], 0, 0, 0);
+        }
     };
 
     // Prologue: stages 0 .. STAGES-2 in LDS (or in flight), then stage 0's
@@ -323,7 +351,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
                 if (kk + 1 < KSTEPS) {
 #pragma unroll
                     for (int j = 0; j < NRD; ++j)
-                        if (read_slot<NRD>(j, 0, NMMA) == i) read_op(nxt, j, s, kk + 1);
+                        if (read_slot<NRD, SPREAD>(j, 0, NMMA) == i) read_op(nxt, j, s, kk + 1);
                 } else if (has_next) {
                     if (i == BSLOT) {
                         if constexpr (LOADER == LOAD_DMA) {
@@ -337,7 +365,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
                     }
 #pragma unroll
                     for (int j = 0; j < NRD; ++j)
-                        if (read_slot<NRD>(j, BSLOT + 1, NMMA - BSLOT - 1) == i) read_op(nxt, j, sn, 0);
+                        if (read_slot<NRD, SPREAD>(j, BSLOT + 1, NMMA - BSLOT - 1) == i) read_op(nxt, j, sn, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -353,15 +381,18 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     }
     for (; kt < KT; ++kt) stage.template operator()<0>(kt);
 
-    // Epilogue on the accumulators, one write of C.  Lane l, register
-    // 4*r4 + e of block (mi, ni) holds
-    //   C[m0 + wm*WTM + mi*32 + l%32][n0 + wn*WTN + ni*32 + 8*r4 + 4*(l/32) + e].
+    // Epilogue on the accumulators, one write of C.  Lane l holds, of block
+    // (mi, ni), the 4 consecutive columns
+    //   MF = 32, register 4*r4 + e: C[mi*32 + l%32][ni*32 + 8*r4 + 4*(l/32) + e]
+    //   MF = 16, register e:        C[mi*16 + l%16][ni*16 + 4*(l/16) + e]
+    // relative to the wave's sub-tile origin (m0 + wm*WTM, n0 + wn*WTN).
     // With LOAD_DMA, N % 8 == 0, so a column quad is all in or all out.
+    constexpr int NQ = NACC / 4;  // column quads per lane and block
 #pragma unroll
     for (int ni = 0; ni < TN; ++ni) {
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const int n = n0 + wn * WTN + ni * 32 + 8 * r4 + 4 * (lane >> 5);
+        for (int r4 = 0; r4 < NQ; ++r4) {
+            const int n = n0 + wn * WTN + ni * MF + (MF == 32 ? 8 * r4 + 4 * (lane >> 5) : 4 * (lane >> 4));
             const bool quad = n + 4 <= N;
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (EPI != EPI_NONE) {
@@ -377,7 +408,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
             }
 #pragma unroll
             for (int mi = 0; mi < TM; ++mi) {
-                const int m = m0 + wm * WTM + mi * 32 + (lane & 31);
+                const int m = m0 + wm * WTM + mi * MF + (lane % MF);
                 if (m >= M || n >= N) continue;
                 f16x4 o;
 #pragma unroll

@@ -70,6 +70,8 @@ class Tile:
     loader: str          # "dma" | "reg"
     cslot: int = 0
     wpe: int = 1         # waves per SIMD (= workgroups per CU, 4-wave workgroups)
+    mf: int = 32         # MFMA shape: 32 -> 32x32x16, 16 -> 16x16x32
+    spread: int = 0      # LDS reads spread evenly over a k-step's slots
 
     kind = "tile"
 
@@ -79,7 +81,9 @@ class Tile:
                                                    self.stages, self.group, self.bslot, self.dstride)
         if self.loader == "reg":
             n += "_c%d" % self.cslot
-        return n + ("_o%d" % self.wpe if self.wpe != 1 else "")
+        n += "_o%d" % self.wpe if self.wpe != 1 else ""
+        n += "_m16" if self.mf == 16 else ""
+        return n + ("_sp" if self.spread else "")
 
     # derived quantities, as in TilePipeCfg (csrc/tile_pipe_kernel.h)
     @property
@@ -89,18 +93,18 @@ class Tile:
     def derived(self):
         nw = self.wm * self.wn
         wtm, wtn = self.bm // self.wm, self.bn // self.wn
-        tm, tn = wtm // 32, wtn // 32
+        tm, tn = wtm // self.mf, wtn // self.mf
         ca, cb = self.bk // 8, self.bn // 8
-        ksteps = self.bk // 16
+        ksteps = self.bk // (16 if self.mf == 32 else 32)
         a_ins = self.bm * ca // 64 // nw
         b_ins = self.bk * cb // 64 // nw
         return dict(nw=nw, wtm=wtm, wtn=wtn, tm=tm, tn=tn, ca=ca, cb=cb, ksteps=ksteps, a_ins=a_ins, b_ins=b_ins,
-                    per_stage=a_ins + b_ins, nmma=tm * tn, nrd=tm + 2 * tn)
+                    per_stage=a_ins + b_ins, nmma=tm * tn, nrd=tm + 2 * tn, nacc=self.mf * self.mf // 64)
 
     def macro(self) -> str:
-        return "TILE_CFG(%d, %d, %d, %d, %d, %d, %d, %d, %d, %s, %d, %d, \"%s\")" % (
+        return "TILE_CFG(%d, %d, %d, %d, %d, %d, %d, %d, %d, %s, %d, %d, %d, %d, \"%s\")" % (
             self.bm, self.bn, self.bk, self.wm, self.wn, self.stages, self.group, self.bslot, self.dstride,
-            "LOAD_DMA" if self.loader == "dma" else "LOAD_REG", self.cslot, self.wpe, self.name)
+            "LOAD_DMA" if self.loader == "dma" else "LOAD_REG", self.cslot, self.wpe, self.mf, self.spread, self.name)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -133,8 +137,10 @@ def valid(c) -> bool:
         b_ins = SK_BK * SK_BN * 2 // 16 // (SK_WAVES * 64)
         a_ins = 16 * c.mb * SK_BK * 2 // 4 // (SK_WAVES * 64)
         return c.stages >= 2 and (c.stages - 2) * (a_ins + b_ins) <= 63 and c.lds_bytes <= LDS_PER_CU
+    if c.mf not in (16, 32):
+        return False
     d = c.derived()
-    if d["ksteps"] % 2 or d["wtm"] % 32 or d["wtn"] % 32 or d["tm"] < 1 or d["tn"] < 1:
+    if d["ksteps"] % 2 or d["wtm"] % c.mf or d["wtn"] % c.mf or d["tm"] < 1 or d["tn"] < 1:
         return False
     if not (pow2(d["ca"]) and pow2(d["cb"]) and d["cb"] >= 4):
         return False
@@ -156,7 +162,7 @@ def valid(c) -> bool:
         if c.cslot + (ps - 1) * c.dstride >= d["ksteps"] * d["nmma"]:
             return False
     # registers per lane: accumulators + two fragment sets + staging (reg loader) + ~40 of addressing
-    acc = d["tm"] * d["tn"] * 16
+    acc = d["tm"] * d["tn"] * d["nacc"]
     frags = 2 * (d["tm"] * 4 + d["tn"] * 4)
     stg = 4 * ps if c.loader == "reg" else 0
     return acc + frags + stg + 40 <= REGS_PER_LANE // c.wpe
@@ -175,6 +181,11 @@ def space() -> list:
         out.append(Tile(128, 128, 64, 2, 2, st, 4, 1, 1, "dma"))
     out.append(Tile(128, 128, 64, 2, 2, 2, 4, 1, 1, "dma", wpe=2))
     out.append(Tile(128, 128, 128, 2, 2, 2, 4, 1, 1, "dma"))
+    for bs, ds in ((3, 3), (8, 4), (8, 2)):
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", mf=16, spread=1))
+    out.append(Tile(256, 256, 64, 2, 2, 2, 8, 8, 4, "dma", mf=16, spread=1))
+    out.append(Tile(128, 128, 64, 2, 2, 3, 4, 3, 2, "dma", mf=16, spread=1))
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 8, 4, "reg", mf=16, spread=1))
     for ds in (1, 2):
         out.append(Tile(256, 256, 64, 2, 2, 2, 4, 3, ds, "reg"))
     out.append(Tile(256, 128, 64, 2, 2, 2, 4, 3, 2, "reg"))
@@ -253,11 +264,12 @@ def sweep_workloads():
                 {}, ["SEL_DMA_SMALL"]))
     out.append(("ragged_4095x3001x1000", W["ragged_4095x3001x1000"], {}, ["SEL_REG_SMALL"]))
     out.append(("gemm_4096_offset1", W["gemm_4096"], {"offset": 1}, ["SEL_REG_BIG"]))
-    out.append(("skinny_16x16384x8192", W["skinny_16x16384x8192"], {}, ["SEL_SKINNY16"]))
-    out.append(("skinny_32x16384x8192", dataclasses.replace(W["skinny_16x16384x8192"], name="skinny_32", M=32), {},
-                ["SEL_SKINNY32"]))
-    out.append(("skinny_64x16384x8192", dataclasses.replace(W["skinny_16x16384x8192"], name="skinny_64", M=64), {},
-                ["SEL_SKINNY64"]))
+    # HBM-bound: B (256 MiB) is rotated over 3 copies so the 256 MB Infinity Cache cannot serve it
+    out.append(("skinny_16x16384x8192", W["skinny_16x16384x8192"], {"rotate": 3}, ["SEL_SKINNY16"]))
+    out.append(("skinny_32x16384x8192", dataclasses.replace(W["skinny_16x16384x8192"], name="skinny_32", M=32),
+                {"rotate": 3}, ["SEL_SKINNY32"]))
+    out.append(("skinny_64x16384x8192", dataclasses.replace(W["skinny_16x16384x8192"], name="skinny_64", M=64),
+                {"rotate": 3}, ["SEL_SKINNY64"]))
     return out
 
 
@@ -313,7 +325,9 @@ def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str
             t[off:] = torch.from_numpy(np.ascontiguousarray(x).reshape(-1)).to(dev)
             return t[off:].view(*x.shape)
 
-        dA, dB = place(A), place(B)
+        dA = place(A)
+        dBs = [place(B) for _ in range(opts.get("rotate", 1))]
+        dB = dBs[0]
         db = place(bias) if bias is not None else None
         cbuf = torch.empty(w.M * w.N + off, dtype=torch.float16, device=dev)
         dC = cbuf[off:].view(w.M, w.N)
@@ -326,23 +340,25 @@ def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str
         for i, info in enumerate(infos):
             if (info["name"], name) in done:
                 continue
-            args = (i, w.M, w.N, w.K, dA.data_ptr(), dB.data_ptr(), db.data_ptr() if db is not None else None,
-                    dC.data_ptr(), epi, stream.cuda_stream)
-            st = lib.gemm_f16_with_config(*args)
+            def args(r=0):
+                return (i, w.M, w.N, w.K, dA.data_ptr(), dBs[r % len(dBs)].data_ptr(),
+                        db.data_ptr() if db is not None else None, dC.data_ptr(), epi, stream.cuda_stream)
+            st = lib.gemm_f16_with_config(*args())
             if st == 6:  # GEMM_ERR_UNSUPPORTED: this config cannot run this call
                 continue
             if st != 0:
                 raise RuntimeError("config %s on %s: status %d" % (info["name"], name, st))
-            for _ in range(3):
-                lib.gemm_f16_with_config(*args)
+            for r in range(3):
+                lib.gemm_f16_with_config(*args(r + 1))
             torch.cuda.synchronize()
             evs = []
-            for _ in range(iters):
+            for r in range(iters):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                lib.gemm_f16_with_config(*args)
+                lib.gemm_f16_with_config(*args(r + 1))
                 e1.record(stream)
                 evs.append((e0, e1))
+            lib.gemm_f16_with_config(*args(0))   # the screened output comes from the first copy of B
             torch.cuda.synchronize()
             us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
             med = us[len(us) // 2]
@@ -358,7 +374,7 @@ def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str
             out.flush()
             print("%-28s %-48s %9.1f us %7.1f TF %s" % (name, info["name"], med, rec["tflops"],
                                                         "ok" if ok else "FAIL rel=%.2e" % rel), flush=True)
-        del dA, dB, db, cbuf, dC
+        del dA, dB, dBs, db, cbuf, dC
         torch.cuda.empty_cache()
     out.close()
 
@@ -395,7 +411,8 @@ def select(results_path: str, table_path: str = TABLE, summary_path: str | None 
                "(%s). Do not edit by hand; rerun the sweep." % os.path.basename(results_path))
     if summary_path:
         lines = ["# Offline sweep of the tile and skinny kernels", "",
-                 "Median of %s HIP-event-timed launches per (configuration, workload) on one MI355X;" % "20",
+                 "Median of %s HIP-event-timed launches per (configuration, workload) on one MI355X; the skinny" % "20",
+                 "workloads rotate 3 copies of B so the Infinity Cache cannot serve it;",
                  "outputs screened against a float32 PyTorch reference on sampled rows (parity proper is the",
                  "oracle tests). Command: `python -m dense_tiled_gemm_04_amd.sweep --run RESULTS` on the GPU, then",
                  "`--select RESULTS` here.", "", "## Chosen per shape class", "",

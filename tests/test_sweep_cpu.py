@@ -60,9 +60,10 @@ def test_product_table_entries_are_in_budget():
     assert set(sel) == set(sweep.CLASSES) and all(0 <= v < n for v in sel.values())
     for t in tiles:
         f = [x.strip() for x in t.split(",")]
-        c = sweep.Tile(*map(int, f[:9]), "dma" if f[9] == "LOAD_DMA" else "reg", int(f[10]), int(f[11]))
+        c = sweep.Tile(*map(int, f[:9]), "dma" if f[9] == "LOAD_DMA" else "reg", int(f[10]), int(f[11]),
+                       int(f[12]), int(f[13]))
         assert sweep.valid(c), c
-        assert f[12].strip('"') == c.name
+        assert f[14].strip('"') == c.name
     for s in skinny:
         f = [x.strip() for x in s.split(",")]
         assert sweep.valid(sweep.Skinny(int(f[0]), int(f[1])))
