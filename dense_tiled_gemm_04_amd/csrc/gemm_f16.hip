@@ -82,7 +82,7 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
 const Config kConfigs[] = {GEMM_F16_CONFIGS};
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 static_assert(SEL_SKINNY16 < kNumConfigs && SEL_SKINNY32 < kNumConfigs && SEL_SKINNY64 < kNumConfigs &&
-                  SEL_DMA_BIG < kNumConfigs && SEL_DMA_SMALL < kNumConfigs && SEL_REG_BIG < kNumConfigs &&
+                  SEL_DMA_HUGE < kNumConfigs && SEL_DMA_BIG < kNumConfigs && SEL_DMA_SMALL < kNumConfigs && SEL_REG_BIG < kNumConfigs &&
                   SEL_REG_SMALL < kNumConfigs,
               "shape-class defaults index the table");
 
@@ -132,8 +132,9 @@ int pick_default(const Call& c) {
         if (supports(kConfigs[idx], c)) return idx;
     }
     const int64_t tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256);
-    const bool big = tiles256 >= 256;  // at least one 256x256 tile per CU
-    const int dma = big ? SEL_DMA_BIG : SEL_DMA_SMALL;
+    const bool big = tiles256 >= 256;    // at least one 256x256 tile per CU
+    const bool huge = tiles256 >= 1024;  // four or more rounds of them
+    const int dma = huge ? SEL_DMA_HUGE : (big ? SEL_DMA_BIG : SEL_DMA_SMALL);
     if (supports(kConfigs[dma], c)) return dma;
     return big ? SEL_REG_BIG : SEL_REG_SMALL;
 }

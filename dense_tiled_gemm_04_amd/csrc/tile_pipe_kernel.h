@@ -66,10 +66,23 @@ __device__ __forceinline__ int swz_a(int r) {
 //  MF = 16: a half-wave touches rows {8g + 4h + j : j < 4} for two
 //  consecutive g, two chunks per row; XOR by an even value made of (kr mod 4)
 //  and bit 3 of kr spreads those 16 chunks over distinct bank groups.
+//  Row widths that are a multiple of 8 chunks but not a power of two (BN =
+//  192: 384-byte rows, so consecutive rows start half a 256-byte bank window
+//  apart) use XOR values below 8, which keep a chunk inside its aligned group
+//  of 8 and so inside the row. Rows r and r+1 are already half a window apart,
+//  so only pairs of rows need separating: XOR by 4 for MF = 32, and for MF = 16
+//  by 2 * ((r/2) mod 2) + 4 * ((r/8) mod 2).
 template <int BN, int MF>
 __device__ __forceinline__ int swz_b(int kr) {
     constexpr int CB = BN / 8;
-    if constexpr (MF == 32) {
+    if constexpr ((CB & (CB - 1)) != 0) {
+        static_assert(CB % 8 == 0 && (BN * 2) % 256 == 128, "non-power-of-two rows: 128-byte offset per row");
+        if constexpr (MF == 32) {
+            return 4 * ((kr >> 1) & 1);
+        } else {
+            return 2 * ((kr >> 1) & 1) + 4 * ((kr >> 3) & 1);
+        }
+    } else if constexpr (MF == 32) {
         return (4 * (kr & 3)) & (CB - 1);
     } else {
         return (2 * ((kr & 3) | (((kr >> 3) & 1) << 2))) & (CB - 1);
@@ -94,7 +107,7 @@ struct TilePipeCfg {
     static_assert(MF == 32 || MF == 16, "MFMA shape");
     static_assert(KSTEPS % 2 == 0, "even k-steps per stage (fragment ping-pong)");
     static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile of whole MFMA blocks");
-    static_assert((CA & (CA - 1)) == 0 && (CB & (CB - 1)) == 0 && CB >= 4, "chunk counts");
+    static_assert((CA & (CA - 1)) == 0 && CB >= 4 && ((CB & (CB - 1)) == 0 || CB % 8 == 0), "chunk counts");
     static_assert((BM * CA) % (64 * NW) == 0 && (BK * CB) % (64 * NW) == 0, "copy split over waves");
     static_assert(STAGES >= 2 && PER_STAGE * (STAGES - 1) <= 63, "vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
@@ -174,9 +187,13 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     // P = (i * NW + wave) * 64 + lane of the A (j < A_INS, i = j) or the B
     // (i = j - A_INS) tile, which is lane-contiguous; its source is the
     // logical chunk that the swizzle puts at P.
-    uint32_t a_off[A_INS], b_off[B_INS];  // LOAD_DMA: byte offsets from the tile origin
-    int a_ck[A_INS], b_kr[B_INS], b_cn[B_INS];  // LOAD_REG: k offset in stage / k-row / column
-    const f16* a_row[A_INS];                   // LOAD_REG: row pointer (rows clamped to M-1)
+    // Copy sources.  LOAD_DMA: byte offsets from the tile origin of the stage
+    // (rows clamped to M-1, columns to the last chunk).  LOAD_REG: per chunk,
+    // the k offset in the stage and the row pointer (rows clamped to M-1) for
+    // A, the k-row and column for B.
+    uint32_t a_off[A_INS], b_off[B_INS];
+    int a_ck[A_INS], b_kr[B_INS], b_cn[B_INS];
+    const f16* a_row[A_INS];
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
         const int P = (i * NW + wave) * 64 + lane;
@@ -393,7 +410,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
 #pragma unroll
         for (int r4 = 0; r4 < NQ; ++r4) {
             const int n = n0 + wn * WTN + ni * MF + (MF == 32 ? 8 * r4 + 4 * (lane >> 5) : 4 * (lane >> 4));
-            const bool quad = n + 4 <= N;
+            const bool quad = LOADER == LOAD_DMA || n + 4 <= N;  // LOAD_DMA: N % 8 == 0
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (EPI != EPI_NONE) {
                 if (quad) {

@@ -28,7 +28,8 @@ Steps:
    (config, workload) is appended to the results file, and a restarted run
    skips the records already there.
 4. ``--select`` picks, for each shape class the dispatcher knows (skinny
-   M <= 16/32/64, LDS-DMA big/small, register loader big/small), the
+   M <= 16/32/64; LDS-DMA huge (several rounds of 256x256 tiles per CU),
+   big (about one round) or small; register loader big or small), the
    configuration with the lowest geometric-mean time over that class's
    workloads. It writes csrc/config_table.inc with just those configurations
    and a Markdown summary of the measurements.
@@ -142,7 +143,8 @@ def valid(c) -> bool:
     d = c.derived()
     if d["ksteps"] % 2 or d["wtm"] % c.mf or d["wtn"] % c.mf or d["tm"] < 1 or d["tn"] < 1:
         return False
-    if not (pow2(d["ca"]) and pow2(d["cb"]) and d["cb"] >= 4):
+    cb_ok = pow2(d["cb"]) or (d["cb"] % 8 == 0 and (c.bn * 2) % 256 == 128)   # e.g. BN = 192
+    if not (pow2(d["ca"]) and cb_ok and d["cb"] >= 4):
         return False
     if (c.bm * d["ca"]) % (64 * d["nw"]) or (c.bk * d["cb"]) % (64 * d["nw"]):
         return False
@@ -161,11 +163,16 @@ def valid(c) -> bool:
             return False
         if c.cslot + (ps - 1) * c.dstride >= d["ksteps"] * d["nmma"]:
             return False
-    # registers per lane: accumulators + two fragment sets + staging (reg loader) + ~40 of addressing
+    # registers per lane: accumulators, two fragment sets, staging (register loader), one copy offset per
+    # chunk and ~56 of addressing and temporaries.  With one wave per SIMD the accumulators sit in the 256 AGPRs and the
+    # rest must fit the 256 VGPRs; with more waves all of it shares 512 / waves.
     acc = d["tm"] * d["tn"] * d["nacc"]
     frags = 2 * (d["tm"] * 4 + d["tn"] * 4)
     stg = 4 * ps if c.loader == "reg" else 0
-    return acc + frags + stg + 40 <= REGS_PER_LANE // c.wpe
+    rest = frags + stg + ps + 56
+    if c.wpe == 1:
+        return acc <= REGS_PER_LANE // 2 and rest <= REGS_PER_LANE // 2
+    return acc + rest <= REGS_PER_LANE // c.wpe
 
 
 def space() -> list:
@@ -192,6 +199,10 @@ def space() -> list:
     out.append(Tile(128, 256, 64, 2, 2, 2, 4, 3, 2, "reg"))
     for wpe in (1, 2):
         out.append(Tile(128, 128, 64, 2, 2, 2, 4, 1, 1, "reg", wpe=wpe))
+    # 192-wide tiles: 3001 columns are 16 tiles of 192 (one full round of 256 tiles at 256 x 192)
+    out.append(Tile(256, 192, 64, 2, 2, 2, 4, 1, 2, "reg"))
+    out.append(Tile(128, 192, 64, 2, 2, 2, 4, 1, 1, "reg", wpe=2))
+    out.append(Tile(256, 192, 64, 2, 2, 2, 4, 1, 2, "dma"))
     out.append(Tile(128, 128, 128, 2, 2, 2, 4, 1, 1, "reg", wpe=2))
     for mb, sts in ((1, (4, 6, 8)), (2, (4, 6)), (4, (3, 5))):
         for st in sts:
@@ -199,8 +210,8 @@ def space() -> list:
     return [c for c in out if valid(c)]
 
 
-CLASSES = ["SEL_SKINNY16", "SEL_SKINNY32", "SEL_SKINNY64", "SEL_DMA_BIG", "SEL_DMA_SMALL", "SEL_REG_BIG",
-           "SEL_REG_SMALL"]
+CLASSES = ["SEL_SKINNY16", "SEL_SKINNY32", "SEL_SKINNY64", "SEL_DMA_HUGE", "SEL_DMA_BIG", "SEL_DMA_SMALL",
+           "SEL_REG_BIG", "SEL_REG_SMALL"]
 
 
 def class_of(c, cls: str) -> bool:
@@ -258,7 +269,7 @@ def sweep_workloads():
     W = wl.WORKLOADS
     out = []
     out.append(("gemm_4096", W["gemm_4096"], {}, ["SEL_DMA_BIG"]))
-    out.append(("mlp_up_8192x16384x4096", W["mlp_up_8192x16384x4096"], {}, ["SEL_DMA_BIG"]))
+    out.append(("mlp_up_8192x16384x4096", W["mlp_up_8192x16384x4096"], {}, ["SEL_DMA_HUGE"]))
     out.append(("gemm_256", W["gemm_256"], {}, ["SEL_DMA_SMALL"]))
     out.append(("gemm_2048", dataclasses.replace(W["gemm_4096"], name="gemm_2048", M=2048, N=2048, K=2048, seed=5),
                 {}, ["SEL_DMA_SMALL"]))
@@ -381,6 +392,10 @@ def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str
 
 def select(results_path: str, table_path: str = TABLE, summary_path: str | None = None) -> dict:
     recs = [json.loads(l) for l in open(results_path) if l.strip()]
+    # classes come from the current workload table, so a reclassification needs no new measurements
+    wl_classes = {name: classes for name, _w, _o, classes in sweep_workloads()}
+    for r in recs:
+        r["classes"] = wl_classes.get(r["workload"], r["classes"])
     by_name = {c.name: c for c in space()}
     chosen, scores = {}, {}
     for cls in CLASSES:
