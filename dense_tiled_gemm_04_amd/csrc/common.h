@@ -113,7 +113,12 @@ __device__ __forceinline__ void dma_global_16(const void* sbase, uint32_t voff, 
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                  : "memory");
 }
-// Through a buffer resource: offsets past num_records read as 0.
+// Through a buffer resource: each dword that is not wholly below num_records
+// reads as 0.  16 bytes per lane.
+__device__ __forceinline__ void dma_buffer_16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "s"(lds)
+                 : "memory");
+}
 // 16 bytes per lane, marked non-temporal: for data streamed exactly once (the
 // skinny path's B), so it does not displace reused lines in the caches.
 __device__ __forceinline__ void dma_buffer_16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {

@@ -82,7 +82,8 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
 const Config kConfigs[] = {GEMM_F16_CONFIGS};
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 static_assert(SEL_SKINNY16 < kNumConfigs && SEL_SKINNY32 < kNumConfigs && SEL_SKINNY64 < kNumConfigs &&
-                  SEL_DMA_HUGE < kNumConfigs && SEL_DMA_BIG < kNumConfigs && SEL_DMA_SMALL < kNumConfigs && SEL_REG_BIG < kNumConfigs &&
+                  SEL_DMA_HUGE < kNumConfigs && SEL_DMA_BIG < kNumConfigs && SEL_DMA_SMALL < kNumConfigs &&
+                  SEL_BUF_BIG < kNumConfigs && SEL_BUF_SMALL < kNumConfigs && SEL_REG_BIG < kNumConfigs &&
                   SEL_REG_SMALL < kNumConfigs,
               "shape-class defaults index the table");
 
@@ -122,6 +123,17 @@ bool supports(const Config& cfg, const Call& c) {
     if (cfg.loader == LOAD_DMA)
         return vec_ok && c.K % cfg.bk == 0 && (int64_t)cfg.bm * c.K * 2 < (int64_t)INT32_MAX &&
                (int64_t)cfg.bk * c.N * 2 < (int64_t)INT32_MAX;
+    if (cfg.loader == LOAD_BUF) {
+        // 31-bit buffer sizes and offsets: all of A and B, and one stage's tiles.
+        const int64_t lim = (int64_t)INT32_MAX - 64;
+        const bool fits = c.M * c.K * 2 < lim && c.K * c.N * 2 < lim &&
+                          ((int64_t)cfg.bm * c.K + cfg.bk) * 2 < lim && ((int64_t)cfg.bk * c.N + cfg.bn) * 2 < lim;
+        // Odd N: B's range is padded by 2 bytes past its end; allowed only
+        // when the end is not on a 4 KiB page boundary, so the pad lies in the
+        // page of the last element.
+        const bool pad_ok = c.N % 2 == 0 || ((uintptr_t)c.B + (uintptr_t)(c.K * c.N * 2)) % 4096 != 0;
+        return c.K % 8 == 0 && fits && pad_ok;
+    }
     return true;  // register loader: any shape, any 2-byte alignment
 }
 
@@ -136,6 +148,9 @@ int pick_default(const Call& c) {
     const bool huge = tiles256 >= 1024;  // four or more rounds of them
     const int dma = huge ? SEL_DMA_HUGE : (big ? SEL_DMA_BIG : SEL_DMA_SMALL);
     if (supports(kConfigs[dma], c)) return dma;
+    // unaligned or ragged: buffer LDS-DMA when K % 8 == 0, else the register loader
+    const int buf = big ? SEL_BUF_BIG : SEL_BUF_SMALL;
+    if (supports(kConfigs[buf], c)) return buf;
     return big ? SEL_REG_BIG : SEL_REG_SMALL;
 }
 
@@ -205,7 +220,7 @@ int gemm_f16_num_configs(void) { return kNumConfigs; }
 int gemm_f16_config_info(int idx, char* buf, int buflen) {
     if (idx < 0 || idx >= kNumConfigs) return -GEMM_ERR_NO_CONFIG;
     const Config& c = kConfigs[idx];
-    static const char* loaders[] = {"dma", "reg"};
+    static const char* loaders[] = {"dma", "reg", "buf"};
     char tmp[512];
     int n = snprintf(tmp, sizeof(tmp),
                      "{\"idx\": %d, \"name\": \"%s\", \"kind\": \"%s\", \"bm\": %d, \"bn\": %d, \"bk\": %d, "

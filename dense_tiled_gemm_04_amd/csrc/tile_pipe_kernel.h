@@ -34,6 +34,19 @@
 //      Requires K % BK == 0, N % 8 == 0, A/B/C 16-byte aligned and bias
 //      8-byte aligned. Rows past M re-read row M-1, and columns past N
 //      re-read the last chunk; neither is stored.
+//    - LOAD_BUF: the same LDS-DMA ring, issued through buffer resources
+//      (buffer_load_dwordx4 ... lds), for unaligned shapes: any M and N,
+//      K % 8 == 0, any 2-byte alignment of A, B, C and bias. The hardware
+//      range check of a buffer load works per dword: a dword whose last byte
+//      lies at or past num_records reads as zero. B's resource ends at the
+//      end of B, so the k-rows past K of the last stage read as zeros. Its
+//      num_records is padded by 2 bytes when N is odd, because there a chunk
+//      that holds the last element of B can start 2 bytes off the dword grid
+//      of the end. The host only allows that pad when it stays inside the
+//      page of the last element. Columns past N read the next row; they
+//      reach only output columns past N, which are never stored. A chunks at
+//      k >= K are redirected to an offset past num_records and read as zeros
+//      (K % 8 == 0, so no chunk straddles K). Rows past M re-read row M-1.
 //    - LOAD_REG: any M, N, K and any 2-byte alignment. Two LDS stages and one
 //      set of staging registers. In stage kt, slot CSLOT+j writes register j
 //      (stage kt+1, loaded one stage earlier) to LDS with ds_write_b128, and
@@ -49,7 +62,7 @@
 
 namespace gk {
 
-enum Loader { LOAD_DMA = 0, LOAD_REG = 1 };
+enum Loader { LOAD_DMA = 0, LOAD_REG = 1, LOAD_BUF = 2 };
 
 // A-tile swizzle: logical chunk c of row r lives at chunk c ^ swz_a(r).  Over
 // any 16 consecutive rows (one ds_read_b128 quarter-wave), the 16 physical
@@ -134,9 +147,10 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     constexpr int KSTEPS = Cfg::KSTEPS, A_INS = Cfg::A_INS, B_INS = Cfg::B_INS, PER_STAGE = Cfg::PER_STAGE;
     constexpr int NMMA = Cfg::NMMA, NRD = Cfg::NRD;
     constexpr int LAST = (KSTEPS - 1) * NMMA + BSLOT;  // stage slot of the barrier
+    constexpr bool RING = LOADER != LOAD_REG;          // LDS-DMA ring of STAGES buffers
     static_assert(BSLOT >= 0 && BSLOT + 1 < NMMA, "barrier slot inside the last k-step, reads after it");
     static_assert(DSTRIDE >= 1 && (PER_STAGE - 1) * DSTRIDE < LAST, "every copy is issued before the barrier");
-    static_assert(LOADER == LOAD_DMA || (STAGES == 2 && CSLOT >= 0 && CSLOT + PER_STAGE <= LAST + 1 &&
+    static_assert(RING || (STAGES == 2 && CSLOT >= 0 && CSLOT + PER_STAGE <= LAST + 1 &&
                                          CSLOT + (PER_STAGE - 1) * DSTRIDE < KSTEPS * NMMA),
                   "register loader: 2 stages; every LDS write precedes the barrier; every reload fits "
                   "in the stage");
@@ -188,9 +202,10 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     // (i = j - A_INS) tile, which is lane-contiguous; its source is the
     // logical chunk that the swizzle puts at P.
     // Copy sources.  LOAD_DMA: byte offsets from the tile origin of the stage
-    // (rows clamped to M-1, columns to the last chunk).  LOAD_REG: per chunk,
-    // the k offset in the stage and the row pointer (rows clamped to M-1) for
-    // A, the k-row and column for B.
+    // (rows clamped to M-1, columns to the last chunk).  LOAD_BUF: the same
+    // with unclamped columns, plus the k offset of each A chunk.  LOAD_REG:
+    // per chunk, the k offset in the stage and the row pointer (rows clamped
+    // to M-1) for A, the k-row and column for B.
     uint32_t a_off[A_INS], b_off[B_INS];
     int a_ck[A_INS], b_kr[B_INS], b_cn[B_INS];
     const f16* a_row[A_INS];
@@ -199,10 +214,9 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         const int P = (i * NW + wave) * 64 + lane;
         const int r = P / CA, c = (P % CA) ^ swz_a<BK>(r);
         const int m = min(m0 + r, M - 1);
-        if constexpr (LOADER == LOAD_DMA) {
-            a_off[i] = (uint32_t)(((m - m0) * K + 8 * c) * 2);
-        } else {
-            a_ck[i] = 8 * c;
+        if constexpr (RING) a_off[i] = (uint32_t)(((m - m0) * K + 8 * c) * 2);
+        if constexpr (LOADER != LOAD_DMA) a_ck[i] = 8 * c;
+        if constexpr (LOADER == LOAD_REG) {
             a_row[i] = p.A + (size_t)m * K;
         }
     }
@@ -213,6 +227,8 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         if constexpr (LOADER == LOAD_DMA) {
             const int n = min(n0 + 8 * c, N - 8) - n0;
             b_off[i] = (uint32_t)((kr * N + n) * 2);
+        } else if constexpr (LOADER == LOAD_BUF) {
+            b_off[i] = (uint32_t)((kr * N + 8 * c) * 2);
         } else {
             b_kr[i] = kr;
             b_cn[i] = n0 + 8 * c;
@@ -224,13 +240,35 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     const uint32_t a_lds0 = lds_addr(a_lds) + wave_s * 64 * 16;
     const uint32_t b_lds0 = lds_addr(b_lds) + wave_s * 64 * 16;
 
-    // LOAD_DMA: copy j of stage kt into ring buffer sb.
+    // LOAD_BUF: buffer resources of stage kt.  A: from the stage's tile origin
+    // to the end of A.  B: from the stage's tile origin to the end of B (plus
+    // the 2-byte pad for odd N).  Both byte counts fit 31 bits (host check).
+    const int b_pad = (N & 1) ? 2 : 0;
+    auto rsrc_a = [&](int kt) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(a_row0 + (size_t)kt * BK * 2), (short)0,
+                                                 (M - m0) * K * 2 - kt * BK * 2, 0x00020000);
+    };
+    auto rsrc_b = [&](int kt) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(b_col0 + (size_t)kt * BK * N * 2), (short)0,
+                                                 K * N * 2 + b_pad - n0 * 2 - kt * BK * N * 2, 0x00020000);
+    };
+    // Ring loaders: copy j of stage kt into ring buffer sb.
     auto dma_op = [&](int j, int kt, int sb) {
         if (j < A_INS) {
-            dma_global_16(a_row0 + (size_t)kt * BK * 2, a_off[j], a_lds0 + sb * A_STAGE + j * NW * 64 * 16);
+            const uint32_t lds = a_lds0 + sb * A_STAGE + j * NW * 64 * 16;
+            if constexpr (LOADER == LOAD_BUF) {
+                dma_buffer_16(rsrc_a(kt), a_ck[j] < K - kt * BK ? a_off[j] : 0x80000000u, lds);
+            } else {
+                dma_global_16(a_row0 + (size_t)kt * BK * 2, a_off[j], lds);
+            }
         } else {
             const int i = j - A_INS;
-            dma_global_16(b_col0 + (size_t)kt * BK * N * 2, b_off[i], b_lds0 + sb * B_STAGE + i * NW * 64 * 16);
+            const uint32_t lds = b_lds0 + sb * B_STAGE + i * NW * 64 * 16;
+            if constexpr (LOADER == LOAD_BUF) {
+                dma_buffer_16(rsrc_b(kt), b_off[i], lds);
+            } else {
+                dma_global_16(b_col0 + (size_t)kt * BK * N * 2, b_off[i], lds);
+            }
         }
     };
     // LOAD_REG: load copy j of stage kt into a register, then write it to LDS.
@@ -309,7 +347,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
 
     // Prologue: stages 0 .. STAGES-2 in LDS (or in flight), then stage 0's
     // first fragments.
-    if constexpr (LOADER == LOAD_DMA) {
+    if constexpr (RING) {
 #pragma unroll
         for (int st = 0; st < STAGES - 1; ++st)
             if (st < KT)
@@ -339,11 +377,11 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     }
 
     int s = 0;  // ring buffer of the stage being computed
-    // PHASE 2: every stage the copies of this stage refer to exists (LOAD_DMA:
-    // kt+STAGES-1; LOAD_REG: kt+1 written and kt+2 loaded), so they are issued
-    // unconditionally and the DMA wait count is exact.  PHASE 1 (LOAD_REG
-    // only): the last write, no reload.  PHASE 0: no copy work; the DMA
-    // loader waits for everything.
+    // PHASE 2: every stage the copies of this stage refer to exists (ring
+    // loaders: kt+STAGES-1; LOAD_REG: kt+1 written and kt+2 loaded), so they
+    // are issued unconditionally and the DMA wait count is exact.  PHASE 1
+    // (LOAD_REG only): the last write, no reload.  PHASE 0: no copy work; the
+    // ring loaders wait for everything.
     auto stage = [&]<int PHASE>(int kt) {
         const bool has_next = PHASE > 0 || kt + 1 < KT;
         const int sn = (s + 1 == STAGES) ? 0 : s + 1;
@@ -355,7 +393,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
             for (int i = 0; i < NMMA; ++i) {
                 mma_op(cur, i);
                 const int slot = kk * NMMA + i;
-                if constexpr (LOADER == LOAD_DMA && PHASE == 2) {
+                if constexpr (RING && PHASE == 2) {
                     if (slot % DSTRIDE == 0 && slot / DSTRIDE < PER_STAGE) dma_op(slot / DSTRIDE, kt + STAGES - 1, sd);
                 }
                 if constexpr (LOADER == LOAD_REG && PHASE >= 1) {
@@ -371,7 +409,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
                         if (read_slot<NRD, SPREAD>(j, 0, NMMA) == i) read_op(nxt, j, s, kk + 1);
                 } else if (has_next) {
                     if (i == BSLOT) {
-                        if constexpr (LOADER == LOAD_DMA) {
+                        if constexpr (RING) {
                             if constexpr (PHASE == 2) {
                                 wait_vmcnt<(STAGES - 2) * PER_STAGE>();
                             } else {
@@ -390,7 +428,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         s = sn;
     };
     int kt = 0;
-    if constexpr (LOADER == LOAD_DMA) {
+    if constexpr (RING) {
         for (; kt < KT - (STAGES - 1); ++kt) stage.template operator()<2>(kt);
     } else {
         for (; kt < KT - 2; ++kt) stage.template operator()<2>(kt);
@@ -417,7 +455,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
                     const f16x4 b4 = *(const f16x4_u*)(p.bias + n);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) bv[e] = (float)b4[e];
-                } else if (LOADER == LOAD_REG) {
+                } else if (LOADER != LOAD_DMA) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         if (n + e < N) bv[e] = (float)p.bias[n + e];

@@ -12,7 +12,8 @@ Steps:
 
 1. ``space()`` enumerates kernel configurations. The tile kernel's knobs are
    block tile, K-block, waves, LDS stages, tile-order group, barrier slot,
-   copy stride, loader and waves per SIMD; the skinny kernel's are rows per
+   copy stride, loader (LDS-DMA, buffer LDS-DMA or registers), MFMA shape,
+   read spreading and waves per SIMD; the skinny kernel's are rows per
    workgroup and stages. ``valid()`` mirrors the kernels' static_asserts and
    applies the budgets: at most 160 KiB of LDS per workgroup (per CU when two
    workgroups share one), and the 512 registers per lane (VGPR + AGPR) shared
@@ -29,7 +30,8 @@ Steps:
    skips the records already there.
 4. ``--select`` picks, for each shape class the dispatcher knows (skinny
    M <= 16/32/64; LDS-DMA huge (several rounds of 256x256 tiles per CU),
-   big (about one round) or small; register loader big or small), the
+   big (about one round) or small; buffer LDS-DMA (unaligned, K % 8 == 0)
+   big or small; register loader (K % 8 != 0) big or small), the
    configuration with the lowest geometric-mean time over that class's
    workloads. It writes csrc/config_table.inc with just those configurations
    and a Markdown summary of the measurements.
@@ -68,7 +70,7 @@ class Tile:
     group: int
     bslot: int
     dstride: int
-    loader: str          # "dma" | "reg"
+    loader: str          # "dma" | "buf" | "reg"
     cslot: int = 0
     wpe: int = 1         # waves per SIMD (= workgroups per CU, 4-wave workgroups)
     mf: int = 32         # MFMA shape: 32 -> 32x32x16, 16 -> 16x16x32
@@ -105,7 +107,7 @@ class Tile:
     def macro(self) -> str:
         return "TILE_CFG(%d, %d, %d, %d, %d, %d, %d, %d, %d, %s, %d, %d, %d, %d, \"%s\")" % (
             self.bm, self.bn, self.bk, self.wm, self.wn, self.stages, self.group, self.bslot, self.dstride,
-            "LOAD_DMA" if self.loader == "dma" else "LOAD_REG", self.cslot, self.wpe, self.mf, self.spread, self.name)
+            {"dma": "LOAD_DMA", "buf": "LOAD_BUF", "reg": "LOAD_REG"}[self.loader], self.cslot, self.wpe, self.mf, self.spread, self.name)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -138,7 +140,7 @@ def valid(c) -> bool:
         b_ins = SK_BK * SK_BN * 2 // 16 // (SK_WAVES * 64)
         a_ins = 16 * c.mb * SK_BK * 2 // 4 // (SK_WAVES * 64)
         return c.stages >= 2 and (c.stages - 2) * (a_ins + b_ins) <= 63 and c.lds_bytes <= LDS_PER_CU
-    if c.mf not in (16, 32):
+    if c.mf not in (16, 32) or c.loader not in ("dma", "buf", "reg"):
         return False
     d = c.derived()
     if d["ksteps"] % 2 or d["wtm"] % c.mf or d["wtn"] % c.mf or d["tm"] < 1 or d["tn"] < 1:
@@ -164,12 +166,12 @@ def valid(c) -> bool:
         if c.cslot + (ps - 1) * c.dstride >= d["ksteps"] * d["nmma"]:
             return False
     # registers per lane: accumulators, two fragment sets, staging (register loader), one copy offset per
-    # chunk and ~56 of addressing and temporaries.  With one wave per SIMD the accumulators sit in the 256 AGPRs and the
+    # chunk (plus the k offset of each A chunk for the buffer loader) and ~56 of addressing and temporaries.  With one wave per SIMD the accumulators sit in the 256 AGPRs and the
     # rest must fit the 256 VGPRs; with more waves all of it shares 512 / waves.
     acc = d["tm"] * d["tn"] * d["nacc"]
     frags = 2 * (d["tm"] * 4 + d["tn"] * 4)
     stg = 4 * ps if c.loader == "reg" else 0
-    rest = frags + stg + ps + 56
+    rest = frags + stg + ps + (d["a_ins"] if c.loader == "buf" else 0) + 56
     if c.wpe == 1:
         return acc <= REGS_PER_LANE // 2 and rest <= REGS_PER_LANE // 2
     return acc + rest <= REGS_PER_LANE // c.wpe
@@ -204,6 +206,16 @@ def space() -> list:
     out.append(Tile(128, 192, 64, 2, 2, 2, 4, 1, 1, "reg", wpe=2))
     out.append(Tile(256, 192, 64, 2, 2, 2, 4, 1, 2, "dma"))
     out.append(Tile(128, 128, 128, 2, 2, 2, 4, 1, 1, "reg", wpe=2))
+    # buffer LDS-DMA (unaligned and ragged shapes with K % 8 == 0): the shapes of the best aligned ones
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 3, 1, "buf"))
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 8, 2, "buf", mf=16, spread=1))
+    out.append(Tile(256, 192, 64, 2, 2, 2, 4, 1, 2, "buf"))
+    out.append(Tile(256, 128, 64, 2, 2, 3, 4, 3, 2, "buf"))
+    out.append(Tile(128, 256, 64, 2, 2, 3, 4, 3, 2, "buf"))
+    for st in (3, 4):
+        out.append(Tile(128, 128, 64, 2, 2, st, 4, 1, 1, "buf"))
+    out.append(Tile(128, 128, 64, 2, 2, 3, 4, 3, 2, "buf", mf=16, spread=1))
+    out.append(Tile(128, 192, 64, 2, 2, 3, 4, 1, 1, "buf"))
     for mb, sts in ((1, (4, 6, 8)), (2, (4, 6)), (4, (3, 5))):
         for st in sts:
             out.append(Skinny(mb, st))
@@ -211,18 +223,24 @@ def space() -> list:
 
 
 CLASSES = ["SEL_SKINNY16", "SEL_SKINNY32", "SEL_SKINNY64", "SEL_DMA_HUGE", "SEL_DMA_BIG", "SEL_DMA_SMALL",
-           "SEL_REG_BIG", "SEL_REG_SMALL"]
+           "SEL_BUF_BIG", "SEL_BUF_SMALL", "SEL_REG_BIG", "SEL_REG_SMALL"]
 
 
 def class_of(c, cls: str) -> bool:
     """Whether configuration c may serve shape class cls.  The skinny classes
     (M <= 16/32/64, aligned) accept any skinny kernel with enough rows and any
-    LDS-DMA tile configuration; the dispatcher falls back if it cannot run."""
+    LDS-DMA tile configuration; the dispatcher falls back if it cannot run.
+    The buffer classes (unaligned, K % 8 == 0) accept the buffer and the
+    register loader, which both run every call of the class."""
     if cls.startswith("SEL_SKINNY"):
         if c.kind == "skinny":
             return 16 * c.mb >= int(cls[len("SEL_SKINNY"):])
         return c.loader == "dma"
-    return c.kind == "tile" and c.loader == ("dma" if "_DMA_" in cls else "reg")
+    if c.kind != "tile":
+        return False
+    if "_BUF_" in cls:
+        return c.loader in ("buf", "reg")
+    return c.loader == cls.split("_")[1].lower()
 
 
 def emit_table(configs: list, sel: dict, path: str, header: str) -> None:
@@ -273,8 +291,13 @@ def sweep_workloads():
     out.append(("gemm_256", W["gemm_256"], {}, ["SEL_DMA_SMALL"]))
     out.append(("gemm_2048", dataclasses.replace(W["gemm_4096"], name="gemm_2048", M=2048, N=2048, K=2048, seed=5),
                 {}, ["SEL_DMA_SMALL"]))
-    out.append(("ragged_4095x3001x1000", W["ragged_4095x3001x1000"], {}, ["SEL_REG_SMALL"]))
-    out.append(("gemm_4096_offset1", W["gemm_4096"], {"offset": 1}, ["SEL_REG_BIG"]))
+    out.append(("ragged_4095x3001x1000", W["ragged_4095x3001x1000"], {}, ["SEL_BUF_SMALL"]))
+    out.append(("gemm_4096_offset1", W["gemm_4096"], {"offset": 1}, ["SEL_BUF_BIG"]))
+    # K % 8 != 0: only the register loader runs these
+    out.append(("ragged_4095x3001x1004", dataclasses.replace(W["ragged_4095x3001x1000"], name="ragged_k1004",
+                                                             K=1004, seed=6), {}, ["SEL_REG_SMALL"]))
+    out.append(("gemm_4096x4096x4092", dataclasses.replace(W["gemm_4096"], name="gemm_k4092", K=4092, seed=7),
+                {}, ["SEL_REG_BIG"]))
     # HBM-bound: B (256 MiB) is rotated over 3 copies so the 256 MB Infinity Cache cannot serve it
     out.append(("skinny_16x16384x8192", W["skinny_16x16384x8192"], {"rotate": 3}, ["SEL_SKINNY16"]))
     out.append(("skinny_32x16384x8192", dataclasses.replace(W["skinny_16x16384x8192"], name="skinny_32", M=32),

@@ -28,8 +28,14 @@
  * Pointers: A, B, bias and C are DEVICE pointers (memory the caller allocated
  * on the current HIP device).  Any 2-byte-aligned pointer is accepted;
  * 16-byte alignment of A, B and C together with K % 8 == 0 and N % 8 == 0
- * enables the vectorised paths, otherwise a slower element-wise path runs.
- * Misalignment is never an error.
+ * enables the fastest paths.  Other shapes with K % 8 == 0 load through
+ * range-checked buffer copies, and the rest through registers with
+ * element-wise edges.  Misalignment is never an error.
+ *
+ * Reads: the library reads only A, B and bias, with one exception.  With odd N
+ * it may read the 2 bytes that follow the end of B, and then only when they lie
+ * in the same 4 KiB page as B's last element, so the read cannot fault.  Those
+ * bytes reach only output columns past N, which are never written.
  *
  * Ownership: the caller owns every buffer.  The library never allocates,
  * frees or retains caller memory.  C must not overlap A, B or bias.

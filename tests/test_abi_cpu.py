@@ -91,6 +91,11 @@ def test_forced_config_rejections():
         assert g.gemm_f16_raw(65 + 64, 64, 64, FAKE, FAKE, None, FAKE, 0, 0, config=idx) == 6
     for idx in vec:
         assert g.gemm_f16_raw(256, 3001, 1000, FAKE, FAKE, FAKE, FAKE, 1, 0, config=idx) == 6
+    # the buffer loader needs K % 8 == 0
+    buf = [c["idx"] for c in g.configs() if c["kind"] == "tile" and c["loader"] == "buf"]
+    assert buf
+    for idx in buf:
+        assert g.gemm_f16_raw(256, 3001, 1001, FAKE, FAKE, FAKE, FAKE, 1, 0, config=idx) == 6
 
 
 def _kind(idx):
@@ -105,15 +110,26 @@ def test_dispatch_shape_classes():
     # fused MLP up-projection
     c = _kind(sel(8192, 16384, 4096, FAKE, FAKE, FAKE, FAKE, 2))
     assert c["kind"] == "tile" and c["loader"] == "dma"
-    # ragged N = 3001: register loader (unaligned rows)
+    # ragged N = 3001, K % 8 == 0: buffer LDS-DMA loader (rows not 16-byte aligned)
     c = _kind(sel(4095, 3001, 1000, FAKE, FAKE, FAKE, FAKE, 1))
-    assert c["kind"] == "tile" and c["loader"] == "reg"
+    assert c["kind"] == "tile" and c["loader"] == "buf"
+    # ... unless N is odd and B ends on a 4 KiB page boundary (the 2-byte pad would cross it)
+    page_end_B = 1 << 40  # FAKE-style address; B + K*N*2 lands on a page boundary
+    c = _kind(sel(4095, 3001, 1024, FAKE, page_end_B - 1024 * 3001 * 2, FAKE, FAKE, 1))
+    assert c["loader"] == "reg"
+    c = _kind(sel(4095, 3001, 1024, FAKE, page_end_B - 1024 * 3001 * 2 + 2, FAKE, FAKE, 1))
+    assert c["loader"] == "buf"
     # skinny M = 16
     c = _kind(sel(16, 16384, 8192, FAKE, FAKE, FAKE, FAKE, 2))
     assert c["kind"] == "skinny" and c["bm"] >= 16
-    # K not a multiple of the K-block: register loader
+    # K not a multiple of the K-block, K % 8 == 0: buffer loader
     c = _kind(sel(1024, 1024, 1000, FAKE, FAKE, None, FAKE, 0))
+    assert c["kind"] == "tile" and c["loader"] == "buf"
+    # K % 8 != 0: register loader
+    c = _kind(sel(1024, 1024, 1001, FAKE, FAKE, None, FAKE, 0))
     assert c["kind"] == "tile" and c["loader"] == "reg"
-    # misaligned base (2-byte aligned only): register loader
+    # misaligned base (2-byte aligned only): buffer loader, or registers when K % 8 != 0
     c = _kind(sel(1024, 1024, 1024, FAKE + 2, FAKE, None, FAKE, 0))
+    assert c["loader"] == "buf"
+    c = _kind(sel(1024, 1024, 1020, FAKE + 2, FAKE + 2, None, FAKE + 2, 0))
     assert c["loader"] == "reg"

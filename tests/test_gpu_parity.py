@@ -36,6 +36,8 @@ def configs_for(lib, M, N, K, epi):
             continue
         if c["loader"] == "dma" and K % c["bk"] != 0:
             continue
+        if c["loader"] == "buf" and K % 8 != 0:
+            continue
         if c["kind"] == "skinny" or c["loader"] == "dma":
             if K % 8 or N % 8:
                 continue
@@ -255,10 +257,95 @@ def test_misaligned_views(lib):
     import dense_tiled_gemm_04_amd as g
     Av, Bv, Cv = ab[1:].view(M, K), bb[1:].view(K, N), cb[1:].view(M, N)
     cfg = g.config_info(g.select_config(Av, Bv, dev(bias), "bias_gelu", out=Cv))
-    assert cfg["loader"] == "reg"
+    assert cfg["loader"] == "buf"
     g.gemm_f16(Av, Bv, dev(bias), "bias_gelu", out=Cv)
     torch.cuda.synchronize()
     assert_parity(Cv.cpu().numpy(), ref, "misaligned")
+    # every configuration that accepts the misaligned views
+    for c in lib.configs():
+        if c["kind"] != "tile" or c["loader"] == "dma":
+            continue
+        Cv.zero_()
+        g.gemm_f16(Av, Bv, dev(bias), "bias_gelu", out=Cv, config=c["idx"])
+        torch.cuda.synchronize()
+        assert_parity(Cv.cpu().numpy(), ref, ("misaligned", c["name"]))
+
+
+# ---------------------------------------------------------------------------
+# buffer LDS-DMA loader: unaligned rows, K tails, odd N and the end of B
+# ---------------------------------------------------------------------------
+def _buf_configs(lib):
+    out = [c["idx"] for c in lib.configs() if c["kind"] == "tile" and c["loader"] == "buf"]
+    assert out
+    return out
+
+
+@pytest.mark.parametrize("shape", [(333, 277, 104), (259, 129, 1000), (130, 3001, 200), (1, 1, 8), (17, 33, 8),
+                                   (300, 515, 64), (513, 7, 40)])
+def test_buffer_loader_shapes(lib, shape):
+    M, N, K = shape
+    A, B, bias = workloads.make_inputs("ragged_4095x3001x1000", M=M, N=N, K=K)
+    ref = oracle.gemm(A, B, bias, "bias")
+    for idx in _buf_configs(lib):
+        got = run(lib, A, B, bias, "bias", config=idx)
+        m = assert_parity(got, ref, (shape, lib.config_info(idx)["name"]))
+        assert m["frac_exact"] > 0.97, m
+
+
+@pytest.mark.parametrize("shape", [(70, 301, 200), (5, 3, 8), (260, 2049, 64)])
+def test_buffer_loader_last_element_of_B(lib, shape):
+    # B is zero except its last element, so C[:, N-1] = A[:, K-1] * B[K-1][N-1] and every other column is 0.
+    # With odd N the chunk holding that element may start off the dword grid of B's end.
+    M, N, K = shape
+    A, _, _ = workloads.make_inputs("ragged_4095x3001x1000", M=M, N=N, K=K)
+    B = np.zeros((K, N), np.float16)
+    B[K - 1, N - 1] = np.float16(1.5)
+    ref = oracle.gemm(A, B)
+    for idx in _buf_configs(lib):
+        got = run(lib, A, B, None, "none", config=idx)
+        assert np.array_equal(got.view(np.uint16), ref.view(np.uint16)), lib.config_info(idx)["name"]
+
+
+def test_buffer_loader_B_end_on_page_boundary(lib):
+    # Odd N with B ending exactly on a 4 KiB boundary: the buffer loader's 2-byte pad would cross into the
+    # next page, so the dispatcher must pick another loader, and a forced buffer config is refused.
+    import dense_tiled_gemm_04_amd as g
+    M, N, K = 100, 301, 64
+    A, B, bias = workloads.make_inputs("ragged_4095x3001x1000", M=M, N=N, K=K)
+    ref = oracle.gemm(A, B, bias, "bias")
+    store = torch.zeros(K * N + 8192, dtype=torch.float16, device="cuda")
+    end = store.data_ptr() + store.numel() * 2
+    end_page = (end // 4096) * 4096
+    first = (end_page - K * N * 2 - store.data_ptr()) // 2
+    assert first >= 0
+    Bv = store[first:first + K * N].view(K, N)
+    assert (Bv.data_ptr() + K * N * 2) % 4096 == 0
+    Bv.copy_(dev(B))
+    cfg = g.config_info(g.select_config(dev(A), Bv, dev(bias), "bias"))
+    assert cfg["loader"] == "reg"
+    got = g.gemm_f16(dev(A), Bv, dev(bias), "bias")
+    torch.cuda.synchronize()
+    assert_parity(got.cpu().numpy(), ref, "page-end B")
+    with pytest.raises(Exception):
+        g.gemm_f16(dev(A), Bv, dev(bias), "bias", config=_buf_configs(lib)[0])
+
+
+def test_k_tail_does_not_read_next_row(lib):
+    # Infinities in column 0 of some rows of A.  A loader that let the next row's first elements into the
+    # K tail of a row (multiplied by the zero rows of B past K) would turn that row into NaN.
+    M, N, K = 130, 264, 200
+    A, B, bias = workloads.make_inputs("ragged_4095x3001x1000", M=M, N=N, K=K)
+    B[0] = np.where(B[0] == 0, np.float16(0.5), B[0])
+    inf_rows = [1, 64, 65, 129]
+    A[inf_rows, 0] = np.float16(np.inf)
+    ref = oracle.gemm(A, B, bias, "bias")
+    keep = np.setdiff1d(np.arange(M), inf_rows)
+    cfgs = configs_for(lib, M, N, K, "bias") + [None]
+    for idx in cfgs:
+        got = run(lib, A, B, bias, "bias", config=idx)
+        name = lib.config_info(idx)["name"] if idx is not None else "default"
+        assert_parity(got[keep], ref[keep], ("finite rows", name))
+        assert np.array_equal(got[inf_rows].view(np.uint16), ref[inf_rows].view(np.uint16)), name
 
 
 def test_degenerate_sizes(lib):

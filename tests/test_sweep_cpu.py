@@ -60,7 +60,7 @@ def test_product_table_entries_are_in_budget():
     assert set(sel) == set(sweep.CLASSES) and all(0 <= v < n for v in sel.values())
     for t in tiles:
         f = [x.strip() for x in t.split(",")]
-        c = sweep.Tile(*map(int, f[:9]), "dma" if f[9] == "LOAD_DMA" else "reg", int(f[10]), int(f[11]),
+        c = sweep.Tile(*map(int, f[:9]), f[9][len("LOAD_"):].lower(), int(f[10]), int(f[11]),
                        int(f[12]), int(f[13]))
         assert sweep.valid(c), c
         assert f[14].strip('"') == c.name
