@@ -1,4 +1,5 @@
-"""CPU oracle for the fp16 GEMM + fused bias / bias+GELU epilogue (Python side).
+"""CPU oracle for the fp16 GEMM + fused bias / bias+GELU epilogue, and for the
+row-wise softmax (Python side).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  It shares no code with
@@ -59,6 +60,8 @@ def _load():
     lib.oracle_gelu.argtypes = [ctypes.c_double]
     lib.oracle_gelu.restype = ctypes.c_double
     lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_softmax_rows_f16.argtypes = [i64, i64, p, p, p, ctypes.c_int]
+    lib.oracle_softmax_rows_f16.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -122,6 +125,22 @@ def gemm_points(A, B, bias, epilogue: str, rows, cols, want_y: bool = False, thr
         raise RuntimeError("oracle_gemm_f16_points failed (%d)" % rc)
     out = out.view(np.float16)
     return (out, Y) if want_y else out
+
+
+def softmax_rows(X, want_y: bool = False, threads: int = 0):
+    """Row-wise softmax of an fp16 matrix in fp64, rounded once to fp16 (see the C file)."""
+    lib = _load()
+    X16 = _bits(X)
+    if X16.ndim != 2:
+        raise ValueError("expected a 2-D matrix")
+    rows, cols = X16.shape
+    Y = np.empty((rows, cols), dtype=np.uint16)
+    Yd = np.empty((rows, cols), dtype=np.float64) if want_y else None
+    rc = lib.oracle_softmax_rows_f16(rows, cols, _ptr(X16), _ptr(Y), _ptr(Yd), threads)
+    if rc != 0:
+        raise RuntimeError("oracle_softmax_rows_f16 failed (%d)" % rc)
+    Y = Y.view(np.float16)
+    return (Y, Yd) if want_y else Y
 
 
 def f16_decode(bits) -> np.ndarray:

@@ -210,3 +210,50 @@ int oracle_max_threads(void) {
     return 1;
 #endif
 }
+
+/*
+ * Row-wise softmax of an fp16 matrix, the tutorial's register-resident
+ * reduction kernel: per row, a max reduction, then a sum reduction of the
+ * shifted exponentials, then the normalisation (news article on TileLang
+ * kernel design, paragraph on the fused epilogue, whose last sentences
+ * describe the row softmax built from fragment-level max and sum
+ * reductions; blog post on TileLang, the "three-piece set" section, item 2:
+ * one kernel per row-wise normalisation, with no intermediate in HBM).  The
+ * pages give no formula; this is the standard definition, shifted by the
+ * row maximum as such kernels do:
+ *   m    = max_j x[i][j]                 (NaN entries never win the comparison)
+ *   e_j  = exp(x[i][j] - m)              fp64, libm exp
+ *   s    = sum_j e_j                     fp64, increasing j
+ *   y_j  = e_j / s                       fp64
+ *   Y[i][j] = fp16_round_nearest_even(y_j)
+ * In IEEE arithmetic this gives: -inf entries -> 0; a row of all -inf
+ * (m = -inf, x - m = NaN) -> NaN everywhere; a +inf or NaN entry makes s NaN,
+ * so the whole row is NaN.  Yd (optional) receives the fp64 y before rounding.
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_softmax_rows_f16(int64_t rows, int64_t cols, const uint16_t* X, uint16_t* Y, double* Yd,
+                            int nthreads) {
+    if (rows < 0 || cols < 0) return -1;
+    if (rows == 0 || cols == 0) return 0;
+    if (!X || !Y) return -1;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 8)
+#endif
+    for (int64_t i = 0; i < rows; ++i) {
+        const uint16_t* x = X + i * cols;
+        double m = -INFINITY;
+        for (int64_t j = 0; j < cols; ++j) {
+            double v = oracle_f16_decode(x[j]);
+            if (v > m) m = v;
+        }
+        double s = 0.0;
+        for (int64_t j = 0; j < cols; ++j) s += exp(oracle_f16_decode(x[j]) - m);
+        for (int64_t j = 0; j < cols; ++j) {
+            double y = exp(oracle_f16_decode(x[j]) - m) / s;
+            if (Yd) Yd[i * cols + j] = y;
+            Y[i * cols + j] = oracle_f16_encode(y);
+        }
+    }
+    return 0;
+}
