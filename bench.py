@@ -15,6 +15,10 @@ Prints ONE JSON line:
               traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE
               counters (profiles/), null if the kernel sources changed since.
   cpu_baseline = the CPU oracle (fp64, all host threads) on a bounded sample.
+
+--workload softmax_* benchmarks the library's row softmax instead (one step =
+one softmax_rows_f16 call over the whole matrix; value in GB/s of X read plus Y
+written, against the HBM peak; copies of X rotated past the Infinity Cache).
 """
 from __future__ import annotations
 
@@ -120,6 +124,112 @@ def hbm_calibration(g, torch) -> int:
     return 0
 
 
+def cpu_baseline_softmax(w, X, target_s: float = 10.0):
+    """Time the CPU oracle's row softmax on the first R rows (R grown as for the GEMM sample)."""
+    import numpy as np
+    import oracle
+
+    threads = oracle.max_threads()
+    r, rows, dt = min(w.rows, 64), 0, 0.0
+    while True:
+        t = time.perf_counter()
+        oracle.softmax_rows(np.ascontiguousarray(X[:r]), threads=threads)
+        rows, dt = r, time.perf_counter() - t
+        if dt >= 1.0 or r >= w.rows:
+            break
+        r = min(w.rows, r * 4)
+    if dt < target_s and rows < w.rows:
+        r = int(min(w.rows, max(rows, rows * target_s / max(dt, 1e-6))))
+        t = time.perf_counter()
+        oracle.softmax_rows(np.ascontiguousarray(X[:r]), threads=threads)
+        rows, dt = r, time.perf_counter() - t
+    passes = 1
+    if rows == w.rows and dt < target_s:
+        # the whole matrix takes less than the target: repeat it for a steadier figure
+        passes = max(1, int(target_s / max(dt, 1e-6)))
+        t = time.perf_counter()
+        for _ in range(passes):
+            oracle.softmax_rows(X, threads=threads)
+        dt = (time.perf_counter() - t) / passes
+    return {"value": 4.0 * rows * w.cols / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "rows 0..%d of Y (%d x %d outputs), fp64 oracle, %.3f s wall per pass, %d pass(es)"
+                      % (rows - 1, rows, w.cols, dt, passes)}
+
+
+def bench_softmax(args, g, torch, w) -> int:
+    """Row softmax: X copies rotated (the 256 MB Infinity Cache must not serve them), HIP events on the
+    launch stream around exactly `steps` launches."""
+    import workloads
+
+    X = workloads.make_softmax_input(w)
+    rotate = args.rotate if args.rotate is not None else 3
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dXs = [torch.from_numpy(X).to(dev) for _ in range(rotate)]
+    dY = torch.empty_like(dXs[0])
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    pXs, pY = [x.data_ptr() for x in dXs], dY.data_ptr()
+    lib = g.load()
+
+    def step(i):
+        st = lib.softmax_rows_f16(w.rows, w.cols, pXs[i % rotate], pY, sh)
+        if st != 0:
+            raise g.GemmError(st)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = w.algorithmic_bytes / (ms * 1e-3) / 1e9
+
+    for i in range(5):
+        torch.softmax(dXs[i % rotate], dim=-1)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_t = max(10, min(args.steps, 100))
+    t0.record(stream)
+    for i in range(n_t):
+        torch.softmax(dXs[i % rotate], dim=-1)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    torch_ms = t0.elapsed_time(t1) / n_t
+
+    kernel = "softmax_" + g.softmax_path(w.rows, w.cols)
+    roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+            "traffic": load_traffic(w.name, kernel), "kernel": kernel,
+            "algorithmic_bytes_per_launch": w.algorithmic_bytes, "avg_launch_us": ms * 1e3}
+    cpu = None if args.no_cpu_baseline else cpu_baseline_softmax(w, X)
+    out = {
+        "metric": "fp16 row softmax GB/s (X read + Y written once) + % of MI355X HBM peak",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 in/out, f32 arithmetic",
+        "data": "synthetic",
+        "config": {"workload": w.name, "rows": w.rows, "cols": w.cols,
+                   "inputs": "seeded numpy draws (%s), X copies rotated: %d" % (w.note, rotate)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "context": {"torch_softmax_ms": round(torch_ms, 6),
+                    "torch_GBps": round(w.algorithmic_bytes / (torch_ms * 1e-3) / 1e9, 1)},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +262,8 @@ def main() -> int:
     g.load()
     if args.hbm_calibration:
         return hbm_calibration(g, torch)
+    if args.workload in workloads.SOFTMAX_WORKLOADS:
+        return bench_softmax(args, g, torch, workloads.SOFTMAX_WORKLOADS[args.workload])
     w = workloads.WORKLOADS[args.workload]
     A, B, bias = workloads.make_inputs(w)
     hbm_bound = w.flops / w.algorithmic_bytes < 100.0

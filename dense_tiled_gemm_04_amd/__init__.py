@@ -9,7 +9,9 @@ raises: there is no CPU or PyTorch fallback.
 Computes C = fp16(epi(A @ B)), epi in {none, bias, bias_gelu} with GELU in its
 exact erf form, fp32 accumulation (TileLang tutorial: blog post "Designing
 High-Performance GPU Kernels with TileLang", section "Step 4"; news article on
-TileLang kernel design, paragraphs on the tiled GEMM and the fused epilogue).
+TileLang kernel design, paragraphs on the tiled GEMM and the fused epilogue),
+and the row-wise softmax of an fp16 matrix (same news article, the closing
+sentences of the fused-epilogue paragraph).
 """
 from __future__ import annotations
 
@@ -25,11 +27,13 @@ STATUS = {
     0: "GEMM_OK", 1: "GEMM_ERR_INVALID_DIM", 2: "GEMM_ERR_NULL_POINTER", 3: "GEMM_ERR_BAD_EPILOGUE",
     4: "GEMM_ERR_LAUNCH", 5: "GEMM_ERR_NO_CONFIG", 6: "GEMM_ERR_UNSUPPORTED", 7: "GEMM_ERR_MISALIGNED",
 }
-# every symbol include/gemm_f16.h declares
+# every symbol include/gemm_f16.h and include/softmax_f16.h declare
 EXPORTS = [
     "gemm_f16", "gemm_f16_status_string", "gemm_f16_num_configs", "gemm_f16_config_info",
     "gemm_f16_select_config", "gemm_f16_with_config", "vector_add_f32",
+    "softmax_rows_f16", "softmax_rows_f16_path",
 ]
+SOFTMAX_PATHS = {0: "none", 1: "wave", 2: "workgroup", 3: "online"}
 
 _lib = None
 
@@ -64,6 +68,10 @@ def load():
     lib.gemm_f16_config_info.restype = i32
     lib.vector_add_f32.argtypes = [i64, vp, vp, vp, vp]
     lib.vector_add_f32.restype = i32
+    lib.softmax_rows_f16.argtypes = [i64, i64, vp, vp, vp]
+    lib.softmax_rows_f16.restype = i32
+    lib.softmax_rows_f16_path.argtypes = [i64, i64]
+    lib.softmax_rows_f16_path.restype = i32
     _lib = lib
     return lib
 
@@ -100,6 +108,15 @@ def gemm_f16_raw(M, N, K, A, B, bias, C, epilogue: int, stream=0, config: int | 
 
 def select_config_raw(M, N, K, A, B, bias, C, epilogue: int) -> int:
     return int(load().gemm_f16_select_config(M, N, K, A, B, bias, C, epilogue))
+
+
+def softmax_rows_raw(rows, cols, X, Y, stream=0) -> int:
+    return int(load().softmax_rows_f16(rows, cols, X, Y, stream))
+
+
+def softmax_path(rows: int, cols: int) -> str:
+    """Which softmax kernel a call of this shape runs: none, wave, workgroup or online."""
+    return SOFTMAX_PATHS[int(load().softmax_rows_f16_path(rows, cols))]
 
 
 # ---------------------------------------------------------------------------
@@ -169,6 +186,25 @@ def select_config(A, B, bias=None, epilogue: str = "none", out=None) -> int:
     if r < -1:
         raise GemmError(-r)
     return r
+
+
+def softmax_f16(X, out=None):
+    """Row-wise softmax of a contiguous float16 GPU matrix on the current stream; returns Y.
+    out may be X itself (in place)."""
+    import torch
+    _check(X, "X", 2)
+    rows, cols = X.shape
+    if out is None:
+        out = torch.empty_like(X)
+    else:
+        _check(out, "out", 2)
+        if tuple(out.shape) != (rows, cols):
+            raise ValueError("out must be [%d, %d]" % (rows, cols))
+    with torch.cuda.device(X.device):
+        st = softmax_rows_raw(rows, cols, X.data_ptr(), out.data_ptr(), _stream_handle())
+    if st != 0:
+        raise GemmError(st)
+    return out
 
 
 def vector_add(a, b, out=None):

@@ -9,15 +9,18 @@ import pytest
 import dense_tiled_gemm_04_amd as g
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gemm_f16.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(g.LIB_PATH), reason="libgemm_f16.so not built")
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", src, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", src, flags=re.M))
+    return sorted(names)
 
 
 def test_header_and_binding_agree():
@@ -133,3 +136,18 @@ def test_dispatch_shape_classes():
     assert c["loader"] == "buf"
     c = _kind(sel(1024, 1024, 1020, FAKE + 2, FAKE + 2, None, FAKE + 2, 0))
     assert c["loader"] == "reg"
+
+
+def test_softmax_validation_and_paths():
+    # bad arguments are rejected before any launch
+    assert g.softmax_rows_raw(-1, 4, FAKE, FAKE) == 1
+    assert g.softmax_rows_raw(4, 1 << 31, FAKE, FAKE) == 1
+    assert g.softmax_rows_raw(4, 4, None, FAKE) == 2
+    assert g.softmax_rows_raw(4, 4, FAKE, None) == 2
+    assert g.softmax_rows_raw(4, 4, FAKE + 1, FAKE) == 7
+    assert g.softmax_rows_raw(0, 4, None, None) == 0
+    assert g.softmax_rows_raw(4, 0, None, None) == 0
+    assert g.softmax_path(0, 10) == "none"
+    assert g.softmax_path(10, 1) == "wave" and g.softmax_path(10, 4096) == "wave"
+    assert g.softmax_path(10, 4097) == "workgroup" and g.softmax_path(10, 16384) == "workgroup"
+    assert g.softmax_path(10, 16385) == "online"

@@ -93,6 +93,45 @@ def make_inputs(w: Workload | str, M: int | None = None, N: int | None = None, K
     return A, B, bias
 
 
+@dataclasses.dataclass(frozen=True)
+class SoftmaxWorkload:
+    """Row-wise softmax of an fp16 [rows][cols] matrix (the pages give no shapes for it)."""
+    name: str
+    rows: int
+    cols: int
+    seed: int
+    dist: tuple            # ("normal", variance) or ("uniform", lo, hi)
+    note: str = ""
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """X read once and Y written once, fp16."""
+        return 2 * 2 * self.rows * self.cols
+
+
+SOFTMAX_WORKLOADS = {
+    w.name: w
+    for w in [
+        SoftmaxWorkload("softmax_8192x16384", 8192, 16384, 5, ("normal", 4.0),
+                        "row softmax over the MLP up-projection's output shape; logits N(0, 2^2)"),
+        SoftmaxWorkload("softmax_4095x3001", 4095, 3001, 6, ("normal", 4.0),
+                        "ragged rows: neither dimension a multiple of a chunk or a workgroup"),
+        SoftmaxWorkload("softmax_65536x256", 65536, 256, 7, ("normal", 4.0),
+                        "short rows: one wave per row"),
+    ]
+}
+
+
+def make_softmax_input(w: SoftmaxWorkload | str, rows: int | None = None, cols: int | None = None) -> np.ndarray:
+    """X as a float16 numpy array, drawn as for the GEMM inputs (rows/cols override the shape)."""
+    if isinstance(w, str):
+        w = SOFTMAX_WORKLOADS[w]
+    rows = w.rows if rows is None else rows
+    cols = w.cols if cols is None else cols
+    rng = np.random.default_rng(w.seed)
+    return _draw(rng, w.dist, (rows, cols)).astype(np.float16)
+
+
 def random_f16(seed: int, shape, lo: float = -1.0, hi: float = 1.0) -> np.ndarray:
     """Plain uniform fp16 draws for ad-hoc test shapes."""
     rng = np.random.default_rng(seed)
