@@ -1,5 +1,5 @@
-"""CPU oracle for the fp16 GEMM + fused bias / bias+GELU epilogue, and for the
-row-wise softmax (Python side).
+"""CPU oracle for the fp16 GEMM + fused bias / bias+GELU epilogue, the row-wise
+softmax and the attention forward pass (Python side).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  It shares no code with
@@ -62,6 +62,9 @@ def _load():
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_softmax_rows_f16.argtypes = [i64, i64, p, p, p, ctypes.c_int]
     lib.oracle_softmax_rows_f16.restype = ctypes.c_int
+    lib.oracle_attention_f16.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, ctypes.c_int, ctypes.c_double,
+                                         ctypes.c_int]
+    lib.oracle_attention_f16.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -141,6 +144,30 @@ def softmax_rows(X, want_y: bool = False, threads: int = 0):
         raise RuntimeError("oracle_softmax_rows_f16 failed (%d)" % rc)
     Y = Y.view(np.float16)
     return (Y, Yd) if want_y else Y
+
+
+def attention(Q, K, V, causal: bool = False, scale: float | None = None, want_y: bool = False,
+              threads: int = 0):
+    """Attention forward in fp64, rounded once to fp16.  Q [B,H,Nq,D], K and V [B,H,Nkv,D] (fp16).
+    scale defaults to 1/sqrt(D); causal masks keys j > i (top-left aligned)."""
+    lib = _load()
+    Q16, K16, V16 = _bits(Q), _bits(K), _bits(V)
+    if Q16.ndim != 4 or K16.shape != V16.shape or K16.ndim != 4:
+        raise ValueError("expected Q [B,H,Nq,D] and K, V [B,H,Nkv,D]")
+    Bn, Hn, Nq, D = Q16.shape
+    if K16.shape[0] != Bn or K16.shape[1] != Hn or K16.shape[3] != D:
+        raise ValueError("Q, K, V shapes disagree")
+    Nkv = K16.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    O = np.empty(Q16.shape, dtype=np.uint16)
+    Od = np.empty(Q16.shape, dtype=np.float64) if want_y else None
+    rc = lib.oracle_attention_f16(Bn, Hn, Nq, Nkv, D, _ptr(Q16), _ptr(K16), _ptr(V16), _ptr(O), _ptr(Od),
+                                  1 if causal else 0, float(scale), threads)
+    if rc != 0:
+        raise RuntimeError("oracle_attention_f16 failed (%d)" % rc)
+    O = O.view(np.float16)
+    return (O, Od) if want_y else O
 
 
 def f16_decode(bits) -> np.ndarray:

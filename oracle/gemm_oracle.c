@@ -257,3 +257,78 @@ int oracle_softmax_rows_f16(int64_t rows, int64_t cols, const uint16_t* X, uint1
     }
     return 0;
 }
+
+/*
+ * Attention forward, the tutorial's FlashAttention workload (news article on
+ * TileLang kernel design, paragraph on FlashAttention: query, key and value
+ * tiles, an online softmax with running maxima, normalising sums and rescale
+ * factors, causal and non-causal variants, checked against PyTorch's scaled
+ * dot-product attention; blog post on TileLang, "three-piece set" section,
+ * item 3).  The tiled online form only reorganises this plain definition, so
+ * the oracle is the definition itself, in fp64:
+ *   for each batch b, head h and query row i:
+ *     s_j = scale * sum_d Q[i][d] K[j][d]     over the allowed keys j
+ *           (j < Nkv; causal: also j <= i, the top-left-aligned mask of
+ *            PyTorch's is_causal)
+ *     m   = max_j s_j,  p_j = exp(s_j - m),  l = sum_j p_j
+ *     O[i][d] = fp16_round_nearest_even( sum_j p_j V[j][d] / l )
+ * Q is [B][H][Nq][D], K and V are [B][H][Nkv][D], O is [B][H][Nq][D], all
+ * row-major fp16.  Sums run in increasing d and j.  A query row with no
+ * allowed key (causal with Nkv == 0 only) is not defined; Nkv must be >= 1.
+ * Od (optional) receives the fp64 values before rounding.
+ * Returns 0, or -1 on a bad argument or an allocation failure.
+ */
+int oracle_attention_f16(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, const uint16_t* Q,
+                         const uint16_t* K, const uint16_t* V, uint16_t* O, double* Od, int causal, double scale,
+                         int nthreads) {
+    if (B < 0 || H < 0 || Nq < 0 || Nkv < 1 || D < 1) return -1;
+    if (B == 0 || H == 0 || Nq == 0) return 0;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+    {
+        double* s = (double*)malloc((size_t)Nkv * sizeof(double));
+        double* acc = (double*)malloc((size_t)D * sizeof(double));
+        if (!s || !acc) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            failed = 1;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 4)
+#endif
+            for (int64_t r = 0; r < B * H * Nq; ++r) {
+                const int64_t bh = r / Nq, i = r % Nq;
+                const uint16_t* q = Q + r * D;
+                const uint16_t* k = K + bh * Nkv * D;
+                const uint16_t* v = V + bh * Nkv * D;
+                const int64_t nj = causal ? (i + 1 < Nkv ? i + 1 : Nkv) : Nkv;
+                double m = -INFINITY;
+                for (int64_t j = 0; j < nj; ++j) {
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < D; ++d) dot += oracle_f16_decode(q[d]) * oracle_f16_decode(k[j * D + d]);
+                    s[j] = scale * dot;
+                    if (s[j] > m) m = s[j];
+                }
+                double l = 0.0;
+                for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+                for (int64_t j = 0; j < nj; ++j) {
+                    const double p = exp(s[j] - m);
+                    l += p;
+                    for (int64_t d = 0; d < D; ++d) acc[d] += p * oracle_f16_decode(v[j * D + d]);
+                }
+                for (int64_t d = 0; d < D; ++d) {
+                    const double y = acc[d] / l;
+                    if (Od) Od[r * D + d] = y;
+                    O[r * D + d] = oracle_f16_encode(y);
+                }
+            }
+        }
+        free(s);
+        free(acc);
+    }
+    return failed ? -1 : 0;
+}
