@@ -65,6 +65,9 @@ def _load():
     lib.oracle_attention_f16.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, ctypes.c_int, ctypes.c_double,
                                          ctypes.c_int]
     lib.oracle_attention_f16.restype = ctypes.c_int
+    lib.oracle_attention_f16_rows.argtypes = [i64, i64, i64, i64, i64, p, p, p, ctypes.c_int, ctypes.c_double, i64,
+                                              p, p, p, ctypes.c_int]
+    lib.oracle_attention_f16_rows.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -166,6 +169,26 @@ def attention(Q, K, V, causal: bool = False, scale: float | None = None, want_y:
                                   1 if causal else 0, float(scale), threads)
     if rc != 0:
         raise RuntimeError("oracle_attention_f16 failed (%d)" % rc)
+    O = O.view(np.float16)
+    return (O, Od) if want_y else O
+
+
+def attention_rows(Q, K, V, rows, causal: bool = False, scale: float | None = None, want_y: bool = False,
+                   threads: int = 0):
+    """Selected output rows of attention(): rows are flat indices (b*H + h)*Nq + i; returns [len(rows), D]."""
+    lib = _load()
+    Q16, K16, V16 = _bits(Q), _bits(K), _bits(V)
+    Bn, Hn, Nq, D = Q16.shape
+    Nkv = K16.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    O = np.empty((r.shape[0], D), dtype=np.uint16)
+    Od = np.empty((r.shape[0], D), dtype=np.float64) if want_y else None
+    rc = lib.oracle_attention_f16_rows(Bn, Hn, Nq, Nkv, D, _ptr(Q16), _ptr(K16), _ptr(V16), 1 if causal else 0,
+                                       float(scale), r.shape[0], _ptr(r), _ptr(O), _ptr(Od), threads)
+    if rc != 0:
+        raise RuntimeError("oracle_attention_f16_rows failed (%d)" % rc)
     O = O.view(np.float16)
     return (O, Od) if want_y else O
 

@@ -273,16 +273,56 @@ int oracle_softmax_rows_f16(int64_t rows, int64_t cols, const uint16_t* X, uint1
  *     m   = max_j s_j,  p_j = exp(s_j - m),  l = sum_j p_j
  *     O[i][d] = fp16_round_nearest_even( sum_j p_j V[j][d] / l )
  * Q is [B][H][Nq][D], K and V are [B][H][Nkv][D], O is [B][H][Nq][D], all
- * row-major fp16.  Sums run in increasing d and j.  A query row with no
- * allowed key (causal with Nkv == 0 only) is not defined; Nkv must be >= 1.
+ * row-major fp16.  Sums run in increasing d and j.  Nkv must be >= 1, so
+ * every query row has at least key 0.
  * Od (optional) receives the fp64 values before rounding.
  * Returns 0, or -1 on a bad argument or an allocation failure.
  */
-int oracle_attention_f16(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, const uint16_t* Q,
-                         const uint16_t* K, const uint16_t* V, uint16_t* O, double* Od, int causal, double scale,
-                         int nthreads) {
-    if (B < 0 || H < 0 || Nq < 0 || Nkv < 1 || D < 1) return -1;
+/* One query row: output row r = (b*H + h)*Nq + i of O (and of Od when given). */
+static void attention_row(int64_t H, int64_t Nq, int64_t Nkv, int64_t D, const uint16_t* Q, const uint16_t* K,
+                          const uint16_t* V, int64_t r, int causal, double scale, double* s, double* acc,
+                          uint16_t* O_row, double* Od_row) {
+    const int64_t bh = r / Nq, i = r % Nq;
+    (void)H;
+    const uint16_t* q = Q + r * D;
+    const uint16_t* k = K + bh * Nkv * D;
+    const uint16_t* v = V + bh * Nkv * D;
+    const int64_t nj = causal ? (i + 1 < Nkv ? i + 1 : Nkv) : Nkv;
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nj; ++j) {
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += oracle_f16_decode(q[d]) * oracle_f16_decode(k[j * D + d]);
+        s[j] = scale * dot;
+        if (s[j] > m) m = s[j];
+    }
+    double l = 0.0;
+    for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+    for (int64_t j = 0; j < nj; ++j) {
+        const double pj = exp(s[j] - m);
+        l += pj;
+        for (int64_t d = 0; d < D; ++d) acc[d] += pj * oracle_f16_decode(v[j * D + d]);
+    }
+    for (int64_t d = 0; d < D; ++d) {
+        const double y = acc[d] / l;
+        if (Od_row) Od_row[d] = y;
+        O_row[d] = oracle_f16_encode(y);
+    }
+}
+
+/*
+ * rows == NULL: every output row r = (b*H + h)*Nq + i, into O[r*D ..].
+ * rows != NULL: only the nrows rows listed (each in [0, B*H*Nq)), into
+ * O[t*D ..] for the t-th listed row; for checking large shapes at samples.
+ */
+static int attention_impl(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, const uint16_t* Q,
+                          const uint16_t* K, const uint16_t* V, uint16_t* O, double* Od, int causal, double scale,
+                          int64_t nrows, const int64_t* rows, int nthreads) {
+    if (B < 0 || H < 0 || Nq < 0 || Nkv < 1 || D < 1 || nrows < 0) return -1;
     if (B == 0 || H == 0 || Nq == 0) return 0;
+    const int64_t total = rows ? nrows : B * H * Nq;
+    if (rows)
+        for (int64_t t = 0; t < nrows; ++t)
+            if (rows[t] < 0 || rows[t] >= B * H * Nq) return -1;
     int failed = 0;
 #ifdef _OPENMP
     if (nthreads <= 0) nthreads = omp_get_max_threads();
@@ -300,35 +340,25 @@ int oracle_attention_f16(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t 
 #ifdef _OPENMP
 #pragma omp for schedule(dynamic, 4)
 #endif
-            for (int64_t r = 0; r < B * H * Nq; ++r) {
-                const int64_t bh = r / Nq, i = r % Nq;
-                const uint16_t* q = Q + r * D;
-                const uint16_t* k = K + bh * Nkv * D;
-                const uint16_t* v = V + bh * Nkv * D;
-                const int64_t nj = causal ? (i + 1 < Nkv ? i + 1 : Nkv) : Nkv;
-                double m = -INFINITY;
-                for (int64_t j = 0; j < nj; ++j) {
-                    double dot = 0.0;
-                    for (int64_t d = 0; d < D; ++d) dot += oracle_f16_decode(q[d]) * oracle_f16_decode(k[j * D + d]);
-                    s[j] = scale * dot;
-                    if (s[j] > m) m = s[j];
-                }
-                double l = 0.0;
-                for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
-                for (int64_t j = 0; j < nj; ++j) {
-                    const double p = exp(s[j] - m);
-                    l += p;
-                    for (int64_t d = 0; d < D; ++d) acc[d] += p * oracle_f16_decode(v[j * D + d]);
-                }
-                for (int64_t d = 0; d < D; ++d) {
-                    const double y = acc[d] / l;
-                    if (Od) Od[r * D + d] = y;
-                    O[r * D + d] = oracle_f16_encode(y);
-                }
+            for (int64_t t = 0; t < total; ++t) {
+                const int64_t r = rows ? rows[t] : t;
+                attention_row(H, Nq, Nkv, D, Q, K, V, r, causal, scale, s, acc, O + t * D, Od ? Od + t * D : NULL);
             }
         }
         free(s);
         free(acc);
     }
     return failed ? -1 : 0;
+}
+
+int oracle_attention_f16(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, const uint16_t* Q,
+                         const uint16_t* K, const uint16_t* V, uint16_t* O, double* Od, int causal, double scale,
+                         int nthreads) {
+    return attention_impl(B, H, Nq, Nkv, D, Q, K, V, O, Od, causal, scale, 0, NULL, nthreads);
+}
+
+int oracle_attention_f16_rows(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, const uint16_t* Q,
+                              const uint16_t* K, const uint16_t* V, int causal, double scale, int64_t nrows,
+                              const int64_t* rows, uint16_t* O_rows, double* Od_rows, int nthreads) {
+    return attention_impl(B, H, Nq, Nkv, D, Q, K, V, O_rows, Od_rows, causal, scale, nrows, rows, nthreads);
 }

@@ -122,3 +122,14 @@ def test_rejects_zero_keys():
     Q, K, V = _draw(8, 1, 1, 3, 1, 4)
     with pytest.raises(RuntimeError):
         oracle.attention(Q, K[:, :, :0], V[:, :, :0])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_selected_rows_equal_the_full_computation(causal):
+    Q, K, V = _draw(9, 2, 3, 21, 17, 8)
+    full = oracle.attention(Q, K, V, causal=causal).reshape(-1, 8)
+    rows = np.array([0, 5, 20, 21, 62, 63, 125, 64, 3])
+    part = oracle.attention_rows(Q, K, V, rows, causal=causal)
+    assert np.array_equal(part.view(np.uint16), full[rows].view(np.uint16))
+    with pytest.raises(RuntimeError):
+        oracle.attention_rows(Q, K, V, np.array([2 * 3 * 21]), causal=causal)
