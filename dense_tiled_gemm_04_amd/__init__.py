@@ -10,8 +10,9 @@ Computes C = fp16(epi(A @ B)), epi in {none, bias, bias_gelu} with GELU in its
 exact erf form, fp32 accumulation (TileLang tutorial: blog post "Designing
 High-Performance GPU Kernels with TileLang", section "Step 4"; news article on
 TileLang kernel design, paragraphs on the tiled GEMM and the fused epilogue),
-and the row-wise softmax of an fp16 matrix (same news article, the closing
-sentences of the fused-epilogue paragraph).
+the row-wise softmax of an fp16 matrix (same news article, the closing
+sentences of the fused-epilogue paragraph) and the attention forward pass
+(same news article, paragraph on FlashAttention).
 """
 from __future__ import annotations
 
@@ -27,11 +28,11 @@ STATUS = {
     0: "GEMM_OK", 1: "GEMM_ERR_INVALID_DIM", 2: "GEMM_ERR_NULL_POINTER", 3: "GEMM_ERR_BAD_EPILOGUE",
     4: "GEMM_ERR_LAUNCH", 5: "GEMM_ERR_NO_CONFIG", 6: "GEMM_ERR_UNSUPPORTED", 7: "GEMM_ERR_MISALIGNED",
 }
-# every symbol include/gemm_f16.h and include/softmax_f16.h declare
+# every symbol the headers under include/ declare
 EXPORTS = [
     "gemm_f16", "gemm_f16_status_string", "gemm_f16_num_configs", "gemm_f16_config_info",
     "gemm_f16_select_config", "gemm_f16_with_config", "vector_add_f32",
-    "softmax_rows_f16", "softmax_rows_f16_path",
+    "softmax_rows_f16", "softmax_rows_f16_path", "flash_attn_fwd_f16",
 ]
 SOFTMAX_PATHS = {0: "none", 1: "wave", 2: "workgroup", 3: "online"}
 
@@ -72,6 +73,8 @@ def load():
     lib.softmax_rows_f16.restype = i32
     lib.softmax_rows_f16_path.argtypes = [i64, i64]
     lib.softmax_rows_f16_path.restype = i32
+    lib.flash_attn_fwd_f16.argtypes = [i64, i64, i64, i64, i64, vp, vp, vp, vp, i32, ctypes.c_float, vp]
+    lib.flash_attn_fwd_f16.restype = i32
     _lib = lib
     return lib
 
@@ -202,6 +205,37 @@ def softmax_f16(X, out=None):
             raise ValueError("out must be [%d, %d]" % (rows, cols))
     with torch.cuda.device(X.device):
         st = softmax_rows_raw(rows, cols, X.data_ptr(), out.data_ptr(), _stream_handle())
+    if st != 0:
+        raise GemmError(st)
+    return out
+
+
+def flash_attn_raw(B, H, Nq, Nkv, D, Q, K, V, O, causal: bool, scale: float, stream=0) -> int:
+    return int(load().flash_attn_fwd_f16(B, H, Nq, Nkv, D, Q, K, V, O, 1 if causal else 0, float(scale), stream))
+
+
+def flash_attn(Q, K, V, causal: bool = False, scale: float | None = None, out=None):
+    """Attention forward on contiguous float16 GPU tensors Q [B,H,Nq,D], K and V [B,H,Nkv,D] on the current
+    stream; D is 64 or 128, scale defaults to 1/sqrt(D), causal masks keys j > i.  Returns O [B,H,Nq,D]."""
+    import math
+    import torch
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
+        _check(t, n, 4)
+    Bn, Hn, Nq, D = Q.shape
+    if tuple(K.shape) != tuple(V.shape) or K.shape[0] != Bn or K.shape[1] != Hn or K.shape[3] != D:
+        raise ValueError("K and V must be [B, H, Nkv, D] matching Q [B, H, Nq, D]")
+    Nkv = K.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(Q)
+    else:
+        _check(out, "out", 4)
+        if tuple(out.shape) != tuple(Q.shape):
+            raise ValueError("out must have Q's shape")
+    with torch.cuda.device(Q.device):
+        st = flash_attn_raw(Bn, Hn, Nq, Nkv, D, Q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr(), causal,
+                            scale, _stream_handle())
     if st != 0:
         raise GemmError(st)
     return out

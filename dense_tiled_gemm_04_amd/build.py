@@ -1,8 +1,9 @@
 """Build the gfx950 HIP library libgemm_f16.so in-tree with hipcc.
 
-Two translation units: csrc/gemm_f16.hip (every GEMM kernel instantiation and
-the C ABI of include/gemm_f16.h) and csrc/softmax.hip (the row softmax, C ABI
-in include/softmax_f16.h).  Flags: gfx950 only, -O3, no
+Three translation units: csrc/gemm_f16.hip (every GEMM kernel instantiation and
+the C ABI of include/gemm_f16.h), csrc/softmax.hip (the row softmax, C ABI in
+include/softmax_f16.h) and csrc/attention.hip (the attention forward pass, C ABI
+in include/attention_f16.h).  Flags: gfx950 only, -O3, no
 fast-math, packed-fp32 VALU instructions disabled.
 """
 from __future__ import annotations
@@ -17,9 +18,9 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libgemm_f16.so")
-SOURCES = [os.path.join(CSRC, "gemm_f16.hip"), os.path.join(CSRC, "softmax.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("gemm_f16.hip", "softmax.hip", "attention.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("common.h", "tile_pipe_kernel.h", "skinny_kernel.h")] + [
-    os.path.join(INCLUDE, "gemm_f16.h"), os.path.join(INCLUDE, "softmax_f16.h")
+    os.path.join(INCLUDE, "gemm_f16.h"), os.path.join(INCLUDE, "softmax_f16.h"), os.path.join(INCLUDE, "attention_f16.h")
 ]
 
 

@@ -1,0 +1,307 @@
+// Attention forward (FlashAttention) on gfx950 for fp16 Q, K, V with fp32
+// softmax state: the tutorial's fused attention kernel (news article on TileLang
+// kernel design, paragraph on FlashAttention: query, key and value tiles, no
+// attention matrix in global memory, an online softmax with running maxima,
+// normalising sums and rescale factors, tiled matrix-core products, causal and
+// non-causal; blog post on TileLang, "three-piece set" section, item 3).
+//
+//   O[i] = sum_j softmax_j(scale * Q[i] . K[j]) V[j],  j < Nkv (causal: j <= i)
+//
+// One workgroup = 4 wave64s owns a block of 128 query rows of one (batch, head);
+// wave w owns rows 32w .. 32w+31 of it.  Per 64-key block:
+//  * K and V tiles [64][D] sit in LDS, double-buffered; the next block's tiles
+//    are copied by LDS-DMA (buffer_load_dwordx4 ... lds) while this block is
+//    computed.  The buffer range check ends at key Nkv, so keys past the end
+//    read as zeros (their scores are masked to -inf as well).
+//  * Scores are computed transposed, S^T = K . Q^T, with
+//    v_mfma_f32_32x32x16_f16: the A operand is K straight from LDS (ds_read_b128,
+//    a key row is K-contiguous), the B operand is Q^T held in registers for the
+//    whole loop.  In that layout lane l owns query row l % 32 and 16 keys per
+//    32-key block, so the running max, the rescale factor and the running sum
+//    of a row live in one lane (plus its partner lane l ^ 32).
+//  * O^T += V^T . P^T with the same MFMA.  The B operand P^T needs, per lane,
+//    8 keys of its query row; within every 16-key step the MFMA's k index is
+//    mapped to keys so that these 8 are exactly 8 consecutive accumulator
+//    registers of S^T (k = 8 (l/32) + 4 h + t  <->  key 8 h + 4 (l/32) + t).
+//    P is converted to fp16 in place and needs no shuffle.  The A operand V^T
+//    comes from two LDS transpose reads (ds_read_b64_tr_b16) per 16-key step,
+//    using the same key mapping.
+//  * The softmax state is fp32 and scaled by log2(e), so every exponential is one
+//    v_exp_f32.  The probabilities enter the PV product rounded to fp16, and the
+//    row sum adds those same rounded values, so each output row is an exact
+//    convex combination of value rows up to fp32 rounding.
+//  * Causal: key blocks past the workgroup's last row are never visited; a wave
+//    skips the blocks that lie wholly past its own rows; masks are applied only
+//    in blocks that cross the diagonal or the end of the keys.  Workgroups are
+//    launched longest-first.
+// LDS tiles are XOR-swizzled in 16-byte chunks so that both read forms are free
+// of bank conflicts.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "attention_f16.h"
+#include "common.h"
+#include "gemm_f16.h"
+
+using namespace gk;
+
+namespace {
+
+constexpr int FA_BM = 128;   // query rows per workgroup
+constexpr int FA_BN = 64;    // keys per block
+constexpr int FA_NW = 4;     // waves per workgroup
+constexpr float kLog2e = 1.44269504088896341f;
+
+struct FaArgs {
+    const f16* Q;
+    const f16* K;
+    const f16* V;
+    f16* O;
+    int Nq, Nkv;
+    int q_blocks;
+    float scale_log2;  // scale * log2(e)
+};
+
+// K tile [64][D]: logical chunk c of key row j at c ^ swz_k(j).  A ds_read_b128
+// quarter-wave reads one logical chunk of 16 consecutive rows; the XOR puts
+// them in 16 distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int swz_k(int j) {
+    return D == 128 ? (j & 15) : ((j >> 1) & 7);
+}
+// V tile [64][D]: a transpose read touches 4 consecutive rows x 64 bytes per
+// half-wave; the XOR spreads those 16 chunks over distinct bank groups
+// (D = 128: rows 256 bytes apart, shift by 4 chunks per row; D = 64: rows 128
+// bytes apart, pairs of rows share a 256-byte window, shift every other pair).
+template <int D>
+__device__ __forceinline__ int swz_v(int j) {
+    return D == 128 ? 4 * (j & 3) : 4 * ((j >> 1) & 1);
+}
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(FA_NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+flash_attn_fwd_kernel(FaArgs p) {
+    constexpr int CH = D / 8;                    // 16-byte chunks per row
+    constexpr int TILE = FA_BN * D * 2;          // bytes of one K or V tile
+    constexpr int INS = FA_BN * CH / (FA_NW * 64);  // copies per lane per tile
+    constexpr int KS = D / 16;                   // k-steps of the score product
+    constexpr int JB = FA_BN / 32;               // 32-key blocks per key block
+    constexpr int DB = D / 32;                   // 32-column blocks of the output
+    static_assert(D == 64 || D == 128, "head dimension");
+    static_assert(INS * FA_NW * 64 == FA_BN * CH, "copy split");
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K[2] | V[2]
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int Nq = p.Nq, Nkv = p.Nkv;
+    int qb = (int)(blockIdx.x % (unsigned)p.q_blocks);
+    const int64_t bh = blockIdx.x / (unsigned)p.q_blocks;
+    if (CAUSAL) qb = p.q_blocks - 1 - qb;  // longest rows first
+    const int q0 = qb * FA_BM;
+    const int row0 = q0 + 32 * wave_s;      // first query row of this wave
+    const int i = row0 + (lane & 31);       // this lane's query row
+    const f16* Qp = p.Q + bh * (int64_t)Nq * D;
+    f16* Op = p.O + bh * (int64_t)Nq * D;
+
+    // Q^T fragments for the whole loop: lane l holds Q[i][16 ks + 8 (l/32) .. +7].
+    f16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        if (i < Nq) {
+            qf[ks] = *(const f16x8*)(Qp + (int64_t)i * D + 16 * ks + 8 * (lane >> 5));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qf[ks][e] = (f16)0.0f;
+        }
+    }
+
+    // copies: destination chunk P = (t * 4 + wave) * 64 + lane of a tile, key row P / CH
+    const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.K + bh * (int64_t)Nkv * D), (short)0, Nkv * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.V + bh * (int64_t)Nkv * D), (short)0, Nkv * D * 2, 0x00020000);
+    uint32_t k_off[INS], v_off[INS];
+#pragma unroll
+    for (int t = 0; t < INS; ++t) {
+        const int P = (t * FA_NW + wave) * 64 + lane, jr = P / CH, pc = P % CH;
+        k_off[t] = (uint32_t)((jr * D + 8 * (pc ^ swz_k<D>(jr))) * 2);
+        v_off[t] = (uint32_t)((jr * D + 8 * (pc ^ swz_v<D>(jr))) * 2);
+    }
+    const uint32_t lds0 = lds_addr((GK_LDS char*)smem) + wave_s * 64 * 16;
+    auto issue = [&](int jb, int buf) {
+        const uint32_t kv = (uint32_t)jb * FA_BN * D * 2;
+#pragma unroll
+        for (int t = 0; t < INS; ++t) {
+            dma_buffer_16(k_rsrc, k_off[t] + kv, lds0 + buf * TILE + t * FA_NW * 64 * 16);
+            dma_buffer_16(v_rsrc, v_off[t] + kv, lds0 + (2 + buf) * TILE + t * FA_NW * 64 * 16);
+        }
+    };
+
+    // LDS read offsets (bytes within a tile)
+    int k_rd[JB][KS];
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int jr = 32 * jj + (lane & 31), c = 2 * ks + (lane >> 5);
+            k_rd[jj][ks] = jr * D * 2 + ((c ^ swz_k<D>(jr)) << 4);
+        }
+    // V^T: lane L = 16 g + 4 jq + q addresses V[key][col .. col+3] and receives
+    // 4 keys of column 16 (g & 1) + L % 16; keys 16 step + 4 (g >> 1) + 8 h + jq.
+    int v_rd[2][DB];
+    {
+        const int g = lane >> 4, jq = (lane >> 2) & 3, q = lane & 3;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int jr = 4 * (g >> 1) + 8 * h + jq, col = 32 * db + 16 * (g & 1) + 4 * q;
+                v_rd[h][db] = jr * D * 2 + (((col >> 3) ^ swz_v<D>(jr)) << 4) + ((col & 7) << 1);
+            }
+    }
+    // the V swizzle depends on the key row only through (j & 3) / ((j >> 1) & 1),
+    // which a shift by a multiple of 16 keys keeps, so one offset per (h, db)
+    // serves every 16-key step at + 16 step * D * 2 bytes.
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    const int kv_blocks_all = (Nkv + FA_BN - 1) / FA_BN;
+    const int kv_blocks = CAUSAL ? min(kv_blocks_all, (q0 + FA_BM - 1) / FA_BN + 1) : kv_blocks_all;
+    if (kv_blocks > 0) issue(0, 0);
+
+    for (int jb = 0; jb < kv_blocks; ++jb) {
+        const int buf = jb & 1;
+        wait_vmcnt0();
+        __syncthreads();  // block jb in LDS for every wave; block jb-1's buffer free
+        if (jb + 1 < kv_blocks) issue(jb + 1, buf ^ 1);
+        const int kv0 = jb * FA_BN;
+        if (CAUSAL && kv0 > row0 + 31) continue;  // every key of the block is past this wave's rows
+
+        const GK_LDS char* Ks = (const GK_LDS char*)smem + buf * TILE;
+        const GK_LDS char* Vs = (const GK_LDS char*)smem + (2 + buf) * TILE;
+        f32x16 s[JB];
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[jj][r] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const f16x8 kf = *(const GK_LDS f16x8*)(Ks + k_rd[jj][ks]);
+                s[jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[jj], 0, 0, 0);
+            }
+        }
+        // scale (into the log2 domain), mask, block max
+        const bool need_mask = kv0 + FA_BN > Nkv || (CAUSAL && kv0 + FA_BN - 1 > row0);
+        float mb = -INFINITY;
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float v = s[jj][r] * p.scale_log2;
+                if (need_mask) {
+                    const int j = kv0 + 32 * jj + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (j >= Nkv || (CAUSAL && j > i)) v = -INFINITY;
+                }
+                s[jj][r] = v;
+                mb = fmaxf(mb, v);
+            }
+        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+        const float m_new = fmaxf(m_run, mb);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;  // a row with no key yet: keep p = 0
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        // probabilities, rounded to fp16 for the P^T operand; the row sum adds the
+        // same rounded values, so the weights applied to V sum to one
+        f16x8 pf[JB][2];
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const f16 ph = (f16)__builtin_amdgcn_exp2f(s[jj][r] - m_use);
+                l_run += (float)ph;
+                pf[jj][r >> 3][r & 7] = ph;
+            }
+        // O^T += V^T . P^T, 16 keys per step
+#pragma unroll
+        for (int st = 0; st < FA_BN / 16; ++st) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const f16x4 v0 = lds_read_tr16_b64(Vs + v_rd[0][db] + st * 16 * D * 2);
+                const f16x4 v1 = lds_read_tr16_b64(Vs + v_rd[1][db] + st * 16 * D * 2);
+                const f16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[st >> 1][st & 1], oacc[db], 0, 0, 0);
+            }
+        }
+    }
+
+    // normalise and write: lane l, register r of block db holds O[i][32 db + 8 (r/4) + 4 (l/32) + r % 4]
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = 1.0f / l_tot;
+    if (i < Nq) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                f16x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = (f16)(oacc[db][4 * r4 + e] * inv);
+                *(f16x4*)(Op + (int64_t)i * D + 32 * db + 8 * r4 + 4 * (lane >> 5)) = o;
+            }
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const FaArgs& a, int64_t BH, hipStream_t s) {
+    hipLaunchKernelGGL((flash_attn_fwd_kernel<D, CAUSAL>), dim3((unsigned)(BH * a.q_blocks)), dim3(FA_NW * 64), 0, s,
+                       a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+int flash_attn_fwd_f16(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, const void* Q, const void* K,
+                       const void* V, void* O, int causal, float scale, void* stream) {
+    if (B < 0 || H < 0 || Nq < 0 || Nkv < 0 || D < 0) return GEMM_ERR_INVALID_DIM;
+    if (B == 0 || H == 0 || Nq == 0) return GEMM_OK;
+    if (Nkv == 0) return GEMM_ERR_INVALID_DIM;  // a query with no key has no softmax
+    if (D != 64 && D != 128) return GEMM_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return GEMM_ERR_INVALID_DIM;
+    if (!Q || !K || !V || !O) return GEMM_ERR_NULL_POINTER;
+    if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) % 16 != 0) return GEMM_ERR_MISALIGNED;
+    const int64_t q_blocks = (Nq + FA_BM - 1) / FA_BM;
+    // 32-bit buffer sizes per (batch, head) slab and a 32-bit grid
+    if (Nkv * D * 2 > INT32_MAX - 1024 || Nq > INT32_MAX / 2 || B * H * q_blocks > INT32_MAX)
+        return GEMM_ERR_INVALID_DIM;
+    FaArgs a;
+    a.Q = (const f16*)Q;
+    a.K = (const f16*)K;
+    a.V = (const f16*)V;
+    a.O = (f16*)O;
+    a.Nq = (int)Nq;
+    a.Nkv = (int)Nkv;
+    a.q_blocks = (int)q_blocks;
+    a.scale_log2 = scale * kLog2e;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (D == 128) {
+        e = causal ? launch<128, true>(a, B * H, s) : launch<128, false>(a, B * H, s);
+    } else {
+        e = causal ? launch<64, true>(a, B * H, s) : launch<64, false>(a, B * H, s);
+    }
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -151,3 +151,15 @@ def test_softmax_validation_and_paths():
     assert g.softmax_path(10, 1) == "wave" and g.softmax_path(10, 4096) == "wave"
     assert g.softmax_path(10, 4097) == "workgroup" and g.softmax_path(10, 16384) == "workgroup"
     assert g.softmax_path(10, 16385) == "online"
+
+
+def test_attention_validation():
+    fa = g.flash_attn_raw
+    assert fa(-1, 1, 4, 4, 64, FAKE, FAKE, FAKE, FAKE, False, 0.1) == 1
+    assert fa(1, 1, 4, 0, 64, FAKE, FAKE, FAKE, FAKE, False, 0.1) == 1     # no key
+    assert fa(1, 1, 4, 4, 64, FAKE, FAKE, FAKE, FAKE, False, float("nan")) == 1
+    assert fa(1, 1, 4, 4, 96, FAKE, FAKE, FAKE, FAKE, False, 0.1) == 6     # head dimension
+    assert fa(1, 1, 4, 4, 64, None, FAKE, FAKE, FAKE, False, 0.1) == 2
+    assert fa(1, 1, 4, 4, 64, FAKE + 8, FAKE, FAKE, FAKE, False, 0.1) == 7
+    assert fa(0, 1, 4, 4, 64, None, None, None, None, False, 0.1) == 0
+    assert fa(1, 1, 0, 0, 64, None, None, None, None, True, 0.1) == 0

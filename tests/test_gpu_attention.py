@@ -1,0 +1,119 @@
+"""GPU parity of the attention forward pass (through the C ABI) against the CPU oracle.
+
+Covers both head dimensions, causal and non-causal masks, query and key lengths
+that are not multiples of the 128-row query block or the 64-key block, more
+queries than keys and the reverse, one key, explicit scales, constant values,
+very peaked scores, and the four attention workloads at full size on sampled
+query rows (first and last rows, block edges, random rows), which the oracle
+computes row by row with the same absolute row index.  Bar: relative Frobenius
+error <= 2e-3 and max |o - ref| / (1 + |ref|) <= 1e-2 (the GEMM's), no NaN.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def run(lib, Q, K, V, causal, scale=None):
+    o = lib.flash_attn(dev(Q), dev(K), dev(V), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.cpu().numpy()
+
+
+SHAPES = [  # B, H, Nq, Nkv
+    (1, 1, 1, 1), (1, 2, 100, 100), (2, 3, 129, 129), (1, 1, 200, 77), (1, 1, 77, 300),
+    (1, 2, 513, 513), (2, 2, 256, 1000), (1, 1, 64, 64), (1, 3, 130, 65),
+]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_shapes(lib, shape, causal, D):
+    B, H, Nq, Nkv = shape
+    rng = np.random.default_rng(Nq * 7 + Nkv + D)
+    Q = rng.standard_normal((B, H, Nq, D)).astype(np.float16)
+    K = rng.standard_normal((B, H, Nkv, D)).astype(np.float16)
+    V = rng.standard_normal((B, H, Nkv, D)).astype(np.float16)
+    ref = oracle.attention(Q, K, V, causal=causal)
+    got = run(lib, Q, K, V, causal)
+    assert_parity(got, ref, (shape, causal, D))
+
+
+@pytest.mark.parametrize("scale", [0.0, 0.05, 1.0])
+def test_explicit_scales(lib, scale):
+    Q, K, V = workloads.make_attention_inputs("attn_b2_h16_n1000_d64_causal", B=1, H=2, Nq=300, Nkv=300)
+    for causal in (False, True):
+        ref = oracle.attention(Q, K, V, causal=causal, scale=scale)
+        got = run(lib, Q, K, V, causal, scale=scale)
+        assert_parity(got, ref, (scale, causal))
+
+
+def test_constant_values_and_peaked_scores(lib):
+    rng = np.random.default_rng(3)
+    D, N = 128, 300
+    Q = (rng.standard_normal((1, 2, N, D)) * 4).astype(np.float16)   # scores with a spread of ~60: near one-hot
+    K = (rng.standard_normal((1, 2, N, D)) * 4).astype(np.float16)
+    V = np.full((1, 2, N, D), 0.75, np.float16)
+    for causal in (False, True):
+        got = run(lib, Q, K, V, causal)
+        assert np.all(got == np.float16(0.75)), causal        # any convex combination of equal rows
+        V2 = rng.standard_normal((1, 2, N, D)).astype(np.float16)
+        ref = oracle.attention(Q, K, V2, causal=causal)
+        assert_parity(run(lib, Q, K, V2, causal), ref, ("peaked", causal))
+
+
+def _sample_rows(B, H, Nq, seed, n_random=192):
+    rng = np.random.default_rng(seed)
+    per_head = [0, 1, 127, 128, Nq // 2, Nq - 2, Nq - 1]
+    rows = set()
+    for b, h in ((0, 0), (B - 1, H - 1), (B // 2, H // 2)):
+        for i in per_head:
+            if 0 <= i < Nq:
+                rows.add((b * H + h) * Nq + i)
+    rows.update(rng.integers(0, B * H * Nq, n_random).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", list(workloads.ATTENTION_WORKLOADS))
+def test_workloads_sampled(lib, name):
+    w = workloads.ATTENTION_WORKLOADS[name]
+    Q, K, V = workloads.make_attention_inputs(w)
+    got = run(lib, Q, K, V, w.causal).reshape(-1, w.D)
+    rows = _sample_rows(w.B, w.H, w.Nq, w.seed)
+    ref = oracle.attention_rows(Q, K, V, rows, causal=w.causal)
+    assert_parity(got[rows], ref, name)
+    assert not np.isnan(got).any()
+
+
+def test_errors_and_empty(lib):
+    import dense_tiled_gemm_04_amd as g
+    z = lambda *s: torch.zeros(s, dtype=torch.float16, device="cuda")
+    assert tuple(g.flash_attn(z(1, 1, 0, 64), z(1, 1, 5, 64), z(1, 1, 5, 64)).shape) == (1, 1, 0, 64)
+    with pytest.raises(g.GemmError):
+        g.flash_attn(z(1, 1, 4, 96), z(1, 1, 4, 96), z(1, 1, 4, 96))
+    with pytest.raises(g.GemmError):
+        g.flash_attn(z(1, 1, 4, 64), z(1, 1, 0, 64), z(1, 1, 0, 64))
+    with pytest.raises(ValueError):
+        g.flash_attn(z(1, 1, 4, 64), z(1, 1, 4, 64), z(1, 1, 5, 64))
+
+
+def test_determinism(lib):
+    import dense_tiled_gemm_04_amd as g
+    Q, K, V = (dev(x) for x in workloads.make_attention_inputs("attn_b4_h32_n4096_d128_causal", B=1, H=2, Nq=1024,
+                                                               Nkv=1024))
+    a = g.flash_attn(Q, K, V, causal=True)
+    b = g.flash_attn(Q, K, V, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))

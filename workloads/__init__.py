@@ -132,6 +132,67 @@ def make_softmax_input(w: SoftmaxWorkload | str, rows: int | None = None, cols: 
     return _draw(rng, w.dist, (rows, cols)).astype(np.float16)
 
 
+@dataclasses.dataclass(frozen=True)
+class AttentionWorkload:
+    """Attention forward: Q [B,H,Nq,D], K and V [B,H,Nkv,D], fp16 (the pages give no shapes for it)."""
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nkv: int
+    D: int
+    causal: bool
+    seed: int
+    note: str = ""
+
+    @property
+    def pairs(self) -> int:
+        """(query, key) pairs the softmax runs over: Nq*Nkv, or the top-left causal triangle."""
+        if not self.causal:
+            return self.Nq * self.Nkv
+        n = min(self.Nq, self.Nkv)
+        return n * (n + 1) // 2 + max(0, self.Nq - self.Nkv) * self.Nkv
+
+    @property
+    def flops(self) -> int:
+        """2 * D for Q.K plus 2 * D for P.V per allowed pair, per (batch, head)."""
+        return 4 * self.B * self.H * self.D * self.pairs
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        return 2 * self.B * self.H * self.D * (2 * self.Nq + 2 * self.Nkv)
+
+
+ATTENTION_WORKLOADS = {
+    w.name: w
+    for w in [
+        AttentionWorkload("attn_b4_h32_n4096_d128", 4, 32, 4096, 4096, 128, False, 8,
+                          "non-causal self-attention, 32 heads of 128 at sequence 4096"),
+        AttentionWorkload("attn_b4_h32_n4096_d128_causal", 4, 32, 4096, 4096, 128, True, 9,
+                          "causal self-attention, 32 heads of 128 at sequence 4096"),
+        AttentionWorkload("attn_b2_h16_n1000_d64_causal", 2, 16, 1000, 1000, 64, True, 10,
+                          "ragged causal self-attention, head dimension 64"),
+        AttentionWorkload("attn_b1_h8_q777_kv1500_d128", 1, 8, 777, 1500, 128, False, 11,
+                          "cross-attention, ragged query and key lengths"),
+    ]
+}
+
+
+def make_attention_inputs(w: AttentionWorkload | str, B=None, H=None, Nq=None, Nkv=None):
+    """Q, K, V as float16 numpy arrays, each N(0, 1), drawn in that order (shape overrides allowed)."""
+    if isinstance(w, str):
+        w = ATTENTION_WORKLOADS[w]
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    Nq = w.Nq if Nq is None else Nq
+    Nkv = w.Nkv if Nkv is None else Nkv
+    rng = np.random.default_rng(w.seed)
+    Q = rng.standard_normal((B, H, Nq, w.D)).astype(np.float16)
+    K = rng.standard_normal((B, H, Nkv, w.D)).astype(np.float16)
+    V = rng.standard_normal((B, H, Nkv, w.D)).astype(np.float16)
+    return Q, K, V
+
+
 def random_f16(seed: int, shape, lo: float = -1.0, hi: float = 1.0) -> np.ndarray:
     """Plain uniform fp16 draws for ad-hoc test shapes."""
     rng = np.random.default_rng(seed)
