@@ -19,6 +19,9 @@ Prints ONE JSON line:
 --workload softmax_* benchmarks the library's row softmax instead (one step =
 one softmax_rows_f16 call over the whole matrix; value in GB/s of X read plus Y
 written, against the HBM peak; copies of X rotated past the Infinity Cache).
+--workload attn_* benchmarks the attention forward pass (one step = one
+flash_attn_fwd_f16 call; value in TFLOP/s counting 4*D per allowed query-key
+pair, against the MFMA peak; PyTorch's fused SDPA timed alongside).
 """
 from __future__ import annotations
 
@@ -230,6 +233,120 @@ def bench_softmax(args, g, torch, w) -> int:
     return 0
 
 
+def cpu_baseline_attention(w, Q, K, V, target_s: float = 10.0):
+    """Time the CPU oracle on the first R query rows of (batch 0, head 0) and beyond (R grown as above)."""
+    import numpy as np
+    import oracle
+
+    threads = oracle.max_threads()
+    total = w.B * w.H * w.Nq
+    r, rows, dt = min(total, 64), 0, 0.0
+    while True:
+        idx = np.arange(r, dtype=np.int64)
+        t = time.perf_counter()
+        oracle.attention_rows(Q, K, V, idx, causal=w.causal, threads=threads)
+        rows, dt = r, time.perf_counter() - t
+        if dt >= 1.0 or r >= total:
+            break
+        r = min(total, r * 4)
+    if dt < target_s and rows < total:
+        r = int(min(total, max(rows, rows * target_s / max(dt, 1e-6))))
+        idx = np.arange(r, dtype=np.int64)
+        t = time.perf_counter()
+        oracle.attention_rows(Q, K, V, idx, causal=w.causal, threads=threads)
+        rows, dt = r, time.perf_counter() - t
+    flops = 0
+    for flat in range(rows):
+        i = flat % w.Nq
+        flops += 4 * w.D * (min(i + 1, w.Nkv) if w.causal else w.Nkv)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "query rows 0..%d in (batch, head, row) order, all keys, fp64 oracle, %.2f s wall"
+                      % (rows - 1, dt)}
+
+
+def bench_attention(args, g, torch, w) -> int:
+    """Attention forward: Q, K, V resident in HBM, HIP events on the launch stream around `steps` launches."""
+    import math
+    import workloads
+
+    Q, K, V = workloads.make_attention_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dQ, dK, dV = (torch.from_numpy(x).to(dev) for x in (Q, K, V))
+    dO = torch.empty_like(dQ)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    lib = g.load()
+    scale = 1.0 / math.sqrt(w.D)
+    ptrs = (dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), dO.data_ptr())
+
+    def step():
+        st = lib.flash_attn_fwd_f16(w.B, w.H, w.Nq, w.Nkv, w.D, *ptrs, 1 if w.causal else 0, scale, sh)
+        if st != 0:
+            raise g.GemmError(st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tflops = w.flops / (ms * 1e-3) / 1e12
+
+    # context: PyTorch's scaled dot-product attention on the same tensors, fused backends only
+    torch_ms, backend = None, None
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+            f = lambda: torch.nn.functional.scaled_dot_product_attention(dQ, dK, dV, is_causal=w.causal)
+            for _ in range(3):
+                f()
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n_t = max(5, min(args.steps, 50))
+            t0.record(stream)
+            for _ in range(n_t):
+                f()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            torch_ms = t0.elapsed_time(t1) / n_t
+            backend = "flash/efficient"
+    except RuntimeError as e:
+        backend = "unavailable: %s" % str(e).splitlines()[0][:120]
+
+    roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+            "frac": tflops / PEAK_FP16_TFLOPS, "traffic": load_traffic(w.name, "flash_attn_fwd"),
+            "kernel": "flash_attn_fwd", "algorithmic_flops_per_launch": w.flops,
+            "algorithmic_bytes_per_launch": w.algorithmic_bytes, "avg_launch_us": ms * 1e3}
+    cpu = None if args.no_cpu_baseline else cpu_baseline_attention(w, Q, K, V)
+    out = {
+        "metric": "fp16 attention forward TFLOP/s (4*D per allowed query-key pair) + % of MI355X MFMA peak",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 in/out, f32 accumulate and softmax",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nkv": w.Nkv, "D": w.D, "causal": w.causal,
+                   "inputs": "seeded numpy draws, Q, K, V ~ N(0, 1) (%s)" % w.note},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "context": {"torch_sdpa_ms": round(torch_ms, 6) if torch_ms else None, "torch_sdpa_backend": backend,
+                    "torch_tflops": round(w.flops / (torch_ms * 1e-3) / 1e12, 3) if torch_ms else None},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,6 +381,8 @@ def main() -> int:
         return hbm_calibration(g, torch)
     if args.workload in workloads.SOFTMAX_WORKLOADS:
         return bench_softmax(args, g, torch, workloads.SOFTMAX_WORKLOADS[args.workload])
+    if args.workload in workloads.ATTENTION_WORKLOADS:
+        return bench_attention(args, g, torch, workloads.ATTENTION_WORKLOADS[args.workload])
     w = workloads.WORKLOADS[args.workload]
     A, B, bias = workloads.make_inputs(w)
     hbm_bound = w.flops / w.algorithmic_bytes < 100.0
