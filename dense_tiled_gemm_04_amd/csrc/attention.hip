@@ -26,10 +26,15 @@
 //    P is converted to fp16 in place and needs no shuffle.  The A operand V^T
 //    comes from two LDS transpose reads (ds_read_b64_tr_b16) per 16-key step,
 //    using the same key mapping.
-//  * The softmax state is fp32 and scaled by log2(e), so every exponential is one
-//    v_exp_f32.  The probabilities enter the PV product rounded to fp16, and the
-//    row sum adds those same rounded values, so each output row is an exact
-//    convex combination of value rows up to fp32 rounding.
+//  * The softmax state is fp32 and in the log2 domain: each probability is one
+//    FMA (the scale folded in) and one v_exp_f32.  The reference maximum is
+//    raised lazily, only when a row's maximum grows by more than 2^8, so the
+//    accumulators are rarely rescaled and probabilities stay below 256.  The
+//    probabilities enter the PV product rounded to fp16 in pairs, and the row
+//    sum adds those same rounded values (v_dot2 with ones), so each output row
+//    is an exact convex combination of value rows up to fp32 rounding.
+//  * Key blocks that need no mask for any row of the workgroup run a loop body
+//    without mask code; the boundary blocks run a second loop with it.
 //  * Causal: key blocks past the workgroup's last row are never visited; a wave
 //    skips the blocks that lie wholly past its own rows; masks are applied only
 //    in blocks that cross the diagonal or the end of the keys.  Workgroups are
@@ -52,6 +57,10 @@ constexpr int FA_BM = 128;   // query rows per workgroup
 constexpr int FA_BN = 64;    // keys per block
 constexpr int FA_NW = 4;     // waves per workgroup
 constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kLazyLog2 = 8.0f;  // rescale when a row maximum grows by more than 2^8
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 struct FaArgs {
     const f16* Q;
@@ -79,7 +88,7 @@ __device__ __forceinline__ int swz_v(int j) {
     return D == 128 ? 4 * (j & 3) : 4 * ((j >> 1) & 1);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PRESCALE>
 __global__ void __launch_bounds__(FA_NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 flash_attn_fwd_kernel(FaArgs p) {
     constexpr int CH = D / 8;                    // 16-byte chunks per row
@@ -169,68 +178,97 @@ flash_attn_fwd_kernel(FaArgs p) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+    // Softmax state of this lane's row, in the log2 domain: m_run is the
+    // reference maximum (raised lazily, see below), l_run the sum of the fp16
+    // probabilities applied so far (this lane's half of the keys).
     float m_run = -INFINITY, l_run = 0.0f;
+    const float c = PRESCALE ? 1.0f : p.scale_log2;
+    const f16x2 ones = {(f16)1.0f, (f16)1.0f};
 
     const int kv_blocks_all = (Nkv + FA_BN - 1) / FA_BN;
     const int kv_blocks = CAUSAL ? min(kv_blocks_all, (q0 + FA_BM - 1) / FA_BN + 1) : kv_blocks_all;
-    if (kv_blocks > 0) issue(0, 0);
+    // Blocks [0, n_plain) need no mask for any row of the workgroup: every key
+    // exists and (causal) no key lies past the workgroup's first row.
+    int n_plain = min(Nkv / FA_BN, kv_blocks);
+    if (CAUSAL) n_plain = min(n_plain, (q0 + 1) / FA_BN);
 
-    for (int jb = 0; jb < kv_blocks; ++jb) {
+    auto block = [&]<bool MASK>(int jb) {
         const int buf = jb & 1;
         wait_vmcnt0();
         __syncthreads();  // block jb in LDS for every wave; block jb-1's buffer free
         if (jb + 1 < kv_blocks) issue(jb + 1, buf ^ 1);
         const int kv0 = jb * FA_BN;
-        if (CAUSAL && kv0 > row0 + 31) continue;  // every key of the block is past this wave's rows
+        if (CAUSAL && MASK && kv0 > row0 + 31) return;  // every key of the block is past this wave's rows
 
         const GK_LDS char* Ks = (const GK_LDS char*)smem + buf * TILE;
         const GK_LDS char* Vs = (const GK_LDS char*)smem + (2 + buf) * TILE;
-        f32x16 s[JB];
+        // S^T = K . Q^T; the two 32-key accumulators alternate so that no MFMA
+        // waits for the one before it
+        f32x16 sc[JB];
 #pragma unroll
-        for (int jj = 0; jj < JB; ++jj) {
+        for (int jj = 0; jj < JB; ++jj)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[jj][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) sc[jj][r] = 0.0f;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int jj = 0; jj < JB; ++jj) {
                 const f16x8 kf = *(const GK_LDS f16x8*)(Ks + k_rd[jj][ks]);
-                s[jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[jj], 0, 0, 0);
+                sc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], sc[jj], 0, 0, 0);
             }
+        if constexpr (PRESCALE) {
+#pragma unroll
+            for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sc[jj][r] *= p.scale_log2;
         }
-        // scale (into the log2 domain), mask, block max
-        const bool need_mask = kv0 + FA_BN > Nkv || (CAUSAL && kv0 + FA_BN - 1 > row0);
+        if constexpr (MASK) {
+#pragma unroll
+            for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = kv0 + 32 * jj + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (j >= Nkv || (CAUSAL && j > i)) sc[jj][r] = -INFINITY;
+                }
+        }
+        // block maximum of the row (unscaled; c > 0), then in the log2 domain
         float mb = -INFINITY;
 #pragma unroll
         for (int jj = 0; jj < JB; ++jj)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float v = s[jj][r] * p.scale_log2;
-                if (need_mask) {
-                    const int j = kv0 + 32 * jj + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    if (j >= Nkv || (CAUSAL && j > i)) v = -INFINITY;
-                }
-                s[jj][r] = v;
-                mb = fmaxf(mb, v);
-            }
+            for (int r = 0; r < 16; ++r) mb = fmaxf(mb, sc[jj][r]);
         mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-        const float m_new = fmaxf(m_run, mb);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;  // a row with no key yet: keep p = 0
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
-        l_run *= alpha;
+        const float mc = mb * c;
+        // Lazy rescaling: the reference maximum moves only when some row's block
+        // maximum exceeds it by more than 2^8, so probabilities stay below 256
+        // (exact enough in fp16, far from overflow) and the accumulators are
+        // rescaled rarely.  The first block always sets it (m_run = -inf), and
+        // that block holds key 0, which every row may see.
+        if (__any(mc > m_run + kLazyLog2)) {
+            const float m_new = fmaxf(m_run, mc);
+            const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        // probabilities, rounded to fp16 for the P^T operand; the row sum adds the
-        // same rounded values, so the weights applied to V sum to one
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+        // probabilities: exp2(s c - m) as one FMA and one v_exp_f32, rounded in
+        // pairs to fp16 (v_cvt_pk_f16_f32) for the P^T operand; the row sum adds
+        // those same rounded pairs (v_dot2_f32_f16 with ones), so the weights
+        // applied to V sum to one
         f16x8 pf[JB][2];
 #pragma unroll
         for (int jj = 0; jj < JB; ++jj)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const f16 ph = (f16)__builtin_amdgcn_exp2f(s[jj][r] - m_use);
-                l_run += (float)ph;
-                pf[jj][r >> 3][r & 7] = ph;
+            for (int k = 0; k < 8; ++k) {
+                const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[jj][2 * k], c, -m_run));
+                const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[jj][2 * k + 1], c, -m_run));
+                const f16x2 h = __builtin_convertvector((f32x2){a, b}, f16x2);
+                l_run = __builtin_amdgcn_fdot2(h, ones, l_run, false);
+                pf[jj][k >> 2][2 * (k & 3)] = h[0];
+                pf[jj][k >> 2][2 * (k & 3) + 1] = h[1];
             }
         // O^T += V^T . P^T, 16 keys per step
 #pragma unroll
@@ -243,7 +281,12 @@ flash_attn_fwd_kernel(FaArgs p) {
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[st >> 1][st & 1], oacc[db], 0, 0, 0);
             }
         }
-    }
+    };
+
+    if (kv_blocks > 0) issue(0, 0);
+    int jb = 0;
+    for (; jb < n_plain; ++jb) block.template operator()<false>(jb);
+    for (; jb < kv_blocks; ++jb) block.template operator()<true>(jb);
 
     // normalise and write: lane l, register r of block db holds O[i][32 db + 8 (r/4) + 4 (l/32) + r % 4]
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
@@ -261,11 +304,17 @@ flash_attn_fwd_kernel(FaArgs p) {
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PRESCALE>
 hipError_t launch(const FaArgs& a, int64_t BH, hipStream_t s) {
-    hipLaunchKernelGGL((flash_attn_fwd_kernel<D, CAUSAL>), dim3((unsigned)(BH * a.q_blocks)), dim3(FA_NW * 64), 0, s,
-                       a);
+    hipLaunchKernelGGL((flash_attn_fwd_kernel<D, CAUSAL, PRESCALE>), dim3((unsigned)(BH * a.q_blocks)),
+                       dim3(FA_NW * 64), 0, s, a);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const FaArgs& a, int64_t BH, bool causal, bool prescale, hipStream_t s) {
+    if (prescale) return causal ? launch<D, true, true>(a, BH, s) : launch<D, false, true>(a, BH, s);
+    return causal ? launch<D, true, false>(a, BH, s) : launch<D, false, false>(a, BH, s);
 }
 
 }  // namespace
@@ -278,7 +327,7 @@ int flash_attn_fwd_f16(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
     if (B == 0 || H == 0 || Nq == 0) return GEMM_OK;
     if (Nkv == 0) return GEMM_ERR_INVALID_DIM;  // a query with no key has no softmax
     if (D != 64 && D != 128) return GEMM_ERR_UNSUPPORTED;
-    if (!isfinite(scale)) return GEMM_ERR_INVALID_DIM;
+    if (!isfinite(scale) || fabsf(scale) > 1e30f) return GEMM_ERR_INVALID_DIM;
     if (!Q || !K || !V || !O) return GEMM_ERR_NULL_POINTER;
     if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) % 16 != 0) return GEMM_ERR_MISALIGNED;
     const int64_t q_blocks = (Nq + FA_BM - 1) / FA_BM;
@@ -296,11 +345,11 @@ int flash_attn_fwd_f16(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
     a.scale_log2 = scale * kLog2e;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    if (D == 128) {
-        e = causal ? launch<128, true>(a, B * H, s) : launch<128, false>(a, B * H, s);
-    } else {
-        e = causal ? launch<64, true>(a, B * H, s) : launch<64, false>(a, B * H, s);
-    }
+    // a positive scale is folded into the exponent's FMA (the row maximum of the
+    // raw scores is the maximum of the scaled ones); otherwise scores are
+    // scaled first
+    const bool prescale = !(scale > 0.0f);
+    e = D == 128 ? launch_d<128>(a, B * H, causal != 0, prescale, s) : launch_d<64>(a, B * H, causal != 0, prescale, s);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
