@@ -40,13 +40,24 @@ PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 
 
-def kernel_source_digest() -> str:
+# Sources each kernel family is built from; a change to any of them voids that family's recorded traffic.
+KERNEL_SOURCES = {
+    "gemm": ["common.h", "tile_pipe_kernel.h", "skinny_kernel.h", "gemm_f16.hip", "config_table.inc"],
+    "softmax": ["common.h", "softmax.hip"],
+    "attention": ["common.h", "attention.hip"],
+}
+
+
+def kernel_family(workload: str) -> str:
+    return "softmax" if workload.startswith("softmax") else "attention" if workload.startswith("attn") else "gemm"
+
+
+def kernel_source_digest(family: str = "gemm") -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_tiled_gemm_04_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".h", ".hip")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+    for f in sorted(KERNEL_SOURCES[family]):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
 
 
@@ -59,7 +70,8 @@ def load_traffic(workload: str, kernel: str):
         rec = json.load(open(path)).get(workload)
     except (ValueError, OSError):
         return None
-    if not rec or rec.get("source_sha256") != kernel_source_digest() or rec.get("kernel") != kernel:
+    if not rec or rec.get("source_sha256") != kernel_source_digest(kernel_family(workload)) or \
+            rec.get("kernel") != kernel:
         return None
     return rec.get("hbm_bytes_per_launch")
 

@@ -35,6 +35,8 @@
 //    is an exact convex combination of value rows up to fp32 rounding.
 //  * Key blocks that need no mask for any row of the workgroup run a loop body
 //    without mask code; the boundary blocks run a second loop with it.
+//  * Workgroup ids are remapped so that each XCD runs a contiguous range of
+//    (batch, head, query block) tiles: a head's K and V are fetched into one L2.
 //  * Causal: key blocks past the workgroup's last row are never visited; a wave
 //    skips the blocks that lie wholly past its own rows; masks are applied only
 //    in blocks that cross the diagonal or the end of the keys.  Workgroups are
@@ -104,8 +106,12 @@ flash_attn_fwd_kernel(FaArgs p) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int Nq = p.Nq, Nkv = p.Nkv;
-    int qb = (int)(blockIdx.x % (unsigned)p.q_blocks);
-    const int64_t bh = blockIdx.x / (unsigned)p.q_blocks;
+    // Consecutive workgroup ids are dealt round-robin over the 8 XCDs; the remap
+    // gives each XCD a contiguous run of ids, so the query blocks of one (batch,
+    // head) share one L2 and fetch that head's K and V once per XCD.
+    const int lid = xcd_contiguous_id((int)blockIdx.x, (int)gridDim.x);
+    int qb = lid % p.q_blocks;
+    const int64_t bh = lid / p.q_blocks;
     if (CAUSAL) qb = p.q_blocks - 1 - qb;  // longest rows first
     const int q0 = qb * FA_BM;
     const int row0 = q0 + 32 * wave_s;      // first query row of this wave
