@@ -32,6 +32,7 @@ STATUS = {
 EXPORTS = [
     "gemm_f16", "gemm_f16_status_string", "gemm_f16_num_configs", "gemm_f16_config_info",
     "gemm_f16_select_config", "gemm_f16_with_config", "vector_add_f32",
+    "gemm_f16_ex", "gemm_f16_select_config_ex", "gemm_f16_with_config_ex",
     "softmax_rows_f16", "softmax_rows_f16_path", "flash_attn_fwd_f16",
 ]
 SOFTMAX_PATHS = {0: "none", 1: "wave", 2: "workgroup", 3: "online"}
@@ -61,6 +62,12 @@ def load():
     lib.gemm_f16_with_config.restype = i32
     lib.gemm_f16_select_config.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32]
     lib.gemm_f16_select_config.restype = i32
+    lib.gemm_f16_ex.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, vp, i64, i32, vp]
+    lib.gemm_f16_ex.restype = i32
+    lib.gemm_f16_with_config_ex.argtypes = [i32, i64, i64, i64, vp, i64, vp, i64, vp, vp, i64, i32, vp]
+    lib.gemm_f16_with_config_ex.restype = i32
+    lib.gemm_f16_select_config_ex.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, vp, i64, i32]
+    lib.gemm_f16_select_config_ex.restype = i32
     lib.gemm_f16_status_string.argtypes = [i32]
     lib.gemm_f16_status_string.restype = ctypes.c_char_p
     lib.gemm_f16_num_configs.argtypes = []
@@ -113,6 +120,18 @@ def select_config_raw(M, N, K, A, B, bias, C, epilogue: int) -> int:
     return int(load().gemm_f16_select_config(M, N, K, A, B, bias, C, epilogue))
 
 
+def gemm_f16_ex_raw(M, N, K, A, lda, B, ldb, bias, C, ldc, epilogue: int, stream=0,
+                    config: int | None = None) -> int:
+    lib = load()
+    if config is None:
+        return int(lib.gemm_f16_ex(M, N, K, A, lda, B, ldb, bias, C, ldc, epilogue, stream))
+    return int(lib.gemm_f16_with_config_ex(config, M, N, K, A, lda, B, ldb, bias, C, ldc, epilogue, stream))
+
+
+def select_config_ex_raw(M, N, K, A, lda, B, ldb, bias, C, ldc, epilogue: int) -> int:
+    return int(load().gemm_f16_select_config_ex(M, N, K, A, lda, B, ldb, bias, C, ldc, epilogue))
+
+
 def softmax_rows_raw(rows, cols, X, Y, stream=0) -> int:
     return int(load().softmax_rows_f16(rows, cols, X, Y, stream))
 
@@ -139,18 +158,40 @@ def _check(t, name, ndim):
         raise ValueError("%s must be contiguous (row-major)" % name)
 
 
+def _check_rows(t, name):
+    """A 2-D float16 GPU matrix stored row-major with unit column stride (possibly a
+    sub-matrix of a wider array); returns its leading dimension."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != torch.float16:
+        raise TypeError("%s must be float16, got %s" % (name, t.dtype))
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be on the GPU" % name)
+    rows, cols = t.shape
+    if rows > 1 and cols > 1 and t.stride(1) != 1:
+        raise ValueError("%s must be row-major with unit column stride" % name)
+    ld = t.stride(0) if rows > 1 else cols
+    if rows > 1 and ld < cols:
+        raise ValueError("%s rows overlap (stride %d < %d columns)" % (name, ld, cols))
+    return max(ld, cols)
+
+
 def _stream_handle():
     import torch
     return torch.cuda.current_stream().cuda_stream
 
 
 def gemm_f16(A, B, bias=None, epilogue: str = "none", out=None, config: int | None = None):
-    """C = fp16(epi(A @ B [+ bias])) on the current stream; returns C (torch.float16 [M, N])."""
+    """C = fp16(epi(A @ B [+ bias])) on the current stream; returns C (torch.float16 [M, N]).
+    A, B and out may be row-major sub-matrices of wider arrays (unit column stride)."""
     import torch
     if epilogue not in EPILOGUES:
         raise ValueError("epilogue must be one of %s" % list(EPILOGUES))
-    _check(A, "A", 2)
-    _check(B, "B", 2)
+    lda = _check_rows(A, "A")
+    ldb = _check_rows(B, "B")
     M, K = A.shape
     K2, N = B.shape
     if K != K2:
@@ -167,12 +208,12 @@ def gemm_f16(A, B, bias=None, epilogue: str = "none", out=None, config: int | No
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=A.device)
     else:
-        _check(out, "out", 2)
         if tuple(out.shape) != (M, N):
             raise ValueError("out must be [%d, %d]" % (M, N))
+    ldc = _check_rows(out, "out")
     with torch.cuda.device(A.device):
-        st = gemm_f16_raw(M, N, K, A.data_ptr(), B.data_ptr(), bias.data_ptr() if epi != 0 else None,
-                          out.data_ptr(), epi, _stream_handle(), config)
+        st = gemm_f16_ex_raw(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, bias.data_ptr() if epi != 0 else None,
+                             out.data_ptr(), ldc, epi, _stream_handle(), config)
     if st != 0:
         raise GemmError(st)
     return out
@@ -184,8 +225,9 @@ def select_config(A, B, bias=None, epilogue: str = "none", out=None) -> int:
     N = B.shape[1]
     epi = EPILOGUES[epilogue]
     optr = out.data_ptr() if out is not None else 256  # a 256-byte-aligned stand-in address
-    r = select_config_raw(M, N, K, A.data_ptr(), B.data_ptr(), bias.data_ptr() if bias is not None else None,
-                          optr, epi)
+    ldc = _check_rows(out, "out") if out is not None else N
+    r = select_config_ex_raw(M, N, K, A.data_ptr(), _check_rows(A, "A"), B.data_ptr(), _check_rows(B, "B"),
+                             bias.data_ptr() if bias is not None else None, optr, ldc, epi)
     if r < -1:
         raise GemmError(-r)
     return r

@@ -18,11 +18,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 enum Epilogue { EPI_NONE = 0, EPI_BIAS = 1, EPI_BIAS_GELU = 2 };
 
 struct GemmArgs {
-    const f16* A;     // [M][K]
-    const f16* B;     // [K][N]
+    const f16* A;     // [M][K], row stride lda
+    const f16* B;     // [K][N], row stride ldb
     const f16* bias;  // [N] or null
-    f16* C;           // [M][N]
+    f16* C;           // [M][N], row stride ldc
     int M, N, K;
+    int lda, ldb, ldc;  // leading dimensions in elements (>= K, N, N)
     int tiles_m, tiles_n;
     int k_split;      // skinny path: number of K slices (1 = none)
     float* partial;   // skinny path: [k_split][M][N] fp32 partial sums (k_split > 1)

@@ -94,13 +94,17 @@ struct Call {
     const void *A, *B, *bias;
     void* C;
     int epi;
+    int64_t lda, ldb, ldc;  // leading dimensions (row strides) in elements
 };
 
 int validate(const Call& c) {
     if (c.M < 0 || c.N < 0 || c.K < 0 || c.M > INT32_MAX || c.N > INT32_MAX || c.K > INT32_MAX)
         return GEMM_ERR_INVALID_DIM;
     if (c.epi < GEMM_EPI_NONE || c.epi > GEMM_EPI_BIAS_GELU) return GEMM_ERR_BAD_EPILOGUE;
+    if (c.lda < 0 || c.ldb < 0 || c.ldc < 0 || c.lda > INT32_MAX || c.ldb > INT32_MAX || c.ldc > INT32_MAX)
+        return GEMM_ERR_INVALID_DIM;
     if (c.M == 0 || c.N == 0) return GEMM_OK;
+    if (c.ldc < c.N || (c.K > 0 && (c.lda < c.K || c.ldb < c.N))) return GEMM_ERR_INVALID_DIM;
     if (!c.C) return GEMM_ERR_NULL_POINTER;
     if (c.K > 0 && (!c.A || !c.B)) return GEMM_ERR_NULL_POINTER;
     if (c.epi != GEMM_EPI_NONE && !c.bias) return GEMM_ERR_NULL_POINTER;
@@ -113,25 +117,28 @@ int validate(const Call& c) {
 // Whether config `cfg` can run call `c` (validated, M, N > 0).
 bool supports(const Config& cfg, const Call& c) {
     const bool epi_bias_ok = (c.epi == GEMM_EPI_NONE) || aligned(c.bias, 8);
+    // 16-byte-aligned rows: aligned bases and leading dimensions that are multiples of 8 elements
     const bool vec_ok = aligned(c.A, 16) && aligned(c.B, 16) && aligned(c.C, 16) && c.K % 8 == 0 &&
-                        c.N % 8 == 0 && epi_bias_ok;
+                        c.N % 8 == 0 && c.lda % 8 == 0 && c.ldb % 8 == 0 && c.ldc % 8 == 0 && epi_bias_ok;
+    const int64_t a_end = (c.M - 1) * c.lda + c.K;  // elements from A to the end of its last row
+    const int64_t b_end = (c.K - 1) * c.ldb + c.N;  // same for B
     if (cfg.kind == KIND_SKINNY) {
         // 32-bit buffer offsets: B rows up to K + SK_BK (the last stage's tail) and all of A
-        return vec_ok && c.M <= cfg.bm && (c.K + SK_BK) * c.N * 2 < (int64_t)INT32_MAX &&
-               c.M * c.K * 2 < (int64_t)INT32_MAX;
+        return vec_ok && c.M <= cfg.bm && (c.K + SK_BK) * c.ldb * 2 < (int64_t)INT32_MAX &&
+               c.M * c.lda * 2 < (int64_t)INT32_MAX;
     }
     if (cfg.loader == LOAD_DMA)
-        return vec_ok && c.K % cfg.bk == 0 && (int64_t)cfg.bm * c.K * 2 < (int64_t)INT32_MAX &&
-               (int64_t)cfg.bk * c.N * 2 < (int64_t)INT32_MAX;
+        return vec_ok && c.K % cfg.bk == 0 && (int64_t)cfg.bm * c.lda * 2 < (int64_t)INT32_MAX &&
+               (int64_t)cfg.bk * c.ldb * 2 < (int64_t)INT32_MAX;
     if (cfg.loader == LOAD_BUF) {
         // 31-bit buffer sizes and offsets: all of A and B, and one stage's tiles.
         const int64_t lim = (int64_t)INT32_MAX - 64;
-        const bool fits = c.M * c.K * 2 < lim && c.K * c.N * 2 < lim &&
-                          ((int64_t)cfg.bm * c.K + cfg.bk) * 2 < lim && ((int64_t)cfg.bk * c.N + cfg.bn) * 2 < lim;
-        // Odd N: B's range is padded by 2 bytes past its end; allowed only
-        // when the end is not on a 4 KiB page boundary, so the pad lies in the
-        // page of the last element.
-        const bool pad_ok = c.N % 2 == 0 || ((uintptr_t)c.B + (uintptr_t)(c.K * c.N * 2)) % 4096 != 0;
+        const bool fits = c.K > 0 && a_end * 2 < lim && b_end * 2 < lim &&
+                          ((int64_t)cfg.bm * c.lda + cfg.bk) * 2 < lim && ((int64_t)cfg.bk * c.ldb + cfg.bn) * 2 < lim;
+        // Odd N: B's range is padded by 2 bytes past the end of its last row;
+        // allowed only when that end is not on a 4 KiB page boundary, so the
+        // pad lies in the page of the last element.
+        const bool pad_ok = c.N % 2 == 0 || ((uintptr_t)c.B + (uintptr_t)(b_end * 2)) % 4096 != 0;
         return c.K % 8 == 0 && fits && pad_ok;
     }
     return true;  // register loader: any shape, any 2-byte alignment
@@ -163,6 +170,9 @@ int run(const Config& cfg, const Call& c, hipStream_t stream) {
     a.M = (int)c.M;
     a.N = (int)c.N;
     a.K = (int)c.K;
+    a.lda = (int)c.lda;
+    a.ldb = (int)c.ldb;
+    a.ldc = (int)c.ldc;
     a.k_split = 1;
     a.partial = nullptr;
     if (cfg.kind == KIND_SKINNY) {
@@ -237,18 +247,23 @@ int gemm_f16_config_info(int idx, char* buf, int buflen) {
     return n;
 }
 
-int gemm_f16_select_config(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias, void* C,
-                           int epilogue) {
-    Call c{M, N, K, A, B, bias, C, epilogue};
+int gemm_f16_select_config_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                              const void* bias, void* C, int64_t ldc, int epilogue) {
+    Call c{M, N, K, A, B, bias, C, epilogue, lda, ldb, ldc};
     int st = validate(c);
     if (st != GEMM_OK) return -st;
     if (M == 0 || N == 0) return -1;
     return pick_default(c);
 }
 
-int gemm_f16_with_config(int idx, int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias,
-                         void* C, int epilogue, void* stream) {
-    Call c{M, N, K, A, B, bias, C, epilogue};
+int gemm_f16_select_config(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias, void* C,
+                           int epilogue) {
+    return gemm_f16_select_config_ex(M, N, K, A, K, B, N, bias, C, N, epilogue);
+}
+
+int gemm_f16_with_config_ex(int idx, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                            int64_t ldb, const void* bias, void* C, int64_t ldc, int epilogue, void* stream) {
+    Call c{M, N, K, A, B, bias, C, epilogue, lda, ldb, ldc};
     int st = validate(c);
     if (st != GEMM_OK) return st;
     if (idx < 0 || idx >= kNumConfigs) return GEMM_ERR_NO_CONFIG;
@@ -257,13 +272,23 @@ int gemm_f16_with_config(int idx, int64_t M, int64_t N, int64_t K, const void* A
     return run(kConfigs[idx], c, (hipStream_t)stream);
 }
 
-int gemm_f16(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias, void* C, int epilogue,
-             void* stream) {
-    Call c{M, N, K, A, B, bias, C, epilogue};
+int gemm_f16_with_config(int idx, int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias,
+                         void* C, int epilogue, void* stream) {
+    return gemm_f16_with_config_ex(idx, M, N, K, A, K, B, N, bias, C, N, epilogue, stream);
+}
+
+int gemm_f16_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                const void* bias, void* C, int64_t ldc, int epilogue, void* stream) {
+    Call c{M, N, K, A, B, bias, C, epilogue, lda, ldb, ldc};
     int st = validate(c);
     if (st != GEMM_OK) return st;
     if (M == 0 || N == 0) return GEMM_OK;
     return run(kConfigs[pick_default(c)], c, (hipStream_t)stream);
+}
+
+int gemm_f16(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias, void* C, int epilogue,
+             void* stream) {
+    return gemm_f16_ex(M, N, K, A, K, B, N, bias, C, N, epilogue, stream);
 }
 
 int vector_add_f32(int64_t n, const float* A, const float* B, float* C, void* stream) {

@@ -47,16 +47,17 @@ gemm_skinny_kernel(GemmArgs p) {
     GK_LDS char* const b_lds = smem;
     GK_LDS char* const a_lds = smem + STAGES * B_STAGE;
 
-    const int M = p.M, N = p.N, K = p.K;
+    const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb, ldc = p.ldc;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n0 = blockIdx.x * SK_BN;
     const int KT = (K + SK_BK - 1) / SK_BK;
 
-    // Buffer resources: B covers exactly K*N elements, so k-rows >= K read 0.
-    const __amdgpu_buffer_rsrc_t b_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)p.B, (short)0, (int)min((int64_t)K * N * 2, (int64_t)0x7fffffff), 0x00020000);
-    const __amdgpu_buffer_rsrc_t a_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, (int)min((int64_t)M * K * 2, (int64_t)0x7fffffff), 0x00020000);
+    // Buffer resources: B ends with its last row (element (K-1)*ldb + N), so
+    // k-rows >= K read 0; A ends with its last row.
+    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)p.B, (short)0, (int)min(((int64_t)(K - 1) * ldb + N) * 2, (int64_t)0x7fffffff), 0x00020000);
+    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)p.A, (short)0, (int)min(((int64_t)(M - 1) * lda + K) * 2, (int64_t)0x7fffffff), 0x00020000);
 
     // Per-lane DMA source offsets within one stage.
     uint32_t b_off[B_INS];
@@ -66,7 +67,7 @@ gemm_skinny_kernel(GemmArgs p) {
         const int kr = P >> 3, pc = P & 7;
         const int c = pc ^ sk_swz_b(kr);
         const int n = min(n0 + 8 * c, N - 8);              // past-N columns re-read the last chunk
-        b_off[i] = (uint32_t)((kr * N + n) * 2);
+        b_off[i] = (uint32_t)((kr * ldb + n) * 2);
     }
     // A stage: [MR][SK_BK] fp16 = 16 chunks per row, chunk c of row m at c ^ (m & 15).
     // Rows >= M are clamped to M-1 (results never stored); a dword past K in a
@@ -82,7 +83,7 @@ gemm_skinny_kernel(GemmArgs p) {
         const int c = pc ^ (m & 15);
         const int mm = min(m, M - 1);
         a_kcol[i] = 8 * c + 2 * w;                         // k offset within the stage
-        a_off[i] = (uint32_t)((mm * K + a_kcol[i]) * 2);
+        a_off[i] = (uint32_t)((mm * lda + a_kcol[i]) * 2);
     }
 
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
@@ -90,7 +91,7 @@ gemm_skinny_kernel(GemmArgs p) {
     const uint32_t a_lds0 = lds_addr(a_lds) + wave_s * 64 * 4;
     auto issue = [&](int kt, int s) {
         const int kbase = kt * SK_BK;
-        const uint32_t b_so = (uint32_t)kbase * N * 2;
+        const uint32_t b_so = (uint32_t)kbase * ldb * 2;
 #pragma unroll
         for (int i = 0; i < B_INS; ++i)
             dma_buffer_16_nt(b_rsrc, b_off[i] + b_so, b_lds0 + s * B_STAGE + i * SK_WAVES * 64 * 16);
@@ -170,7 +171,7 @@ gemm_skinny_kernel(GemmArgs p) {
             f16x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = (f16)apply_epilogue<EPI>(acc[mb][e], bv[e]);
-            *(f16x4*)(p.C + (size_t)m * N + n) = o;
+            *(f16x4*)(p.C + (size_t)m * ldc + n) = o;
         }
     }
 }

@@ -31,8 +31,8 @@
 //    - LOAD_DMA: HBM/L2 -> LDS by LDS-DMA (global_load_lds_dwordx4), so no
 //      VGPR is spent on staging. STAGES ring buffers. The copies of stage
 //      kt+STAGES-1 are issued at every DSTRIDE-th slot of stage kt.
-//      Requires K % BK == 0, N % 8 == 0, A/B/C 16-byte aligned and bias
-//      8-byte aligned. Rows past M re-read row M-1, and columns past N
+//      Requires K % BK == 0, N % 8 == 0, 16-byte-aligned rows of A, B and C
+//      (bases and leading dimensions) and an 8-byte-aligned bias. Rows past M re-read row M-1, and columns past N
 //      re-read the last chunk; neither is stored.
 //    - LOAD_BUF: the same LDS-DMA ring, issued through buffer resources
 //      (buffer_load_dwordx4 ... lds), for unaligned shapes: any M and N,
@@ -159,7 +159,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     GK_LDS char* const a_lds = (GK_LDS char*)smem_raw;           // [STAGES][BM][BK]
     GK_LDS char* const b_lds = a_lds + STAGES * A_STAGE;         // [STAGES][BK][BN]
 
-    const int M = p.M, N = p.N, K = p.K;
+    const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb, ldc = p.ldc;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     int tm, tn;
@@ -214,10 +214,10 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         const int P = (i * NW + wave) * 64 + lane;
         const int r = P / CA, c = (P % CA) ^ swz_a<BK>(r);
         const int m = min(m0 + r, M - 1);
-        if constexpr (RING) a_off[i] = (uint32_t)(((m - m0) * K + 8 * c) * 2);
+        if constexpr (RING) a_off[i] = (uint32_t)(((m - m0) * lda + 8 * c) * 2);
         if constexpr (LOADER != LOAD_DMA) a_ck[i] = 8 * c;
         if constexpr (LOADER == LOAD_REG) {
-            a_row[i] = p.A + (size_t)m * K;
+            a_row[i] = p.A + (size_t)m * lda;
         }
     }
 #pragma unroll
@@ -226,31 +226,33 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         const int kr = P / CB, c = (P % CB) ^ swz_b<BN, MF>(kr);
         if constexpr (LOADER == LOAD_DMA) {
             const int n = min(n0 + 8 * c, N - 8) - n0;
-            b_off[i] = (uint32_t)((kr * N + n) * 2);
+            b_off[i] = (uint32_t)((kr * ldb + n) * 2);
         } else if constexpr (LOADER == LOAD_BUF) {
-            b_off[i] = (uint32_t)((kr * N + 8 * c) * 2);
+            b_off[i] = (uint32_t)((kr * ldb + 8 * c) * 2);
         } else {
             b_kr[i] = kr;
             b_cn[i] = n0 + 8 * c;
         }
     }
-    const char* const a_row0 = (const char*)(p.A + (size_t)m0 * K);
+    const char* const a_row0 = (const char*)(p.A + (size_t)m0 * lda);
     const char* const b_col0 = (const char*)(p.B + n0);
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t a_lds0 = lds_addr(a_lds) + wave_s * 64 * 16;
     const uint32_t b_lds0 = lds_addr(b_lds) + wave_s * 64 * 16;
 
     // LOAD_BUF: buffer resources of stage kt.  A: from the stage's tile origin
-    // to the end of A.  B: from the stage's tile origin to the end of B (plus
-    // the 2-byte pad for odd N).  Both byte counts fit 31 bits (host check).
+    // to the end of A's last row.  B: from the stage's tile origin to the end
+    // of B's last row (plus the 2-byte pad for odd N).  Both byte counts fit
+    // 31 bits (host check).
     const int b_pad = (N & 1) ? 2 : 0;
     auto rsrc_a = [&](int kt) {
         return __builtin_amdgcn_make_buffer_rsrc((void*)(a_row0 + (size_t)kt * BK * 2), (short)0,
-                                                 (M - m0) * K * 2 - kt * BK * 2, 0x00020000);
+                                                 ((M - 1 - m0) * lda + K) * 2 - kt * BK * 2, 0x00020000);
     };
     auto rsrc_b = [&](int kt) {
-        return __builtin_amdgcn_make_buffer_rsrc((void*)(b_col0 + (size_t)kt * BK * N * 2), (short)0,
-                                                 K * N * 2 + b_pad - n0 * 2 - kt * BK * N * 2, 0x00020000);
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(b_col0 + (size_t)kt * BK * ldb * 2), (short)0,
+                                                 ((K - 1) * ldb + N) * 2 + b_pad - n0 * 2 - kt * BK * ldb * 2,
+                                                 0x00020000);
     };
     // Ring loaders: copy j of stage kt into ring buffer sb.
     auto dma_op = [&](int j, int kt, int sb) {
@@ -267,7 +269,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
             if constexpr (LOADER == LOAD_BUF) {
                 dma_buffer_16(rsrc_b(kt), b_off[i], lds);
             } else {
-                dma_global_16(b_col0 + (size_t)kt * BK * N * 2, b_off[i], lds);
+                dma_global_16(b_col0 + (size_t)kt * BK * ldb * 2, b_off[i], lds);
             }
         }
     };
@@ -288,7 +290,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         } else {
             const int i = j - A_INS;
             const int k = kt * BK + b_kr[i], n = b_cn[i];
-            const f16* src = p.B + (size_t)k * N + n;
+            const f16* src = p.B + (size_t)k * ldb + n;
             if (k < K) {
                 if (n + 8 <= N) {
                     v = *(const f16x8_u*)src;
@@ -468,7 +470,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
                 f16x4 o;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[e] = (f16)apply_epilogue<EPI>(acc[mi][ni][4 * r4 + e], bv[e]);
-                f16* dst = p.C + (size_t)m * N + n;
+                f16* dst = p.C + (size_t)m * ldc + n;
                 if (quad) {
                     *(f16x4_u*)dst = o;
                 } else {

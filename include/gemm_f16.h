@@ -33,8 +33,8 @@
  * element-wise edges.  Misalignment is never an error.
  *
  * Reads: the library reads only A, B and bias, with one exception.  With odd N
- * it may read the 2 bytes that follow the end of B, and then only when they lie
- * in the same 4 KiB page as B's last element, so the read cannot fault.  Those
+ * it may read the 2 bytes that follow B's last element, and then only when they
+ * lie in the same 4 KiB page as that element, so the read cannot fault.  Those
  * bytes reach only output columns past N, which are never written.
  *
  * Ownership: the caller owns every buffer.  The library never allocates,
@@ -92,6 +92,23 @@ int gemm_f16(int64_t M, int64_t N, int64_t K,
              const void* A, const void* B, const void* bias, void* C,
              int epilogue, void* stream);
 
+/*
+ * The same product on row-major matrices with leading dimensions (row strides,
+ * in elements): A[i][k] at A + i*lda + k, B[k][j] at B + k*ldb + j, C[i][j] at
+ * C + i*ldc + j, so A, B and C may be sub-matrices of larger row-major arrays
+ * (e.g. a column slice).  Requires lda >= K and ldb >= N when K > 0, and
+ * ldc >= N; otherwise GEMM_ERR_INVALID_DIM (also for strides above 2^31 - 1).
+ * Elements between the end of a row and the next row start are never written;
+ * the padding of A and B may be read, but only inside the arrays' extent
+ * (plus, with odd N, the 2 bytes after B's last element, under the rule given
+ * for gemm_f16).  The fast paths additionally want lda, ldb and ldc to be
+ * multiples of 8.  gemm_f16() is gemm_f16_ex() with lda = K, ldb = ldc = N.
+ */
+int gemm_f16_ex(int64_t M, int64_t N, int64_t K,
+                const void* A, int64_t lda, const void* B, int64_t ldb,
+                const void* bias, void* C, int64_t ldc,
+                int epilogue, void* stream);
+
 /* Static, NUL-terminated name of a status code ("GEMM_OK", ...). */
 const char* gemm_f16_status_string(int status);
 
@@ -118,6 +135,15 @@ int gemm_f16_select_config(int64_t M, int64_t N, int64_t K,
 int gemm_f16_with_config(int idx, int64_t M, int64_t N, int64_t K,
                          const void* A, const void* B, const void* bias, void* C,
                          int epilogue, void* stream);
+
+/* The strided forms of the two calls above (leading dimensions as in gemm_f16_ex). */
+int gemm_f16_select_config_ex(int64_t M, int64_t N, int64_t K,
+                              const void* A, int64_t lda, const void* B, int64_t ldb,
+                              const void* bias, void* C, int64_t ldc, int epilogue);
+int gemm_f16_with_config_ex(int idx, int64_t M, int64_t N, int64_t K,
+                            const void* A, int64_t lda, const void* B, int64_t ldb,
+                            const void* bias, void* C, int64_t ldc,
+                            int epilogue, void* stream);
 
 /*
  * Element-wise fp32 vector add C[i] = A[i] + B[i], 0 <= i < n (the tutorial's

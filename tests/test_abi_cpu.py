@@ -163,3 +163,20 @@ def test_attention_validation():
     assert fa(1, 1, 4, 4, 64, FAKE + 8, FAKE, FAKE, FAKE, False, 0.1) == 7
     assert fa(0, 1, 4, 4, 64, None, None, None, None, False, 0.1) == 0
     assert fa(1, 1, 0, 0, 64, None, None, None, None, True, 0.1) == 0
+
+
+def test_strided_validation_and_dispatch():
+    ex = g.gemm_f16_ex_raw
+    assert ex(64, 64, 64, FAKE, 63, FAKE, 64, None, FAKE, 64, 0) == 1      # lda < K
+    assert ex(64, 64, 64, FAKE, 64, FAKE, 63, None, FAKE, 64, 0) == 1      # ldb < N
+    assert ex(64, 64, 64, FAKE, 64, FAKE, 64, None, FAKE, 63, 0) == 1      # ldc < N
+    assert ex(64, 64, 64, FAKE, -1, FAKE, 64, None, FAKE, 64, 0) == 1
+    assert ex(64, 64, 64, FAKE, 1 << 31, FAKE, 64, None, FAKE, 64, 0) == 1
+    assert ex(0, 64, 64, None, 0, None, 0, None, None, 0, 0) == 0          # empty: no-op
+    sel = g.select_config_ex_raw
+    # dense strides: same choice as the dense entry point
+    assert sel(4096, 4096, 4096, FAKE, 4096, FAKE, 4096, None, FAKE, 4096, 0) == \
+        g.select_config_raw(4096, 4096, 4096, FAKE, FAKE, None, FAKE, 0)
+    # padded but 16-byte-aligned rows keep the LDS-DMA path; unaligned rows take another loader
+    assert g.config_info(sel(4096, 4096, 4096, FAKE, 4104, FAKE, 4160, None, FAKE, 4112, 0))["loader"] == "dma"
+    assert g.config_info(sel(4096, 4096, 4096, FAKE, 4101, FAKE, 4096, None, FAKE, 4096, 0))["loader"] != "dma"

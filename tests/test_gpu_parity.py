@@ -405,3 +405,39 @@ def test_vector_add(lib):
     z = g.vector_add(x[1:], x[:-1])
     torch.cuda.synchronize()
     assert torch.equal(z, x[1:] + x[:-1])
+
+
+# ---------------------------------------------------------------------------
+# strided layouts: A, B and C as column slices of wider row-major arrays
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(300, 520, 256), (333, 277, 104), (16, 1032, 384), (257, 136, 192), (45, 200, 136)])
+@pytest.mark.parametrize("pad", [24, 5])
+def test_strided_submatrices_every_config(lib, shape, pad):
+    import dense_tiled_gemm_04_amd as g
+    M, N, K = shape
+    A, B, bias = workloads.make_inputs("ragged_4095x3001x1000", M=M, N=N, K=K)
+    ref = oracle.gemm(A, B, bias, "bias_gelu")
+    lda, ldb, ldc = K + pad, N + pad, N + pad + 8
+    Abuf = torch.zeros((M, lda), dtype=torch.float16, device="cuda")
+    Bbuf = torch.zeros((K, ldb), dtype=torch.float16, device="cuda")
+    Abuf[:, pad:pad + K] = dev(A)
+    Bbuf[:, 0:N] = dev(B)
+    Av, Bv = Abuf[:, pad:pad + K], Bbuf[:, 0:N]
+    assert Av.stride() == (lda, 1) and Bv.stride() == (ldb, 1)
+    db = dev(bias)
+    ran = []
+    for c in lib.configs() + [None]:
+        Cbuf = torch.full((M, ldc), -7.0, dtype=torch.float16, device="cuda")
+        Cv = Cbuf[:, 8:8 + N]
+        try:
+            g.gemm_f16(Av, Bv, db, "bias_gelu", out=Cv, config=None if c is None else c["idx"])
+        except g.GemmError as e:
+            assert c is not None and e.status == 6, e   # only "this config cannot run this call"
+            continue
+        torch.cuda.synchronize()
+        host = Cbuf.cpu().numpy()
+        name = "default" if c is None else c["name"]
+        assert np.all(host[:, :8] == np.float16(-7.0)) and np.all(host[:, 8 + N:] == np.float16(-7.0)), name
+        assert_parity(host[:, 8:8 + N], ref, (shape, pad, name))
+        ran.append(name)
+    assert "default" in ran and len(ran) >= 3, ran
