@@ -56,7 +56,8 @@
 //      chunk that straddles the end of a row (N) or of K. Zeros are written
 //      past K (in both A and B) and past N, and rows past M are clamped.
 //  * Tile order. XCD-contiguous remap of the workgroup id, then a grouped
-//    raster of GROUP_M tile-rows.
+//    raster of GROUP_M tile-rows (GROUP_M = 1: row-major after the remap;
+//    GROUP_M = 0: row-major without the remap, the unswizzled baseline).
 #pragma once
 #include "common.h"
 
@@ -163,7 +164,11 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     int tm, tn;
-    {
+    if constexpr (GROUP_M == 0) {
+        // plain row-major tile order, no XCD remap (the unswizzled baseline of the tile-order ablation)
+        tm = (int)blockIdx.x / p.tiles_n;
+        tn = (int)blockIdx.x % p.tiles_n;
+    } else {
         const int nwg = p.tiles_m * p.tiles_n;
         grouped_tile<GROUP_M>(xcd_contiguous_id((int)blockIdx.x, nwg), p.tiles_m, p.tiles_n, tm, tn);
     }

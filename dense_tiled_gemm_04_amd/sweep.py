@@ -216,6 +216,11 @@ def space() -> list:
         out.append(Tile(128, 128, 64, 2, 2, st, 4, 1, 1, "buf"))
     out.append(Tile(128, 128, 64, 2, 2, 3, 4, 3, 2, "buf", mf=16, spread=1))
     out.append(Tile(128, 192, 64, 2, 2, 3, 4, 1, 1, "buf"))
+    # tile-order ablation of the two large-tile schedules: no swizzle (g0), XCD remap only (g1)
+    for g in (0, 1, 8):
+        out.append(Tile(256, 256, 64, 2, 2, 2, g, 8, 2, "dma", mf=16, spread=1))
+    for g in (0, 1):
+        out.append(Tile(256, 256, 64, 2, 2, 2, g, 3, 1, "dma"))
     for mb, sts in ((1, (4, 6, 8)), (2, (4, 6)), (4, (3, 5))):
         for st in sts:
             out.append(Skinny(mb, st))
@@ -467,6 +472,47 @@ def select(results_path: str, table_path: str = TABLE, summary_path: str | None 
     return chosen
 
 
+def ablation(results_path: str, out_path: str) -> None:
+    """Markdown tables of the tile-order and pipeline-depth ablations from the sweep results: each row is one
+    schedule with only the ablated knob varied (the tutorial's use_swizzle switch and num_stages)."""
+    recs = [json.loads(l) for l in open(results_path) if l.strip()]
+    t = {(r["config"], r["workload"]): r for r in recs if r.get("ok")}
+    by_name = {c.name: c for c in space()}
+    lines = ["# Ablations: tile order (swizzle) and LDS stages", "",
+             "Median of 20 HIP-event-timed launches per cell on one MI355X, from the same sweep records as the",
+             "configuration table (`python -m dense_tiled_gemm_04_amd.sweep --run RESULTS` on the GPU, then",
+             "`--ablation RESULTS`).", "",
+             "## Tile order", "",
+             "g0: row-major tile order, no XCD remap (swizzle off). g1: XCD-contiguous remap, row-major.",
+             "g4 / g8: XCD remap plus a grouped raster of 4 / 8 tile-rows (swizzle on).", ""]
+    wls = ["gemm_4096", "mlp_up_8192x16384x4096", "gemm_2048", "gemm_4096_offset1"]
+    lines += ["| schedule | workload | g0 us | g1 us | g4 us | g8 us |", "|---|---|---|---|---|---|"]
+    bases = sorted({c.name.replace("_g%d_" % c.group, "_gX_") for c in by_name.values()
+                    if c.kind == "tile" and c.group == 0})
+    for base in bases:
+        for w in wls:
+            cells = []
+            for g in (0, 1, 4, 8):
+                r = t.get((base.replace("_gX_", "_g%d_" % g), w))
+                cells.append("%.1f" % r["median_us"] if r else "-")
+            if cells.count("-") < 3:
+                lines.append("| %s | %s | %s |" % (base, w, " | ".join(cells)))
+    lines += ["", "## LDS stages", "", "Same schedule, 2, 3 or 4 LDS stages (where the LDS budget allows).", "",
+              "| schedule | workload | s2 us | s3 us | s4 us |", "|---|---|---|---|---|"]
+    fams = sorted({c.name.replace("_s%d_" % c.stages, "_sX_") for c in by_name.values()
+                   if c.kind == "tile" and c.loader != "reg"})
+    for fam in fams:
+        for w in wls + ["ragged_4095x3001x1000"]:
+            cells = []
+            for st in (2, 3, 4):
+                r = t.get((fam.replace("_sX_", "_s%d_" % st), w))
+                cells.append("%.1f" % r["median_us"] if r else "-")
+            if cells.count("-") <= 1:
+                lines.append("| %s | %s | %s |" % (fam, w, " | ".join(cells)))
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--list", action="store_true", help="print the sweep space")
@@ -475,6 +521,9 @@ def main() -> int:
     ap.add_argument("--only", default=None, help="comma-separated sweep workload names for --run")
     ap.add_argument("--select", metavar="RESULTS", help="pick per-class defaults, write csrc/config_table.inc")
     ap.add_argument("--summary", default=None, help="Markdown summary path for --select")
+    ap.add_argument("--ablation", metavar="RESULTS", help="write the tile-order / stages ablation tables")
+    ap.add_argument("--ablation-out", default=os.path.join(ROOT, "profiles",
+                                                           "ablation__tile_order_and_stages__gemm_workloads.md"))
     a = ap.parse_args()
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
@@ -487,6 +536,8 @@ def main() -> int:
         run(a.run, only=a.only)
     if a.select:
         print(json.dumps(select(a.select, summary_path=a.summary), indent=1))
+    if a.ablation:
+        ablation(a.ablation, a.ablation_out)
     return 0
 
 
