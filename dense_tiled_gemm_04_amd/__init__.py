@@ -33,6 +33,7 @@ EXPORTS = [
     "gemm_f16", "gemm_f16_status_string", "gemm_f16_num_configs", "gemm_f16_config_info",
     "gemm_f16_select_config", "gemm_f16_with_config", "vector_add_f32",
     "gemm_f16_ex", "gemm_f16_select_config_ex", "gemm_f16_with_config_ex",
+    "gemm_f16_bt", "gemm_f16_bt_select_config", "gemm_f16_bt_with_config",
     "softmax_rows_f16", "softmax_rows_f16_path", "flash_attn_fwd_f16",
 ]
 SOFTMAX_PATHS = {0: "none", 1: "wave", 2: "workgroup", 3: "online"}
@@ -68,6 +69,12 @@ def load():
     lib.gemm_f16_with_config_ex.restype = i32
     lib.gemm_f16_select_config_ex.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, vp, i64, i32]
     lib.gemm_f16_select_config_ex.restype = i32
+    lib.gemm_f16_bt.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, vp, i64, i32, vp]
+    lib.gemm_f16_bt.restype = i32
+    lib.gemm_f16_bt_with_config.argtypes = [i32, i64, i64, i64, vp, i64, vp, i64, vp, vp, i64, i32, vp]
+    lib.gemm_f16_bt_with_config.restype = i32
+    lib.gemm_f16_bt_select_config.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, vp, i64, i32]
+    lib.gemm_f16_bt_select_config.restype = i32
     lib.gemm_f16_status_string.argtypes = [i32]
     lib.gemm_f16_status_string.restype = ctypes.c_char_p
     lib.gemm_f16_num_configs.argtypes = []
@@ -132,6 +139,18 @@ def select_config_ex_raw(M, N, K, A, lda, B, ldb, bias, C, ldc, epilogue: int) -
     return int(load().gemm_f16_select_config_ex(M, N, K, A, lda, B, ldb, bias, C, ldc, epilogue))
 
 
+def gemm_f16_bt_raw(M, N, K, A, lda, Bt, ldb, bias, C, ldc, epilogue: int, stream=0,
+                    config: int | None = None) -> int:
+    lib = load()
+    if config is None:
+        return int(lib.gemm_f16_bt(M, N, K, A, lda, Bt, ldb, bias, C, ldc, epilogue, stream))
+    return int(lib.gemm_f16_bt_with_config(config, M, N, K, A, lda, Bt, ldb, bias, C, ldc, epilogue, stream))
+
+
+def select_config_bt_raw(M, N, K, A, lda, Bt, ldb, bias, C, ldc, epilogue: int) -> int:
+    return int(load().gemm_f16_bt_select_config(M, N, K, A, lda, Bt, ldb, bias, C, ldc, epilogue))
+
+
 def softmax_rows_raw(rows, cols, X, Y, stream=0) -> int:
     return int(load().softmax_rows_f16(rows, cols, X, Y, stream))
 
@@ -184,8 +203,10 @@ def _stream_handle():
     return torch.cuda.current_stream().cuda_stream
 
 
-def gemm_f16(A, B, bias=None, epilogue: str = "none", out=None, config: int | None = None):
+def gemm_f16(A, B, bias=None, epilogue: str = "none", out=None, config: int | None = None,
+             b_transposed: bool = False):
     """C = fp16(epi(A @ B [+ bias])) on the current stream; returns C (torch.float16 [M, N]).
+    With b_transposed, B is given as Bt [N, K] (a linear layer's weight) and C = epi(A @ Bt^T).
     A, B and out may be row-major sub-matrices of wider arrays (unit column stride)."""
     import torch
     if epilogue not in EPILOGUES:
@@ -193,7 +214,7 @@ def gemm_f16(A, B, bias=None, epilogue: str = "none", out=None, config: int | No
     lda = _check_rows(A, "A")
     ldb = _check_rows(B, "B")
     M, K = A.shape
-    K2, N = B.shape
+    N, K2 = B.shape if b_transposed else B.shape[::-1]
     if K != K2:
         raise ValueError("inner dimensions differ: A is %s, B is %s" % (tuple(A.shape), tuple(B.shape)))
     if A.device != B.device:
@@ -212,22 +233,24 @@ def gemm_f16(A, B, bias=None, epilogue: str = "none", out=None, config: int | No
             raise ValueError("out must be [%d, %d]" % (M, N))
     ldc = _check_rows(out, "out")
     with torch.cuda.device(A.device):
-        st = gemm_f16_ex_raw(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, bias.data_ptr() if epi != 0 else None,
-                             out.data_ptr(), ldc, epi, _stream_handle(), config)
+        fn = gemm_f16_bt_raw if b_transposed else gemm_f16_ex_raw
+        st = fn(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, bias.data_ptr() if epi != 0 else None,
+                out.data_ptr(), ldc, epi, _stream_handle(), config)
     if st != 0:
         raise GemmError(st)
     return out
 
 
-def select_config(A, B, bias=None, epilogue: str = "none", out=None) -> int:
+def select_config(A, B, bias=None, epilogue: str = "none", out=None, b_transposed: bool = False) -> int:
     """Index of the configuration gemm_f16 would launch (-1 for an empty output)."""
     M, K = A.shape
-    N = B.shape[1]
+    N = B.shape[0] if b_transposed else B.shape[1]
     epi = EPILOGUES[epilogue]
     optr = out.data_ptr() if out is not None else 256  # a 256-byte-aligned stand-in address
     ldc = _check_rows(out, "out") if out is not None else N
-    r = select_config_ex_raw(M, N, K, A.data_ptr(), _check_rows(A, "A"), B.data_ptr(), _check_rows(B, "B"),
-                             bias.data_ptr() if bias is not None else None, optr, ldc, epi)
+    fn = select_config_bt_raw if b_transposed else select_config_ex_raw
+    r = fn(M, N, K, A.data_ptr(), _check_rows(A, "A"), B.data_ptr(), _check_rows(B, "B"),
+           bias.data_ptr() if bias is not None else None, optr, ldc, epi)
     if r < -1:
         raise GemmError(-r)
     return r

@@ -4,7 +4,8 @@ Three translation units: csrc/gemm_f16.hip (every GEMM kernel instantiation and
 the C ABI of include/gemm_f16.h), csrc/softmax.hip (the row softmax, C ABI in
 include/softmax_f16.h) and csrc/attention.hip (the attention forward pass, C ABI
 in include/attention_f16.h).  Flags: gfx950 only, -O3, no
-fast-math, packed-fp32 VALU instructions disabled.
+fast-math, packed-fp32 VALU instructions disabled, a pragma-unroll threshold
+high enough for the fully unrolled MFMA schedules.
 """
 from __future__ import annotations
 
@@ -35,6 +36,9 @@ def compile_cmd(out: str, save_temps_dir: str | None = None) -> list[str]:
     cmd = [
         hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++20", "-shared", "-fPIC",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # the fenced MFMA schedules are fully unrolled loops of a few thousand instructions; a refused
+        # unroll leaves the fragment and accumulator arrays in scratch memory
+        "-mllvm", "-pragma-unroll-threshold=200000",
         "-I" + INCLUDE, "-I" + CSRC, "-o", out,
     ] + SOURCES
     if save_temps_dir:

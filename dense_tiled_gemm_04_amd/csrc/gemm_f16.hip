@@ -26,17 +26,18 @@ struct Config {
     int stages;
     int bslot, dstride, cslot, wpe;  // tile schedule: barrier slot, copy stride, LDS-write slot, waves/SIMD
     int mfma, spread;                // tile MFMA shape (32: 32x32x16, 16: 16x16x32), spread LDS reads
+    int bt;                          // 1: B given transposed (Bt[N][K])
     int lds_bytes;
     int threads;
     launch_fn launch[3];     // indexed by epilogue
 };
 
 template <int BM, int BN, int BK, int WM, int WN, int ST, int G, int BS, int DS, int LOADER, int CS, int WPE, int MF,
-          int SP, int EPI>
+          int SP, int BT, int EPI>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(WM * WN * 64);
-    hipLaunchKernelGGL((gemm_tile_pipe_kernel<BM, BN, BK, WM, WN, ST, G, EPI, BS, DS, LOADER, CS, WPE, MF, SP>), grid,
-                       block, 0, s, a);
+    hipLaunchKernelGGL((gemm_tile_pipe_kernel<BM, BN, BK, WM, WN, ST, G, EPI, BS, DS, LOADER, CS, WPE, MF, SP, BT>),
+                       grid, block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -50,21 +51,21 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
 // Tile config: block tile BM x BN x BK, WM x WN waves, ST LDS stages, tile
 // order group G, barrier slot BS, copy stride DS, loader, LDS-write slot CS
 // (register loader), waves per SIMD WPE, MFMA shape MF (32 or 16), spread
-// LDS reads SP.
-#define TILE_CFG(BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, NAME)                 \
+// LDS reads SP, B transposed BT.
+#define TILE_CFG(BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, BT, NAME)             \
     Config {                                                                                       \
-        NAME, KIND_TILE, BM, BN, BK, WM, WN, LOADER, G, ST, BS, DS, CS, WPE, MF, SP,               \
-            TilePipeCfg<BM, BN, BK, WM, WN, ST, MF>::LDS_BYTES, WM * WN * 64,                      \
+        NAME, KIND_TILE, BM, BN, BK, WM, WN, LOADER, G, ST, BS, DS, CS, WPE, MF, SP, BT,           \
+            TilePipeCfg<BM, BN, BK, WM, WN, ST, MF, BT>::LDS_BYTES, WM * WN * 64,                  \
         {                                                                                          \
-            launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, 0>,            \
-                launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, 1>,        \
-                launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, 2>         \
+            launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, BT, 0>,        \
+                launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, BT, 1>,    \
+                launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, BT, 2>     \
         }                                                                                          \
     }
 
 #define SKINNY_CFG(MB, ST, NAME)                                                                    \
     Config {                                                                                       \
-        NAME, KIND_SKINNY, 16 * MB, SK_BN, SK_BK, 1, SK_WAVES, -1, 1, ST, 0, 0, 0, 1, 16, 0,       \
+        NAME, KIND_SKINNY, 16 * MB, SK_BN, SK_BK, 1, SK_WAVES, -1, 1, ST, 0, 0, 0, 1, 16, 0, 0,    \
             ST * (16 * MB * SK_BK * 2 + SK_BK * SK_BN * 2), SK_WAVES * 64,                         \
         {                                                                                          \
             launch_skinny<MB, ST, 0>, launch_skinny<MB, ST, 1>, launch_skinny<MB, ST, 2>           \
@@ -84,7 +85,8 @@ constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 static_assert(SEL_SKINNY16 < kNumConfigs && SEL_SKINNY32 < kNumConfigs && SEL_SKINNY64 < kNumConfigs &&
                   SEL_DMA_HUGE < kNumConfigs && SEL_DMA_BIG < kNumConfigs && SEL_DMA_SMALL < kNumConfigs &&
                   SEL_BUF_BIG < kNumConfigs && SEL_BUF_SMALL < kNumConfigs && SEL_REG_BIG < kNumConfigs &&
-                  SEL_REG_SMALL < kNumConfigs,
+                  SEL_REG_SMALL < kNumConfigs && SEL_BT_BIG < kNumConfigs && SEL_BT_SMALL < kNumConfigs &&
+                  SEL_BT_BUF < kNumConfigs && SEL_BT_REG < kNumConfigs,
               "shape-class defaults index the table");
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -95,6 +97,7 @@ struct Call {
     void* C;
     int epi;
     int64_t lda, ldb, ldc;  // leading dimensions (row strides) in elements
+    bool bt = false;        // B given transposed: Bt[N][K], row stride ldb >= K
 };
 
 int validate(const Call& c) {
@@ -104,7 +107,7 @@ int validate(const Call& c) {
     if (c.lda < 0 || c.ldb < 0 || c.ldc < 0 || c.lda > INT32_MAX || c.ldb > INT32_MAX || c.ldc > INT32_MAX)
         return GEMM_ERR_INVALID_DIM;
     if (c.M == 0 || c.N == 0) return GEMM_OK;
-    if (c.ldc < c.N || (c.K > 0 && (c.lda < c.K || c.ldb < c.N))) return GEMM_ERR_INVALID_DIM;
+    if (c.ldc < c.N || (c.K > 0 && (c.lda < c.K || c.ldb < (c.bt ? c.K : c.N)))) return GEMM_ERR_INVALID_DIM;
     if (!c.C) return GEMM_ERR_NULL_POINTER;
     if (c.K > 0 && (!c.A || !c.B)) return GEMM_ERR_NULL_POINTER;
     if (c.epi != GEMM_EPI_NONE && !c.bias) return GEMM_ERR_NULL_POINTER;
@@ -116,12 +119,13 @@ int validate(const Call& c) {
 
 // Whether config `cfg` can run call `c` (validated, M, N > 0).
 bool supports(const Config& cfg, const Call& c) {
+    if ((cfg.bt != 0) != c.bt) return false;  // each B layout has its own configurations
     const bool epi_bias_ok = (c.epi == GEMM_EPI_NONE) || aligned(c.bias, 8);
     // 16-byte-aligned rows: aligned bases and leading dimensions that are multiples of 8 elements
     const bool vec_ok = aligned(c.A, 16) && aligned(c.B, 16) && aligned(c.C, 16) && c.K % 8 == 0 &&
                         c.N % 8 == 0 && c.lda % 8 == 0 && c.ldb % 8 == 0 && c.ldc % 8 == 0 && epi_bias_ok;
     const int64_t a_end = (c.M - 1) * c.lda + c.K;  // elements from A to the end of its last row
-    const int64_t b_end = (c.K - 1) * c.ldb + c.N;  // same for B
+    const int64_t b_end = c.bt ? (c.N - 1) * c.ldb + c.K : (c.K - 1) * c.ldb + c.N;  // same for B (or Bt)
     if (cfg.kind == KIND_SKINNY) {
         // 32-bit buffer offsets: B rows up to K + SK_BK (the last stage's tail) and all of A
         return vec_ok && c.M <= cfg.bm && (c.K + SK_BK) * c.ldb * 2 < (int64_t)INT32_MAX &&
@@ -129,22 +133,31 @@ bool supports(const Config& cfg, const Call& c) {
     }
     if (cfg.loader == LOAD_DMA)
         return vec_ok && c.K % cfg.bk == 0 && (int64_t)cfg.bm * c.lda * 2 < (int64_t)INT32_MAX &&
-               (int64_t)cfg.bk * c.ldb * 2 < (int64_t)INT32_MAX;
+               (int64_t)(c.bt ? cfg.bn : cfg.bk) * c.ldb * 2 < (int64_t)INT32_MAX;
     if (cfg.loader == LOAD_BUF) {
         // 31-bit buffer sizes and offsets: all of A and B, and one stage's tiles.
         const int64_t lim = (int64_t)INT32_MAX - 64;
         const bool fits = c.K > 0 && a_end * 2 < lim && b_end * 2 < lim &&
-                          ((int64_t)cfg.bm * c.lda + cfg.bk) * 2 < lim && ((int64_t)cfg.bk * c.ldb + cfg.bn) * 2 < lim;
+                          ((int64_t)cfg.bm * c.lda + cfg.bk) * 2 < lim &&
+                          (c.bt ? (int64_t)cfg.bn * c.ldb + cfg.bk : (int64_t)cfg.bk * c.ldb + cfg.bn) * 2 < lim;
         // Odd N: B's range is padded by 2 bytes past the end of its last row;
         // allowed only when that end is not on a 4 KiB page boundary, so the
         // pad lies in the page of the last element.
-        const bool pad_ok = c.N % 2 == 0 || ((uintptr_t)c.B + (uintptr_t)(b_end * 2)) % 4096 != 0;
+        // (Bt needs no pad: its rows past N are clamped and its k-chunks past K
+        // are sent out of range, like A's.)
+        const bool pad_ok = c.bt || c.N % 2 == 0 || ((uintptr_t)c.B + (uintptr_t)(b_end * 2)) % 4096 != 0;
         return c.K % 8 == 0 && fits && pad_ok;
     }
     return true;  // register loader: any shape, any 2-byte alignment
 }
 
 int pick_default(const Call& c) {
+    if (c.bt) {
+        const int64_t tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256);
+        const int dma = tiles256 >= 256 ? SEL_BT_BIG : SEL_BT_SMALL;
+        if (supports(kConfigs[dma], c)) return dma;
+        return supports(kConfigs[SEL_BT_BUF], c) ? SEL_BT_BUF : SEL_BT_REG;
+    }
     // skinny M: bandwidth path streaming B once
     if (c.M <= 64) {
         const int idx = c.M <= 16 ? SEL_SKINNY16 : (c.M <= 32 ? SEL_SKINNY32 : SEL_SKINNY64);
@@ -236,10 +249,10 @@ int gemm_f16_config_info(int idx, char* buf, int buflen) {
                      "{\"idx\": %d, \"name\": \"%s\", \"kind\": \"%s\", \"bm\": %d, \"bn\": %d, \"bk\": %d, "
                      "\"waves_m\": %d, \"waves_n\": %d, \"loader\": \"%s\", \"group_m\": %d, \"stages\": %d, "
                      "\"bslot\": %d, \"dstride\": %d, \"cslot\": %d, \"waves_per_simd\": %d, "
-                     "\"mfma\": %d, \"spread\": %d, \"lds_bytes\": %d, \"threads\": %d}",
+                     "\"mfma\": %d, \"spread\": %d, \"b_transposed\": %d, \"lds_bytes\": %d, \"threads\": %d}",
                      idx, c.name, c.kind == KIND_TILE ? "tile" : "skinny", c.bm, c.bn, c.bk, c.wm, c.wn,
                      c.kind == KIND_TILE ? loaders[c.loader] : "lds_dma", c.group_m, c.stages, c.bslot,
-                     c.dstride, c.cslot, c.wpe, c.mfma, c.spread, c.lds_bytes, c.threads);
+                     c.dstride, c.cslot, c.wpe, c.mfma, c.spread, c.bt, c.lds_bytes, c.threads);
     if (buf && buflen > 0) {
         strncpy(buf, tmp, (size_t)buflen - 1);
         buf[buflen - 1] = '\0';
@@ -284,6 +297,35 @@ int gemm_f16_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
     if (st != GEMM_OK) return st;
     if (M == 0 || N == 0) return GEMM_OK;
     return run(kConfigs[pick_default(c)], c, (hipStream_t)stream);
+}
+
+int gemm_f16_bt(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* Bt, int64_t ldb,
+                const void* bias, void* C, int64_t ldc, int epilogue, void* stream) {
+    Call c{M, N, K, A, Bt, bias, C, epilogue, lda, ldb, ldc, true};
+    int st = validate(c);
+    if (st != GEMM_OK) return st;
+    if (M == 0 || N == 0) return GEMM_OK;
+    return run(kConfigs[pick_default(c)], c, (hipStream_t)stream);
+}
+
+int gemm_f16_bt_select_config(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* Bt, int64_t ldb,
+                              const void* bias, void* C, int64_t ldc, int epilogue) {
+    Call c{M, N, K, A, Bt, bias, C, epilogue, lda, ldb, ldc, true};
+    int st = validate(c);
+    if (st != GEMM_OK) return -st;
+    if (M == 0 || N == 0) return -1;
+    return pick_default(c);
+}
+
+int gemm_f16_bt_with_config(int idx, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* Bt,
+                            int64_t ldb, const void* bias, void* C, int64_t ldc, int epilogue, void* stream) {
+    Call c{M, N, K, A, Bt, bias, C, epilogue, lda, ldb, ldc, true};
+    int st = validate(c);
+    if (st != GEMM_OK) return st;
+    if (idx < 0 || idx >= kNumConfigs) return GEMM_ERR_NO_CONFIG;
+    if (M == 0 || N == 0) return GEMM_OK;
+    if (!supports(kConfigs[idx], c)) return GEMM_ERR_UNSUPPORTED;
+    return run(kConfigs[idx], c, (hipStream_t)stream);
 }
 
 int gemm_f16(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias, void* C, int epilogue,

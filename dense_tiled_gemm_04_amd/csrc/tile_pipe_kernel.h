@@ -55,6 +55,10 @@
 //      accepts unaligned addresses. Element-wise loads are used only for a
 //      chunk that straddles the end of a row (N) or of K. Zeros are written
 //      past K (in both A and B) and past N, and rows past M are clamped.
+//  * BT = 1: B is given transposed, Bt[N][K] row-major (the layout of a linear
+//    layer's weight), and C = A . Bt^T.  Its tiles [BN][BK] are copied, laid
+//    out and read exactly like A's (K-contiguous rows, ds_read_b128), with rows
+//    past N clamped and (LOAD_BUF) k-chunks past K sent out of range.
 //  * Tile order. XCD-contiguous remap of the workgroup id, then a grouped
 //    raster of GROUP_M tile-rows (GROUP_M = 1: row-major after the remap;
 //    GROUP_M = 0: row-major without the remap, the unswizzled baseline).
@@ -103,7 +107,7 @@ __device__ __forceinline__ int swz_b(int kr) {
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int MF = 32>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int MF = 32, int BT = 0>
 struct TilePipeCfg {
     static constexpr int NW = WM * WN;
     static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave sub-tile
@@ -114,15 +118,16 @@ struct TilePipeCfg {
     static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE);
     static constexpr int KSTEPS = BK / KS;              // k-steps per stage
     static constexpr int A_INS = BM * CA / 64 / NW;     // 16-byte copies per lane and stage
-    static constexpr int B_INS = BK * CB / 64 / NW;
+    static constexpr int B_INS = BT ? BN * CA / 64 / NW : BK * CB / 64 / NW;
     static constexpr int PER_STAGE = A_INS + B_INS;
     static constexpr int NMMA = TM * TN;                // MFMAs (slots) per k-step
-    static constexpr int NRD = TM + 2 * TN;             // LDS reads per k-step
+    static constexpr int NB = BT ? TN : 2 * TN;         // B fragment reads per k-step
+    static constexpr int NRD = TM + NB;                 // LDS reads per k-step
     static_assert(MF == 32 || MF == 16, "MFMA shape");
     static_assert(KSTEPS % 2 == 0, "even k-steps per stage (fragment ping-pong)");
     static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile of whole MFMA blocks");
     static_assert((CA & (CA - 1)) == 0 && CB >= 4 && ((CB & (CB - 1)) == 0 || CB % 8 == 0), "chunk counts");
-    static_assert((BM * CA) % (64 * NW) == 0 && (BK * CB) % (64 * NW) == 0, "copy split over waves");
+    static_assert((BM * CA) % (64 * NW) == 0 && (BT ? BN * CA : BK * CB) % (64 * NW) == 0, "copy split over waves");
     static_assert(STAGES >= 2 && PER_STAGE * (STAGES - 1) <= 63, "vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
@@ -138,15 +143,15 @@ typedef f16x8 f16x8_u __attribute__((aligned(2)));
 typedef f16x4 f16x4_u __attribute__((aligned(2)));
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int GROUP_M, int EPI, int BSLOT, int DSTRIDE,
-          int LOADER, int CSLOT, int WPE, int MF, int SPREAD>
+          int LOADER, int CSLOT, int WPE, int MF, int SPREAD, int BT>
 __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 gemm_tile_pipe_kernel(GemmArgs p) {
-    using Cfg = TilePipeCfg<BM, BN, BK, WM, WN, STAGES, MF>;
+    using Cfg = TilePipeCfg<BM, BN, BK, WM, WN, STAGES, MF, BT>;
     constexpr int KS = Cfg::KS;
     constexpr int NW = Cfg::NW, WTM = Cfg::WTM, WTN = Cfg::WTN, TM = Cfg::TM, TN = Cfg::TN;
     constexpr int CA = Cfg::CA, CB = Cfg::CB, A_STAGE = Cfg::A_STAGE, B_STAGE = Cfg::B_STAGE;
     constexpr int KSTEPS = Cfg::KSTEPS, A_INS = Cfg::A_INS, B_INS = Cfg::B_INS, PER_STAGE = Cfg::PER_STAGE;
-    constexpr int NMMA = Cfg::NMMA, NRD = Cfg::NRD;
+    constexpr int NMMA = Cfg::NMMA, NRD = Cfg::NRD, NB = Cfg::NB;
     constexpr int LAST = (KSTEPS - 1) * NMMA + BSLOT;  // stage slot of the barrier
     constexpr bool RING = LOADER != LOAD_REG;          // LDS-DMA ring of STAGES buffers
     static_assert(BSLOT >= 0 && BSLOT + 1 < NMMA, "barrier slot inside the last k-step, reads after it");
@@ -191,8 +196,8 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     // MF = 32: kb = 8 (g / 2) (+ 16 kk + 4 h), nb = 16 (g % 2) within a 32-column block;
     // MF = 16: kb = 8 g (+ 32 kk + 4 h), nb = 0 within a 16-column block.
     // Neither the k-step nor the half h changes the swizzle of the row.
-    int b_rd[TN];
-    {
+    int b_rd[BT ? 1 : TN];
+    if constexpr (!BT) {
         const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
         const int kr = (MF == 32 ? 8 * (g >> 1) : 8 * g) + j;
 #pragma unroll
@@ -200,6 +205,16 @@ gemm_tile_pipe_kernel(GemmArgs p) {
             const int nl = wn * WTN + ni * MF + (MF == 32 ? 16 * (g & 1) : 0) + 4 * q;
             b_rd[ni] = kr * BN * 2 + (((nl >> 3) ^ swz_b<BN, MF>(kr)) << 4) + ((nl & 7) << 1);
         }
+    }
+    // BT: B is held transposed, Bt[n][k], and its LDS tile [BN][BK] is laid out
+    // and read exactly like A's: lane l reads Bt[n = row(l)][KS kk + 8 (l / MF) .. +7].
+    int bt_rd[BT ? KSTEPS : 1];
+    if constexpr (BT) {
+        const int row = wn * WTN + (lane % MF);
+        const int s = swz_a<BK>(row);
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk)
+            bt_rd[kk] = row * BK * 2 + ((((KS / 8) * kk + lane / MF) ^ s) << 4);
     }
 
     // Copy j (0 <= j < PER_STAGE) of a stage: destination chunk
@@ -212,8 +227,9 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     // per chunk, the k offset in the stage and the row pointer (rows clamped
     // to M-1) for A, the k-row and column for B.
     uint32_t a_off[A_INS], b_off[B_INS];
-    int a_ck[A_INS], b_kr[B_INS], b_cn[B_INS];
+    int a_ck[A_INS], b_kr[B_INS], b_cn[B_INS], b_ck[B_INS];
     const f16* a_row[A_INS];
+    const f16* b_row[B_INS];
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
         const int P = (i * NW + wave) * 64 + lane;
@@ -228,19 +244,28 @@ gemm_tile_pipe_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
         const int P = (i * NW + wave) * 64 + lane;
-        const int kr = P / CB, c = (P % CB) ^ swz_b<BN, MF>(kr);
-        if constexpr (LOADER == LOAD_DMA) {
-            const int n = min(n0 + 8 * c, N - 8) - n0;
-            b_off[i] = (uint32_t)((kr * ldb + n) * 2);
-        } else if constexpr (LOADER == LOAD_BUF) {
-            b_off[i] = (uint32_t)((kr * ldb + 8 * c) * 2);
+        if constexpr (BT) {  // as for A: row n of Bt (clamped to N-1), k chunk c
+            const int r = P / CA, c = (P % CA) ^ swz_a<BK>(r);
+            const int n = min(n0 + r, N - 1);
+            if constexpr (RING) b_off[i] = (uint32_t)(((n - n0) * ldb + 8 * c) * 2);
+            if constexpr (LOADER != LOAD_DMA) b_ck[i] = 8 * c;
+            if constexpr (LOADER == LOAD_REG) b_row[i] = p.B + (size_t)n * ldb;
         } else {
-            b_kr[i] = kr;
-            b_cn[i] = n0 + 8 * c;
+            const int kr = P / CB, c = (P % CB) ^ swz_b<BN, MF>(kr);
+            if constexpr (LOADER == LOAD_DMA) {
+                const int n = min(n0 + 8 * c, N - 8) - n0;
+                b_off[i] = (uint32_t)((kr * ldb + n) * 2);
+            } else if constexpr (LOADER == LOAD_BUF) {
+                b_off[i] = (uint32_t)((kr * ldb + 8 * c) * 2);
+            } else {
+                b_kr[i] = kr;
+                b_cn[i] = n0 + 8 * c;
+            }
         }
     }
     const char* const a_row0 = (const char*)(p.A + (size_t)m0 * lda);
-    const char* const b_col0 = (const char*)(p.B + n0);
+    // origin of the B tile: column n0 of B, or row n0 of Bt
+    const char* const b_col0 = (const char*)(BT ? p.B + (size_t)n0 * ldb : p.B + n0);
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t a_lds0 = lds_addr(a_lds) + wave_s * 64 * 16;
     const uint32_t b_lds0 = lds_addr(b_lds) + wave_s * 64 * 16;
@@ -255,9 +280,14 @@ gemm_tile_pipe_kernel(GemmArgs p) {
                                                  ((M - 1 - m0) * lda + K) * 2 - kt * BK * 2, 0x00020000);
     };
     auto rsrc_b = [&](int kt) {
-        return __builtin_amdgcn_make_buffer_rsrc((void*)(b_col0 + (size_t)kt * BK * ldb * 2), (short)0,
-                                                 ((K - 1) * ldb + N) * 2 + b_pad - n0 * 2 - kt * BK * ldb * 2,
-                                                 0x00020000);
+        if constexpr (BT) {  // to the end of Bt's last row, like A
+            return __builtin_amdgcn_make_buffer_rsrc((void*)(b_col0 + (size_t)kt * BK * 2), (short)0,
+                                                     ((N - 1 - n0) * ldb + K) * 2 - kt * BK * 2, 0x00020000);
+        } else {
+            return __builtin_amdgcn_make_buffer_rsrc((void*)(b_col0 + (size_t)kt * BK * ldb * 2), (short)0,
+                                                     ((K - 1) * ldb + N) * 2 + b_pad - n0 * 2 - kt * BK * ldb * 2,
+                                                     0x00020000);
+        }
     };
     // Ring loaders: copy j of stage kt into ring buffer sb.
     auto dma_op = [&](int j, int kt, int sb) {
@@ -271,8 +301,12 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         } else {
             const int i = j - A_INS;
             const uint32_t lds = b_lds0 + sb * B_STAGE + i * NW * 64 * 16;
-            if constexpr (LOADER == LOAD_BUF) {
+            if constexpr (LOADER == LOAD_BUF && BT) {
+                dma_buffer_16(rsrc_b(kt), b_ck[i] < K - kt * BK ? b_off[i] : 0x80000000u, lds);
+            } else if constexpr (LOADER == LOAD_BUF) {
                 dma_buffer_16(rsrc_b(kt), b_off[i], lds);
+            } else if constexpr (BT) {
+                dma_global_16(b_col0 + (size_t)kt * BK * 2, b_off[i], lds);
             } else {
                 dma_global_16(b_col0 + (size_t)kt * BK * ldb * 2, b_off[i], lds);
             }
@@ -285,6 +319,17 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         if (j < A_INS) {
             const int k = kt * BK + a_ck[j];
             const f16* src = a_row[j] + k;
+            if (k + 8 <= K) {
+                v = *(const f16x8_u*)src;
+            } else if (k < K) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (k + e < K) v[e] = src[e];
+            }
+        } else if constexpr (BT) {
+            const int i = j - A_INS;
+            const int k = kt * BK + b_ck[i];
+            const f16* src = b_row[i] + k;
             if (k + 8 <= K) {
                 v = *(const f16x8_u*)src;
             } else if (k < K) {
@@ -325,26 +370,38 @@ gemm_tile_pipe_kernel(GemmArgs p) {
             for (int r = 0; r < NACC; ++r) acc[mi][ni][r] = 0.0f;
 
     // Two fragment sets: the reads of k-step kk+1 land in one while the MFMAs
-    // of k-step kk consume the other.  Read j: 0 -> A[0]; 1..2TN -> halves of
-    // B[(j-1)/2]; then A[1..TM-1] -- the order in which MFMA row 0 needs them.
+    // of k-step kk consume the other.  Read j: 0 -> A[0]; 1..NB -> B (halves of
+    // B[(j-1)/2] by transpose reads, or Bt[j-1] whole with BT); then A[1..TM-1]
+    // -- the order in which MFMA row 0 needs them.
     f16x8 fa[2][TM];
-    f16x4 fb[2][TN][2];
+    f16x4 fb[2][BT ? 1 : TN][2];
+    f16x8 fbt[2][BT ? TN : 1];
     auto read_op = [&](int set, int j, int sb, int kk) {
         const GK_LDS char* As = a_lds + sb * A_STAGE;
         const GK_LDS char* Bs = b_lds + sb * B_STAGE;
         if (j == 0) {
             fa[set][0] = *(const GK_LDS f16x8*)(As + a_rd[kk]);
-        } else if (j <= 2 * TN) {
-            const int ni = (j - 1) / 2, h = (j - 1) % 2;
-            fb[set][ni][h] = lds_read_tr16_b64(Bs + b_rd[ni] + (KS * kk + 4 * h) * BN * 2);
+        } else if (j <= NB) {
+            if constexpr (BT) {
+                const int ni = j - 1;
+                fbt[set][ni] = *(const GK_LDS f16x8*)(Bs + bt_rd[kk] + ni * MF * BK * 2);
+            } else {
+                const int ni = (j - 1) / 2, h = (j - 1) % 2;
+                fb[set][ni][h] = lds_read_tr16_b64(Bs + b_rd[ni] + (KS * kk + 4 * h) * BN * 2);
+            }
         } else {
-            const int mi = j - 2 * TN;
+            const int mi = j - NB;
             fa[set][mi] = *(const GK_LDS f16x8*)(As + a_rd[kk] + mi * MF * BK * 2);
         }
     };
     auto mma_op = [&](int set, int i) {
         const int mi = i / TN, ni = i % TN;
-        const f16x8 b = __builtin_shufflevector(fb[set][ni][0], fb[set][ni][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        f16x8 b;
+        if constexpr (BT) {
+            b = fbt[set][ni];
+        } else {
+            b = __builtin_shufflevector(fb[set][ni][0], fb[set][ni][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        }
         if constexpr (MF == 32) {
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, fa[set][mi], acc[mi][ni], 0, 0, 0);
         } else {

@@ -75,6 +75,7 @@ class Tile:
     wpe: int = 1         # waves per SIMD (= workgroups per CU, 4-wave workgroups)
     mf: int = 32         # MFMA shape: 32 -> 32x32x16, 16 -> 16x16x32
     spread: int = 0      # LDS reads spread evenly over a k-step's slots
+    bt: int = 0          # B given transposed (Bt[N][K])
 
     kind = "tile"
 
@@ -86,7 +87,8 @@ class Tile:
             n += "_c%d" % self.cslot
         n += "_o%d" % self.wpe if self.wpe != 1 else ""
         n += "_m16" if self.mf == 16 else ""
-        return n + ("_sp" if self.spread else "")
+        n += "_sp" if self.spread else ""
+        return n + ("_bt" if self.bt else "")
 
     # derived quantities, as in TilePipeCfg (csrc/tile_pipe_kernel.h)
     @property
@@ -100,14 +102,16 @@ class Tile:
         ca, cb = self.bk // 8, self.bn // 8
         ksteps = self.bk // (16 if self.mf == 32 else 32)
         a_ins = self.bm * ca // 64 // nw
-        b_ins = self.bk * cb // 64 // nw
+        b_ins = (self.bn * ca if self.bt else self.bk * cb) // 64 // nw
         return dict(nw=nw, wtm=wtm, wtn=wtn, tm=tm, tn=tn, ca=ca, cb=cb, ksteps=ksteps, a_ins=a_ins, b_ins=b_ins,
-                    per_stage=a_ins + b_ins, nmma=tm * tn, nrd=tm + 2 * tn, nacc=self.mf * self.mf // 64)
+                    per_stage=a_ins + b_ins, nmma=tm * tn, nrd=tm + (tn if self.bt else 2 * tn),
+                    nacc=self.mf * self.mf // 64)
 
     def macro(self) -> str:
-        return "TILE_CFG(%d, %d, %d, %d, %d, %d, %d, %d, %d, %s, %d, %d, %d, %d, \"%s\")" % (
+        return "TILE_CFG(%d, %d, %d, %d, %d, %d, %d, %d, %d, %s, %d, %d, %d, %d, %d, \"%s\")" % (
             self.bm, self.bn, self.bk, self.wm, self.wn, self.stages, self.group, self.bslot, self.dstride,
-            {"dma": "LOAD_DMA", "buf": "LOAD_BUF", "reg": "LOAD_REG"}[self.loader], self.cslot, self.wpe, self.mf, self.spread, self.name)
+            {"dma": "LOAD_DMA", "buf": "LOAD_BUF", "reg": "LOAD_REG"}[self.loader], self.cslot, self.wpe, self.mf,
+            self.spread, self.bt, self.name)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -148,7 +152,7 @@ def valid(c) -> bool:
     cb_ok = pow2(d["cb"]) or (d["cb"] % 8 == 0 and (c.bn * 2) % 256 == 128)   # e.g. BN = 192
     if not (pow2(d["ca"]) and cb_ok and d["cb"] >= 4):
         return False
-    if (c.bm * d["ca"]) % (64 * d["nw"]) or (c.bk * d["cb"]) % (64 * d["nw"]):
+    if (c.bm * d["ca"]) % (64 * d["nw"]) or ((c.bn * d["ca"]) if c.bt else (c.bk * d["cb"])) % (64 * d["nw"]):
         return False
     ps = d["per_stage"]
     if c.stages < 2 or ps * (c.stages - 1) > 63:
@@ -221,6 +225,16 @@ def space() -> list:
         out.append(Tile(256, 256, 64, 2, 2, 2, g, 8, 2, "dma", mf=16, spread=1))
     for g in (0, 1):
         out.append(Tile(256, 256, 64, 2, 2, 2, g, 3, 1, "dma"))
+    # B given transposed (Bt[N][K], a linear layer's weight): the shapes of the best plain schedules
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 8, 2, "dma", mf=16, spread=1, bt=1))
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 3, 1, "dma", bt=1))
+    out.append(Tile(128, 128, 64, 2, 2, 3, 4, 1, 1, "dma", bt=1))
+    out.append(Tile(128, 128, 64, 2, 2, 3, 4, 3, 2, "dma", mf=16, spread=1, bt=1))
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 3, 1, "buf", bt=1))
+    out.append(Tile(128, 192, 64, 2, 2, 3, 4, 1, 1, "buf", bt=1))
+    out.append(Tile(128, 128, 64, 2, 2, 3, 4, 1, 1, "buf", bt=1))
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 3, 2, "reg", bt=1))
+    out.append(Tile(128, 128, 64, 2, 2, 2, 4, 1, 1, "reg", wpe=2, bt=1))
     for mb, sts in ((1, (4, 6, 8)), (2, (4, 6)), (4, (3, 5))):
         for st in sts:
             out.append(Skinny(mb, st))
@@ -228,7 +242,8 @@ def space() -> list:
 
 
 CLASSES = ["SEL_SKINNY16", "SEL_SKINNY32", "SEL_SKINNY64", "SEL_DMA_HUGE", "SEL_DMA_BIG", "SEL_DMA_SMALL",
-           "SEL_BUF_BIG", "SEL_BUF_SMALL", "SEL_REG_BIG", "SEL_REG_SMALL"]
+           "SEL_BUF_BIG", "SEL_BUF_SMALL", "SEL_REG_BIG", "SEL_REG_SMALL",
+           "SEL_BT_BIG", "SEL_BT_SMALL", "SEL_BT_BUF", "SEL_BT_REG"]
 
 
 def class_of(c, cls: str) -> bool:
@@ -240,8 +255,16 @@ def class_of(c, cls: str) -> bool:
     if cls.startswith("SEL_SKINNY"):
         if c.kind == "skinny":
             return 16 * c.mb >= int(cls[len("SEL_SKINNY"):])
-        return c.loader == "dma"
+        return c.loader == "dma" and not c.bt
     if c.kind != "tile":
+        return False
+    if cls.startswith("SEL_BT_"):   # B transposed: LDS-DMA (big/small), buffer or register loader
+        if not c.bt:
+            return False
+        kind = cls[len("SEL_BT_"):]
+        return c.loader == {"BIG": "dma", "SMALL": "dma", "BUF": "buf", "REG": "reg"}[kind] or \
+            (kind == "BUF" and c.loader == "reg")
+    if c.bt:
         return False
     if "_BUF_" in cls:
         return c.loader in ("buf", "reg")
@@ -303,6 +326,14 @@ def sweep_workloads():
                                                              K=1004, seed=6), {}, ["SEL_REG_SMALL"]))
     out.append(("gemm_4096x4096x4092", dataclasses.replace(W["gemm_4096"], name="gemm_k4092", K=4092, seed=7),
                 {}, ["SEL_REG_BIG"]))
+    # B given transposed (Bt[N][K])
+    out.append(("gemm_4096_bt", W["gemm_4096"], {"bt": True}, ["SEL_BT_BIG"]))
+    out.append(("mlp_up_8192x16384x4096_bt", W["mlp_up_8192x16384x4096"], {"bt": True}, ["SEL_BT_BIG"]))
+    out.append(("gemm_2048_bt", dataclasses.replace(W["gemm_4096"], name="gemm_2048", M=2048, N=2048, K=2048, seed=5),
+                {"bt": True}, ["SEL_BT_SMALL"]))
+    out.append(("ragged_4095x3001x1000_bt", W["ragged_4095x3001x1000"], {"bt": True}, ["SEL_BT_BUF"]))
+    out.append(("ragged_4095x3001x1004_bt", dataclasses.replace(W["ragged_4095x3001x1000"], name="ragged_k1004",
+                                                                K=1004, seed=6), {"bt": True}, ["SEL_BT_REG"]))
     # HBM-bound: B (256 MiB) is rotated over 3 copies so the 256 MB Infinity Cache cannot serve it
     out.append(("skinny_16x16384x8192", W["skinny_16x16384x8192"], {"rotate": 3}, ["SEL_SKINNY16"]))
     out.append(("skinny_32x16384x8192", dataclasses.replace(W["skinny_16x16384x8192"], name="skinny_32", M=32),
@@ -334,6 +365,8 @@ def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str
     i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     lib.gemm_f16_with_config.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, i32, vp]
     lib.gemm_f16_with_config.restype = i32
+    lib.gemm_f16_bt_with_config.argtypes = [i32, i64, i64, i64, vp, i64, vp, i64, vp, vp, i64, i32, vp]
+    lib.gemm_f16_bt_with_config.restype = i32
     lib.gemm_f16_config_info.argtypes = [i32, ctypes.c_char_p, i32]
     n_cfg = lib.gemm_f16_num_configs()
     infos = []
@@ -364,9 +397,11 @@ def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str
             t[off:] = torch.from_numpy(np.ascontiguousarray(x).reshape(-1)).to(dev)
             return t[off:].view(*x.shape)
 
+        bt = opts.get("bt", False)
         dA = place(A)
-        dBs = [place(B) for _ in range(opts.get("rotate", 1))]
-        dB = dBs[0]
+        # the kernels get Bt[N][K] for the transposed workloads; the reference keeps B[K][N]
+        dBs = [place(np.ascontiguousarray(B.T) if bt else B) for _ in range(opts.get("rotate", 1))]
+        dB = dBs[0].t().contiguous() if bt else dBs[0]
         db = place(bias) if bias is not None else None
         cbuf = torch.empty(w.M * w.N + off, dtype=torch.float16, device=dev)
         dC = cbuf[off:].view(w.M, w.N)
@@ -379,25 +414,31 @@ def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str
         for i, info in enumerate(infos):
             if (info["name"], name) in done:
                 continue
+            if bt:
+                call = lambda *a: lib.gemm_f16_bt_with_config(a[0], a[1], a[2], a[3], a[4], w.K, a[5], w.K, a[6],
+                                                              a[7], w.N, a[8], a[9])
+            else:
+                call = lib.gemm_f16_with_config
+
             def args(r=0):
                 return (i, w.M, w.N, w.K, dA.data_ptr(), dBs[r % len(dBs)].data_ptr(),
                         db.data_ptr() if db is not None else None, dC.data_ptr(), epi, stream.cuda_stream)
-            st = lib.gemm_f16_with_config(*args())
+            st = call(*args())
             if st == 6:  # GEMM_ERR_UNSUPPORTED: this config cannot run this call
                 continue
             if st != 0:
                 raise RuntimeError("config %s on %s: status %d" % (info["name"], name, st))
             for r in range(3):
-                lib.gemm_f16_with_config(*args(r + 1))
+                call(*args(r + 1))
             torch.cuda.synchronize()
             evs = []
             for r in range(iters):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                lib.gemm_f16_with_config(*args(r + 1))
+                call(*args(r + 1))
                 e1.record(stream)
                 evs.append((e0, e1))
-            lib.gemm_f16_with_config(*args(0))   # the screened output comes from the first copy of B
+            call(*args(0))   # the screened output comes from the first copy of B
             torch.cuda.synchronize()
             us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
             med = us[len(us) // 2]

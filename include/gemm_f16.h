@@ -109,6 +109,18 @@ int gemm_f16_ex(int64_t M, int64_t N, int64_t K,
                 const void* bias, void* C, int64_t ldc,
                 int epilogue, void* stream);
 
+/*
+ * C = epi(A . Bt^T) with B given transposed: Bt is fp16 [N][K] row-major with
+ * row stride ldb >= K (the layout of a linear layer's weight, out-features x
+ * in-features), so C[i][j] = epi(sum_k A[i][k] * Bt[j][k]).  Everything else
+ * (lda, ldc, epilogue, errors, streams) is as in gemm_f16_ex; ldb < K with
+ * K > 0 is GEMM_ERR_INVALID_DIM.  No bytes past Bt's last element are read.
+ */
+int gemm_f16_bt(int64_t M, int64_t N, int64_t K,
+                const void* A, int64_t lda, const void* Bt, int64_t ldb,
+                const void* bias, void* C, int64_t ldc,
+                int epilogue, void* stream);
+
 /* Static, NUL-terminated name of a status code ("GEMM_OK", ...). */
 const char* gemm_f16_status_string(int status);
 
@@ -142,6 +154,15 @@ int gemm_f16_select_config_ex(int64_t M, int64_t N, int64_t K,
                               const void* bias, void* C, int64_t ldc, int epilogue);
 int gemm_f16_with_config_ex(int idx, int64_t M, int64_t N, int64_t K,
                             const void* A, int64_t lda, const void* B, int64_t ldb,
+                            const void* bias, void* C, int64_t ldc,
+                            int epilogue, void* stream);
+
+/* The same two calls for a transposed B (as in gemm_f16_bt). */
+int gemm_f16_bt_select_config(int64_t M, int64_t N, int64_t K,
+                              const void* A, int64_t lda, const void* Bt, int64_t ldb,
+                              const void* bias, void* C, int64_t ldc, int epilogue);
+int gemm_f16_bt_with_config(int idx, int64_t M, int64_t N, int64_t K,
+                            const void* A, int64_t lda, const void* Bt, int64_t ldb,
                             const void* bias, void* C, int64_t ldc,
                             int epilogue, void* stream);
 

@@ -180,3 +180,23 @@ def test_strided_validation_and_dispatch():
     # padded but 16-byte-aligned rows keep the LDS-DMA path; unaligned rows take another loader
     assert g.config_info(sel(4096, 4096, 4096, FAKE, 4104, FAKE, 4160, None, FAKE, 4112, 0))["loader"] == "dma"
     assert g.config_info(sel(4096, 4096, 4096, FAKE, 4101, FAKE, 4096, None, FAKE, 4096, 0))["loader"] != "dma"
+
+
+def test_b_transposed_validation_and_dispatch():
+    bt = g.gemm_f16_bt_raw
+    assert bt(64, 64, 64, FAKE, 64, FAKE, 63, None, FAKE, 64, 0) == 1      # ldb < K for Bt [N][K]
+    assert bt(64, 64, 64, FAKE, 63, FAKE, 64, None, FAKE, 64, 0) == 1      # lda < K
+    assert bt(0, 64, 64, None, 0, None, 0, None, None, 0, 0) == 0
+    sel = g.select_config_bt_raw
+    c = g.config_info(sel(4096, 4096, 4096, FAKE, 4096, FAKE, 4096, None, FAKE, 4096, 0))
+    assert c["b_transposed"] == 1 and c["loader"] == "dma"
+    c = g.config_info(sel(4095, 3001, 1000, FAKE, 1000, FAKE, 1000, FAKE, FAKE, 3001, 1))
+    assert c["b_transposed"] == 1 and c["loader"] in ("buf", "reg")
+    c = g.config_info(sel(4095, 3001, 1001, FAKE, 1001, FAKE, 1001, FAKE, FAKE, 3001, 1))
+    assert c["b_transposed"] == 1 and c["loader"] == "reg"
+    # plain-layout calls never pick a transposed config, and forced mismatches are refused
+    for c in g.configs():
+        if c["b_transposed"]:
+            assert g.gemm_f16_raw(256, 256, 256, FAKE, FAKE, None, FAKE, 0, 0, config=c["idx"]) == 6
+        else:
+            assert bt(256, 256, 256, FAKE, 256, FAKE, 256, None, FAKE, 256, 0, config=c["idx"]) == 6

@@ -32,6 +32,8 @@ def configs_for(lib, M, N, K, epi):
     """All compiled configs able to run this (aligned, contiguous) call."""
     out = []
     for c in lib.configs():
+        if c["b_transposed"]:
+            continue
         if c["kind"] == "skinny" and M > c["bm"]:
             continue
         if c["loader"] == "dma" and K % c["bk"] != 0:
@@ -263,7 +265,7 @@ def test_misaligned_views(lib):
     assert_parity(Cv.cpu().numpy(), ref, "misaligned")
     # every configuration that accepts the misaligned views
     for c in lib.configs():
-        if c["kind"] != "tile" or c["loader"] == "dma":
+        if c["kind"] != "tile" or c["loader"] == "dma" or c["b_transposed"]:
             continue
         Cv.zero_()
         g.gemm_f16(Av, Bv, dev(bias), "bias_gelu", out=Cv, config=c["idx"])
@@ -275,7 +277,7 @@ def test_misaligned_views(lib):
 # buffer LDS-DMA loader: unaligned rows, K tails, odd N and the end of B
 # ---------------------------------------------------------------------------
 def _buf_configs(lib):
-    out = [c["idx"] for c in lib.configs() if c["kind"] == "tile" and c["loader"] == "buf"]
+    out = [c["idx"] for c in lib.configs() if c["kind"] == "tile" and c["loader"] == "buf" and not c["b_transposed"]]
     assert out
     return out
 
@@ -441,3 +443,76 @@ def test_strided_submatrices_every_config(lib, shape, pad):
         assert_parity(host[:, 8:8 + N], ref, (shape, pad, name))
         ran.append(name)
     assert "default" in ran and len(ran) >= 3, ran
+
+
+# ---------------------------------------------------------------------------
+# B given transposed: Bt [N][K] (a linear layer's weight layout), C = A . Bt^T
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(300, 520, 256), (333, 277, 104), (16, 1032, 384), (257, 136, 192),
+                                   (130, 264, 200), (5, 3001, 7), (64, 64, 64)])
+@pytest.mark.parametrize("epi", ["none", "bias_gelu"])
+def test_b_transposed_every_config(lib, shape, epi):
+    import dense_tiled_gemm_04_amd as g
+    M, N, K = shape
+    A, B, bias = workloads.make_inputs("mlp_up_8192x16384x4096", M=M, N=N, K=K)
+    if epi == "none":
+        bias = None
+    ref = oracle.gemm(A, B, bias, epi)
+    Bt = dev(np.ascontiguousarray(B.T))
+    dA, db = dev(A), (dev(bias) if bias is not None else None)
+    ran = []
+    for c in [c for c in lib.configs() if c["b_transposed"]] + [None]:
+        try:
+            out = g.gemm_f16(dA, Bt, db, epi, b_transposed=True, config=None if c is None else c["idx"])
+        except g.GemmError as e:
+            assert c is not None and e.status == 6, e
+            continue
+        torch.cuda.synchronize()
+        name = "default" if c is None else c["name"]
+        m = assert_parity(out.cpu().numpy(), ref, (shape, epi, name))
+        assert m["frac_exact"] > 0.97, (name, m)
+        ran.append(name)
+    assert "default" in ran and len(ran) >= 2, ran
+
+
+def test_b_transposed_strided_and_k_tail_isolation(lib):
+    # Bt as a column slice of a wider array, K not a multiple of the K-block, and infinities in column 0 of some
+    # Bt rows: a loader that let the next Bt row into the K tail of a row (times the zeroed A tail) would turn
+    # a whole output column into NaN.
+    import dense_tiled_gemm_04_amd as g
+    M, N, K = 130, 264, 200
+    A, B, bias = workloads.make_inputs("ragged_4095x3001x1000", M=M, N=N, K=K)
+    A[:, 0] = np.where(A[:, 0] == 0, np.float16(0.5), A[:, 0])
+    Bt = np.ascontiguousarray(B.T)
+    inf_cols = [1, 64, 65, 263]
+    Bt[inf_cols, 0] = np.float16(np.inf)
+    ref = oracle.gemm(A, np.ascontiguousarray(Bt.T), bias, "bias")
+    keep = np.setdiff1d(np.arange(N), inf_cols)
+    buf = torch.zeros((N, K + 40), dtype=torch.float16, device="cuda")
+    buf[:, 8:8 + K] = dev(Bt)
+    Btv = buf[:, 8:8 + K]
+    for c in [c for c in lib.configs() if c["b_transposed"]] + [None]:
+        try:
+            out = g.gemm_f16(dev(A), Btv, dev(bias), "bias", b_transposed=True,
+                             config=None if c is None else c["idx"])
+        except g.GemmError as e:
+            assert c is not None and e.status == 6, e
+            continue
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        name = "default" if c is None else c["name"]
+        assert_parity(got[:, keep], ref[:, keep], ("finite columns", name))
+        assert np.array_equal(got[:, inf_cols].view(np.uint16), ref[:, inf_cols].view(np.uint16)), name
+
+
+@pytest.mark.parametrize("name", ["mlp_up_8192x16384x4096"])
+def test_b_transposed_workload_sampled(lib, name):
+    import dense_tiled_gemm_04_amd as g
+    w = workloads.WORKLOADS[name]
+    A, B, bias = workloads.make_inputs(w)
+    out = g.gemm_f16(dev(A), dev(np.ascontiguousarray(B.T)), dev(bias), w.epilogue, b_transposed=True)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    r, c = _sample_points(w.M, w.N, 17, n_random=20000)
+    ref = oracle.gemm_points(A, B, bias, w.epilogue, r, c)
+    assert_parity(got[r, c][None, :], ref[None, :], name)

@@ -61,9 +61,9 @@ def test_product_table_entries_are_in_budget():
     for t in tiles:
         f = [x.strip() for x in t.split(",")]
         c = sweep.Tile(*map(int, f[:9]), f[9][len("LOAD_"):].lower(), int(f[10]), int(f[11]),
-                       int(f[12]), int(f[13]))
+                       int(f[12]), int(f[13]), int(f[14]))
         assert sweep.valid(c), c
-        assert f[14].strip('"') == c.name
+        assert f[15].strip('"') == c.name
     for s in skinny:
         f = [x.strip() for x in s.split(",")]
         assert sweep.valid(sweep.Skinny(int(f[0]), int(f[1])))
