@@ -22,6 +22,9 @@ written, against the HBM peak; copies of X rotated past the Infinity Cache).
 --workload attn_* benchmarks the attention forward pass (one step = one
 flash_attn_fwd_f16 call; value in TFLOP/s counting 4*D per allowed query-key
 pair, against the MFMA peak; PyTorch's fused SDPA timed alongside).
+--b-transposed stores the GEMM's B as Bt[N][K] (a linear layer's weight) and
+calls gemm_f16_bt; torch.nn.functional.linear on the same tensors is the
+comparison.
 """
 from __future__ import annotations
 
@@ -369,6 +372,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=None,
                     help="copies of B to rotate through (default: 3 for HBM-bound workloads, else 1)")
+    ap.add_argument("--b-transposed", action="store_true",
+                    help="GEMM workloads: B stored transposed, Bt[N][K], through gemm_f16_bt")
     ap.add_argument("--hbm-calibration", action="store_true",
                     help="run only the fp32 vector-add kernel on buffers of known size (the reference "
                          "point that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes)")
@@ -403,7 +408,9 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     dA = torch.from_numpy(A).to(dev)
-    dBs = [torch.from_numpy(B).to(dev) for _ in range(rotate)]
+    bt = args.b_transposed
+    Bdev = np.ascontiguousarray(B.T) if bt else B
+    dBs = [torch.from_numpy(Bdev).to(dev) for _ in range(rotate)]
     db = torch.from_numpy(bias).to(dev) if bias is not None else None
     dC = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
     epi = g.EPILOGUES[w.epilogue]
@@ -412,13 +419,23 @@ def main() -> int:
     pA, pC = dA.data_ptr(), dC.data_ptr()
     pBs = [b.data_ptr() for b in dBs]
     pb = db.data_ptr() if db is not None else None
-    cfg_idx = args.config if args.config is not None else g.select_config_raw(w.M, w.N, w.K, pA, pBs[0], pb, pC, epi)
-    cfg = g.config_info(cfg_idx)
     lib = g.load()
+    if bt:
+        ld = (w.K, w.K, w.N)  # lda, ldb (row length of Bt), ldc
+        cfg_idx = args.config if args.config is not None else \
+            g.select_config_bt_raw(w.M, w.N, w.K, pA, ld[0], pBs[0], ld[1], pb, pC, ld[2], epi)
+    else:
+        cfg_idx = args.config if args.config is not None else g.select_config_raw(w.M, w.N, w.K, pA, pBs[0], pb, pC, epi)
+    cfg = g.config_info(cfg_idx)
 
     def step(i):
-        st = lib.gemm_f16_with_config(cfg_idx, w.M, w.N, w.K, pA, pBs[i % rotate], pb, pC, epi, sh) \
-            if args.config is not None else lib.gemm_f16(w.M, w.N, w.K, pA, pBs[i % rotate], pb, pC, epi, sh)
+        if bt:
+            st = lib.gemm_f16_bt_with_config(cfg_idx, w.M, w.N, w.K, pA, ld[0], pBs[i % rotate], ld[1], pb, pC,
+                                             ld[2], epi, sh) if args.config is not None else \
+                lib.gemm_f16_bt(w.M, w.N, w.K, pA, ld[0], pBs[i % rotate], ld[1], pb, pC, ld[2], epi, sh)
+        else:
+            st = lib.gemm_f16_with_config(cfg_idx, w.M, w.N, w.K, pA, pBs[i % rotate], pb, pC, epi, sh) \
+                if args.config is not None else lib.gemm_f16(w.M, w.N, w.K, pA, pBs[i % rotate], pb, pC, epi, sh)
         if st != 0:
             raise g.GemmError(st)
 
@@ -437,9 +454,9 @@ def main() -> int:
     tflops = w.flops / (ms * 1e-3) / 1e12
     gbs = w.algorithmic_bytes / (ms * 1e-3) / 1e9
 
-    # context: the vendor BLAS on the same tensors (torch.matmul; + bias + gelu eagerly if fused)
+    # context: the vendor BLAS on the same tensors (torch.matmul, or F.linear for Bt; + bias + gelu eagerly if fused)
     def torch_step(i):
-        c = torch.matmul(dA, dBs[i % rotate])
+        c = torch.nn.functional.linear(dA, dBs[i % rotate]) if bt else torch.matmul(dA, dBs[i % rotate])
         if w.epilogue == "bias":
             c = c + db
         elif w.epilogue == "bias_gelu":
@@ -458,7 +475,7 @@ def main() -> int:
     torch.cuda.synchronize()
     torch_ms = t0.elapsed_time(t1) / n_t
 
-    traffic = load_traffic(w.name, cfg["name"])
+    traffic = load_traffic(w.name + ("_bt" if bt else ""), cfg["name"])
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": gbs / PEAK_HBM_GBS, "traffic": traffic}
@@ -488,10 +505,11 @@ def main() -> int:
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "epilogue": w.epilogue,
+                   "b_layout": "Bt[N][K]" if bt else "B[K][N]",
                    "inputs": "seeded numpy draws (%s), B copies rotated: %d" % (w.note, rotate)},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "context": {"torch_matmul_ms": round(torch_ms, 6),
+        "context": {("torch_linear_ms" if bt else "torch_matmul_ms"): round(torch_ms, 6),
                     "torch_tflops": round(w.flops / (torch_ms * 1e-3) / 1e12, 3),
                     "algorithmic_GBps": round(gbs, 1)},
     }
