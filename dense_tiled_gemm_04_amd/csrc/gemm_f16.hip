@@ -41,10 +41,10 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int MB, int STAGES, int EPI>
+template <int MB, int STAGES, int BT, int EPI>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.tiles_n), block(SK_WAVES * 64);
-    hipLaunchKernelGGL((gemm_skinny_kernel<MB, STAGES, EPI>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_skinny_kernel<MB, STAGES, EPI, BT>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -63,12 +63,13 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
         }                                                                                          \
     }
 
-#define SKINNY_CFG(MB, ST, NAME)                                                                    \
+// Skinny config: 16*MB rows, ST LDS stages, B transposed BT.
+#define SKINNY_CFG(MB, ST, BT, NAME)                                                                \
     Config {                                                                                       \
-        NAME, KIND_SKINNY, 16 * MB, SK_BN, SK_BK, 1, SK_WAVES, -1, 1, ST, 0, 0, 0, 1, 16, 0, 0,    \
+        NAME, KIND_SKINNY, 16 * MB, SK_BN, SK_BK, 1, SK_WAVES, -1, 1, ST, 0, 0, 0, 1, 16, 0, BT,   \
             ST * (16 * MB * SK_BK * 2 + SK_BK * SK_BN * 2), SK_WAVES * 64,                         \
         {                                                                                          \
-            launch_skinny<MB, ST, 0>, launch_skinny<MB, ST, 1>, launch_skinny<MB, ST, 2>           \
+            launch_skinny<MB, ST, BT, 0>, launch_skinny<MB, ST, BT, 1>, launch_skinny<MB, ST, BT, 2> \
         }                                                                                          \
     }
 
@@ -86,7 +87,8 @@ static_assert(SEL_SKINNY16 < kNumConfigs && SEL_SKINNY32 < kNumConfigs && SEL_SK
                   SEL_DMA_HUGE < kNumConfigs && SEL_DMA_BIG < kNumConfigs && SEL_DMA_SMALL < kNumConfigs &&
                   SEL_BUF_BIG < kNumConfigs && SEL_BUF_SMALL < kNumConfigs && SEL_REG_BIG < kNumConfigs &&
                   SEL_REG_SMALL < kNumConfigs && SEL_BT_BIG < kNumConfigs && SEL_BT_SMALL < kNumConfigs &&
-                  SEL_BT_BUF < kNumConfigs && SEL_BT_REG < kNumConfigs,
+                  SEL_BT_BUF < kNumConfigs && SEL_BT_REG < kNumConfigs && SEL_BT_SKINNY16 < kNumConfigs &&
+                  SEL_BT_SKINNY32 < kNumConfigs && SEL_BT_SKINNY64 < kNumConfigs,
               "shape-class defaults index the table");
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -127,9 +129,10 @@ bool supports(const Config& cfg, const Call& c) {
     const int64_t a_end = (c.M - 1) * c.lda + c.K;  // elements from A to the end of its last row
     const int64_t b_end = c.bt ? (c.N - 1) * c.ldb + c.K : (c.K - 1) * c.ldb + c.N;  // same for B (or Bt)
     if (cfg.kind == KIND_SKINNY) {
-        // 32-bit buffer offsets: B rows up to K + SK_BK (the last stage's tail) and all of A
-        return vec_ok && c.M <= cfg.bm && (c.K + SK_BK) * c.ldb * 2 < (int64_t)INT32_MAX &&
-               c.M * c.lda * 2 < (int64_t)INT32_MAX;
+        // 32-bit buffer offsets: B rows up to K + SK_BK (the last stage's tail), or all of Bt, and all of A
+        const bool b_fits = c.bt ? (b_end + SK_BK) * 2 < (int64_t)INT32_MAX
+                                 : (c.K + SK_BK) * c.ldb * 2 < (int64_t)INT32_MAX;
+        return vec_ok && c.M <= cfg.bm && b_fits && c.M * c.lda * 2 < (int64_t)INT32_MAX;
     }
     if (cfg.loader == LOAD_DMA)
         return vec_ok && c.K % cfg.bk == 0 && (int64_t)cfg.bm * c.lda * 2 < (int64_t)INT32_MAX &&
@@ -153,6 +156,10 @@ bool supports(const Config& cfg, const Call& c) {
 
 int pick_default(const Call& c) {
     if (c.bt) {
+        if (c.M <= 64) {  // skinny M: bandwidth path streaming Bt once
+            const int idx = c.M <= 16 ? SEL_BT_SKINNY16 : (c.M <= 32 ? SEL_BT_SKINNY32 : SEL_BT_SKINNY64);
+            if (supports(kConfigs[idx], c)) return idx;
+        }
         const int64_t tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256);
         const int dma = tiles256 >= 256 ? SEL_BT_BIG : SEL_BT_SMALL;
         if (supports(kConfigs[dma], c)) return dma;

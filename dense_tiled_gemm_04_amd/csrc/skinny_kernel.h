@@ -16,6 +16,10 @@
 //  * wave w computes the 16-column block w of the panel with
 //    v_mfma_f32_16x16x32_f16, B fragments via the LDS transpose read;
 //  * the fused epilogue runs on the accumulators; C is written once.
+// With B given transposed (Bt[N][K], a linear layer's weight) the panel is
+// 64 rows of Bt, k-contiguous: its stage is laid out and read like A's (one
+// 16-byte LDS read per fragment instead of two transpose reads), and k-chunks
+// past K are sent out of range as A's are.
 #pragma once
 #include "common.h"
 
@@ -32,7 +36,7 @@ __device__ __forceinline__ int sk_swz_b(int kr) {
     return 2 * (((kr >> 1) & 1) | (((kr >> 3) & 1) << 1));
 }
 
-template <int MB, int STAGES, int EPI>
+template <int MB, int STAGES, int EPI, int BT>
 __global__ void __launch_bounds__(SK_WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 gemm_skinny_kernel(GemmArgs p) {
     constexpr int NT = SK_WAVES * 64;
@@ -53,21 +57,32 @@ gemm_skinny_kernel(GemmArgs p) {
     const int KT = (K + SK_BK - 1) / SK_BK;
 
     // Buffer resources: B ends with its last row (element (K-1)*ldb + N), so
-    // k-rows >= K read 0; A ends with its last row.
+    // k-rows >= K read 0; A ends with its last row, and so does Bt.
+    const int64_t b_elems = BT ? (int64_t)(N - 1) * ldb + K : (int64_t)(K - 1) * ldb + N;
     const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)p.B, (short)0, (int)min(((int64_t)(K - 1) * ldb + N) * 2, (int64_t)0x7fffffff), 0x00020000);
+        (void*)p.B, (short)0, (int)min(b_elems * 2, (int64_t)0x7fffffff), 0x00020000);
     const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)p.A, (short)0, (int)min(((int64_t)(M - 1) * lda + K) * 2, (int64_t)0x7fffffff), 0x00020000);
 
     // Per-lane DMA source offsets within one stage.
     uint32_t b_off[B_INS];
+    int b_kc[B_INS];  // BT: k offset of the chunk within the stage
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
         const int P = (i * SK_WAVES + wave) * 64 + lane;  // destination chunk in the stage
-        const int kr = P >> 3, pc = P & 7;
-        const int c = pc ^ sk_swz_b(kr);
-        const int n = min(n0 + 8 * c, N - 8);              // past-N columns re-read the last chunk
-        b_off[i] = (uint32_t)((kr * ldb + n) * 2);
+        if constexpr (BT) {
+            // Bt stage: [SK_BN][SK_BK], 16 chunks per row, chunk c of row r at c ^ (r & 15);
+            // rows past N re-read row N-1 (their columns are never stored)
+            const int r = P >> 4, c = (P & 15) ^ (r & 15);
+            b_kc[i] = 8 * c;
+            b_off[i] = (uint32_t)(((int64_t)min(n0 + r, N - 1) * ldb + 8 * c) * 2);
+        } else {
+            const int kr = P >> 3, pc = P & 7;
+            const int c = pc ^ sk_swz_b(kr);
+            const int n = min(n0 + 8 * c, N - 8);          // past-N columns re-read the last chunk
+            b_off[i] = (uint32_t)((kr * ldb + n) * 2);
+            b_kc[i] = 0;
+        }
     }
     // A stage: [MR][SK_BK] fp16 = 16 chunks per row, chunk c of row m at c ^ (m & 15).
     // Rows >= M are clamped to M-1 (results never stored); a dword past K in a
@@ -91,10 +106,16 @@ gemm_skinny_kernel(GemmArgs p) {
     const uint32_t a_lds0 = lds_addr(a_lds) + wave_s * 64 * 4;
     auto issue = [&](int kt, int s) {
         const int kbase = kt * SK_BK;
-        const uint32_t b_so = (uint32_t)kbase * ldb * 2;
 #pragma unroll
-        for (int i = 0; i < B_INS; ++i)
-            dma_buffer_16_nt(b_rsrc, b_off[i] + b_so, b_lds0 + s * B_STAGE + i * SK_WAVES * 64 * 16);
+        for (int i = 0; i < B_INS; ++i) {
+            uint32_t off;
+            if constexpr (BT) {  // k-chunks past K (K % 8 == 0) read as zero
+                off = (kbase + b_kc[i] < K) ? b_off[i] + (uint32_t)kbase * 2 : 0x80000000u;
+            } else {
+                off = b_off[i] + (uint32_t)kbase * ldb * 2;
+            }
+            dma_buffer_16_nt(b_rsrc, off, b_lds0 + s * B_STAGE + i * SK_WAVES * 64 * 16);
+        }
 #pragma unroll
         for (int i = 0; i < A_INS; ++i) {
             const uint32_t off = (kbase + a_kcol[i] < K) ? a_off[i] + (uint32_t)kbase * 2 : 0x80000000u;
@@ -117,14 +138,20 @@ gemm_skinny_kernel(GemmArgs p) {
         const int nl = wave * 16 + 4 * q;                  // column within the panel
 #pragma unroll
         for (int ks = 0; ks < SK_BK / 32; ++ks) {
-            f16x4 half_[2];
+            f16x8 bf;
+            if constexpr (BT) {  // lane l: Bt[n = 16 wave + l%16][k = 32 ks + 8 (l/16) .. +7]
+                const int r = wave * 16 + (lane & 15);
+                bf = *(const GK_LDS f16x8*)(Bs + r * SK_BK * 2 + (((4 * ks + g) ^ (r & 15)) << 4));
+            } else {
+                f16x4 half_[2];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int kr = 32 * ks + 8 * g + 4 * h + j;
-                const int c = (nl >> 3) ^ sk_swz_b(kr);
-                half_[h] = lds_read_tr16_b64(Bs + kr * SK_BN * 2 + (c << 4) + ((nl & 7) << 1));
+                for (int h = 0; h < 2; ++h) {
+                    const int kr = 32 * ks + 8 * g + 4 * h + j;
+                    const int c = (nl >> 3) ^ sk_swz_b(kr);
+                    half_[h] = lds_read_tr16_b64(Bs + kr * SK_BN * 2 + (c << 4) + ((nl & 7) << 1));
+                }
+                bf = __builtin_shufflevector(half_[0], half_[1], 0, 1, 2, 3, 4, 5, 6, 7);
             }
-            const f16x8 bf = __builtin_shufflevector(half_[0], half_[1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int m = 16 * mb + (lane & 15);

@@ -373,7 +373,16 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     // of k-step kk consume the other.  Read j: 0 -> A[0]; 1..NB -> B (halves of
     // B[(j-1)/2] by transpose reads, or Bt[j-1] whole with BT); then A[1..TM-1]
     // -- the order in which MFMA row 0 needs them.
-    f16x8 fa[2][TM];
+    // INPLACE (SPREAD bit 1): B keeps two sets, A only one.  MFMA slot i uses
+    // A[i / TN], so A[mi] is free after slot (mi+1) TN - 1 and is refilled
+    // there with the next k-step's row mi; A[TM-1], busy to the end of the
+    // k-step, is refilled at slot 0 of the k-step that needs it, (TM-1) TN
+    // slots ahead of its first use.  That saves TM fragment registers, which
+    // keeps the 16x16 schedules' accumulators in place.
+    constexpr bool INPLACE = (SPREAD & 2) != 0;
+    constexpr bool PINNED = (SPREAD & 4) != 0;
+    static_assert(!INPLACE || TM >= 2, "in-place A refill needs two MFMA rows");
+    f16x8 fa[INPLACE ? 1 : 2][TM];
     f16x4 fb[2][BT ? 1 : TN][2];
     f16x8 fbt[2][BT ? TN : 1];
     auto read_op = [&](int set, int j, int sb, int kk) {
@@ -394,18 +403,35 @@ gemm_tile_pipe_kernel(GemmArgs p) {
             fa[set][mi] = *(const GK_LDS f16x8*)(As + a_rd[kk] + mi * MF * BK * 2);
         }
     };
+    // INPLACE reads: A row mi into the single A set, B read jb (0 <= jb < NB) into set `set`.
+    auto read_a = [&](int mi, int sb, int kk) {
+        fa[0][mi] = *(const GK_LDS f16x8*)(a_lds + sb * A_STAGE + a_rd[kk] + mi * MF * BK * 2);
+    };
+    auto read_b = [&](int set, int jb, int sb, int kk) {
+        const GK_LDS char* Bs = b_lds + sb * B_STAGE;
+        if constexpr (BT) {
+            fbt[set][jb] = *(const GK_LDS f16x8*)(Bs + bt_rd[kk] + jb * MF * BK * 2);
+        } else {
+            fb[set][jb / 2][jb % 2] = lds_read_tr16_b64(Bs + b_rd[jb / 2] + (KS * kk + 4 * (jb % 2)) * BN * 2);
+        }
+    };
     auto mma_op = [&](int set, int i) {
         const int mi = i / TN, ni = i % TN;
+        const int aset = INPLACE ? 0 : set;
         f16x8 b;
         if constexpr (BT) {
             b = fbt[set][ni];
         } else {
             b = __builtin_shufflevector(fb[set][ni][0], fb[set][ni][1], 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        if constexpr (MF == 32) {
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, fa[set][mi], acc[mi][ni], 0, 0, 0);
+        if constexpr (PINNED && MF == 32) {
+            asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc[mi][ni]) : "v"(b), "v"(fa[aset][mi]));
+        } else if constexpr (PINNED) {
+            asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc[mi][ni]) : "v"(b), "v"(fa[aset][mi]));
+        } else if constexpr (MF == 32) {
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, fa[aset][mi], acc[mi][ni], 0, 0, 0);
         } else {
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, fa[set][mi], acc[mi][ni], 0, 0, 0);
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, fa[aset][mi], acc[mi][ni], 0, 0, 0);
         }
     };
 
@@ -436,8 +462,15 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     }
     __syncthreads();
     if (KT > 0) {
+        if constexpr (INPLACE) {  // A[TM-1] is read at slot 0 of the k-step
 #pragma unroll
-        for (int j = 0; j < NRD; ++j) read_op(0, j, 0, 0);
+            for (int jb = 0; jb < NB; ++jb) read_b(0, jb, 0, 0);
+#pragma unroll
+            for (int mi = 0; mi + 1 < TM; ++mi) read_a(mi, 0, 0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NRD; ++j) read_op(0, j, 0, 0);
+        }
     }
 
     int s = 0;  // ring buffer of the stage being computed
@@ -467,10 +500,37 @@ gemm_tile_pipe_kernel(GemmArgs p) {
                     if (slot >= CSLOT && (slot - CSLOT) % DSTRIDE == 0 && (slot - CSLOT) / DSTRIDE < PER_STAGE)
                         gload_op((slot - CSLOT) / DSTRIDE, kt + 2);
                 }
-                if (kk + 1 < KSTEPS) {
+                if constexpr (INPLACE) {
+                    if (i == 0) read_a(TM - 1, s, kk);  // before this stage's barrier: stage s is still live
+                    if (kk + 1 < KSTEPS) {
+#pragma unroll
+                        for (int jb = 0; jb < NB; ++jb)
+                            if (read_slot<NB, 1>(jb, 0, NMMA) == i) read_b(nxt, jb, s, kk + 1);
+#pragma unroll
+                        for (int mi = 0; mi + 1 < TM; ++mi)
+                            if ((mi + 1) * TN - 1 == i) read_a(mi, s, kk + 1);
+                    } else if (has_next) {
+                        if (i == BSLOT) {
+                            if constexpr (RING) {
+                                if constexpr (PHASE == 2) {
+                                    wait_vmcnt<(STAGES - 2) * PER_STAGE>();
+                                } else {
+                                    wait_vmcnt0();
+                                }
+                            }
+                            __syncthreads();
+                        }
+#pragma unroll
+                        for (int jb = 0; jb < NB; ++jb)
+                            if (read_slot<NB, 1>(jb, BSLOT + 1, NMMA - BSLOT - 1) == i) read_b(nxt, jb, sn, 0);
+#pragma unroll
+                        for (int mi = 0; mi + 1 < TM; ++mi)
+                            if (max((mi + 1) * TN - 1, BSLOT + 1) == i) read_a(mi, sn, 0);
+                    }
+                } else if (kk + 1 < KSTEPS) {
 #pragma unroll
                     for (int j = 0; j < NRD; ++j)
-                        if (read_slot<NRD, SPREAD>(j, 0, NMMA) == i) read_op(nxt, j, s, kk + 1);
+                        if (read_slot<NRD, (SPREAD & 1)>(j, 0, NMMA) == i) read_op(nxt, j, s, kk + 1);
                 } else if (has_next) {
                     if (i == BSLOT) {
                         if constexpr (RING) {
@@ -484,13 +544,31 @@ gemm_tile_pipe_kernel(GemmArgs p) {
                     }
 #pragma unroll
                     for (int j = 0; j < NRD; ++j)
-                        if (read_slot<NRD, SPREAD>(j, BSLOT + 1, NMMA - BSLOT - 1) == i) read_op(nxt, j, sn, 0);
+                        if (read_slot<NRD, (SPREAD & 1)>(j, BSLOT + 1, NMMA - BSLOT - 1) == i) read_op(nxt, j, sn, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
         s = sn;
     };
+    // PINNED: the MFMAs are inline asm on accumulators pinned to AGPRs, so the
+    // compiler inserts no MFMA hazard waits around them.  Fragments come from
+    // LDS (covered by lgkmcnt waits on the asm operands), and each accumulator
+    // is reused only a full k-step later.  Left to cover here: the zeroing
+    // writes before the first MFMA, and the epilogue's reads of the last
+    // results (16 passes + 2 for 32x32, less for 16x16).  Each accumulator
+    // passes through an empty volatile asm on the near side of the s_nops,
+    // which orders its writes (reads) before (after) them.
+    auto pin_order = [&]() {
+#pragma unroll
+        for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < TN; ++ni) asm volatile("" : "+a"(acc[mi][ni]));
+    };
+    if constexpr (PINNED) {
+        pin_order();
+        asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+    }
     int kt = 0;
     if constexpr (RING) {
         for (; kt < KT - (STAGES - 1); ++kt) stage.template operator()<2>(kt);
@@ -499,6 +577,10 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         if (kt < KT - 1) stage.template operator()<1>(kt++);
     }
     for (; kt < KT; ++kt) stage.template operator()<0>(kt);
+    if constexpr (PINNED) {
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        pin_order();
+    }
 
     // Epilogue on the accumulators, one write of C.  Lane l holds, of block
     // (mi, ni), the 4 consecutive columns

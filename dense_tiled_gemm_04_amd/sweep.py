@@ -74,7 +74,8 @@ class Tile:
     cslot: int = 0
     wpe: int = 1         # waves per SIMD (= workgroups per CU, 4-wave workgroups)
     mf: int = 32         # MFMA shape: 32 -> 32x32x16, 16 -> 16x16x32
-    spread: int = 0      # LDS reads spread evenly over a k-step's slots
+    spread: int = 0      # schedule flags: 1 LDS reads spread evenly over a k-step's slots, 2 A refilled in
+                         # place (one A fragment set), 4 MFMAs as asm on accumulators pinned to AGPRs
     bt: int = 0          # B given transposed (Bt[N][K])
 
     kind = "tile"
@@ -87,7 +88,8 @@ class Tile:
             n += "_c%d" % self.cslot
         n += "_o%d" % self.wpe if self.wpe != 1 else ""
         n += "_m16" if self.mf == 16 else ""
-        n += "_sp" if self.spread else ""
+        n += "_ip" if self.spread & 2 else ("_sp" if self.spread & 1 else "")
+        n += "_pa" if self.spread & 4 else ""
         return n + ("_bt" if self.bt else "")
 
     # derived quantities, as in TilePipeCfg (csrc/tile_pipe_kernel.h)
@@ -118,20 +120,21 @@ class Tile:
 class Skinny:
     mb: int
     stages: int
+    bt: int = 0          # B given transposed (Bt[N][K])
 
     kind = "skinny"
     loader = "lds_dma"
 
     @property
     def name(self) -> str:
-        return "skinny_m%d_s%d" % (16 * self.mb, self.stages)
+        return "skinny_m%d_s%d" % (16 * self.mb, self.stages) + ("_bt" if self.bt else "")
 
     @property
     def lds_bytes(self) -> int:
         return self.stages * (16 * self.mb * SK_BK * 2 + SK_BK * SK_BN * 2)
 
     def macro(self) -> str:
-        return "SKINNY_CFG(%d, %d, \"%s\")" % (self.mb, self.stages, self.name)
+        return "SKINNY_CFG(%d, %d, %d, \"%s\")" % (self.mb, self.stages, self.bt, self.name)
 
 
 def pow2(x: int) -> bool:
@@ -148,6 +151,8 @@ def valid(c) -> bool:
         return False
     d = c.derived()
     if d["ksteps"] % 2 or d["wtm"] % c.mf or d["wtn"] % c.mf or d["tm"] < 1 or d["tn"] < 1:
+        return False
+    if not 0 <= c.spread <= 7 or (c.spread & 2 and d["tm"] < 2):
         return False
     cb_ok = pow2(d["cb"]) or (d["cb"] % 8 == 0 and (c.bn * 2) % 256 == 128)   # e.g. BN = 192
     if not (pow2(d["ca"]) and cb_ok and d["cb"] >= 4):
@@ -173,7 +178,7 @@ def valid(c) -> bool:
     # chunk (plus the k offset of each A chunk for the buffer loader) and ~56 of addressing and temporaries.  With one wave per SIMD the accumulators sit in the 256 AGPRs and the
     # rest must fit the 256 VGPRs; with more waves all of it shares 512 / waves.
     acc = d["tm"] * d["tn"] * d["nacc"]
-    frags = 2 * (d["tm"] * 4 + d["tn"] * 4)
+    frags = (1 if c.spread & 2 else 2) * d["tm"] * 4 + 2 * d["tn"] * 4
     stg = 4 * ps if c.loader == "reg" else 0
     rest = frags + stg + ps + (d["a_ins"] if c.loader == "buf" else 0) + 56
     if c.wpe == 1:
@@ -235,15 +240,37 @@ def space() -> list:
     out.append(Tile(128, 128, 64, 2, 2, 3, 4, 1, 1, "buf", bt=1))
     out.append(Tile(256, 256, 64, 2, 2, 2, 4, 3, 2, "reg", bt=1))
     out.append(Tile(128, 128, 64, 2, 2, 2, 4, 1, 1, "reg", wpe=2, bt=1))
-    for mb, sts in ((1, (4, 6, 8)), (2, (4, 6)), (4, (3, 5))):
-        for st in sts:
-            out.append(Skinny(mb, st))
+    # accumulators pinned to AGPRs (asm MFMAs): the 16x16 schedules then keep their accumulators in place
+    for bs, ds in ((8, 2), (8, 4), (3, 3)):
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", mf=16, spread=5))
+    for bs, ds in ((8, 2), (8, 4), (16, 2), (24, 2), (32, 2), (3, 2)):
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", mf=16, spread=6))
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 8, 2, "buf", mf=16, spread=6))
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 3, 1, "dma", spread=6))
+    for bs, ds in ((8, 2), (16, 2), (24, 2), (32, 2)):
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", mf=16, spread=6, bt=1))
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 8, 2, "buf", mf=16, spread=6, bt=1))
+    for bs, ds in ((3, 1), (3, 2)):
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", spread=4))
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 3, 2, "dma", spread=6))
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 8, 2, "buf", mf=16, spread=5))
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 3, 1, "buf", spread=4))
+    out.append(Tile(128, 128, 64, 2, 2, 3, 4, 1, 1, "dma", spread=4))
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 8, 2, "dma", mf=16, spread=5, bt=1))
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 8, 4, "dma", mf=16, spread=5, bt=1))
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 3, 1, "dma", spread=4, bt=1))
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 8, 2, "buf", mf=16, spread=5, bt=1))
+    for bt in (0, 1):
+        for mb, sts in ((1, (4, 6, 8)), (2, (4, 6)), (4, (3, 5))):
+            for st in sts:
+                out.append(Skinny(mb, st, bt))
     return [c for c in out if valid(c)]
 
 
 CLASSES = ["SEL_SKINNY16", "SEL_SKINNY32", "SEL_SKINNY64", "SEL_DMA_HUGE", "SEL_DMA_BIG", "SEL_DMA_SMALL",
            "SEL_BUF_BIG", "SEL_BUF_SMALL", "SEL_REG_BIG", "SEL_REG_SMALL",
-           "SEL_BT_BIG", "SEL_BT_SMALL", "SEL_BT_BUF", "SEL_BT_REG"]
+           "SEL_BT_BIG", "SEL_BT_SMALL", "SEL_BT_BUF", "SEL_BT_REG",
+           "SEL_BT_SKINNY16", "SEL_BT_SKINNY32", "SEL_BT_SKINNY64"]
 
 
 def class_of(c, cls: str) -> bool:
@@ -252,10 +279,11 @@ def class_of(c, cls: str) -> bool:
     LDS-DMA tile configuration; the dispatcher falls back if it cannot run.
     The buffer classes (unaligned, K % 8 == 0) accept the buffer and the
     register loader, which both run every call of the class."""
-    if cls.startswith("SEL_SKINNY"):
+    if cls.startswith("SEL_SKINNY") or cls.startswith("SEL_BT_SKINNY"):
+        bt = cls.startswith("SEL_BT_")
         if c.kind == "skinny":
-            return 16 * c.mb >= int(cls[len("SEL_SKINNY"):])
-        return c.loader == "dma" and not c.bt
+            return bool(c.bt) == bt and 16 * c.mb >= int(cls.split("SKINNY")[1])
+        return c.loader == "dma" and bool(c.bt) == bt
     if c.kind != "tile":
         return False
     if cls.startswith("SEL_BT_"):   # B transposed: LDS-DMA (big/small), buffer or register loader
@@ -340,6 +368,12 @@ def sweep_workloads():
                 {"rotate": 3}, ["SEL_SKINNY32"]))
     out.append(("skinny_64x16384x8192", dataclasses.replace(W["skinny_16x16384x8192"], name="skinny_64", M=64),
                 {"rotate": 3}, ["SEL_SKINNY64"]))
+    # the same with B given transposed: decode through a linear layer's weight
+    out.append(("skinny_16x16384x8192_bt", W["skinny_16x16384x8192"], {"rotate": 3, "bt": True}, ["SEL_BT_SKINNY16"]))
+    out.append(("skinny_32x16384x8192_bt", dataclasses.replace(W["skinny_16x16384x8192"], name="skinny_32", M=32),
+                {"rotate": 3, "bt": True}, ["SEL_BT_SKINNY32"]))
+    out.append(("skinny_64x16384x8192_bt", dataclasses.replace(W["skinny_16x16384x8192"], name="skinny_64", M=64),
+                {"rotate": 3, "bt": True}, ["SEL_BT_SKINNY64"]))
     return out
 
 
@@ -428,11 +462,19 @@ def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str
                 continue
             if st != 0:
                 raise RuntimeError("config %s on %s: status %d" % (info["name"], name, st))
+            # Sustained timing, as the benchmark sees it: the power limit sets the clock
+            # within milliseconds, so warm up for >= 5 ms of work and time >= 25 ms.
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
             for r in range(3):
                 call(*args(r + 1))
+            e1.record(stream)
             torch.cuda.synchronize()
+            t_one = max(e0.elapsed_time(e1) / 3, 1e-3)   # ms
+            for r in range(int(math.ceil(5.0 / t_one))):
+                call(*args(r + 1))
             evs = []
-            for r in range(iters):
+            for r in range(max(iters, int(math.ceil(25.0 / t_one)))):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
                 call(*args(r + 1))
@@ -495,7 +537,8 @@ def select(results_path: str, table_path: str = TABLE, summary_path: str | None 
                "(%s). Do not edit by hand; rerun the sweep." % os.path.basename(results_path))
     if summary_path:
         lines = ["# Offline sweep of the tile and skinny kernels", "",
-                 "Median of %s HIP-event-timed launches per (configuration, workload) on one MI355X; the skinny" % "20",
+                 "Median of the HIP-event-timed launches in >= 25 ms of work, after >= 5 ms of warm-up, per (configuration, "
+                 "workload) on one MI355X (the clock has settled under the power limit by then); the skinny",
                  "workloads rotate 3 copies of B so the Infinity Cache cannot serve it;",
                  "outputs screened against a float32 PyTorch reference on sampled rows (parity proper is the",
                  "oracle tests). Command: `python -m dense_tiled_gemm_04_amd.sweep --run RESULTS` on the GPU, then",
@@ -520,7 +563,8 @@ def ablation(results_path: str, out_path: str) -> None:
     t = {(r["config"], r["workload"]): r for r in recs if r.get("ok")}
     by_name = {c.name: c for c in space()}
     lines = ["# Ablations: tile order (swizzle) and LDS stages", "",
-             "Median of 20 HIP-event-timed launches per cell on one MI355X, from the same sweep records as the",
+             "Median of the HIP-event-timed launches in >= 25 ms of work (after >= 5 ms of warm-up) per cell on one "
+             "MI355X, from the same sweep records as the",
              "configuration table (`python -m dense_tiled_gemm_04_amd.sweep --run RESULTS` on the GPU, then",
              "`--ablation RESULTS`).", "",
              "## Tile order", "",

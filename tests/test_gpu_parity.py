@@ -516,3 +516,51 @@ def test_b_transposed_workload_sampled(lib, name):
     r, c = _sample_points(w.M, w.N, 17, n_random=20000)
     ref = oracle.gemm_points(A, B, bias, w.epilogue, r, c)
     assert_parity(got[r, c][None, :], ref[None, :], name)
+
+
+# ---------------------------------------------------------------------------
+# skinny M with B given transposed (decode through a linear layer's weight)
+# ---------------------------------------------------------------------------
+def test_b_transposed_skinny_workload_full(lib):
+    import dense_tiled_gemm_04_amd as g
+    w = workloads.WORKLOADS["skinny_16x16384x8192"]
+    A, B, bias = workloads.make_inputs(w)
+    ref = oracle.gemm(A, B, bias, w.epilogue)
+    out = g.gemm_f16(dev(A), dev(np.ascontiguousarray(B.T)), dev(bias), w.epilogue, b_transposed=True)
+    torch.cuda.synchronize()
+    m = assert_parity(out.cpu().numpy(), ref, w.name + " (Bt)")
+    assert m["frac_exact"] > 0.97
+
+
+@pytest.mark.parametrize("M", [1, 7, 16, 17, 32, 33, 64])
+def test_b_transposed_skinny_shapes_and_k_tail_isolation(lib, M):
+    # every skinny Bt config (and the default) on K with a tail past the 128-deep stage, Bt as a column slice of a
+    # wider array, and infinities in column 0 of some Bt rows: a k-chunk past K that read the next Bt row would
+    # put an infinity into the zeroed A tail's product and turn a whole output column into NaN.
+    import dense_tiled_gemm_04_amd as g
+    N, K = 264, 200
+    A, B, bias = workloads.make_inputs("skinny_16x16384x8192", M=M, N=N, K=K)
+    A[:, 0] = np.where(A[:, 0] == 0, np.float16(0.5), A[:, 0])
+    Bt = np.ascontiguousarray(B.T)
+    inf_cols = [1, 64, 65, 263]
+    Bt[inf_cols, 0] = np.float16(np.inf)
+    ref = oracle.gemm(A, np.ascontiguousarray(Bt.T), bias, "bias_gelu")
+    keep = np.setdiff1d(np.arange(N), inf_cols)
+    buf = torch.zeros((N, K + 40), dtype=torch.float16, device="cuda")
+    buf[:, 8:8 + K] = dev(Bt)
+    Btv = buf[:, 8:8 + K]
+    ran = []
+    for c in [c for c in lib.configs() if c["b_transposed"] and c["kind"] == "skinny"] + [None]:
+        try:
+            out = g.gemm_f16(dev(A), Btv, dev(bias), "bias_gelu", b_transposed=True,
+                             config=None if c is None else c["idx"])
+        except g.GemmError as e:
+            assert c is not None and e.status == 6, e
+            continue
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        name = "default" if c is None else c["name"]
+        assert_parity(got[:, keep], ref[:, keep], (M, "finite columns", name))
+        assert np.array_equal(got[:, inf_cols].view(np.uint16), ref[:, inf_cols].view(np.uint16)), (M, name)
+        ran.append(name)
+    assert "default" in ran and (M > 32 or len(ran) >= 2), ran

@@ -35,6 +35,16 @@ def test_schedule_constraints_mirror_kernel():
     assert not sweep.valid(sweep.Tile(128, 128, 16, 2, 2, 2, 4, 1, 1, "dma"))
 
 
+def test_schedule_flags_in_names_and_limits():
+    # schedule flags: 1 spread reads, 2 in-place A refill (needs two MFMA rows per wave), 4 pinned accumulators
+    t = sweep.Tile(256, 256, 64, 2, 2, 2, 4, 16, 2, "dma", mf=16, spread=6)
+    assert t.name.endswith("_m16_ip_pa") and sweep.valid(t)
+    assert sweep.Tile(256, 256, 64, 2, 2, 2, 4, 8, 2, "dma", mf=16, spread=5).name.endswith("_m16_sp_pa")
+    assert not sweep.valid(sweep.Tile(64, 128, 64, 2, 2, 2, 4, 1, 1, "dma", spread=2))   # one 32-row MFMA per wave
+    assert not sweep.valid(sweep.Tile(256, 256, 64, 2, 2, 2, 4, 3, 1, "dma", spread=8))
+    assert sweep.Skinny(2, 6, 1).name == "skinny_m32_s6_bt"
+
+
 def test_space_is_valid_and_unique():
     sp = sweep.space()
     assert len(sp) >= 20
@@ -66,7 +76,9 @@ def test_product_table_entries_are_in_budget():
         assert f[15].strip('"') == c.name
     for s in skinny:
         f = [x.strip() for x in s.split(",")]
-        assert sweep.valid(sweep.Skinny(int(f[0]), int(f[1])))
+        c = sweep.Skinny(int(f[0]), int(f[1]), int(f[2]))
+        assert sweep.valid(c), c
+        assert f[3].strip('"') == c.name
 
 
 def test_select_picks_fastest_valid_per_class(tmp_path):
