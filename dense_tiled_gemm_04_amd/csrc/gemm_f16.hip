@@ -27,6 +27,7 @@ struct Config {
     int bslot, dstride, cslot, wpe;  // tile schedule: barrier slot, copy stride, LDS-write slot, waves/SIMD
     int mfma, spread;                // tile MFMA shape (32: 32x32x16, 16: 16x16x32), spread LDS reads
     int bt;                          // 1: B given transposed (Bt[N][K])
+    int krot;                        // skinny: K stages walked from stage (workgroup mod KT)
     int lds_bytes;
     int threads;
     launch_fn launch[3];     // indexed by epilogue
@@ -41,10 +42,10 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int MB, int STAGES, int BT, int EPI>
+template <int MB, int STAGES, int BT, int KROT, int EPI>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.tiles_n), block(SK_WAVES * 64);
-    hipLaunchKernelGGL((gemm_skinny_kernel<MB, STAGES, EPI, BT>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_skinny_kernel<MB, STAGES, EPI, BT, KROT>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -54,7 +55,7 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
 // LDS reads SP, B transposed BT.
 #define TILE_CFG(BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, BT, NAME)             \
     Config {                                                                                       \
-        NAME, KIND_TILE, BM, BN, BK, WM, WN, LOADER, G, ST, BS, DS, CS, WPE, MF, SP, BT,           \
+        NAME, KIND_TILE, BM, BN, BK, WM, WN, LOADER, G, ST, BS, DS, CS, WPE, MF, SP, BT, 0,        \
             TilePipeCfg<BM, BN, BK, WM, WN, ST, MF, BT>::LDS_BYTES, WM * WN * 64,                  \
         {                                                                                          \
             launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, BT, 0>,        \
@@ -63,13 +64,14 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
         }                                                                                          \
     }
 
-// Skinny config: 16*MB rows, ST LDS stages, B transposed BT.
-#define SKINNY_CFG(MB, ST, BT, NAME)                                                                \
+// Skinny config: 16*MB rows, ST LDS stages, B transposed BT, rotated K order KR.
+#define SKINNY_CFG(MB, ST, BT, KR, NAME)                                                            \
     Config {                                                                                       \
-        NAME, KIND_SKINNY, 16 * MB, SK_BN, SK_BK, 1, SK_WAVES, -1, 1, ST, 0, 0, 0, 1, 16, 0, BT,   \
+        NAME, KIND_SKINNY, 16 * MB, SK_BN, SK_BK, 1, SK_WAVES, -1, 1, ST, 0, 0, 0, 1, 16, 0, BT, KR, \
             ST * (16 * MB * SK_BK * 2 + SK_BK * SK_BN * 2), SK_WAVES * 64,                         \
         {                                                                                          \
-            launch_skinny<MB, ST, BT, 0>, launch_skinny<MB, ST, BT, 1>, launch_skinny<MB, ST, BT, 2> \
+            launch_skinny<MB, ST, BT, KR, 0>, launch_skinny<MB, ST, BT, KR, 1>,                    \
+                launch_skinny<MB, ST, BT, KR, 2>                                                   \
         }                                                                                          \
     }
 
@@ -256,10 +258,11 @@ int gemm_f16_config_info(int idx, char* buf, int buflen) {
                      "{\"idx\": %d, \"name\": \"%s\", \"kind\": \"%s\", \"bm\": %d, \"bn\": %d, \"bk\": %d, "
                      "\"waves_m\": %d, \"waves_n\": %d, \"loader\": \"%s\", \"group_m\": %d, \"stages\": %d, "
                      "\"bslot\": %d, \"dstride\": %d, \"cslot\": %d, \"waves_per_simd\": %d, "
-                     "\"mfma\": %d, \"spread\": %d, \"b_transposed\": %d, \"lds_bytes\": %d, \"threads\": %d}",
+                     "\"mfma\": %d, \"spread\": %d, \"b_transposed\": %d, \"k_rotate\": %d, \"lds_bytes\": %d, "
+                     "\"threads\": %d}",
                      idx, c.name, c.kind == KIND_TILE ? "tile" : "skinny", c.bm, c.bn, c.bk, c.wm, c.wn,
                      c.kind == KIND_TILE ? loaders[c.loader] : "lds_dma", c.group_m, c.stages, c.bslot,
-                     c.dstride, c.cslot, c.wpe, c.mfma, c.spread, c.bt, c.lds_bytes, c.threads);
+                     c.dstride, c.cslot, c.wpe, c.mfma, c.spread, c.bt, c.krot, c.lds_bytes, c.threads);
     if (buf && buflen > 0) {
         strncpy(buf, tmp, (size_t)buflen - 1);
         buf[buflen - 1] = '\0';

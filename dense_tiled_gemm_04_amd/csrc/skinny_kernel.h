@@ -20,6 +20,11 @@
 // 64 rows of Bt, k-contiguous: its stage is laid out and read like A's (one
 // 16-byte LDS read per fragment instead of two transpose reads), and k-chunks
 // past K are sent out of range as A's are.
+// KROT: workgroup w walks its K stages starting at stage w mod KT (wrapping
+// around).  With Bt, the workgroups' concurrent reads then sit at different
+// offsets within their rows instead of all at the same one, 16 KiB apart,
+// which spreads them over the HBM channels.  Only the fp32 summation order of
+// each column changes.
 #pragma once
 #include "common.h"
 
@@ -36,7 +41,7 @@ __device__ __forceinline__ int sk_swz_b(int kr) {
     return 2 * (((kr >> 1) & 1) | (((kr >> 3) & 1) << 1));
 }
 
-template <int MB, int STAGES, int EPI, int BT>
+template <int MB, int STAGES, int EPI, int BT, int KROT>
 __global__ void __launch_bounds__(SK_WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 gemm_skinny_kernel(GemmArgs p) {
     constexpr int NT = SK_WAVES * 64;
@@ -104,8 +109,10 @@ gemm_skinny_kernel(GemmArgs p) {
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t b_lds0 = lds_addr(b_lds) + wave_s * 64 * 16;
     const uint32_t a_lds0 = lds_addr(a_lds) + wave_s * 64 * 4;
+    const int krot = (KROT && KT > 0) ? (int)(blockIdx.x % (unsigned)KT) : 0;
     auto issue = [&](int kt, int s) {
-        const int kbase = kt * SK_BK;
+        const int ktr = kt + krot < KT ? kt + krot : kt + krot - KT;
+        const int kbase = ktr * SK_BK;
 #pragma unroll
         for (int i = 0; i < B_INS; ++i) {
             uint32_t off;

@@ -121,20 +121,21 @@ class Skinny:
     mb: int
     stages: int
     bt: int = 0          # B given transposed (Bt[N][K])
+    krot: int = 0        # K stages walked from stage (workgroup mod KT)
 
     kind = "skinny"
     loader = "lds_dma"
 
     @property
     def name(self) -> str:
-        return "skinny_m%d_s%d" % (16 * self.mb, self.stages) + ("_bt" if self.bt else "")
+        return "skinny_m%d_s%d" % (16 * self.mb, self.stages) + ("_r" if self.krot else "") + ("_bt" if self.bt else "")
 
     @property
     def lds_bytes(self) -> int:
         return self.stages * (16 * self.mb * SK_BK * 2 + SK_BK * SK_BN * 2)
 
     def macro(self) -> str:
-        return "SKINNY_CFG(%d, %d, %d, \"%s\")" % (self.mb, self.stages, self.bt, self.name)
+        return "SKINNY_CFG(%d, %d, %d, %d, \"%s\")" % (self.mb, self.stages, self.bt, self.krot, self.name)
 
 
 def pow2(x: int) -> bool:
@@ -263,7 +264,8 @@ def space() -> list:
     for bt in (0, 1):
         for mb, sts in ((1, (4, 6, 8)), (2, (4, 6)), (4, (3, 5))):
             for st in sts:
-                out.append(Skinny(mb, st, bt))
+                for kr in (0, 1):
+                    out.append(Skinny(mb, st, bt, kr))
     return [c for c in out if valid(c)]
 
 

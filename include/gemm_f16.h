@@ -133,7 +133,12 @@ const char* gemm_f16_status_string(int status);
 int gemm_f16_num_configs(void);
 
 /* JSON description of config `idx` written into buf (NUL-terminated, truncated
- * to buflen).  Returns the full length, or -GEMM_ERR_NO_CONFIG. */
+ * to buflen).  Returns the full length, or -GEMM_ERR_NO_CONFIG.  Keys: idx,
+ * name, kind ("tile" | "skinny"), bm, bn, bk, waves_m, waves_n, loader,
+ * group_m, stages, bslot, dstride, cslot, waves_per_simd, mfma (32 or 16),
+ * spread (schedule flags: 1 LDS reads spread over the k-step, 2 A fragments
+ * refilled in place, 4 MFMAs on accumulators pinned to AGPRs), b_transposed,
+ * k_rotate (skinny: K order rotated per workgroup), lds_bytes, threads. */
 int gemm_f16_config_info(int idx, char* buf, int buflen);
 
 /* Index of the configuration gemm_f16() would launch for these arguments

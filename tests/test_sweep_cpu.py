@@ -43,6 +43,7 @@ def test_schedule_flags_in_names_and_limits():
     assert not sweep.valid(sweep.Tile(64, 128, 64, 2, 2, 2, 4, 1, 1, "dma", spread=2))   # one 32-row MFMA per wave
     assert not sweep.valid(sweep.Tile(256, 256, 64, 2, 2, 2, 4, 3, 1, "dma", spread=8))
     assert sweep.Skinny(2, 6, 1).name == "skinny_m32_s6_bt"
+    assert sweep.Skinny(1, 4, 1, 1).name == "skinny_m16_s4_r_bt"
 
 
 def test_space_is_valid_and_unique():
@@ -76,9 +77,9 @@ def test_product_table_entries_are_in_budget():
         assert f[15].strip('"') == c.name
     for s in skinny:
         f = [x.strip() for x in s.split(",")]
-        c = sweep.Skinny(int(f[0]), int(f[1]), int(f[2]))
+        c = sweep.Skinny(int(f[0]), int(f[1]), int(f[2]), int(f[3]))
         assert sweep.valid(c), c
-        assert f[3].strip('"') == c.name
+        assert f[4].strip('"') == c.name
 
 
 def test_select_picks_fastest_valid_per_class(tmp_path):
