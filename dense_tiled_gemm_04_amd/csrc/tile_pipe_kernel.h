@@ -155,7 +155,15 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     constexpr int LAST = (KSTEPS - 1) * NMMA + BSLOT;  // stage slot of the barrier
     constexpr bool RING = LOADER != LOAD_REG;          // LDS-DMA ring of STAGES buffers
     static_assert(BSLOT >= 0 && BSLOT + 1 < NMMA, "barrier slot inside the last k-step, reads after it");
-    static_assert(DSTRIDE >= 1 && (PER_STAGE - 1) * DSTRIDE < LAST, "every copy is issued before the barrier");
+    // EARLY (SPREAD bit 3): the copies of stage kt+STAGES go into stage kt's own
+    // buffer right after stage kt's barrier (every wave's reads of it have
+    // completed there), instead of the copies of stage kt+STAGES-1 being
+    // issued from slot 0 of stage kt.  Each copy then has the rest of stage
+    // kt plus stage kt+1 up to its barrier to land.
+    constexpr bool EARLY = (SPREAD & 8) != 0;
+    static_assert(EARLY || (DSTRIDE >= 1 && (PER_STAGE - 1) * DSTRIDE < LAST), "every copy is issued before the barrier");
+    static_assert(!EARLY || (RING && DSTRIDE >= 1 && LAST + 1 + (PER_STAGE - 1) * DSTRIDE < KSTEPS * NMMA),
+                  "early copies: ring loaders, all issued after the barrier within the stage");
     static_assert(RING || (STAGES == 2 && CSLOT >= 0 && CSLOT + PER_STAGE <= LAST + 1 &&
                                          CSLOT + (PER_STAGE - 1) * DSTRIDE < KSTEPS * NMMA),
                   "register loader: 2 stages; every LDS write precedes the barrier; every reload fits "
@@ -381,6 +389,12 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     // keeps the 16x16 schedules' accumulators in place.
     constexpr bool INPLACE = (SPREAD & 2) != 0;
     constexpr bool PINNED = (SPREAD & 4) != 0;
+    // FRONTB (SPREAD bit 4, with INPLACE): the next k-step's B reads go in the
+    // first slots of the k-step (after the barrier on a stage's last k-step)
+    // rather than spread over it, since the next k-step's first MFMA row needs
+    // every B fragment within its first TN slots.
+    constexpr int BSPREAD = (SPREAD & 16) ? 0 : 1;
+    static_assert(!(SPREAD & 16) || INPLACE, "front-loaded B reads belong to the in-place schedule");
     static_assert(!INPLACE || TM >= 2, "in-place A refill needs two MFMA rows");
     f16x8 fa[INPLACE ? 1 : 2][TM];
     f16x4 fb[2][BT ? 1 : TN][2];
@@ -435,16 +449,17 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         }
     };
 
-    // Prologue: stages 0 .. STAGES-2 in LDS (or in flight), then stage 0's
-    // first fragments.
+    // Prologue: stages 0 .. STAGES-2 (EARLY: 0 .. STAGES-1) in LDS or in
+    // flight, then stage 0's first fragments.
     if constexpr (RING) {
+        constexpr int PRE = EARLY ? STAGES : STAGES - 1;
 #pragma unroll
-        for (int st = 0; st < STAGES - 1; ++st)
+        for (int st = 0; st < PRE; ++st)
             if (st < KT)
 #pragma unroll
                 for (int j = 0; j < PER_STAGE; ++j) dma_op(j, st, st);
-        if (KT >= STAGES - 1) {
-            wait_vmcnt<(STAGES - 2) * PER_STAGE>();
+        if (KT >= PRE) {
+            wait_vmcnt<(PRE - 1) * PER_STAGE>();
         } else {
             wait_vmcnt0();
         }
@@ -475,7 +490,8 @@ gemm_tile_pipe_kernel(GemmArgs p) {
 
     int s = 0;  // ring buffer of the stage being computed
     // PHASE 2: every stage the copies of this stage refer to exists (ring
-    // loaders: kt+STAGES-1; LOAD_REG: kt+1 written and kt+2 loaded), so they
+    // loaders: kt+STAGES-1, or kt+STAGES with EARLY; LOAD_REG: kt+1 written
+    // and kt+2 loaded), so they
     // are issued unconditionally and the DMA wait count is exact.  PHASE 1
     // (LOAD_REG only): the last write, no reload.  PHASE 0: no copy work; the
     // ring loaders wait for everything.
@@ -490,7 +506,10 @@ gemm_tile_pipe_kernel(GemmArgs p) {
             for (int i = 0; i < NMMA; ++i) {
                 mma_op(cur, i);
                 const int slot = kk * NMMA + i;
-                if constexpr (RING && PHASE == 2) {
+                if constexpr (RING && PHASE == 2 && EARLY) {
+                    if (slot > LAST && (slot - LAST - 1) % DSTRIDE == 0 && (slot - LAST - 1) / DSTRIDE < PER_STAGE)
+                        dma_op((slot - LAST - 1) / DSTRIDE, kt + STAGES, s);
+                } else if constexpr (RING && PHASE == 2) {
                     if (slot % DSTRIDE == 0 && slot / DSTRIDE < PER_STAGE) dma_op(slot / DSTRIDE, kt + STAGES - 1, sd);
                 }
                 if constexpr (LOADER == LOAD_REG && PHASE >= 1) {
@@ -505,7 +524,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
                     if (kk + 1 < KSTEPS) {
 #pragma unroll
                         for (int jb = 0; jb < NB; ++jb)
-                            if (read_slot<NB, 1>(jb, 0, NMMA) == i) read_b(nxt, jb, s, kk + 1);
+                            if (read_slot<NB, BSPREAD>(jb, 0, NMMA) == i) read_b(nxt, jb, s, kk + 1);
 #pragma unroll
                         for (int mi = 0; mi + 1 < TM; ++mi)
                             if ((mi + 1) * TN - 1 == i) read_a(mi, s, kk + 1);
@@ -522,7 +541,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
                         }
 #pragma unroll
                         for (int jb = 0; jb < NB; ++jb)
-                            if (read_slot<NB, 1>(jb, BSLOT + 1, NMMA - BSLOT - 1) == i) read_b(nxt, jb, sn, 0);
+                            if (read_slot<NB, BSPREAD>(jb, BSLOT + 1, NMMA - BSLOT - 1) == i) read_b(nxt, jb, sn, 0);
 #pragma unroll
                         for (int mi = 0; mi + 1 < TM; ++mi)
                             if (max((mi + 1) * TN - 1, BSLOT + 1) == i) read_a(mi, sn, 0);
@@ -571,7 +590,8 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     }
     int kt = 0;
     if constexpr (RING) {
-        for (; kt < KT - (STAGES - 1); ++kt) stage.template operator()<2>(kt);
+        // PHASE 2 while the stage its copies fill exists: kt+STAGES-1 (EARLY: kt+STAGES) < KT
+        for (; kt < KT - (EARLY ? STAGES : STAGES - 1); ++kt) stage.template operator()<2>(kt);
     } else {
         for (; kt < KT - 2; ++kt) stage.template operator()<2>(kt);
         if (kt < KT - 1) stage.template operator()<1>(kt++);

@@ -75,7 +75,9 @@ class Tile:
     wpe: int = 1         # waves per SIMD (= workgroups per CU, 4-wave workgroups)
     mf: int = 32         # MFMA shape: 32 -> 32x32x16, 16 -> 16x16x32
     spread: int = 0      # schedule flags: 1 LDS reads spread evenly over a k-step's slots, 2 A refilled in
-                         # place (one A fragment set), 4 MFMAs as asm on accumulators pinned to AGPRs
+                         # place (one A fragment set), 4 MFMAs as asm on accumulators pinned to AGPRs,
+                         # 8 copies of stage kt+STAGES issued right after stage kt's barrier, 16 (with 2) the
+                         # next k-step's B reads front-loaded
     bt: int = 0          # B given transposed (Bt[N][K])
 
     kind = "tile"
@@ -90,6 +92,8 @@ class Tile:
         n += "_m16" if self.mf == 16 else ""
         n += "_ip" if self.spread & 2 else ("_sp" if self.spread & 1 else "")
         n += "_pa" if self.spread & 4 else ""
+        n += "_ea" if self.spread & 8 else ""
+        n += "_fb" if self.spread & 16 else ""
         return n + ("_bt" if self.bt else "")
 
     # derived quantities, as in TilePipeCfg (csrc/tile_pipe_kernel.h)
@@ -153,7 +157,7 @@ def valid(c) -> bool:
     d = c.derived()
     if d["ksteps"] % 2 or d["wtm"] % c.mf or d["wtn"] % c.mf or d["tm"] < 1 or d["tn"] < 1:
         return False
-    if not 0 <= c.spread <= 7 or (c.spread & 2 and d["tm"] < 2):
+    if not 0 <= c.spread <= 31 or (c.spread & 2 and d["tm"] < 2) or (c.spread & 16 and not c.spread & 2):
         return False
     cb_ok = pow2(d["cb"]) or (d["cb"] % 8 == 0 and (c.bn * 2) % 256 == 128)   # e.g. BN = 192
     if not (pow2(d["ca"]) and cb_ok and d["cb"] >= 4):
@@ -168,7 +172,10 @@ def valid(c) -> bool:
     last = (d["ksteps"] - 1) * d["nmma"] + c.bslot
     if not (0 <= c.bslot and c.bslot + 1 < d["nmma"]):
         return False
-    if not (c.dstride >= 1 and (ps - 1) * c.dstride < last):
+    if c.spread & 8:   # early copies: ring loaders, all issued after the barrier within the stage
+        if c.loader == "reg" or not (c.dstride >= 1 and last + 1 + (ps - 1) * c.dstride < d["ksteps"] * d["nmma"]):
+            return False
+    elif not (c.dstride >= 1 and (ps - 1) * c.dstride < last):
         return False
     if c.loader == "reg":
         if c.stages != 2 or c.cslot < 0 or c.cslot + ps > last + 1:
@@ -248,8 +255,19 @@ def space() -> list:
         out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", mf=16, spread=6))
     out.append(Tile(256, 256, 64, 2, 2, 2, 4, 8, 2, "buf", mf=16, spread=6))
     out.append(Tile(256, 256, 64, 2, 2, 2, 4, 3, 1, "dma", spread=6))
+    # copies of stage kt+2 issued right after stage kt's barrier (16x16 schedules: 128 MFMA slots per stage)
+    for bs, ds in ((24, 1), (32, 1), (40, 1), (16, 2), (24, 2), (32, 2)):
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", mf=16, spread=14))
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 24, 2, "buf", mf=16, spread=14))
+    # ... and the next k-step's B fragments read first
+    for bs, ds, fl in ((24, 2, 22), (16, 2, 22), (24, 1, 30), (32, 1, 30), (16, 2, 30), (24, 2, 30)):
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", mf=16, spread=fl))
     for bs, ds in ((8, 2), (16, 2), (24, 2), (32, 2)):
         out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", mf=16, spread=6, bt=1))
+    for bs, ds in ((24, 1), (24, 2), (32, 1)):
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", mf=16, spread=14, bt=1))
+    for bs, ds, fl in ((24, 2, 22), (24, 1, 30), (16, 2, 30)):
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", mf=16, spread=fl, bt=1))
     out.append(Tile(256, 256, 64, 2, 2, 2, 4, 8, 2, "buf", mf=16, spread=6, bt=1))
     for bs, ds in ((3, 1), (3, 2)):
         out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", spread=4))
