@@ -608,20 +608,39 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     //   MF = 16, register e:        C[mi*16 + l%16][ni*16 + 4*(l/16) + e]
     // relative to the wave's sub-tile origin (m0 + wm*WTM, n0 + wn*WTN).
     // With LOAD_DMA, N % 8 == 0, so a column quad is all in or all out.
+    //
+    // LDS_EPI (SPREAD bit 5): the stage buffers are free once the last stage
+    // has been read, and the whole fp16 C tile fits in them.  Each wave writes
+    // its sub-tile there in the MFMA layout (8 bytes per lane, rows of WTN
+    // columns whose 16-byte chunks are XOR-swizzled by row), then reads it
+    // back row-contiguous and writes C with 16-byte stores: one store
+    // instruction covers 64/RCH whole row segments of WTN*2 bytes instead of
+    // MF rows x 8 bytes x 4 lanes.  NT_C (SPREAD bit 6): those stores are
+    // marked non-temporal (C is not read again by this kernel).
     constexpr int NQ = NACC / 4;  // column quads per lane and block
+    constexpr bool LDS_EPI = (SPREAD & 32) != 0;
+    constexpr bool NT_C = (SPREAD & 64) != 0;
+    static_assert(!NT_C || LDS_EPI, "non-temporal C stores belong to the LDS epilogue");
+    constexpr int RCH = WTN / 8;                     // 16-byte chunks per sub-tile row
+    constexpr int SWM = (RCH < 16 ? RCH : 16) - 1;   // chunk XOR mask (row bits)
+    static_assert(!LDS_EPI || (BM * BN * 2 <= Cfg::LDS_BYTES && (RCH & (RCH - 1)) == 0 && RCH >= 4 && RCH <= 64),
+                  "LDS epilogue: the C tile fits in the stage buffers; power-of-two chunks per sub-tile row");
+    GK_LDS char* const c_lds = a_lds + wave * (WTM * WTN * 2);  // this wave's sub-tile [WTM][WTN] fp16
+    if constexpr (LDS_EPI) __syncthreads();  // every wave has finished reading the last stage
 #pragma unroll
     for (int ni = 0; ni < TN; ++ni) {
 #pragma unroll
         for (int r4 = 0; r4 < NQ; ++r4) {
-            const int n = n0 + wn * WTN + ni * MF + (MF == 32 ? 8 * r4 + 4 * (lane >> 5) : 4 * (lane >> 4));
-            const bool quad = LOADER == LOAD_DMA || n + 4 <= N;  // LOAD_DMA: N % 8 == 0
+            const int nc = ni * MF + (MF == 32 ? 8 * r4 + 4 * (lane >> 5) : 4 * (lane >> 4));  // column in the sub-tile
+            const int n = n0 + wn * WTN + nc;
+            const bool quad = n + 4 <= N;
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (EPI != EPI_NONE) {
                 if (quad) {
                     const f16x4 b4 = *(const f16x4_u*)(p.bias + n);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) bv[e] = (float)b4[e];
-                } else if (LOADER != LOAD_DMA) {
+                } else if (LOADER != LOAD_DMA) {  // LOAD_DMA: N % 8 == 0, the quad is wholly past N
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         if (n + e < N) bv[e] = (float)p.bias[n + e];
@@ -629,19 +648,54 @@ gemm_tile_pipe_kernel(GemmArgs p) {
             }
 #pragma unroll
             for (int mi = 0; mi < TM; ++mi) {
-                const int m = m0 + wm * WTM + mi * MF + (lane % MF);
-                if (m >= M || n >= N) continue;
+                const int rr = mi * MF + (lane % MF);  // row in the sub-tile
                 f16x4 o;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[e] = (f16)apply_epilogue<EPI>(acc[mi][ni][4 * r4 + e], bv[e]);
-                f16* dst = p.C + (size_t)m * ldc + n;
-                if (quad) {
-                    *(f16x4_u*)dst = o;
+                if constexpr (LDS_EPI) {
+                    *(GK_LDS f16x4*)(c_lds + rr * WTN * 2 + ((((nc >> 3) ^ (rr & SWM))) << 4) + ((nc & 7) << 1)) = o;
                 } else {
+                    const int m = m0 + wm * WTM + rr;
+                    if (m >= M || n >= N) continue;
+                    f16* dst = p.C + (size_t)m * ldc + n;
+                    if (quad) {
+                        *(f16x4_u*)dst = o;
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < N) dst[e] = o[e];
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < N) dst[e] = o[e];
+                    }
                 }
+            }
+        }
+    }
+    if constexpr (LDS_EPI) {
+        __syncthreads();  // the sub-tile's LDS writes precede its reads by other lanes
+        constexpr int RPI = 64 / RCH;  // rows per store instruction
+        // 16-byte stores need 16-byte-aligned rows of C (always so with LOAD_DMA)
+        const bool c_al = LOADER == LOAD_DMA || ((((uintptr_t)p.C) & 15) == 0 && (ldc & 7) == 0);
+        const int c = lane % RCH;
+#pragma unroll
+        for (int it = 0; it < WTM / RPI; ++it) {
+            const int rr = it * RPI + lane / RCH;
+            const f16x8 v = *(const GK_LDS f16x8*)(c_lds + rr * WTN * 2 + ((c ^ (rr & SWM)) << 4));
+            const int m = m0 + wm * WTM + rr, n = n0 + wn * WTN + 8 * c;
+            if (m >= M || n >= N) continue;
+            f16* dst = p.C + (size_t)m * ldc + n;
+            if (n + 8 <= N) {
+                if (c_al) {
+                    if constexpr (NT_C) {
+                        __builtin_nontemporal_store(v, (f16x8*)dst);
+                    } else {
+                        *(f16x8*)dst = v;
+                    }
+                } else {
+                    *(f16x8_u*)dst = v;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (n + e < N) dst[e] = v[e];
             }
         }
     }

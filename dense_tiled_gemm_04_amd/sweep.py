@@ -77,7 +77,8 @@ class Tile:
     spread: int = 0      # schedule flags: 1 LDS reads spread evenly over a k-step's slots, 2 A refilled in
                          # place (one A fragment set), 4 MFMAs as asm on accumulators pinned to AGPRs,
                          # 8 copies of stage kt+STAGES issued right after stage kt's barrier, 16 (with 2) the
-                         # next k-step's B reads front-loaded
+                         # next k-step's B reads front-loaded, 32 C staged through LDS and written with
+                         # row-contiguous 16-byte stores, 64 (with 32) those stores non-temporal
     bt: int = 0          # B given transposed (Bt[N][K])
 
     kind = "tile"
@@ -94,6 +95,8 @@ class Tile:
         n += "_pa" if self.spread & 4 else ""
         n += "_ea" if self.spread & 8 else ""
         n += "_fb" if self.spread & 16 else ""
+        n += "_le" if self.spread & 32 else ""
+        n += "_nt" if self.spread & 64 else ""
         return n + ("_bt" if self.bt else "")
 
     # derived quantities, as in TilePipeCfg (csrc/tile_pipe_kernel.h)
@@ -157,7 +160,13 @@ def valid(c) -> bool:
     d = c.derived()
     if d["ksteps"] % 2 or d["wtm"] % c.mf or d["wtn"] % c.mf or d["tm"] < 1 or d["tn"] < 1:
         return False
-    if not 0 <= c.spread <= 31 or (c.spread & 2 and d["tm"] < 2) or (c.spread & 16 and not c.spread & 2):
+    if not 0 <= c.spread <= 127 or (c.spread & 2 and d["tm"] < 2) or (c.spread & 16 and not c.spread & 2):
+        return False
+    # LDS epilogue: the C tile fits in the stage buffers, power-of-two 16-byte chunks per sub-tile row;
+    # non-temporal C stores only with it
+    if c.spread & 32 and not (c.bm * c.bn * 2 <= c.lds_bytes and pow2(d["wtn"] // 8) and 4 <= d["wtn"] // 8 <= 64):
+        return False
+    if c.spread & 64 and not c.spread & 32:
         return False
     cb_ok = pow2(d["cb"]) or (d["cb"] % 8 == 0 and (c.bn * 2) % 256 == 128)   # e.g. BN = 192
     if not (pow2(d["ca"]) and cb_ok and d["cb"] >= 4):
@@ -279,6 +288,21 @@ def space() -> list:
     out.append(Tile(256, 256, 64, 2, 2, 2, 4, 8, 4, "dma", mf=16, spread=5, bt=1))
     out.append(Tile(256, 256, 64, 2, 2, 2, 4, 3, 1, "dma", spread=4, bt=1))
     out.append(Tile(256, 256, 64, 2, 2, 2, 4, 8, 2, "buf", mf=16, spread=5, bt=1))
+    # C staged through LDS and written with row-contiguous 16-byte stores (+32), non-temporal (+96): the
+    # schedules of every loader and B layout that lead their classes
+    for le in (32, 96):
+        for bs, ds, fl in ((24, 2, 14), (16, 2, 14), (24, 1, 14), (32, 2, 14)):
+            out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", mf=16, spread=fl + le))
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, 24, 2, "buf", mf=16, spread=14 + le))
+        for bs, ds in ((16, 2), (24, 2), (24, 1)):
+            out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", mf=16, spread=30 + le, bt=1))
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, 3, 1, "buf", spread=le, bt=1))
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, 3, 2, "reg", spread=le))
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, 3, 2, "reg", spread=le, bt=1))
+        for st, fl in ((3, 4), (4, 0), (3, 0)):
+            out.append(Tile(128, 128, 64, 2, 2, st, 4, 1, 1, "dma", spread=fl + le))
+            out.append(Tile(128, 128, 64, 2, 2, st, 4, 1, 1, "dma", spread=fl + le, bt=1))
+            out.append(Tile(128, 128, 64, 2, 2, st, 4, 1, 1, "buf", spread=fl + le))
     for bt in (0, 1):
         for mb, sts in ((1, (4, 6, 8)), (2, (4, 6)), (4, (3, 5))):
             for st in sts:
@@ -332,10 +356,20 @@ def emit_table(configs: list, sel: dict, path: str, header: str) -> None:
         f.write("\n".join(lines) + "\n")
 
 
-def build_sweep_lib(verbose: bool = True) -> str:
+def finalists(table_path: str = TABLE) -> list:
+    """A focused re-sweep: the configurations of the current table plus their
+    LDS-epilogue variants (names with _le / _le_nt added), as far as the space
+    holds them."""
+    import re
+
+    keep = set(re.findall(r'"([^"]+)"\)', open(table_path).read()))
+    return [c for c in space() if c.name in keep or c.name.replace("_le_nt", "").replace("_le", "") in keep]
+
+
+def build_sweep_lib(verbose: bool = True, configs: list | None = None) -> str:
     from dense_tiled_gemm_04_amd import build as libbuild
 
-    configs = space()
+    configs = space() if configs is None else configs
     sel = {}
     for cls in CLASSES:
         sel[cls] = next(i for i, c in enumerate(configs) if class_of(c, cls))
@@ -521,7 +555,7 @@ def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str
     out.close()
 
 
-def select(results_path: str, table_path: str = TABLE, summary_path: str | None = None) -> dict:
+def select(results_path: str, table_path: str = TABLE, summary_path: str | None = None, note: str = "") -> dict:
     recs = [json.loads(l) for l in open(results_path) if l.strip()]
     # classes come from the current workload table, so a reclassification needs no new measurements
     wl_classes = {name: classes for name, _w, _o, classes in sweep_workloads()}
@@ -562,7 +596,7 @@ def select(results_path: str, table_path: str = TABLE, summary_path: str | None 
                  "workloads rotate 3 copies of B so the Infinity Cache cannot serve it;",
                  "outputs screened against a float32 PyTorch reference on sampled rows (parity proper is the",
                  "oracle tests). Command: `python -m dense_tiled_gemm_04_amd.sweep --run RESULTS` on the GPU, then",
-                 "`--select RESULTS` here.", "", "## Chosen per shape class", "",
+                 "`--select RESULTS` here."] + ([""] + note.splitlines() if note else []) + ["", "## Chosen per shape class", "",
                  "| class | configuration | geo-mean us |", "|---|---|---|"]
         for cls in CLASSES:
             lines.append("| %s | %s | %.1f |" % (cls, chosen[cls], scores[cls]))
@@ -622,6 +656,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--list", action="store_true", help="print the sweep space")
     ap.add_argument("--build", action="store_true", help="compile libgemm_f16_sweep.so with the whole space")
+    ap.add_argument("--finalists", action="store_true",
+                    help="with --build/--list: only the current table's configurations and their LDS-epilogue "
+                         "variants; with --select: say so in the summary")
     ap.add_argument("--run", metavar="RESULTS", help="time every configuration (GPU); JSONL, resumable")
     ap.add_argument("--only", default=None, help="comma-separated sweep workload names for --run")
     ap.add_argument("--select", metavar="RESULTS", help="pick per-class defaults, write csrc/config_table.inc")
@@ -633,14 +670,17 @@ def main() -> int:
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
     if a.list:
-        for c in space():
+        for c in (finalists() if a.finalists else space()):
             print("%-50s lds=%6d" % (c.name, c.lds_bytes))
     if a.build:
-        build_sweep_lib()
+        build_sweep_lib(configs=finalists() if a.finalists else None)
     if a.run:
         run(a.run, only=a.only)
     if a.select:
-        print(json.dumps(select(a.select, summary_path=a.summary), indent=1))
+        note = ("Focused re-sweep (`--build --finalists`, then `--run`): the configurations of the table in force "
+                "before it, plus\ntheir variants with C staged through LDS (`_le`) and with non-temporal C stores "
+                "(`_le_nt`).") if a.finalists else ""
+        print(json.dumps(select(a.select, summary_path=a.summary, note=note), indent=1))
     if a.ablation:
         ablation(a.ablation, a.ablation_out)
     return 0

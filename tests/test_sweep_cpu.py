@@ -46,6 +46,27 @@ def test_schedule_flags_in_names_and_limits():
     assert sweep.Skinny(1, 4, 1, 1).name == "skinny_m16_s4_r_bt"
 
 
+def test_lds_epilogue_flags():
+    # 32: C staged through the stage buffers (the whole fp16 tile must fit in them), 64: non-temporal C stores,
+    # only together with 32
+    t = sweep.Tile(256, 256, 64, 2, 2, 2, 4, 24, 2, "dma", mf=16, spread=14 + 96)
+    assert t.name.endswith("_m16_ip_pa_ea_le_nt") and sweep.valid(t)
+    assert sweep.valid(sweep.Tile(128, 128, 64, 2, 2, 3, 4, 1, 1, "dma", spread=32))
+    assert sweep.Tile(256, 256, 64, 2, 2, 2, 4, 16, 2, "dma", mf=16, spread=30 + 32, bt=1).name.endswith("_fb_le_bt")
+    assert not sweep.valid(sweep.Tile(256, 256, 64, 2, 2, 2, 4, 24, 2, "dma", mf=16, spread=14 + 64))
+    # a 256x256 tile (128 KiB of fp16) does not fit in two 32-deep stages (96 KiB)
+    assert not sweep.valid(sweep.Tile(256, 256, 32, 2, 2, 2, 4, 3, 1, "dma", spread=32))
+    # 192-wide tiles: 12 chunks per sub-tile row, not a power of two
+    assert not sweep.valid(sweep.Tile(256, 192, 64, 2, 2, 2, 4, 1, 2, "dma", spread=32))
+    # the finalists of a re-sweep are the table's configurations and their epilogue variants, all in the space
+    fin = sweep.finalists()
+    names = {c.name for c in fin}
+    assert all(sweep.valid(c) for c in fin)
+    for n in names:
+        base = n.replace("_le_nt", "").replace("_le", "")
+        assert base in names or n in names
+
+
 def test_space_is_valid_and_unique():
     sp = sweep.space()
     assert len(sp) >= 20
