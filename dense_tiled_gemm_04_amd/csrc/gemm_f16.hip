@@ -25,7 +25,7 @@ struct Config {
     int group_m;
     int stages;
     int bslot, dstride, cslot, wpe;  // tile schedule: barrier slot, copy stride, LDS-write slot, waves/SIMD
-    int mfma, spread;                // tile MFMA shape (32: 32x32x16, 16: 16x16x32), spread LDS reads
+    int mfma, spread;                // MFMA shape (32: 32x32x16, 16: 16x16x32); schedule flags (skinny: 1 = 16-byte A copies)
     int bt;                          // 1: B given transposed (Bt[N][K])
     int krot;                        // skinny: K stages walked from stage (workgroup mod KT)
     int lds_bytes;
@@ -42,10 +42,10 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int MB, int STAGES, int BT, int KROT, int EPI>
+template <int MB, int STAGES, int BT, int KROT, int A16, int EPI>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.tiles_n), block(SK_WAVES * 64);
-    hipLaunchKernelGGL((gemm_skinny_kernel<MB, STAGES, EPI, BT, KROT>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_skinny_kernel<MB, STAGES, EPI, BT, KROT, A16>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -64,14 +64,15 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
         }                                                                                          \
     }
 
-// Skinny config: 16*MB rows, ST LDS stages, B transposed BT, rotated K order KR.
-#define SKINNY_CFG(MB, ST, BT, KR, NAME)                                                            \
+// Skinny config: 16*MB rows, ST LDS stages, B transposed BT, rotated K order KR,
+// 16-byte A copies A16.
+#define SKINNY_CFG(MB, ST, BT, KR, A16, NAME)                                                       \
     Config {                                                                                       \
-        NAME, KIND_SKINNY, 16 * MB, SK_BN, SK_BK, 1, SK_WAVES, -1, 1, ST, 0, 0, 0, 1, 16, 0, BT, KR, \
+        NAME, KIND_SKINNY, 16 * MB, SK_BN, SK_BK, 1, SK_WAVES, -1, 1, ST, 0, 0, 0, 1, 16, A16, BT, KR, \
             ST * (16 * MB * SK_BK * 2 + SK_BK * SK_BN * 2), SK_WAVES * 64,                         \
         {                                                                                          \
-            launch_skinny<MB, ST, BT, KR, 0>, launch_skinny<MB, ST, BT, KR, 1>,                    \
-                launch_skinny<MB, ST, BT, KR, 2>                                                   \
+            launch_skinny<MB, ST, BT, KR, A16, 0>, launch_skinny<MB, ST, BT, KR, A16, 1>,          \
+                launch_skinny<MB, ST, BT, KR, A16, 2>                                              \
         }                                                                                          \
     }
 

@@ -20,6 +20,10 @@
 // 64 rows of Bt, k-contiguous: its stage is laid out and read like A's (one
 // 16-byte LDS read per fragment instead of two transpose reads), and k-chunks
 // past K are sent out of range as A's are.
+// A16: A reaches LDS by 16-byte LDS-DMA (one or a few copies per lane and
+// stage) instead of 4-byte copies (four times as many).  K % 8 == 0 on this
+// path, so a 16-byte chunk of A never straddles K; chunks past K are sent out
+// of range like single dwords.
 // KROT: workgroup w walks its K stages starting at stage w mod KT (wrapping
 // around).  With Bt, the workgroups' concurrent reads then sit at different
 // offsets within their rows instead of all at the same one, 16 KiB apart,
@@ -41,7 +45,7 @@ __device__ __forceinline__ int sk_swz_b(int kr) {
     return 2 * (((kr >> 1) & 1) | (((kr >> 3) & 1) << 1));
 }
 
-template <int MB, int STAGES, int EPI, int BT, int KROT>
+template <int MB, int STAGES, int EPI, int BT, int KROT, int A16>
 __global__ void __launch_bounds__(SK_WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 gemm_skinny_kernel(GemmArgs p) {
     constexpr int NT = SK_WAVES * 64;
@@ -49,8 +53,9 @@ gemm_skinny_kernel(GemmArgs p) {
     constexpr int B_STAGE = SK_BK * SK_BN * 2;       // 16 KiB
     constexpr int A_STAGE = MR * SK_BK * 2;          // 4 KiB per 16 rows
     constexpr int B_INS = B_STAGE / 16 / NT;         // 16-byte DMA per lane
-    constexpr int A_INS = A_STAGE / 4 / NT;          // 4-byte DMA per lane
-    static_assert(B_INS * 16 * NT == B_STAGE && A_INS * 4 * NT == A_STAGE, "stage split");
+    constexpr int A_BYTES = A16 ? 16 : 4;            // bytes per A copy and lane
+    constexpr int A_INS = A_STAGE / A_BYTES / NT;    // A copies per lane
+    static_assert(B_INS * 16 * NT == B_STAGE && A_INS * A_BYTES * NT == A_STAGE, "stage split");
     __shared__ __attribute__((aligned(1024))) char smem_raw[STAGES * (A_STAGE + B_STAGE)];
     GK_LDS char* smem = (GK_LDS char*)smem_raw;
     GK_LDS char* const b_lds = smem;
@@ -90,25 +95,34 @@ gemm_skinny_kernel(GemmArgs p) {
         }
     }
     // A stage: [MR][SK_BK] fp16 = 16 chunks per row, chunk c of row m at c ^ (m & 15).
-    // Rows >= M are clamped to M-1 (results never stored); a dword past K in a
-    // row reads the next row's data, multiplied by B rows that read as zero.
-    // That product is 0 for finite A; to keep it exact even for non-finite A,
-    // dwords past K are redirected out of range (read as 0) below.
+    // Rows >= M are clamped to M-1 (results never stored); a copy past K in a
+    // row would read the next row's data, multiplied by B rows that read as
+    // zero.  That product is 0 for finite A; to keep it exact even for
+    // non-finite A, copies past K are redirected out of range (read as 0) below.
     uint32_t a_off[A_INS];
     int a_kcol[A_INS];
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
-        const int D = (i * SK_WAVES + wave) * 64 + lane;   // destination dword in the stage
-        const int m = D >> 6, pc = (D >> 2) & 15, w = D & 3;
-        const int c = pc ^ (m & 15);
+        int m, c, w;
+        if constexpr (A16) {
+            const int P = (i * SK_WAVES + wave) * 64 + lane;   // destination chunk in the stage
+            m = P >> 4;
+            c = (P & 15) ^ (m & 15);
+            w = 0;
+        } else {
+            const int D = (i * SK_WAVES + wave) * 64 + lane;   // destination dword in the stage
+            m = D >> 6;
+            c = ((D >> 2) & 15) ^ (m & 15);
+            w = D & 3;
+        }
         const int mm = min(m, M - 1);
-        a_kcol[i] = 8 * c + 2 * w;                         // k offset within the stage
+        a_kcol[i] = 8 * c + 2 * w;                             // k offset within the stage
         a_off[i] = (uint32_t)((mm * lda + a_kcol[i]) * 2);
     }
 
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t b_lds0 = lds_addr(b_lds) + wave_s * 64 * 16;
-    const uint32_t a_lds0 = lds_addr(a_lds) + wave_s * 64 * 4;
+    const uint32_t a_lds0 = lds_addr(a_lds) + wave_s * 64 * A_BYTES;
     const int krot = (KROT && KT > 0) ? (int)(blockIdx.x % (unsigned)KT) : 0;
     auto issue = [&](int kt, int s) {
         const int ktr = kt + krot < KT ? kt + krot : kt + krot - KT;
@@ -126,7 +140,11 @@ gemm_skinny_kernel(GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < A_INS; ++i) {
             const uint32_t off = (kbase + a_kcol[i] < K) ? a_off[i] + (uint32_t)kbase * 2 : 0x80000000u;
-            dma_buffer_4(a_rsrc, off, a_lds0 + s * A_STAGE + i * SK_WAVES * 64 * 4);
+            if constexpr (A16) {
+                dma_buffer_16(a_rsrc, off, a_lds0 + s * A_STAGE + i * SK_WAVES * 64 * 16);
+            } else {
+                dma_buffer_4(a_rsrc, off, a_lds0 + s * A_STAGE + i * SK_WAVES * 64 * 4);
+            }
         }
     };
 

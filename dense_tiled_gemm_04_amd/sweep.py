@@ -22,8 +22,8 @@ Steps:
    compiles ``libgemm_f16_sweep.so`` from the library's own sources, with
    -DGEMM_F16_CONFIG_TABLE pointing at that include.
 3. ``--run`` (on the GPU) times every configuration on each sweep workload
-   through the C ABI entry ``gemm_f16_with_config``, as the median of
-   HIP-event-timed launches. It checks each output against a float32
+   through the C ABI entry ``gemm_f16_with_config``: launches back to back
+   after a warm-up, timed in ~1 ms chunks between HIP events (median chunk). It checks each output against a float32
    PyTorch reference on sampled rows; that check is a screen only, and the
    library's parity tests compare with the CPU oracle. One JSON record per
    (config, workload) is appended to the results file, and a restarted run
@@ -129,20 +129,22 @@ class Skinny:
     stages: int
     bt: int = 0          # B given transposed (Bt[N][K])
     krot: int = 0        # K stages walked from stage (workgroup mod KT)
+    a16: int = 0         # A copied by 16-byte LDS-DMA (else 4-byte)
 
     kind = "skinny"
     loader = "lds_dma"
 
     @property
     def name(self) -> str:
-        return "skinny_m%d_s%d" % (16 * self.mb, self.stages) + ("_r" if self.krot else "") + ("_bt" if self.bt else "")
+        return "skinny_m%d_s%d" % (16 * self.mb, self.stages) + ("_r" if self.krot else "") + \
+            ("_a16" if self.a16 else "") + ("_bt" if self.bt else "")
 
     @property
     def lds_bytes(self) -> int:
         return self.stages * (16 * self.mb * SK_BK * 2 + SK_BK * SK_BN * 2)
 
     def macro(self) -> str:
-        return "SKINNY_CFG(%d, %d, %d, %d, \"%s\")" % (self.mb, self.stages, self.bt, self.krot, self.name)
+        return "SKINNY_CFG(%d, %d, %d, %d, %d, \"%s\")" % (self.mb, self.stages, self.bt, self.krot, self.a16, self.name)
 
 
 def pow2(x: int) -> bool:
@@ -153,7 +155,7 @@ def valid(c) -> bool:
     """The kernels' static_asserts plus the LDS and register budgets."""
     if isinstance(c, Skinny):
         b_ins = SK_BK * SK_BN * 2 // 16 // (SK_WAVES * 64)
-        a_ins = 16 * c.mb * SK_BK * 2 // 4 // (SK_WAVES * 64)
+        a_ins = 16 * c.mb * SK_BK * 2 // (16 if c.a16 else 4) // (SK_WAVES * 64)
         return c.stages >= 2 and (c.stages - 2) * (a_ins + b_ins) <= 63 and c.lds_bytes <= LDS_PER_CU
     if c.mf not in (16, 32) or c.loader not in ("dma", "buf", "reg"):
         return False
@@ -308,6 +310,12 @@ def space() -> list:
             for st in sts:
                 for kr in (0, 1):
                     out.append(Skinny(mb, st, bt, kr))
+    # A by 16-byte copies (a quarter of the A copy instructions)
+    for bt in (0, 1):
+        for mb, sts in ((1, (3, 4, 6, 8)), (2, (3, 4, 6)), (4, (3, 5))):
+            for st in sts:
+                for kr in (0, 1):
+                    out.append(Skinny(mb, st, bt, kr, a16=1))
     return [c for c in out if valid(c)]
 
 
@@ -516,8 +524,12 @@ def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str
                 continue
             if st != 0:
                 raise RuntimeError("config %s on %s: status %d" % (info["name"], name, st))
-            # Sustained timing, as the benchmark sees it: the power limit sets the clock
-            # within milliseconds, so warm up for >= 5 ms of work and time >= 25 ms.
+            # Sustained timing, as the benchmark sees it: launches back to back (the
+            # benchmark puts no event between them), since the power limit sets the
+            # clock within milliseconds and the gaps of per-launch events would let
+            # the card rest.  From a short idle: >= 5 ms of warm-up, then >= 25 ms in
+            # chunks of ~1 ms between event pairs; the result is the median chunk's
+            # time per launch.
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for r in range(3):
@@ -525,18 +537,23 @@ def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str
             e1.record(stream)
             torch.cuda.synchronize()
             t_one = max(e0.elapsed_time(e1) / 3, 1e-3)   # ms
+            time.sleep(0.02)
             for r in range(int(math.ceil(5.0 / t_one))):
                 call(*args(r + 1))
+            per = max(1, int(round(1.0 / t_one)))        # launches per chunk
             evs = []
-            for r in range(max(iters, int(math.ceil(25.0 / t_one)))):
+            r = 0
+            for _c in range(max(iters, int(math.ceil(25.0 / (per * t_one))))):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                call(*args(r + 1))
+                for _ in range(per):
+                    call(*args(r + 1))
+                    r += 1
                 e1.record(stream)
                 evs.append((e0, e1))
             call(*args(0))   # the screened output comes from the first copy of B
             torch.cuda.synchronize()
-            us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+            us = sorted(a.elapsed_time(b) * 1e3 / per for a, b in evs)
             med = us[len(us) // 2]
             got = dC[rows].float()
             diff = (got - refh)
@@ -591,8 +608,10 @@ def select(results_path: str, table_path: str = TABLE, summary_path: str | None 
                "(%s). Do not edit by hand; rerun the sweep." % os.path.basename(results_path))
     if summary_path:
         lines = ["# Offline sweep of the tile and skinny kernels", "",
-                 "Median of the HIP-event-timed launches in >= 25 ms of work, after >= 5 ms of warm-up, per (configuration, "
-                 "workload) on one MI355X (the clock has settled under the power limit by then); the skinny",
+                 "Per (configuration, workload) on one MI355X: launches back to back, as in bench.py; after >= 5 ms of "
+                 "warm-up, >= 25 ms in ~1 ms chunks between HIP events, median chunk time per launch (the clock has "
+                 "settled under the power limit by then; records of earlier runs timed each launch between its own "
+                 "events); the skinny",
                  "workloads rotate 3 copies of B so the Infinity Cache cannot serve it;",
                  "outputs screened against a float32 PyTorch reference on sampled rows (parity proper is the",
                  "oracle tests). Command: `python -m dense_tiled_gemm_04_amd.sweep --run RESULTS` on the GPU, then",
@@ -659,6 +678,9 @@ def main() -> int:
     ap.add_argument("--finalists", action="store_true",
                     help="with --build/--list: only the current table's configurations and their LDS-epilogue "
                          "variants; with --select: say so in the summary")
+    ap.add_argument("--subset", default=None, metavar="REGEX",
+                    help="with --build/--list: add the configurations of the space whose names match REGEX (alone: "
+                         "only those)")
     ap.add_argument("--run", metavar="RESULTS", help="time every configuration (GPU); JSONL, resumable")
     ap.add_argument("--only", default=None, help="comma-separated sweep workload names for --run")
     ap.add_argument("--select", metavar="RESULTS", help="pick per-class defaults, write csrc/config_table.inc")
@@ -669,17 +691,24 @@ def main() -> int:
     a = ap.parse_args()
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
+    chosen = finalists() if a.finalists else ([] if a.subset else space())
+    if a.subset:
+        import re
+
+        chosen += [c for c in space() if re.search(a.subset, c.name) and c not in chosen]
     if a.list:
-        for c in (finalists() if a.finalists else space()):
+        for c in chosen:
             print("%-50s lds=%6d" % (c.name, c.lds_bytes))
     if a.build:
-        build_sweep_lib(configs=finalists() if a.finalists else None)
+        build_sweep_lib(configs=chosen)
     if a.run:
         run(a.run, only=a.only)
     if a.select:
-        note = ("Focused re-sweep (`--build --finalists`, then `--run`): the configurations of the table in force "
+        note = ("Focused re-sweep (`--build --finalists%s`, then `--run`): the configurations of the table in force "
                 "before it, plus\ntheir variants with C staged through LDS (`_le`) and with non-temporal C stores "
-                "(`_le_nt`).") if a.finalists else ""
+                "(`_le_nt`)%s." % (" --subset '%s'" % a.subset if a.subset else "",
+                                   ", and the configurations of the space matching `%s`" % a.subset if a.subset else "")
+                ) if a.finalists else ""
         print(json.dumps(select(a.select, summary_path=a.summary, note=note), indent=1))
     if a.ablation:
         ablation(a.ablation, a.ablation_out)

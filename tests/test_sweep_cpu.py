@@ -44,6 +44,9 @@ def test_schedule_flags_in_names_and_limits():
     assert not sweep.valid(sweep.Tile(256, 256, 64, 2, 2, 2, 4, 3, 1, "dma", spread=8))
     assert sweep.Skinny(2, 6, 1).name == "skinny_m32_s6_bt"
     assert sweep.Skinny(1, 4, 1, 1).name == "skinny_m16_s4_r_bt"
+    assert sweep.Skinny(2, 4, 0, 1, a16=1).name == "skinny_m32_s4_r_a16"
+    # 16-byte A copies: 2 per lane and stage at 32 rows (8 with 4-byte copies); 8 stages of M <= 16 still fit
+    assert sweep.valid(sweep.Skinny(1, 8, a16=1)) and not sweep.valid(sweep.Skinny(1, 9, a16=1))
 
 
 def test_lds_epilogue_flags():
@@ -98,9 +101,9 @@ def test_product_table_entries_are_in_budget():
         assert f[15].strip('"') == c.name
     for s in skinny:
         f = [x.strip() for x in s.split(",")]
-        c = sweep.Skinny(int(f[0]), int(f[1]), int(f[2]), int(f[3]))
+        c = sweep.Skinny(int(f[0]), int(f[1]), int(f[2]), int(f[3]), a16=int(f[4]))
         assert sweep.valid(c), c
-        assert f[4].strip('"') == c.name
+        assert f[5].strip('"') == c.name
 
 
 def test_select_picks_fastest_valid_per_class(tmp_path):
