@@ -614,17 +614,22 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     // its sub-tile there in the MFMA layout (8 bytes per lane, rows of WTN
     // columns whose 16-byte chunks are XOR-swizzled by row), then reads it
     // back row-contiguous and writes C with 16-byte stores: one store
-    // instruction covers 64/RCH whole row segments of WTN*2 bytes instead of
-    // MF rows x 8 bytes x 4 lanes.  NT_C (SPREAD bit 6): those stores are
+    // instruction covers 64 consecutive 16-byte chunks of the sub-tile's rows
+    // (RCH = WTN/8 chunks per row) instead of MF rows x 8 bytes x 4 lanes.  NT_C (SPREAD bit 6): those stores are
     // marked non-temporal (C is not read again by this kernel).
     constexpr int NQ = NACC / 4;  // column quads per lane and block
     constexpr bool LDS_EPI = (SPREAD & 32) != 0;
     constexpr bool NT_C = (SPREAD & 64) != 0;
     static_assert(!NT_C || LDS_EPI, "non-temporal C stores belong to the LDS epilogue");
     constexpr int RCH = WTN / 8;                     // 16-byte chunks per sub-tile row
-    constexpr int SWM = (RCH < 16 ? RCH : 16) - 1;   // chunk XOR mask (row bits)
-    static_assert(!LDS_EPI || (BM * BN * 2 <= Cfg::LDS_BYTES && (RCH & (RCH - 1)) == 0 && RCH >= 4 && RCH <= 64),
-                  "LDS epilogue: the C tile fits in the stage buffers; power-of-two chunks per sub-tile row");
+    constexpr bool RCH_P2 = (RCH & (RCH - 1)) == 0;
+    static_assert(!LDS_EPI || (BM * BN * 2 <= Cfg::LDS_BYTES && ((RCH_P2 && RCH >= 4 && RCH <= 64) || RCH == 12)),
+                  "LDS epilogue: the C tile fits in the stage buffers; 4..64 (power of two) or 12 chunks per row");
+    // Chunk swizzle of sub-tile row r.  Power-of-two rows: XOR with the low row
+    // bits (up to 16 rows spread over distinct bank groups).  12-chunk rows
+    // (192 bytes): rows r and r + 4 start at the same bank, so XOR with bits 2-3
+    // of r, which keeps a chunk inside its aligned group of 4 and so inside the row.
+    auto c_swz = [&](int r) { return RCH_P2 ? (r & ((RCH < 16 ? RCH : 16) - 1)) : ((r >> 2) & 3); };
     GK_LDS char* const c_lds = a_lds + wave * (WTM * WTN * 2);  // this wave's sub-tile [WTM][WTN] fp16
     if constexpr (LDS_EPI) __syncthreads();  // every wave has finished reading the last stage
 #pragma unroll
@@ -653,7 +658,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[e] = (f16)apply_epilogue<EPI>(acc[mi][ni][4 * r4 + e], bv[e]);
                 if constexpr (LDS_EPI) {
-                    *(GK_LDS f16x4*)(c_lds + rr * WTN * 2 + ((((nc >> 3) ^ (rr & SWM))) << 4) + ((nc & 7) << 1)) = o;
+                    *(GK_LDS f16x4*)(c_lds + rr * WTN * 2 + (((nc >> 3) ^ c_swz(rr)) << 4) + ((nc & 7) << 1)) = o;
                 } else {
                     const int m = m0 + wm * WTM + rr;
                     if (m >= M || n >= N) continue;
@@ -671,14 +676,14 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     }
     if constexpr (LDS_EPI) {
         __syncthreads();  // the sub-tile's LDS writes precede its reads by other lanes
-        constexpr int RPI = 64 / RCH;  // rows per store instruction
         // 16-byte stores need 16-byte-aligned rows of C (always so with LOAD_DMA)
         const bool c_al = LOADER == LOAD_DMA || ((((uintptr_t)p.C) & 15) == 0 && (ldc & 7) == 0);
-        const int c = lane % RCH;
+        static_assert((WTM * RCH) % 64 == 0, "whole store instructions per sub-tile");
 #pragma unroll
-        for (int it = 0; it < WTM / RPI; ++it) {
-            const int rr = it * RPI + lane / RCH;
-            const f16x8 v = *(const GK_LDS f16x8*)(c_lds + rr * WTN * 2 + ((c ^ (rr & SWM)) << 4));
+        for (int it = 0; it < WTM * RCH / 64; ++it) {
+            const int lc = it * 64 + lane;             // chunk of the sub-tile, row-major
+            const int rr = lc / RCH, c = lc % RCH;
+            const f16x8 v = *(const GK_LDS f16x8*)(c_lds + rr * WTN * 2 + ((c ^ c_swz(rr)) << 4));
             const int m = m0 + wm * WTM + rr, n = n0 + wn * WTN + 8 * c;
             if (m >= M || n >= N) continue;
             f16* dst = p.C + (size_t)m * ldc + n;

@@ -166,7 +166,8 @@ def valid(c) -> bool:
         return False
     # LDS epilogue: the C tile fits in the stage buffers, power-of-two 16-byte chunks per sub-tile row;
     # non-temporal C stores only with it
-    if c.spread & 32 and not (c.bm * c.bn * 2 <= c.lds_bytes and pow2(d["wtn"] // 8) and 4 <= d["wtn"] // 8 <= 64):
+    rch = d["wtn"] // 8
+    if c.spread & 32 and not (c.bm * c.bn * 2 <= c.lds_bytes and ((pow2(rch) and 4 <= rch <= 64) or rch == 12)):
         return False
     if c.spread & 64 and not c.spread & 32:
         return False
@@ -305,6 +306,12 @@ def space() -> list:
             out.append(Tile(128, 128, 64, 2, 2, st, 4, 1, 1, "dma", spread=fl + le))
             out.append(Tile(128, 128, 64, 2, 2, st, 4, 1, 1, "dma", spread=fl + le, bt=1))
             out.append(Tile(128, 128, 64, 2, 2, st, 4, 1, 1, "buf", spread=fl + le))
+    # 256x192 tiles on the 16x16 schedules: 3001 columns are 16 tiles of 192, so 4095x3001 fills the 256 CUs
+    # in one round (256x256 tiles leave 64 idle)
+    for ld in ("buf", "dma"):
+        for bs, ds in ((8, 2), (16, 2), (16, 1), (24, 1)):
+            for le in (0, 32, 96):
+                out.append(Tile(256, 192, 64, 2, 2, 2, 4, bs, ds, ld, mf=16, spread=14 + le))
     for bt in (0, 1):
         for mb, sts in ((1, (4, 6, 8)), (2, (4, 6)), (4, (3, 5))):
             for st in sts:
