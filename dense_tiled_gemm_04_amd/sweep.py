@@ -312,6 +312,13 @@ def space() -> list:
         for bs, ds in ((8, 2), (16, 2), (16, 1), (24, 1)):
             for le in (0, 32, 96):
                 out.append(Tile(256, 192, 64, 2, 2, 2, 4, bs, ds, ld, mf=16, spread=14 + le))
+    # ... and for B given transposed (ragged Bt), plain or with front-loaded B reads
+    for bs, ds in ((8, 2), (16, 2), (16, 1)):
+        for fl in (14, 30):
+            out.append(Tile(256, 192, 64, 2, 2, 2, 4, bs, ds, "buf", mf=16, spread=fl + 96, bt=1))
+    # barrier slot and copy stride around the chosen large-tile schedule, with the staged epilogue
+    for bs, ds in ((8, 2), (32, 1), (40, 1)):
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", mf=16, spread=14 + 96))
     for bt in (0, 1):
         for mb, sts in ((1, (4, 6, 8)), (2, (4, 6)), (4, (3, 5))):
             for st in sts:
