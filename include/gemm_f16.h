@@ -136,9 +136,13 @@ int gemm_f16_num_configs(void);
  * to buflen).  Returns the full length, or -GEMM_ERR_NO_CONFIG.  Keys: idx,
  * name, kind ("tile" | "skinny"), bm, bn, bk, waves_m, waves_n, loader,
  * group_m, stages, bslot, dstride, cslot, waves_per_simd, mfma (32 or 16),
- * spread (schedule flags: 1 LDS reads spread over the k-step, 2 A fragments
- * refilled in place, 4 MFMAs on accumulators pinned to AGPRs), b_transposed,
- * k_rotate (skinny: K order rotated per workgroup), lds_bytes, threads. */
+ * spread (schedule flags of the tile kernel: 1 LDS reads spread over the
+ * k-step, 2 A fragments refilled in place, 4 MFMAs on accumulators pinned to
+ * AGPRs, 8 copies issued right after the stage barrier, 16 the next k-step's
+ * B reads front-loaded, 32 C staged through LDS and written with
+ * row-contiguous 16-byte stores, 64 those stores non-temporal; of the skinny
+ * kernel: 1 A copied with 16-byte LDS-DMA), b_transposed, k_rotate (skinny:
+ * K order rotated per workgroup), lds_bytes, threads. */
 int gemm_f16_config_info(int idx, char* buf, int buflen);
 
 /* Index of the configuration gemm_f16() would launch for these arguments
