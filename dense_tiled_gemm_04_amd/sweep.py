@@ -650,7 +650,7 @@ def ablation(results_path: str, out_path: str) -> None:
     t = {(r["config"], r["workload"]): r for r in recs if r.get("ok")}
     by_name = {c.name: c for c in space()}
     lines = ["# Ablations: tile order (swizzle) and LDS stages", "",
-             "Median of the HIP-event-timed launches in >= 25 ms of work (after >= 5 ms of warm-up) per cell on one "
+             "Back-to-back launches timed in ~1 ms chunks over >= 25 ms (after >= 5 ms of warm-up), median chunk, per cell on one "
              "MI355X, from the same sweep records as the",
              "configuration table (`python -m dense_tiled_gemm_04_amd.sweep --run RESULTS` on the GPU, then",
              "`--ablation RESULTS`).", "",
