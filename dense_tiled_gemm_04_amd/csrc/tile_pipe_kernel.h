@@ -62,6 +62,11 @@
 //  * Tile order. XCD-contiguous remap of the workgroup id, then a grouped
 //    raster of GROUP_M tile-rows (GROUP_M = 1: row-major after the remap;
 //    GROUP_M = 0: row-major without the remap, the unswizzled baseline).
+//  * Epilogue. Bias and GELU run in fp32 on the accumulators; with the LDS
+//    epilogue (SPREAD bit 5) the fp16 tile is then staged in the freed stage
+//    buffers and written back as row-contiguous 16-byte stores (optionally
+//    non-temporal, bit 6), since in a one-round grid every workgroup reaches
+//    its epilogue at once and the C write is exposed in full.
 #pragma once
 #include "common.h"
 
@@ -615,8 +620,9 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     // columns whose 16-byte chunks are XOR-swizzled by row), then reads it
     // back row-contiguous and writes C with 16-byte stores: one store
     // instruction covers 64 consecutive 16-byte chunks of the sub-tile's rows
-    // (RCH = WTN/8 chunks per row) instead of MF rows x 8 bytes x 4 lanes.  NT_C (SPREAD bit 6): those stores are
-    // marked non-temporal (C is not read again by this kernel).
+    // (RCH = WTN/8 chunks per row) instead of MF rows x 8 bytes x 4 lanes.
+    // NT_C (SPREAD bit 6): those stores are marked non-temporal (C is not
+    // read again by this kernel).
     constexpr int NQ = NACC / 4;  // column quads per lane and block
     constexpr bool LDS_EPI = (SPREAD & 32) != 0;
     constexpr bool NT_C = (SPREAD & 64) != 0;
