@@ -564,3 +564,34 @@ def test_b_transposed_skinny_shapes_and_k_tail_isolation(lib, M):
         assert np.array_equal(got[:, inf_cols].view(np.uint16), ref[:, inf_cols].view(np.uint16)), (M, name)
         ran.append(name)
     assert "default" in ran and (M > 32 or len(ran) >= 2), ran
+
+
+def test_mfma16_configs_agree_bitwise(lib):
+    # Every configuration on the 16x16x32 MFMA sums each output's K products in the same order (k-steps of 32 in
+    # increasing k, the MFMA's own order inside a step), whatever its tile width, loader, LDS-staged epilogue or B
+    # layout, and feeds the MFMA the same values in the same lanes.  With the bias epilogue (one fp32 add: nothing
+    # for the compiler to contract) their outputs must be bit-identical, and each matches the oracle.
+    import dense_tiled_gemm_04_amd as g
+    M, N, K = 600, 776, 320  # several 256-row and 192/256-column tiles, ragged M and N, K a multiple of 64
+    A, B, bias = workloads.make_inputs("ragged_4095x3001x1000", M=M, N=N, K=K)
+    Bt = np.ascontiguousarray(B.T)
+    ref = oracle.gemm(A, B, bias, "bias")
+    outs = {}
+    for c in lib.configs():
+        if c["kind"] != "tile" or c["mfma"] != 16:
+            continue
+        try:
+            if c["b_transposed"]:
+                out = g.gemm_f16(dev(A), dev(Bt), dev(bias), "bias", b_transposed=True, config=c["idx"])
+            else:
+                out = g.gemm_f16(dev(A), dev(B), dev(bias), "bias", config=c["idx"])
+        except g.GemmError as e:
+            assert e.status == 6, (c["name"], e)
+            continue
+        torch.cuda.synchronize()
+        outs[c["name"]] = out.cpu().numpy()
+    names = sorted(outs)
+    assert len(names) >= 4, names
+    assert_parity(outs[names[0]], ref, names[0])
+    for n in names[1:]:
+        assert np.array_equal(outs[n].view(np.uint16), outs[names[0]].view(np.uint16)), (n, names[0])
