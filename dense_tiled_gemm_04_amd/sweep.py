@@ -319,6 +319,9 @@ def space() -> list:
     # barrier slot and copy stride around the chosen large-tile schedule, with the staged epilogue
     for bs, ds in ((8, 2), (32, 1), (40, 1)):
         out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", mf=16, spread=14 + 96))
+    # front-loaded B reads (the B-transposed winner's flag) with the staged epilogue, for B[K][N]
+    for bs in (8, 16, 32):
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, 2, "dma", mf=16, spread=30 + 96))
     for bt in (0, 1):
         for mb, sts in ((1, (4, 6, 8)), (2, (4, 6)), (4, (3, 5))):
             for st in sts:
