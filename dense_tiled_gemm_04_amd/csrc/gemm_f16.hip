@@ -56,7 +56,7 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
 #define TILE_CFG(BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, BT, NAME)             \
     Config {                                                                                       \
         NAME, KIND_TILE, BM, BN, BK, WM, WN, LOADER, G, ST, BS, DS, CS, WPE, MF, SP, BT, 0,        \
-            TilePipeCfg<BM, BN, BK, WM, WN, ST, MF, BT>::LDS_BYTES, WM * WN * 64,                  \
+            TilePipeCfg<BM, BN, BK, WM, WN, ST, MF, BT, ((SP) & 128) ? 1 : 0>::LDS_BYTES, WM * WN * 64, \
         {                                                                                          \
             launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, BT, 0>,        \
                 launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, BT, 1>,    \

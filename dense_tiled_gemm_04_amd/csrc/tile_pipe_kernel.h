@@ -112,7 +112,7 @@ __device__ __forceinline__ int swz_b(int kr) {
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int MF = 32, int BT = 0>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int MF = 32, int BT = 0, int AXS = 0>
 struct TilePipeCfg {
     static constexpr int NW = WM * WN;
     static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave sub-tile
@@ -120,7 +120,7 @@ struct TilePipeCfg {
     static constexpr int KS = MF == 32 ? 16 : 32;       // k per MFMA
     static constexpr int CA = BK / 8, CB = BN / 8;      // 16-byte chunks per A / B row
     static constexpr int A_STAGE = BM * BK * 2, B_STAGE = BK * BN * 2;
-    static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE);
+    static constexpr int LDS_BYTES = (STAGES + AXS) * A_STAGE + STAGES * B_STAGE;  // AXS: extra A stages
     static constexpr int KSTEPS = BK / KS;              // k-steps per stage
     static constexpr int A_INS = BM * CA / 64 / NW;     // 16-byte copies per lane and stage
     static constexpr int B_INS = BT ? BN * CA / 64 / NW : BK * CB / 64 / NW;
@@ -151,7 +151,7 @@ template <int BM, int BN, int BK, int WM, int WN, int STAGES, int GROUP_M, int E
           int LOADER, int CSLOT, int WPE, int MF, int SPREAD, int BT>
 __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 gemm_tile_pipe_kernel(GemmArgs p) {
-    using Cfg = TilePipeCfg<BM, BN, BK, WM, WN, STAGES, MF, BT>;
+    using Cfg = TilePipeCfg<BM, BN, BK, WM, WN, STAGES, MF, BT, (SPREAD & 128) ? 1 : 0>;
     constexpr int KS = Cfg::KS;
     constexpr int NW = Cfg::NW, WTM = Cfg::WTM, WTN = Cfg::WTN, TM = Cfg::TM, TN = Cfg::TN;
     constexpr int CA = Cfg::CA, CB = Cfg::CB, A_STAGE = Cfg::A_STAGE, B_STAGE = Cfg::B_STAGE;
@@ -176,7 +176,10 @@ gemm_tile_pipe_kernel(GemmArgs p) {
 
     __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::LDS_BYTES];
     GK_LDS char* const a_lds = (GK_LDS char*)smem_raw;           // [STAGES][BM][BK]
-    GK_LDS char* const b_lds = a_lds + STAGES * A_STAGE;         // [STAGES][BK][BN]
+    // AX (SPREAD bit 7): the A ring is one stage deeper than the B ring.
+    constexpr bool AX = (SPREAD & 128) != 0;
+    constexpr int SA = STAGES + (AX ? 1 : 0);                    // A ring depth
+    GK_LDS char* const b_lds = a_lds + SA * A_STAGE;             // [STAGES][BK][BN]
 
     const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb, ldc = p.ldc;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -302,10 +305,10 @@ gemm_tile_pipe_kernel(GemmArgs p) {
                                                      0x00020000);
         }
     };
-    // Ring loaders: copy j of stage kt into ring buffer sb.
-    auto dma_op = [&](int j, int kt, int sb) {
+    // Ring loaders: copy j of stage kt into ring buffer sa (an A copy, j < A_INS) or sb (a B copy).
+    auto dma_op = [&](int j, int kt, int sa, int sb) {
         if (j < A_INS) {
-            const uint32_t lds = a_lds0 + sb * A_STAGE + j * NW * 64 * 16;
+            const uint32_t lds = a_lds0 + sa * A_STAGE + j * NW * 64 * 16;
             if constexpr (LOADER == LOAD_BUF) {
                 dma_buffer_16(rsrc_a(kt), a_ck[j] < K - kt * BK ? a_off[j] : 0x80000000u, lds);
             } else {
@@ -400,6 +403,8 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     // every B fragment within its first TN slots.
     constexpr int BSPREAD = (SPREAD & 16) ? 0 : 1;
     static_assert(!(SPREAD & 16) || INPLACE, "front-loaded B reads belong to the in-place schedule");
+    static_assert(!AX || (RING && EARLY && INPLACE && STAGES == 2), "deeper A ring: ring loaders, early copies, "
+                  "in-place A, two B stages");
     static_assert(!INPLACE || TM >= 2, "in-place A refill needs two MFMA rows");
     f16x8 fa[INPLACE ? 1 : 2][TM];
     f16x4 fb[2][BT ? 1 : TN][2];
@@ -462,8 +467,16 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         for (int st = 0; st < PRE; ++st)
             if (st < KT)
 #pragma unroll
-                for (int j = 0; j < PER_STAGE; ++j) dma_op(j, st, st);
-        if (KT >= PRE) {
+                for (int j = 0; j < PER_STAGE; ++j) dma_op(j, st, st, st);
+        if constexpr (AX) {  // A of stage 2 as well; stage 0 has landed when A1, B1 and A2 may remain
+            if (KT > 2) {
+#pragma unroll
+                for (int j = 0; j < A_INS; ++j) dma_op(j, 2, 2, 0);
+                wait_vmcnt<PER_STAGE + A_INS>();
+            } else {
+                wait_vmcnt0();
+            }
+        } else if (KT >= PRE) {
             wait_vmcnt<(PRE - 1) * PER_STAGE>();
         } else {
             wait_vmcnt0();
@@ -493,7 +506,8 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         }
     }
 
-    int s = 0;  // ring buffer of the stage being computed
+    int s = 0;   // ring buffer of the stage being computed (B; A too unless AX)
+    int sa = 0;  // AX: A ring buffer of the stage being computed
     // PHASE 2: every stage the copies of this stage refer to exists (ring
     // loaders: kt+STAGES-1, or kt+STAGES with EARLY; LOAD_REG: kt+1 written
     // and kt+2 loaded), so they
@@ -504,6 +518,8 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         const bool has_next = PHASE > 0 || kt + 1 < KT;
         const int sn = (s + 1 == STAGES) ? 0 : s + 1;
         const int sd = (s == 0) ? STAGES - 1 : s - 1;  // buffer of stage kt+STAGES-1 (freed last stage)
+        const int sac = AX ? sa : s;                    // A buffer of this stage
+        const int san = AX ? ((sa + 1 == SA) ? 0 : sa + 1) : sn;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
             const int cur = kk & 1, nxt = cur ^ 1;
@@ -511,11 +527,21 @@ gemm_tile_pipe_kernel(GemmArgs p) {
             for (int i = 0; i < NMMA; ++i) {
                 mma_op(cur, i);
                 const int slot = kk * NMMA + i;
-                if constexpr (RING && PHASE == 2 && EARLY) {
+                if constexpr (RING && EARLY && AX && PHASE >= 1) {
+                    // B of stage kt+2 into this stage's B buffer, then (PHASE 2) A of stage kt+3 into its A buffer
+                    if (slot > LAST && (slot - LAST - 1) % DSTRIDE == 0) {
+                        const int q = (slot - LAST - 1) / DSTRIDE;
+                        if (q < B_INS) {
+                            dma_op(A_INS + q, kt + 2, sac, s);
+                        } else if (PHASE == 2 && q < PER_STAGE) {
+                            dma_op(q - B_INS, kt + 3, sac, s);
+                        }
+                    }
+                } else if constexpr (RING && PHASE == 2 && EARLY && !AX) {
                     if (slot > LAST && (slot - LAST - 1) % DSTRIDE == 0 && (slot - LAST - 1) / DSTRIDE < PER_STAGE)
-                        dma_op((slot - LAST - 1) / DSTRIDE, kt + STAGES, s);
-                } else if constexpr (RING && PHASE == 2) {
-                    if (slot % DSTRIDE == 0 && slot / DSTRIDE < PER_STAGE) dma_op(slot / DSTRIDE, kt + STAGES - 1, sd);
+                        dma_op((slot - LAST - 1) / DSTRIDE, kt + STAGES, s, s);
+                } else if constexpr (RING && PHASE == 2 && !AX) {
+                    if (slot % DSTRIDE == 0 && slot / DSTRIDE < PER_STAGE) dma_op(slot / DSTRIDE, kt + STAGES - 1, sd, sd);
                 }
                 if constexpr (LOADER == LOAD_REG && PHASE >= 1) {
                     if (slot >= CSLOT && slot < CSLOT + PER_STAGE) lwrite_op(slot - CSLOT, sn);
@@ -525,17 +551,25 @@ gemm_tile_pipe_kernel(GemmArgs p) {
                         gload_op((slot - CSLOT) / DSTRIDE, kt + 2);
                 }
                 if constexpr (INPLACE) {
-                    if (i == 0) read_a(TM - 1, s, kk);  // before this stage's barrier: stage s is still live
+                    if (i == 0) read_a(TM - 1, sac, kk);  // before this stage's barrier: stage s is still live
                     if (kk + 1 < KSTEPS) {
 #pragma unroll
                         for (int jb = 0; jb < NB; ++jb)
                             if (read_slot<NB, BSPREAD>(jb, 0, NMMA) == i) read_b(nxt, jb, s, kk + 1);
 #pragma unroll
                         for (int mi = 0; mi + 1 < TM; ++mi)
-                            if ((mi + 1) * TN - 1 == i) read_a(mi, s, kk + 1);
+                            if ((mi + 1) * TN - 1 == i) read_a(mi, sac, kk + 1);
                     } else if (has_next) {
                         if (i == BSLOT) {
-                            if constexpr (RING) {
+                            if constexpr (RING && AX) {
+                                // stage kt+1 (A issued two stages ago, B last stage) must have landed; A of
+                                // stage kt+2, issued last of all last stage (or in the prologue), may remain
+                                if (kt + 2 < KT) {
+                                    wait_vmcnt<A_INS>();
+                                } else {
+                                    wait_vmcnt0();
+                                }
+                            } else if constexpr (RING) {
                                 if constexpr (PHASE == 2) {
                                     wait_vmcnt<(STAGES - 2) * PER_STAGE>();
                                 } else {
@@ -549,7 +583,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
                             if (read_slot<NB, BSPREAD>(jb, BSLOT + 1, NMMA - BSLOT - 1) == i) read_b(nxt, jb, sn, 0);
 #pragma unroll
                         for (int mi = 0; mi + 1 < TM; ++mi)
-                            if (max((mi + 1) * TN - 1, BSLOT + 1) == i) read_a(mi, sn, 0);
+                            if (max((mi + 1) * TN - 1, BSLOT + 1) == i) read_a(mi, san, 0);
                     }
                 } else if (kk + 1 < KSTEPS) {
 #pragma unroll
@@ -574,6 +608,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
             }
         }
         s = sn;
+        sa = san;
     };
     // PINNED: the MFMAs are inline asm on accumulators pinned to AGPRs, so the
     // compiler inserts no MFMA hazard waits around them.  Fragments come from
@@ -594,7 +629,11 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
     }
     int kt = 0;
-    if constexpr (RING) {
+    if constexpr (RING && AX) {
+        // PHASE 2 while A of kt+3 exists, PHASE 1 (B of kt+2 only) for kt = KT-3
+        for (; kt < KT - 3; ++kt) stage.template operator()<2>(kt);
+        if (kt < KT - 2) stage.template operator()<1>(kt++);
+    } else if constexpr (RING) {
         // PHASE 2 while the stage its copies fill exists: kt+STAGES-1 (EARLY: kt+STAGES) < KT
         for (; kt < KT - (EARLY ? STAGES : STAGES - 1); ++kt) stage.template operator()<2>(kt);
     } else {

@@ -78,7 +78,8 @@ class Tile:
                          # place (one A fragment set), 4 MFMAs as asm on accumulators pinned to AGPRs,
                          # 8 copies of stage kt+STAGES issued right after stage kt's barrier, 16 (with 2) the
                          # next k-step's B reads front-loaded, 32 C staged through LDS and written with
-                         # row-contiguous 16-byte stores, 64 (with 32) those stores non-temporal
+                         # row-contiguous 16-byte stores, 64 (with 32) those stores non-temporal, 128 the A ring
+                         # one stage deeper than the B ring
     bt: int = 0          # B given transposed (Bt[N][K])
 
     kind = "tile"
@@ -97,12 +98,14 @@ class Tile:
         n += "_fb" if self.spread & 16 else ""
         n += "_le" if self.spread & 32 else ""
         n += "_nt" if self.spread & 64 else ""
+        n += "_ax" if self.spread & 128 else ""
         return n + ("_bt" if self.bt else "")
 
     # derived quantities, as in TilePipeCfg (csrc/tile_pipe_kernel.h)
     @property
     def lds_bytes(self) -> int:
-        return self.stages * (self.bm * self.bk * 2 + self.bk * self.bn * 2)
+        a_stages = self.stages + (1 if self.spread & 128 else 0)   # deeper A ring
+        return a_stages * self.bm * self.bk * 2 + self.stages * self.bk * self.bn * 2
 
     def derived(self):
         nw = self.wm * self.wn
@@ -162,7 +165,7 @@ def valid(c) -> bool:
     d = c.derived()
     if d["ksteps"] % 2 or d["wtm"] % c.mf or d["wtn"] % c.mf or d["tm"] < 1 or d["tn"] < 1:
         return False
-    if not 0 <= c.spread <= 127 or (c.spread & 2 and d["tm"] < 2) or (c.spread & 16 and not c.spread & 2):
+    if not 0 <= c.spread <= 255 or (c.spread & 2 and d["tm"] < 2) or (c.spread & 16 and not c.spread & 2):
         return False
     # LDS epilogue: the C tile fits in the stage buffers, power-of-two 16-byte chunks per sub-tile row;
     # non-temporal C stores only with it
@@ -170,6 +173,9 @@ def valid(c) -> bool:
     if c.spread & 32 and not (c.bm * c.bn * 2 <= c.lds_bytes and ((pow2(rch) and 4 <= rch <= 64) or rch == 12)):
         return False
     if c.spread & 64 and not c.spread & 32:
+        return False
+    # deeper A ring: ring loaders, early copies, in-place A, two B stages
+    if c.spread & 128 and not (c.loader in ("dma", "buf") and c.spread & 8 and c.spread & 2 and c.stages == 2):
         return False
     cb_ok = pow2(d["cb"]) or (d["cb"] % 8 == 0 and (c.bn * 2) % 256 == 128)   # e.g. BN = 192
     if not (pow2(d["ca"]) and cb_ok and d["cb"] >= 4):
@@ -319,6 +325,10 @@ def space() -> list:
     # barrier slot and copy stride around the chosen large-tile schedule, with the staged epilogue
     for bs, ds in ((8, 2), (32, 1), (40, 1)):
         out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", mf=16, spread=14 + 96))
+    # A ring one stage deeper than B's (160 KiB at 256x256x64): A copies get two stages to land
+    for bs, ds in ((8, 2), (16, 2), (32, 2)):
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", mf=16, spread=14 + 96 + 128))
+    out.append(Tile(256, 256, 64, 2, 2, 2, 4, 16, 2, "dma", mf=16, spread=30 + 96 + 128, bt=1))
     # front-loaded B reads (the B-transposed winner's flag) with the staged epilogue, for B[K][N]
     for bs in (8, 16, 32):
         out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, 2, "dma", mf=16, spread=30 + 96))
@@ -702,6 +712,7 @@ def main() -> int:
     ap.add_argument("--only", default=None, help="comma-separated sweep workload names for --run")
     ap.add_argument("--select", metavar="RESULTS", help="pick per-class defaults, write csrc/config_table.inc")
     ap.add_argument("--summary", default=None, help="Markdown summary path for --select")
+    ap.add_argument("--note", default="", help="extra paragraph for the --select summary")
     ap.add_argument("--ablation", metavar="RESULTS", help="write the tile-order / stages ablation tables")
     ap.add_argument("--ablation-out", default=os.path.join(ROOT, "profiles",
                                                            "ablation__tile_order_and_stages__gemm_workloads.md"))
@@ -726,6 +737,7 @@ def main() -> int:
                 "(`_le_nt`)%s." % (" --subset '%s'" % a.subset if a.subset else "",
                                    ", and the configurations of the space matching `%s`" % a.subset if a.subset else "")
                 ) if a.finalists else ""
+        note = "\n".join(x for x in (note, a.note) if x)
         print(json.dumps(select(a.select, summary_path=a.summary, note=note), indent=1))
     if a.ablation:
         ablation(a.ablation, a.ablation_out)
