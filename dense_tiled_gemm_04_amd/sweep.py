@@ -329,6 +329,9 @@ def space() -> list:
     for bs, ds in ((8, 2), (16, 2), (32, 2)):
         out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, ds, "dma", mf=16, spread=14 + 96 + 128))
     out.append(Tile(256, 256, 64, 2, 2, 2, 4, 16, 2, "dma", mf=16, spread=30 + 96 + 128, bt=1))
+    # ... and with front-loaded B reads for B[K][N] as well
+    for bs in (8, 16):
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, 2, "dma", mf=16, spread=30 + 96 + 128))
     # front-loaded B reads (the B-transposed winner's flag) with the staged epilogue, for B[K][N]
     for bs in (8, 16, 32):
         out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, 2, "dma", mf=16, spread=30 + 96))
@@ -478,7 +481,8 @@ def _reference_rows(A, B, bias, epilogue, rows):
     return r
 
 
-def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str | None = None) -> None:
+def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str | None = None,
+        repeat: int = 1) -> None:
     import ctypes
     import numpy as np
     import torch
@@ -534,29 +538,26 @@ def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str
         ref = _reference_rows(dA, dB, db, w.epilogue, rows)
         refh = ref.half().float()
         epi = epi_ids[w.epilogue]
-        for i, info in enumerate(infos):
-            if (info["name"], name) in done:
-                continue
-            if bt:
-                call = lambda *a: lib.gemm_f16_bt_with_config(a[0], a[1], a[2], a[3], a[4], w.K, a[5], w.K, a[6],
-                                                              a[7], w.N, a[8], a[9])
-            else:
-                call = lib.gemm_f16_with_config
+        if bt:
+            call = lambda *a: lib.gemm_f16_bt_with_config(a[0], a[1], a[2], a[3], a[4], w.K, a[5], w.K, a[6],
+                                                          a[7], w.N, a[8], a[9])
+        else:
+            call = lib.gemm_f16_with_config
 
+        def time_config(i):
+            """Sustained time per launch of config i, as the benchmark sees it: launches back to back (the
+            benchmark puts no event between them), since the power limit sets the clock within milliseconds
+            and the gaps of per-launch events would let the card rest.  From a short idle: >= 5 ms of warm-up,
+            then >= 25 ms in chunks of ~1 ms between event pairs.  Returns the sorted per-launch chunk times
+            (us) and leaves C written from the first copy of B, or None if the config cannot run the call."""
             def args(r=0):
                 return (i, w.M, w.N, w.K, dA.data_ptr(), dBs[r % len(dBs)].data_ptr(),
                         db.data_ptr() if db is not None else None, dC.data_ptr(), epi, stream.cuda_stream)
             st = call(*args())
             if st == 6:  # GEMM_ERR_UNSUPPORTED: this config cannot run this call
-                continue
+                return None
             if st != 0:
-                raise RuntimeError("config %s on %s: status %d" % (info["name"], name, st))
-            # Sustained timing, as the benchmark sees it: launches back to back (the
-            # benchmark puts no event between them), since the power limit sets the
-            # clock within milliseconds and the gaps of per-launch events would let
-            # the card rest.  From a short idle: >= 5 ms of warm-up, then >= 25 ms in
-            # chunks of ~1 ms between event pairs; the result is the median chunk's
-            # time per launch.
+                raise RuntimeError("config %s on %s: status %d" % (infos[i]["name"], name, st))
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for r in range(3):
@@ -580,16 +581,40 @@ def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str
                 evs.append((e0, e1))
             call(*args(0))   # the screened output comes from the first copy of B
             torch.cuda.synchronize()
-            us = sorted(a.elapsed_time(b) * 1e3 / per for a, b in evs)
-            med = us[len(us) // 2]
-            got = dC[rows].float()
-            diff = (got - refh)
-            rel = float(diff.norm() / refh.norm()) if float(refh.norm()) > 0 else float(diff.norm())
-            mx = float((diff.abs() / (1 + refh.abs())).max())
-            ok = bool(rel <= 2e-3 and mx <= 1e-2 and not torch.isnan(got).any())
+            return sorted(a.elapsed_time(b) * 1e3 / per for a, b in evs)
+
+        # With repeat > 1 the configurations are timed round-robin, repeat times each, so that a slow drift
+        # of the card's clock spreads over all of them; a record holds the median of the rounds' medians.
+        todo = [i for i, info in enumerate(infos) if (info["name"], name) not in done]
+        rounds = {i: [] for i in todo}
+        screen = {}
+        for rep in range(repeat):
+            for i in todo:
+                if i in screen and screen[i] is None:
+                    continue
+                us = time_config(i)
+                if us is None:
+                    screen[i] = None
+                    continue
+                rounds[i].append((us[len(us) // 2], us[0]))
+                if rep == 0:
+                    got = dC[rows].float()
+                    diff = (got - refh)
+                    rel = float(diff.norm() / refh.norm()) if float(refh.norm()) > 0 else float(diff.norm())
+                    mx = float((diff.abs() / (1 + refh.abs())).max())
+                    screen[i] = (rel, mx, bool(rel <= 2e-3 and mx <= 1e-2 and not torch.isnan(got).any()))
+        for i in todo:
+            if screen.get(i) is None:
+                continue
+            info = infos[i]
+            rel, mx, ok = screen[i]
+            meds = sorted(m for m, _ in rounds[i])
+            med = meds[len(meds) // 2]
             rec = {"config": info["name"], "idx": i, "workload": name, "classes": classes, "median_us": med,
-                   "min_us": us[0], "tflops": 2.0 * w.M * w.N * w.K / med / 1e6, "rel_fro_vs_fp32": rel,
-                   "max_elem_vs_fp32": mx, "ok": ok, "info": info}
+                   "min_us": min(m for _, m in rounds[i]), "tflops": 2.0 * w.M * w.N * w.K / med / 1e6,
+                   "rel_fro_vs_fp32": rel, "max_elem_vs_fp32": mx, "ok": ok, "info": info}
+            if repeat > 1:
+                rec["round_medians_us"] = [m for m, _ in rounds[i]]
             out.write(json.dumps(rec) + "\n")
             out.flush()
             print("%-28s %-48s %9.1f us %7.1f TF %s" % (name, info["name"], med, rec["tflops"],
@@ -710,6 +735,8 @@ def main() -> int:
                          "only those)")
     ap.add_argument("--run", metavar="RESULTS", help="time every configuration (GPU); JSONL, resumable")
     ap.add_argument("--only", default=None, help="comma-separated sweep workload names for --run")
+    ap.add_argument("--repeat", type=int, default=1,
+                    help="--run: time the configurations round-robin this many times per workload")
     ap.add_argument("--select", metavar="RESULTS", help="pick per-class defaults, write csrc/config_table.inc")
     ap.add_argument("--summary", default=None, help="Markdown summary path for --select")
     ap.add_argument("--note", default="", help="extra paragraph for the --select summary")
@@ -730,7 +757,7 @@ def main() -> int:
     if a.build:
         build_sweep_lib(configs=chosen)
     if a.run:
-        run(a.run, only=a.only)
+        run(a.run, only=a.only, repeat=a.repeat)
     if a.select:
         note = ("Focused re-sweep (`--build --finalists%s`, then `--run`): the configurations of the table in force "
                 "before it, plus\ntheir variants with C staged through LDS (`_le`) and with non-temporal C stores "
