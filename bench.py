@@ -64,6 +64,33 @@ def kernel_source_digest(family: str = "gemm") -> str:
     return h.hexdigest()
 
 
+def interleaved_ms(torch, stream, ours, theirs, launch_ms: float, rounds: int = 6, chunk_ms: float = 2.0):
+    """Ours against the vendor's on equal terms: alternating chunks of ~chunk_ms of back-to-back launches of
+    each step function, every chunk between its own pair of HIP events on the launch stream, after one untimed
+    round.  The power limiter sets the clock within milliseconds, so a vendor loop timed right after ours runs
+    on a hotter card than ours did; alternating puts both through the same states.  Returns the median ms per
+    launch of each side's chunks."""
+    n = max(1, int(round(chunk_ms / max(launch_ms, 1e-3))))
+    evs = ([], [])
+    i = 0
+    for r in range(rounds + 1):
+        for k, f in enumerate((ours, theirs)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                f(i)
+                i += 1
+            e1.record(stream)
+            if r > 0:
+                evs[k].append((e0, e1))
+    torch.cuda.synchronize()
+
+    def med(pairs):
+        t = sorted(a.elapsed_time(b) / n for a, b in pairs)
+        return t[len(t) // 2]
+    return med(evs[0]), med(evs[1])
+
+
 def load_traffic(workload: str, kernel: str):
     """HBM bytes per launch recorded from rocprofv3 counters, if still valid."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -218,6 +245,7 @@ def bench_softmax(args, g, torch, w) -> int:
     t1.record(stream)
     torch.cuda.synchronize()
     torch_ms = t0.elapsed_time(t1) / n_t
+    il_ours, il_torch = interleaved_ms(torch, stream, step, lambda i: torch.softmax(dXs[i % rotate], dim=-1), ms)
 
     kernel = "softmax_" + g.softmax_path(w.rows, w.cols)
     roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
@@ -242,7 +270,9 @@ def bench_softmax(args, g, torch, w) -> int:
         "roofline": roof,
         "cpu_baseline": cpu,
         "context": {"torch_softmax_ms": round(torch_ms, 6),
-                    "torch_GBps": round(w.algorithmic_bytes / (torch_ms * 1e-3) / 1e9, 1)},
+                    "torch_GBps": round(w.algorithmic_bytes / (torch_ms * 1e-3) / 1e9, 1),
+                    "interleaved": {"ours_ms": round(il_ours, 6), "torch_ms": round(il_torch, 6),
+                                    "torch_over_ours": round(il_torch / il_ours, 3)}},
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -313,7 +343,7 @@ def bench_attention(args, g, torch, w) -> int:
     tflops = w.flops / (ms * 1e-3) / 1e12
 
     # context: PyTorch's scaled dot-product attention on the same tensors, fused backends only
-    torch_ms, backend = None, None
+    torch_ms, backend, il = None, None, None
     try:
         from torch.nn.attention import SDPBackend, sdpa_kernel
         with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
@@ -330,6 +360,7 @@ def bench_attention(args, g, torch, w) -> int:
             torch.cuda.synchronize()
             torch_ms = t0.elapsed_time(t1) / n_t
             backend = "flash/efficient"
+            il = interleaved_ms(torch, stream, lambda i: step(), lambda i: f(), ms)
     except RuntimeError as e:
         backend = "unavailable: %s" % str(e).splitlines()[0][:120]
 
@@ -356,7 +387,9 @@ def bench_attention(args, g, torch, w) -> int:
         "roofline": roof,
         "cpu_baseline": cpu,
         "context": {"torch_sdpa_ms": round(torch_ms, 6) if torch_ms else None, "torch_sdpa_backend": backend,
-                    "torch_tflops": round(w.flops / (torch_ms * 1e-3) / 1e12, 3) if torch_ms else None},
+                    "torch_tflops": round(w.flops / (torch_ms * 1e-3) / 1e12, 3) if torch_ms else None,
+                    "interleaved": {"ours_ms": round(il[0], 6), "torch_ms": round(il[1], 6),
+                                    "torch_over_ours": round(il[1] / il[0], 3)} if il else None},
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -474,6 +507,7 @@ def main() -> int:
     t1.record(stream)
     torch.cuda.synchronize()
     torch_ms = t0.elapsed_time(t1) / n_t
+    il_ours, il_torch = interleaved_ms(torch, stream, step, torch_step, ms)
 
     traffic = load_traffic(w.name + ("_bt" if bt else ""), cfg["name"])
     if hbm_bound:
@@ -511,7 +545,9 @@ def main() -> int:
         "cpu_baseline": cpu,
         "context": {("torch_linear_ms" if bt else "torch_matmul_ms"): round(torch_ms, 6),
                     "torch_tflops": round(w.flops / (torch_ms * 1e-3) / 1e12, 3),
-                    "algorithmic_GBps": round(gbs, 1)},
+                    "algorithmic_GBps": round(gbs, 1),
+                    "interleaved": {"ours_ms": round(il_ours, 6), "torch_ms": round(il_torch, 6),
+                                    "torch_over_ours": round(il_torch / il_ours, 3)}},
     }
     print(json.dumps(out), flush=True)
     return 0
