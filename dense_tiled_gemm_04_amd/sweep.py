@@ -332,6 +332,11 @@ def space() -> list:
     # ... and with front-loaded B reads for B[K][N] as well
     for bs in (8, 16):
         out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, 2, "dma", mf=16, spread=30 + 96 + 128))
+    # the same large schedules with the copies issued as buffer loads (the vendor's copy form)
+    for bs in (8, 16):
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, 2, "buf", mf=16, spread=14 + 96))
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, 2, "buf", mf=16, spread=30 + 96, bt=1))
+        out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, 2, "buf", mf=16, spread=30 + 96 + 128, bt=1))
     # front-loaded B reads (the B-transposed winner's flag) with the staged epilogue, for B[K][N]
     for bs in (8, 16, 32):
         out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, 2, "dma", mf=16, spread=30 + 96))
