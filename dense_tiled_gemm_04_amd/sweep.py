@@ -185,7 +185,8 @@ def valid(c) -> bool:
     ps = d["per_stage"]
     if c.stages < 2 or ps * (c.stages - 1) > 63:
         return False
-    if c.lds_bytes * c.wpe > LDS_PER_CU:
+    # wpe is waves per SIMD; a workgroup of nw waves puts nw / 4 of them on each SIMD
+    if d["nw"] % 4 or c.wpe % (d["nw"] // 4) or c.lds_bytes * (c.wpe // (d["nw"] // 4)) > LDS_PER_CU:
         return False
     last = (d["ksteps"] - 1) * d["nmma"] + c.bslot
     if not (0 <= c.bslot and c.bslot + 1 < d["nmma"]):
@@ -332,6 +333,12 @@ def space() -> list:
     # ... and with front-loaded B reads for B[K][N] as well
     for bs in (8, 16):
         out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, 2, "dma", mf=16, spread=30 + 96 + 128))
+    # eight-wave 256x256 tiles (two waves per SIMD, 128x64 or 64x128 per wave): one wave's MFMAs can cover
+    # the other's waits, for 50% more fragment reads per MFMA
+    for wm, wn in ((2, 4), (4, 2)):
+        for bs in (4, 12):
+            out.append(Tile(256, 256, 64, wm, wn, 2, 4, bs, 2, "dma", wpe=2, mf=16, spread=14 + 96))
+        out.append(Tile(256, 256, 64, wm, wn, 2, 4, 8, 2, "dma", wpe=2, mf=16, spread=30 + 96, bt=1))
     # the same large schedules with the copies issued as buffer loads (the vendor's copy form)
     for bs in (8, 16):
         out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, 2, "buf", mf=16, spread=14 + 96))
