@@ -339,6 +339,19 @@ def space() -> list:
         for bs in (4, 12):
             out.append(Tile(256, 256, 64, wm, wn, 2, 4, bs, 2, "dma", wpe=2, mf=16, spread=14 + 96))
         out.append(Tile(256, 256, 64, wm, wn, 2, 4, 8, 2, "dma", wpe=2, mf=16, spread=30 + 96, bt=1))
+    # ... their barrier slot, copy stride and flags (32 MFMA slots per k-step)
+    for bs, ds in ((0, 2), (8, 2), (16, 2), (4, 1), (12, 1), (20, 1), (4, 3)):
+        out.append(Tile(256, 256, 64, 2, 4, 2, 4, bs, ds, "dma", wpe=2, mf=16, spread=14 + 96))
+    out.append(Tile(256, 256, 64, 2, 4, 2, 4, 4, 2, "dma", wpe=2, mf=16, spread=30 + 96))
+    out.append(Tile(256, 256, 64, 2, 4, 2, 4, 4, 2, "dma", wpe=2, mf=16, spread=14 + 32))
+    for bs, ds in ((4, 2), (12, 2), (16, 2), (8, 1)):
+        out.append(Tile(256, 256, 64, 2, 4, 2, 4, bs, ds, "dma", wpe=2, mf=16, spread=30 + 96, bt=1))
+    out.append(Tile(256, 256, 64, 2, 4, 2, 4, 8, 2, "dma", wpe=2, mf=16, spread=14 + 96, bt=1))
+    # wider copy strides (the copies of a stage spread over more of its slots)
+    for bs, ds in ((0, 3), (8, 3), (0, 4)):
+        out.append(Tile(256, 256, 64, 2, 4, 2, 4, bs, ds, "dma", wpe=2, mf=16, spread=14 + 96))
+    for bs, ds in ((4, 3), (8, 3), (0, 4)):
+        out.append(Tile(256, 256, 64, 2, 4, 2, 4, bs, ds, "dma", wpe=2, mf=16, spread=30 + 96, bt=1))
     # the same large schedules with the copies issued as buffer loads (the vendor's copy form)
     for bs in (8, 16):
         out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, 2, "buf", mf=16, spread=14 + 96))
