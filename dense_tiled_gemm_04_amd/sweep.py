@@ -352,6 +352,12 @@ def space() -> list:
         out.append(Tile(256, 256, 64, 2, 4, 2, 4, bs, ds, "dma", wpe=2, mf=16, spread=14 + 96))
     for bs, ds in ((4, 3), (8, 3), (0, 4)):
         out.append(Tile(256, 256, 64, 2, 4, 2, 4, bs, ds, "dma", wpe=2, mf=16, spread=30 + 96, bt=1))
+    # flags around the stride-3 schedules: front-loaded B for B[K][N], plain B reads for Bt, cached C stores
+    for bs in (4, 8):
+        out.append(Tile(256, 256, 64, 2, 4, 2, 4, bs, 3, "dma", wpe=2, mf=16, spread=30 + 96))
+    out.append(Tile(256, 256, 64, 2, 4, 2, 4, 4, 3, "dma", wpe=2, mf=16, spread=14 + 32))
+    out.append(Tile(256, 256, 64, 2, 4, 2, 4, 4, 3, "dma", wpe=2, mf=16, spread=14 + 96, bt=1))
+    out.append(Tile(256, 256, 64, 2, 4, 2, 4, 4, 3, "dma", wpe=2, mf=16, spread=30 + 32, bt=1))
     # the same large schedules with the copies issued as buffer loads (the vendor's copy form)
     for bs in (8, 16):
         out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, 2, "buf", mf=16, spread=14 + 96))
