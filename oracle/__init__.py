@@ -1,5 +1,5 @@
 """CPU oracle for the fp16 GEMM + fused bias / bias+GELU epilogue, the row-wise
-softmax and the attention forward pass (Python side).
+softmax, the attention forward pass and the fp32 vector add (Python side).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  It shares no code with
@@ -68,6 +68,8 @@ def _load():
     lib.oracle_attention_f16_rows.argtypes = [i64, i64, i64, i64, i64, p, p, p, ctypes.c_int, ctypes.c_double, i64,
                                               p, p, p, ctypes.c_int]
     lib.oracle_attention_f16_rows.restype = ctypes.c_int
+    lib.oracle_vector_add_f32.argtypes = [i64, p, p, p]
+    lib.oracle_vector_add_f32.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -191,6 +193,20 @@ def attention_rows(Q, K, V, rows, causal: bool = False, scale: float | None = No
         raise RuntimeError("oracle_attention_f16_rows failed (%d)" % rc)
     O = O.view(np.float16)
     return (O, Od) if want_y else O
+
+
+def vector_add(a, b) -> np.ndarray:
+    """C = A + B on float32 vectors, each element the correctly rounded binary32 sum (see the C file)."""
+    lib = _load()
+    a = np.ascontiguousarray(a, dtype=np.float32).reshape(-1)
+    b = np.ascontiguousarray(b, dtype=np.float32).reshape(-1)
+    if a.shape != b.shape:
+        raise ValueError("length mismatch")
+    c = np.empty_like(a)
+    rc = lib.oracle_vector_add_f32(a.shape[0], _ptr(a), _ptr(b), _ptr(c))
+    if rc != 0:
+        raise RuntimeError("oracle_vector_add_f32 failed (%d)" % rc)
+    return c
 
 
 def f16_decode(bits) -> np.ndarray:

@@ -203,6 +203,28 @@ void oracle_gelu_n(const double* x, double* out, int64_t n) {
     for (int64_t t = 0; t < n; ++t) out[t] = oracle_gelu(x[t]);
 }
 
+/*
+ * fp32 vector add, the tutorial's first kernel: C[i] = A[i] + B[i] on float32
+ * vectors (blog post "Designing High-Performance GPU Kernels with TileLang",
+ * section "Step 3", whose example kernel adds two float32 vectors element by
+ * element; news article on TileLang kernel design, paragraph on the vector-add
+ * kernel).  The pages fix the precision: float32 in and out, so each result
+ * is the IEEE binary32 sum, rounded to nearest-even.  It is formed here as the
+ * fp64 sum of the two values, rounded once to binary32.  Rounding an exact sum
+ * first to binary64 and then to binary32 gives the correctly rounded binary32
+ * sum, because 53 >= 2*24 + 2 (S. A. Figueroa, "When is double rounding
+ * innocuous?", ACM SIGNUM Newsletter 30(3), 1995).  NaN inputs give NaN.
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_vector_add_f32(int64_t n, const float* A, const float* B, float* C) {
+    if (n < 0 || (n > 0 && (!A || !B || !C))) return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        const double s = (double)A[i] + (double)B[i];
+        C[i] = (float)s;
+    }
+    return 0;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

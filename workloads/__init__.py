@@ -199,6 +199,21 @@ def random_f16(seed: int, shape, lo: float = -1.0, hi: float = 1.0) -> np.ndarra
     return rng.uniform(lo, hi, size=shape).astype(np.float16)
 
 
+def random_f32_bits(seed: int, n: int) -> np.ndarray:
+    """n float32 values with uniformly random bit patterns (every class: normal, subnormal, zero, inf, NaN)."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32).view(np.float32)
+
+
+def make_vector_add_inputs(n: int, seed: int = 12):
+    """Two float32 vectors ~ N(0, 1) of length n for the vector add (the pages' first kernel adds two float32
+    vectors; they give no distribution)."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal(n).astype(np.float32)
+    b = rng.standard_normal(n).astype(np.float32)
+    return a, b
+
+
 def input_digest(*arrays) -> str:
     h = hashlib.sha256()
     for a in arrays:
