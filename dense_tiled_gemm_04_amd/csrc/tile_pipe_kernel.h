@@ -646,6 +646,16 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         pin_order();
     }
 
+    // The epilogue's per-lane index math starts from a thread id that passes
+    // through an empty asm here, after the K loop, so the compiler cannot
+    // hoist any of it above the loop, where its registers would add to the
+    // loop's (one such hoisted address once pushed a bias-epilogue kernel past
+    // 256 VGPRs into a scratch spill).
+    int tid_e = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid_e));
+    const int lane_e = tid_e & 63, wave_e = tid_e >> 6;
+    const int wm_e = wave_e / WN, wn_e = wave_e % WN;
+
     // Epilogue on the accumulators, one write of C.  Lane l holds, of block
     // (mi, ni), the 4 consecutive columns
     //   MF = 32, register 4*r4 + e: C[mi*32 + l%32][ni*32 + 8*r4 + 4*(l/32) + e]
@@ -675,14 +685,14 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     // (192 bytes): rows r and r + 4 start at the same bank, so XOR with bits 2-3
     // of r, which keeps a chunk inside its aligned group of 4 and so inside the row.
     auto c_swz = [&](int r) { return RCH_P2 ? (r & ((RCH < 16 ? RCH : 16) - 1)) : ((r >> 2) & 3); };
-    GK_LDS char* const c_lds = a_lds + wave * (WTM * WTN * 2);  // this wave's sub-tile [WTM][WTN] fp16
+    GK_LDS char* const c_lds = a_lds + wave_e * (WTM * WTN * 2);  // this wave's sub-tile [WTM][WTN] fp16
     if constexpr (LDS_EPI) __syncthreads();  // every wave has finished reading the last stage
 #pragma unroll
     for (int ni = 0; ni < TN; ++ni) {
 #pragma unroll
         for (int r4 = 0; r4 < NQ; ++r4) {
-            const int nc = ni * MF + (MF == 32 ? 8 * r4 + 4 * (lane >> 5) : 4 * (lane >> 4));  // column in the sub-tile
-            const int n = n0 + wn * WTN + nc;
+            const int nc = ni * MF + (MF == 32 ? 8 * r4 + 4 * (lane_e >> 5) : 4 * (lane_e >> 4));  // column in the sub-tile
+            const int n = n0 + wn_e * WTN + nc;
             const bool quad = n + 4 <= N;
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (EPI != EPI_NONE) {
@@ -698,14 +708,14 @@ gemm_tile_pipe_kernel(GemmArgs p) {
             }
 #pragma unroll
             for (int mi = 0; mi < TM; ++mi) {
-                const int rr = mi * MF + (lane % MF);  // row in the sub-tile
+                const int rr = mi * MF + (lane_e % MF);  // row in the sub-tile
                 f16x4 o;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[e] = (f16)apply_epilogue<EPI>(acc[mi][ni][4 * r4 + e], bv[e]);
                 if constexpr (LDS_EPI) {
                     *(GK_LDS f16x4*)(c_lds + rr * WTN * 2 + (((nc >> 3) ^ c_swz(rr)) << 4) + ((nc & 7) << 1)) = o;
                 } else {
-                    const int m = m0 + wm * WTM + rr;
+                    const int m = m0 + wm_e * WTM + rr;
                     if (m >= M || n >= N) continue;
                     f16* dst = p.C + (size_t)m * ldc + n;
                     if (quad) {
@@ -726,10 +736,10 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         static_assert((WTM * RCH) % 64 == 0, "whole store instructions per sub-tile");
 #pragma unroll
         for (int it = 0; it < WTM * RCH / 64; ++it) {
-            const int lc = it * 64 + lane;             // chunk of the sub-tile, row-major
+            const int lc = it * 64 + lane_e;             // chunk of the sub-tile, row-major
             const int rr = lc / RCH, c = lc % RCH;
             const f16x8 v = *(const GK_LDS f16x8*)(c_lds + rr * WTN * 2 + ((c ^ c_swz(rr)) << 4));
-            const int m = m0 + wm * WTM + rr, n = n0 + wn * WTN + 8 * c;
+            const int m = m0 + wm_e * WTM + rr, n = n0 + wn_e * WTN + 8 * c;
             if (m >= M || n >= N) continue;
             f16* dst = p.C + (size_t)m * ldc + n;
             if (n + 8 <= N) {

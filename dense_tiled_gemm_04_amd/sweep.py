@@ -72,7 +72,8 @@ class Tile:
     dstride: int
     loader: str          # "dma" | "buf" | "reg"
     cslot: int = 0
-    wpe: int = 1         # waves per SIMD (= workgroups per CU, 4-wave workgroups)
+    wpe: int = 1         # waves per SIMD; a workgroup of wm*wn waves puts wm*wn/4 on each SIMD, so a CU holds
+                         # wpe / (wm*wn/4) workgroups (4 waves: wpe workgroups; 8 waves at wpe 2: one)
     mf: int = 32         # MFMA shape: 32 -> 32x32x16, 16 -> 16x16x32
     spread: int = 0      # schedule flags: 1 LDS reads spread evenly over a k-step's slots, 2 A refilled in
                          # place (one A fragment set), 4 MFMAs as asm on accumulators pinned to AGPRs,

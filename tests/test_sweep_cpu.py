@@ -24,6 +24,22 @@ def test_budget_filter():
     assert sweep.valid(sweep.Skinny(1, 8)) and not sweep.valid(sweep.Skinny(1, 9))
 
 
+def test_eight_wave_budget_rules():
+    # eight waves (2 x 4) put two on each SIMD: wpe must be a multiple of 2, and wpe 2 means one workgroup per CU
+    t = dict(bm=256, bn=256, bk=64, wm=2, wn=4, stages=2, group=4, bslot=4, dstride=3, loader="dma", mf=16,
+             spread=110)
+    assert sweep.valid(sweep.Tile(**t, wpe=2))
+    assert not sweep.valid(sweep.Tile(**t, wpe=1))
+    # wpe 4 would put two such workgroups (2 x 128 KiB of LDS) on one CU
+    assert not sweep.valid(sweep.Tile(**t, wpe=4))
+    # the 4 x 2 layout (64 x 128 per wave) needs two B fragment sets of 8: past the 256 registers per lane
+    assert not sweep.valid(sweep.Tile(**dict(t, wm=4, wn=2), wpe=2))
+    # three stages of 256 x 256 x 64 (192 KiB) exceed the LDS of the CU even for one workgroup
+    assert not sweep.valid(sweep.Tile(**dict(t, stages=3), wpe=2))
+    # a workgroup whose wave count is not a multiple of the 4 SIMDs is rejected
+    assert not sweep.valid(sweep.Tile(256, 256, 64, 2, 3, 2, 4, 4, 3, "dma", wpe=2, mf=16, spread=110))
+
+
 def test_schedule_constraints_mirror_kernel():
     # barrier slot must leave room in the last k-step for the next stage's reads
     assert not sweep.valid(sweep.Tile(128, 128, 64, 2, 2, 2, 4, 3, 1, "dma"))   # 4 MFMAs per k-step
