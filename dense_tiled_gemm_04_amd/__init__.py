@@ -35,6 +35,7 @@ EXPORTS = [
     "gemm_f16_ex", "gemm_f16_select_config_ex", "gemm_f16_with_config_ex",
     "gemm_f16_bt", "gemm_f16_bt_select_config", "gemm_f16_bt_with_config",
     "softmax_rows_f16", "softmax_rows_f16_path", "flash_attn_fwd_f16",
+    "gemm_status_string", "gemm_f16_time",
 ]
 SOFTMAX_PATHS = {0: "none", 1: "wave", 2: "workgroup", 3: "online"}
 
@@ -77,6 +78,10 @@ def load():
     lib.gemm_f16_bt_select_config.restype = i32
     lib.gemm_f16_status_string.argtypes = [i32]
     lib.gemm_f16_status_string.restype = ctypes.c_char_p
+    lib.gemm_status_string.argtypes = [i32]
+    lib.gemm_status_string.restype = ctypes.c_char_p
+    lib.gemm_f16_time.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, i32, vp, i32, ctypes.POINTER(ctypes.c_float)]
+    lib.gemm_f16_time.restype = i32
     lib.gemm_f16_num_configs.argtypes = []
     lib.gemm_f16_num_configs.restype = i32
     lib.gemm_f16_config_info.argtypes = [i32, ctypes.c_char_p, i32]
@@ -149,6 +154,13 @@ def gemm_f16_bt_raw(M, N, K, A, lda, Bt, ldb, bias, C, ldc, epilogue: int, strea
 
 def select_config_bt_raw(M, N, K, A, lda, Bt, ldb, bias, C, ldc, epilogue: int) -> int:
     return int(load().gemm_f16_bt_select_config(M, N, K, A, lda, Bt, ldb, bias, C, ldc, epilogue))
+
+
+def gemm_f16_time_raw(M, N, K, A, B, bias, C, epilogue: int, iters: int, stream=0, config: int = -1):
+    """(status, median ms per launch) of gemm_f16_time: `iters` event-bracketed launches after one untimed."""
+    out = ctypes.c_float(-1.0)
+    st = int(load().gemm_f16_time(config, M, N, K, A, B, bias, C, epilogue, stream, iters, ctypes.byref(out)))
+    return st, float(out.value)
 
 
 def softmax_rows_raw(rows, cols, X, Y, stream=0) -> int:

@@ -5,6 +5,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "gemm_f16.h"
 #include "skinny_kernel.h"
 #include "tile_pipe_kernel.h"
@@ -196,8 +199,6 @@ int run(const Config& cfg, const Call& c, hipStream_t stream) {
     a.lda = (int)c.lda;
     a.ldb = (int)c.ldb;
     a.ldc = (int)c.ldc;
-    a.k_split = 1;
-    a.partial = nullptr;
     if (cfg.kind == KIND_SKINNY) {
         a.tiles_m = 1;
         a.tiles_n = (int)((c.N + SK_BN - 1) / SK_BN);
@@ -247,6 +248,8 @@ const char* gemm_f16_status_string(int status) {
         default: return "GEMM_ERR_UNKNOWN";
     }
 }
+
+const char* gemm_status_string(int status) { return gemm_f16_status_string(status); }
 
 int gemm_f16_num_configs(void) { return kNumConfigs; }
 
@@ -342,6 +345,51 @@ int gemm_f16_bt_with_config(int idx, int64_t M, int64_t N, int64_t K, const void
 int gemm_f16(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias, void* C, int epilogue,
              void* stream) {
     return gemm_f16_ex(M, N, K, A, K, B, N, bias, C, N, epilogue, stream);
+}
+
+int gemm_f16_time(int idx, int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias, void* C,
+                  int epilogue, void* stream, int iters, float* median_ms) {
+    Call c{M, N, K, A, B, bias, C, epilogue, K, N, N};
+    int st = validate(c);
+    if (st != GEMM_OK) return st;
+    if (!median_ms) return GEMM_ERR_NULL_POINTER;
+    if (iters < 1 || iters > GEMM_TIME_MAX_ITERS) return GEMM_ERR_INVALID_DIM;
+    if (idx < -1 || idx >= kNumConfigs) return GEMM_ERR_NO_CONFIG;
+    if (M == 0 || N == 0) {
+        *median_ms = 0.0f;
+        return GEMM_OK;
+    }
+    const int cfg = idx < 0 ? pick_default(c) : idx;
+    if (!supports(kConfigs[cfg], c)) return GEMM_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    // iters + 1 events on the stream: event i before launch i, event i + 1 after it
+    std::vector<hipEvent_t> ev;
+    ev.reserve((size_t)iters + 1);
+    st = GEMM_OK;
+    for (int i = 0; i <= iters; ++i) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) {
+            st = GEMM_ERR_LAUNCH;
+            break;
+        }
+        ev.push_back(e);
+    }
+    if (st == GEMM_OK) st = run(kConfigs[cfg], c, s);  // one untimed launch
+    if (st == GEMM_OK && hipEventRecord(ev[0], s) != hipSuccess) st = GEMM_ERR_LAUNCH;
+    for (int i = 0; st == GEMM_OK && i < iters; ++i) {
+        st = run(kConfigs[cfg], c, s);
+        if (st == GEMM_OK && hipEventRecord(ev[i + 1], s) != hipSuccess) st = GEMM_ERR_LAUNCH;
+    }
+    if (st == GEMM_OK && hipEventSynchronize(ev[iters]) != hipSuccess) st = GEMM_ERR_LAUNCH;
+    std::vector<float> t((size_t)iters);
+    for (int i = 0; st == GEMM_OK && i < iters; ++i)
+        if (hipEventElapsedTime(&t[i], ev[i], ev[i + 1]) != hipSuccess) st = GEMM_ERR_LAUNCH;
+    if (st != GEMM_OK && !ev.empty()) hipStreamSynchronize(s);  // no event may be destroyed while pending
+    for (hipEvent_t e : ev) hipEventDestroy(e);
+    if (st != GEMM_OK) return st;
+    std::sort(t.begin(), t.end());
+    *median_ms = (iters % 2) ? t[iters / 2] : 0.5f * (t[iters / 2 - 1] + t[iters / 2]);
+    return GEMM_OK;
 }
 
 int vector_add_f32(int64_t n, const float* A, const float* B, float* C, void* stream) {

@@ -121,8 +121,37 @@ int gemm_f16_bt(int64_t M, int64_t N, int64_t K,
                 const void* bias, void* C, int64_t ldc,
                 int epilogue, void* stream);
 
-/* Static, NUL-terminated name of a status code ("GEMM_OK", ...). */
+/* Static, NUL-terminated name of a status code ("GEMM_OK", ...).  The two
+ * names are the same function. */
 const char* gemm_f16_status_string(int status);
+const char* gemm_status_string(int status);
+
+/*
+ * Latency of the product, the way the tutorial's timing utility measures a
+ * kernel: the median over repeated launches, each bracketed by events on the
+ * stream (TileLang blog post "Designing High-Performance GPU Kernels with
+ * TileLang", section "Step 2").
+ *
+ * Runs gemm_f16's product (same arguments and layout) once untimed, then
+ * `iters` times back to back on `stream`, with an event recorded before the
+ * first launch and after each one; *median_ms receives the median of the
+ * `iters` per-launch times in milliseconds (the mean of the middle two for an
+ * even count).  idx = -1 launches the configuration gemm_f16 would pick; idx
+ * >= 0 forces configuration idx (GEMM_ERR_NO_CONFIG if out of range,
+ * GEMM_ERR_UNSUPPORTED if it cannot run the call).  C is written iters + 1
+ * times with the same result.
+ *
+ * Unlike every other entry point this call is synchronous: it returns after
+ * the last launch has finished.  All arguments are validated before any HIP
+ * call: besides gemm_f16's checks, median_ms NULL is GEMM_ERR_NULL_POINTER and
+ * iters outside [1, GEMM_TIME_MAX_ITERS] is GEMM_ERR_INVALID_DIM.  M == 0 or
+ * N == 0 launches nothing and reports 0.  A failure of an event call is
+ * GEMM_ERR_LAUNCH.  The events are created and destroyed inside the call.
+ */
+#define GEMM_TIME_MAX_ITERS 100000
+int gemm_f16_time(int idx, int64_t M, int64_t N, int64_t K,
+                  const void* A, const void* B, const void* bias, void* C,
+                  int epilogue, void* stream, int iters, float* median_ms);
 
 /*
  * Kernel configurations compiled into the library (the offline sweep space;

@@ -200,3 +200,35 @@ def test_b_transposed_validation_and_dispatch():
             assert g.gemm_f16_raw(256, 256, 256, FAKE, FAKE, None, FAKE, 0, 0, config=c["idx"]) == 6
         else:
             assert bt(256, 256, 256, FAKE, 256, FAKE, 256, None, FAKE, 256, 0, config=c["idx"]) == 6
+
+
+def test_status_string_alias():
+    lib = ctypes.CDLL(g.LIB_PATH)
+    lib.gemm_status_string.restype = ctypes.c_char_p
+    lib.gemm_status_string.argtypes = [ctypes.c_int]
+    for code, name in g.STATUS.items():
+        assert lib.gemm_status_string(code).decode() == name
+    assert lib.gemm_status_string(-3).decode() == "GEMM_ERR_UNKNOWN"
+
+
+def test_time_helper_validates_before_any_hip_call():
+    # every one of these returns before the first HIP call, so it runs without a GPU
+    lib = g.load()
+    out = ctypes.c_float(-7.0)
+    ref = ctypes.byref(out)
+
+    def t(idx, M, N, K, A, B, bias, C, epi, iters, med=ref):
+        return lib.gemm_f16_time(idx, M, N, K, A, B, bias, C, epi, None, iters, med)
+
+    assert t(-1, 4, 4, 4, FAKE, FAKE, None, FAKE, 0, 0) == 1             # iters < 1
+    assert t(-1, 4, 4, 4, FAKE, FAKE, None, FAKE, 0, 100001) == 1        # iters > GEMM_TIME_MAX_ITERS
+    assert t(-1, 4, 4, 4, FAKE, FAKE, None, FAKE, 0, 5, None) == 2       # median_ms NULL
+    assert t(g.num_configs(), 4, 4, 4, FAKE, FAKE, None, FAKE, 0, 5) == 5
+    assert t(-2, 4, 4, 4, FAKE, FAKE, None, FAKE, 0, 5) == 5
+    assert t(-1, -4, 4, 4, FAKE, FAKE, None, FAKE, 0, 5) == 1
+    assert t(-1, 4, 4, 4, FAKE, FAKE, None, FAKE, 9, 5) == 3
+    assert t(-1, 4, 4, 4, None, FAKE, None, FAKE, 0, 5) == 2
+    assert t(-1, 4, 4, 4, FAKE, FAKE, None, FAKE, 1, 5) == 2             # bias epilogue without bias
+    assert t(-1, 4, 4, 4, FAKE + 1, FAKE, None, FAKE, 0, 5) == 7
+    assert out.value == -7.0                                             # untouched on every error
+    assert t(-1, 0, 4, 4, None, None, None, None, 0, 5) == 0 and out.value == 0.0   # empty: no launch
