@@ -74,27 +74,34 @@ def test_constant_values_and_peaked_scores(lib):
         assert_parity(run(lib, Q, K, V2, causal), ref, ("peaked", causal))
 
 
-def _sample_rows(B, H, Nq, seed, n_random=192):
-    rng = np.random.default_rng(seed)
-    per_head = [0, 1, 127, 128, Nq // 2, Nq - 2, Nq - 1]
-    rows = set()
-    for b, h in ((0, 0), (B - 1, H - 1), (B // 2, H // 2)):
-        for i in per_head:
-            if 0 <= i < Nq:
-                rows.add((b * H + h) * Nq + i)
-    rows.update(rng.integers(0, B * H * Nq, n_random).tolist())
-    return np.array(sorted(rows), dtype=np.int64)
+def _slab_rows(w, max_slabs=8):
+    """Flat row indices of whole (batch, head) slabs: every slab when there are at most max_slabs of them,
+    else the first, the last, the middle and seeded others, max_slabs in all."""
+    nslab = w.B * w.H
+    if nslab <= max_slabs:
+        slabs = list(range(nslab))
+    else:
+        rng = np.random.default_rng(w.seed)
+        pick = {0, nslab - 1, (w.B // 2) * w.H + w.H // 2}
+        while len(pick) < max_slabs:
+            pick.add(int(rng.integers(0, nslab)))
+        slabs = sorted(pick)
+    return slabs, np.concatenate([np.arange(sl * w.Nq, (sl + 1) * w.Nq, dtype=np.int64) for sl in slabs])
 
 
 @pytest.mark.parametrize("name", list(workloads.ATTENTION_WORKLOADS))
-def test_workloads_sampled(lib, name):
+def test_workloads_whole_slabs(lib, name):
+    # Whole (batch, head) slabs of the full-size workloads: every query row of a slab against the oracle.
+    # The two small workloads (32 and 8 slabs) are covered completely.
     w = workloads.ATTENTION_WORKLOADS[name]
     Q, K, V = workloads.make_attention_inputs(w)
     got = run(lib, Q, K, V, w.causal).reshape(-1, w.D)
-    rows = _sample_rows(w.B, w.H, w.Nq, w.seed)
+    slabs, rows = _slab_rows(w, max_slabs=8 if w.Nq >= 4096 else 32)
     ref = oracle.attention_rows(Q, K, V, rows, causal=w.causal)
-    assert_parity(got[rows], ref, name)
+    assert_parity(got[rows], ref, (name, slabs))
     assert not np.isnan(got).any()
+    if w.B * w.H <= 32:
+        assert len(slabs) == w.B * w.H
 
 
 def test_errors_and_empty(lib):

@@ -1,10 +1,10 @@
 """GPU parity: the HIP library (through its C ABI) against the CPU oracle.
 
 Every comparison uses the same seeded inputs on both sides.  Sizes here span
-several tiles with ragged tails; the full workload shapes are checked either
-completely (where the oracle finishes in seconds) or at sampled positions the
-oracle computes one dot product at a time, in the launch configuration the
-benchmark uses (the default dispatch).
+several tiles with ragged tails; every workload shape is checked completely,
+element by element against the oracle's full result, in the launch
+configuration the benchmark uses (the default dispatch), with B given as
+B[K][N] and as Bt[N][K].
 """
 import numpy as np
 import pytest
@@ -119,31 +119,33 @@ def test_workload_skinny_full(lib):
     assert m["frac_exact"] > 0.97
 
 
-def _sample_points(M, N, seed, n_random=20000):
-    rng = np.random.default_rng(seed)
-    r = [rng.integers(0, M, n_random)]
-    c = [rng.integers(0, N, n_random)]
-    # whole rows at the top, bottom and a tile boundary; whole corner blocks
-    for row in (0, M - 1, min(M - 1, 255), min(M - 1, 256)):
-        r.append(np.full(N, row))
-        c.append(np.arange(N))
-    for (i0, j0) in ((0, 0), (M - 40, N - 40), (0, N - 40), (M - 40, 0)):
-        ii, jj = np.meshgrid(np.arange(i0, i0 + 40), np.arange(j0, j0 + 40), indexing="ij")
-        r.append(ii.ravel())
-        c.append(jj.ravel())
-    return np.concatenate(r), np.concatenate(c)
+_FULL_REF = {}
+
+
+def _full_reference(name):
+    """Inputs and the oracle's complete fp16 result of a workload, computed once per session."""
+    if name not in _FULL_REF:
+        _FULL_REF.clear()  # one large workload in memory at a time
+        w = workloads.WORKLOADS[name]
+        A, B, bias = workloads.make_inputs(w)
+        _FULL_REF[name] = (A, B, bias, oracle.gemm(A, B, bias, w.epilogue))
+    return _FULL_REF[name]
 
 
 @pytest.mark.parametrize("name", ["gemm_4096", "mlp_up_8192x16384x4096"])
-def test_workload_large_sampled(lib, name):
+@pytest.mark.parametrize("bt", [False, True])
+def test_workload_large_full(lib, name, bt):
+    import dense_tiled_gemm_04_amd as g
     w = workloads.WORKLOADS[name]
-    A, B, bias = workloads.make_inputs(w)
-    got = run(lib, A, B, bias, w.epilogue)
-    r, c = _sample_points(w.M, w.N, 99)
-    ref = oracle.gemm_points(A, B, bias, w.epilogue, r, c)
-    m = assert_parity(got[r, c], ref, name)
+    A, B, bias, ref = _full_reference(name)
+    Bdev = dev(np.ascontiguousarray(B.T)) if bt else dev(B)
+    out = g.gemm_f16(dev(A), Bdev, dev(bias) if bias is not None else None, w.epilogue, b_transposed=bt)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    del out, Bdev
+    m = assert_parity(got, ref, (name, "Bt" if bt else "B"))
     assert m["frac_exact"] > 0.97, m
-    assert not np.isnan(got.astype(np.float32)).any()
+    assert m["n"] == w.M * w.N
 
 
 # ---------------------------------------------------------------------------
@@ -394,19 +396,80 @@ def test_torch_front_end_errors(lib):
         g.gemm_f16(a.t(), b.t())
 
 
-def test_vector_add(lib):
+def _same_f32_bits(x, y):
+    x, y = np.asarray(x, np.float32), np.asarray(y, np.float32)
+    both_nan = np.isnan(x) & np.isnan(y)
+    return bool(np.all(both_nan | (x.view(np.uint32) == y.view(np.uint32))))
+
+
+@pytest.mark.parametrize("n", [1, 7, 1024, 1000003, 64 * 1024 * 1024 + 5])
+def test_vector_add_matches_oracle(lib, n):
+    # The pages' first kernel: float32 C = A + B, every element the IEEE binary32 sum, so bit-exact.
     import dense_tiled_gemm_04_amd as g
-    for n in (1, 7, 1024, 1000003):
-        x = torch.randn(n, device="cuda")
-        y = torch.randn(n, device="cuda")
-        z = g.vector_add(x, y)
-        torch.cuda.synchronize()
-        assert torch.equal(z, x + y)
-    # unaligned views take the scalar kernel
-    x = torch.randn(1001, device="cuda")
-    z = g.vector_add(x[1:], x[:-1])
+    a, b = workloads.make_vector_add_inputs(n, seed=12 + n % 97)
+    k = min(n, 4096)  # a block of arbitrary bit patterns: subnormals, infinities, NaNs, ties
+    a[:k] = workloads.random_f32_bits(1, k)
+    b[:k] = workloads.random_f32_bits(2, k)
+    ref = oracle.vector_add(a, b)
+    z = g.vector_add(dev(a), dev(b))
     torch.cuda.synchronize()
-    assert torch.equal(z, x[1:] + x[:-1])
+    assert _same_f32_bits(z.cpu().numpy(), ref)
+
+
+def test_vector_add_unaligned_views(lib):
+    # views 4 bytes off the 16-byte grid take the scalar kernel; still bit-exact against the oracle
+    import dense_tiled_gemm_04_amd as g
+    x, y = workloads.make_vector_add_inputs(100_003, seed=13)
+    x[:2048] = workloads.random_f32_bits(3, 2048)
+    dx = dev(x)
+    z = g.vector_add(dx[1:], dx[:-1])
+    torch.cuda.synchronize()
+    assert _same_f32_bits(z.cpu().numpy(), oracle.vector_add(x[1:], x[:-1]))
+
+
+# ---------------------------------------------------------------------------
+# the event-median timing helper
+# ---------------------------------------------------------------------------
+def test_gemm_f16_time_median_and_result(lib):
+    import dense_tiled_gemm_04_amd as g
+    M = N = K = 2048
+    A, B, _ = workloads.make_inputs("gemm_4096", M=M, N=N, K=K)
+    dA, dB = dev(A), dev(B)
+    dC = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    sh = torch.cuda.current_stream().cuda_stream
+    st, med = g.gemm_f16_time_raw(M, N, K, dA.data_ptr(), dB.data_ptr(), None, dC.data_ptr(), 0, 51, sh)
+    assert st == 0 and med > 0
+    # the output of the timed launches is the product
+    r = np.arange(0, M, 37)
+    c = (r * 13) % N
+    ref = oracle.gemm_points(A, B, None, "none", r, c)
+    assert_parity(dC.cpu().numpy()[r, c][None, :], ref[None, :], "gemm_f16_time output")
+    # against the benchmark's way of timing: one event pair around back-to-back launches
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    e0.record(stream)
+    for _ in range(51):
+        assert g.gemm_f16_raw(M, N, K, dA.data_ptr(), dB.data_ptr(), None, dC.data_ptr(), 0, sh) == 0
+    e1.record(stream)
+    torch.cuda.synchronize()
+    avg = e0.elapsed_time(e1) / 51
+    assert 0.5 < med / avg < 2.0, (med, avg)
+    # a forced configuration, and the empty call
+    idx = g.select_config_raw(M, N, K, dA.data_ptr(), dB.data_ptr(), None, dC.data_ptr(), 0)
+    st, med2 = g.gemm_f16_time_raw(M, N, K, dA.data_ptr(), dB.data_ptr(), None, dC.data_ptr(), 0, 5, sh, config=idx)
+    assert st == 0 and med2 > 0
+    assert g.gemm_f16_time_raw(0, N, K, None, None, None, None, 0, 5, sh) == (0, 0.0)
+
+
+def test_gemm_f16_time_rejects_bad_arguments(lib):
+    import dense_tiled_gemm_04_amd as g
+    a = torch.zeros((64, 64), dtype=torch.float16, device="cuda")
+    p = a.data_ptr()
+    assert g.gemm_f16_time_raw(64, 64, 64, p, p, None, p, 0, 0)[0] == 1           # iters < 1
+    assert g.gemm_f16_time_raw(64, 64, 64, p, p, None, p, 0, 100001)[0] == 1      # iters too large
+    assert g.gemm_f16_time_raw(64, 64, 64, p, p, None, p, 0, 5, config=g.num_configs())[0] == 5
+    assert g.gemm_f16_time_raw(-1, 64, 64, p, p, None, p, 0, 5)[0] == 1
+    assert g.gemm_f16_time_raw(64, 64, 64, p, p, None, p, 7, 5)[0] == 3
 
 
 # ---------------------------------------------------------------------------
@@ -503,19 +566,6 @@ def test_b_transposed_strided_and_k_tail_isolation(lib):
         name = "default" if c is None else c["name"]
         assert_parity(got[:, keep], ref[:, keep], ("finite columns", name))
         assert np.array_equal(got[:, inf_cols].view(np.uint16), ref[:, inf_cols].view(np.uint16)), name
-
-
-@pytest.mark.parametrize("name", ["mlp_up_8192x16384x4096"])
-def test_b_transposed_workload_sampled(lib, name):
-    import dense_tiled_gemm_04_amd as g
-    w = workloads.WORKLOADS[name]
-    A, B, bias = workloads.make_inputs(w)
-    out = g.gemm_f16(dev(A), dev(np.ascontiguousarray(B.T)), dev(bias), w.epilogue, b_transposed=True)
-    torch.cuda.synchronize()
-    got = out.cpu().numpy()
-    r, c = _sample_points(w.M, w.N, 17, n_random=20000)
-    ref = oracle.gemm_points(A, B, bias, w.epilogue, r, c)
-    assert_parity(got[r, c][None, :], ref[None, :], name)
 
 
 # ---------------------------------------------------------------------------
