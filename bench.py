@@ -15,6 +15,14 @@ Prints ONE JSON line:
               traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE
               counters (profiles/), null if the kernel sources changed since.
   cpu_baseline = the CPU oracle (fp64, all host threads) on a bounded sample.
+  context   = the vendor BLAS in the same process (sequential and interleaved),
+              the settled rate under the power limiter (context.sustained:
+              >= 5 ms of warm-up, then >= 25 ms of launches in ~1 ms chunks,
+              median chunk), the library's own event-median helper
+              gemm_f16_time, the sha256 of every input, a status per workload,
+              and (GEMM workloads, unless --no-context) the fused bias+GELU MLP
+              up-projection and the skinny HBM-bound shape measured the same
+              way under context.workloads.
 
 --workload softmax_* benchmarks the library's row softmax instead (one step =
 one softmax_rows_f16 call over the whole matrix; value in GB/s of X read plus Y
@@ -395,6 +403,182 @@ def bench_attention(args, g, torch, w) -> int:
     return 0
 
 
+def sustained_ms(torch, stream, step, launch_ms: float, warm_ms: float = 5.0, total_ms: float = 25.0,
+                 chunk_ms: float = 1.0) -> dict:
+    """The settled rate under the power limiter: >= warm_ms of untimed back-to-back launches, then >= total_ms of
+    launches timed in chunks of ~chunk_ms, each chunk between its own pair of HIP events on the launch stream.
+    Returns the median, p10 and p90 over the chunks of the time per launch (ms)."""
+    per = max(1, int(round(chunk_ms / max(launch_ms, 1e-3))))
+    chunks = max(5, int(round(total_ms / max(per * launch_ms, 1e-3))))
+    i = 0
+    for _ in range(max(1, int(round(warm_ms / max(launch_ms, 1e-3))))):
+        step(i)
+        i += 1
+    evs = []
+    for _ in range(chunks):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(per):
+            step(i)
+            i += 1
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) / per for a, b in evs)
+    q = lambda f: t[min(len(t) - 1, int(f * len(t)))]
+    return {"ms": t[len(t) // 2], "p10_ms": q(0.1), "p90_ms": q(0.9), "chunks": chunks, "launches_per_chunk": per,
+            "warmup_ms": warm_ms}
+
+
+def gemm_workload_inputs(w):
+    """Seeded inputs of a GEMM workload plus the sha256 of their bits (numpy streams are not promised stable
+    across versions, so the digest records what was actually used)."""
+    import workloads
+    A, B, bias = workloads.make_inputs(w)
+    return A, B, bias, workloads.input_digest(A, B, bias)
+
+
+def measure_gemm(g, torch, w, A, B, bias, steps: int, warmup: int, bt: bool = False, rotate: int | None = None,
+                 config: int | None = None, vendor: bool = True) -> dict:
+    """One GEMM workload on the GPU: `steps` launches timed between one pair of HIP events on the launch stream
+    after `warmup` untimed ones (synchronised on both sides), then the settled rate, the library's own
+    event-median helper and (optionally) the vendor BLAS in the same process."""
+    import numpy as np
+
+    hbm_bound = w.flops / w.algorithmic_bytes < 100.0
+    rotate = rotate if rotate is not None else (3 if hbm_bound else 1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dA = torch.from_numpy(A).to(dev)
+    Bdev = np.ascontiguousarray(B.T) if bt else B
+    dBs = [torch.from_numpy(Bdev).to(dev) for _ in range(rotate)]
+    db = torch.from_numpy(bias).to(dev) if bias is not None else None
+    dC = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    epi = g.EPILOGUES[w.epilogue]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    pA, pC = dA.data_ptr(), dC.data_ptr()
+    pBs = [b.data_ptr() for b in dBs]
+    pb = db.data_ptr() if db is not None else None
+    lib = g.load()
+    if bt:
+        ld = (w.K, w.K, w.N)  # lda, ldb (row length of Bt), ldc
+        cfg_idx = config if config is not None else \
+            g.select_config_bt_raw(w.M, w.N, w.K, pA, ld[0], pBs[0], ld[1], pb, pC, ld[2], epi)
+    else:
+        cfg_idx = config if config is not None else g.select_config_raw(w.M, w.N, w.K, pA, pBs[0], pb, pC, epi)
+    cfg = g.config_info(cfg_idx)
+
+    def step(i):
+        if bt:
+            st = lib.gemm_f16_bt_with_config(cfg_idx, w.M, w.N, w.K, pA, ld[0], pBs[i % rotate], ld[1], pb, pC,
+                                             ld[2], epi, sh) if config is not None else \
+                lib.gemm_f16_bt(w.M, w.N, w.K, pA, ld[0], pBs[i % rotate], ld[1], pb, pC, ld[2], epi, sh)
+        else:
+            st = lib.gemm_f16_with_config(cfg_idx, w.M, w.N, w.K, pA, pBs[i % rotate], pb, pC, epi, sh) \
+                if config is not None else lib.gemm_f16(w.M, w.N, w.K, pA, pBs[i % rotate], pb, pC, epi, sh)
+        if st != 0:
+            raise g.GemmError(st)
+
+    t_start = time.perf_counter()
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t_start
+    # timed region: synchronised on both sides, HIP events on the launch stream
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    out = {"w": w, "bt": bt, "rotate": rotate, "hbm_bound": hbm_bound, "ms": ms, "cfg": cfg, "warm_s": warm_s,
+           "finite": bool(torch.isfinite(dC).all().item())}
+    out["sustained"] = sustained_ms(torch, stream, step, ms)
+    # the library's own timing entry point (median of event-bracketed launches); it takes one B, so only where
+    # B is not rotated (a single 256 MiB B would be partly served from the Infinity Cache)
+    if not bt and rotate == 1:
+        st, med = g.gemm_f16_time_raw(w.M, w.N, w.K, pA, pBs[0], pb, pC, epi, 51, sh,
+                                      config=-1 if config is None else config)
+        out["helper_median_ms"] = med if st == 0 else None
+    if vendor:
+        # the vendor BLAS on the same tensors (torch.matmul, or F.linear for Bt; + bias + gelu eagerly if fused)
+        def torch_step(i):
+            c = torch.nn.functional.linear(dA, dBs[i % rotate]) if bt else torch.matmul(dA, dBs[i % rotate])
+            if w.epilogue == "bias":
+                c = c + db
+            elif w.epilogue == "bias_gelu":
+                c = torch.nn.functional.gelu(c + db)
+            return c
+        for i in range(5):
+            torch_step(i)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        n_t = max(10, min(steps, 100))
+        t0.record(stream)
+        for i in range(n_t):
+            torch_step(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        out["torch_ms"] = t0.elapsed_time(t1) / n_t
+        out["interleaved"] = interleaved_ms(torch, stream, step, torch_step, ms)
+    del dA, dBs, db, dC
+    torch.cuda.empty_cache()
+    return out
+
+
+def roofline_of(m: dict) -> dict:
+    w = m["w"]
+    ms = m["ms"]
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    gbs = w.algorithmic_bytes / (ms * 1e-3) / 1e9
+    traffic = load_traffic(w.name + ("_bt" if m["bt"] else ""), m["cfg"]["name"])
+    if m["hbm_bound"]:
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / PEAK_FP16_TFLOPS, "traffic": traffic}
+    roof["kernel"] = m["cfg"]["name"]
+    roof["algorithmic_flops_per_launch"] = w.flops
+    roof["algorithmic_bytes_per_launch"] = w.algorithmic_bytes
+    roof["avg_launch_us"] = ms * 1e3
+    return roof
+
+
+def context_line(m: dict) -> dict:
+    """Figures of one measured workload for the context object: timed steps, settled rate, roofline fractions."""
+    w = m["w"]
+    roof = roofline_of(m)
+    sus = m["sustained"]
+    peak = roof["peak"]
+    per = (lambda t: w.algorithmic_bytes / (t * 1e-3) / 1e9) if m["hbm_bound"] else \
+        (lambda t: w.flops / (t * 1e-3) / 1e12)
+    out = {"status": "ok" if m["finite"] else "fail: non-finite output", "kernel": roof["kernel"],
+           "ms_per_step": round(m["ms"], 6), "value": round(roof["achieved"], 3), "unit": roof["unit"],
+           "frac": round(roof["frac"], 4), "bound": roof["bound"], "traffic": roof["traffic"],
+           "sustained": {"ms_per_launch": round(sus["ms"], 6), "p10_ms": round(sus["p10_ms"], 6),
+                         "p90_ms": round(sus["p90_ms"], 6), "value": round(per(sus["ms"]), 3),
+                         "frac": round(per(sus["ms"]) / peak, 4), "chunks": sus["chunks"],
+                         "launches_per_chunk": sus["launches_per_chunk"]},
+           "b_layout": "Bt[N][K]" if m["bt"] else "B[K][N]", "rotated_B_copies": m["rotate"]}
+    if m.get("helper_median_ms") is not None:
+        out["gemm_f16_time_median_ms"] = round(m["helper_median_ms"], 6)
+    if "torch_ms" in m:
+        out["torch_ms"] = round(m["torch_ms"], 6)
+        il = m["interleaved"]
+        out["interleaved"] = {"ours_ms": round(il[0], 6), "torch_ms": round(il[1], 6),
+                              "torch_over_ours": round(il[1] / il[0], 3)}
+    return out
+
+
+# workloads measured beside the headline one, under "context": the metric's fused MLP and the skinny HBM-bound shape
+CONTEXT_WORKLOADS = ["mlp_up_8192x16384x4096", "skinny_16x16384x8192"]
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -403,6 +587,8 @@ def main() -> int:
     ap.add_argument("--workload", default="gemm_4096")
     ap.add_argument("--config", type=int, default=None, help="force a kernel config index")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="GEMM workloads: skip the other workloads measured under context.workloads")
     ap.add_argument("--rotate", type=int, default=None,
                     help="copies of B to rotate through (default: 3 for HBM-bound workloads, else 1)")
     ap.add_argument("--b-transposed", action="store_true",
@@ -417,7 +603,6 @@ def main() -> int:
               "multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import dense_tiled_gemm_04_amd as g
@@ -434,96 +619,58 @@ def main() -> int:
     if args.workload in workloads.ATTENTION_WORKLOADS:
         return bench_attention(args, g, torch, workloads.ATTENTION_WORKLOADS[args.workload])
     w = workloads.WORKLOADS[args.workload]
-    A, B, bias = workloads.make_inputs(w)
-    hbm_bound = w.flops / w.algorithmic_bytes < 100.0
-    rotate = args.rotate if args.rotate is not None else (3 if hbm_bound else 1)
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    dA = torch.from_numpy(A).to(dev)
+    A, B, bias, digest = gemm_workload_inputs(w)
     bt = args.b_transposed
-    Bdev = np.ascontiguousarray(B.T) if bt else B
-    dBs = [torch.from_numpy(Bdev).to(dev) for _ in range(rotate)]
-    db = torch.from_numpy(bias).to(dev) if bias is not None else None
-    dC = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
-    epi = g.EPILOGUES[w.epilogue]
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
-    pA, pC = dA.data_ptr(), dC.data_ptr()
-    pBs = [b.data_ptr() for b in dBs]
-    pb = db.data_ptr() if db is not None else None
-    lib = g.load()
-    if bt:
-        ld = (w.K, w.K, w.N)  # lda, ldb (row length of Bt), ldc
-        cfg_idx = args.config if args.config is not None else \
-            g.select_config_bt_raw(w.M, w.N, w.K, pA, ld[0], pBs[0], ld[1], pb, pC, ld[2], epi)
-    else:
-        cfg_idx = args.config if args.config is not None else g.select_config_raw(w.M, w.N, w.K, pA, pBs[0], pb, pC, epi)
-    cfg = g.config_info(cfg_idx)
-
-    def step(i):
-        if bt:
-            st = lib.gemm_f16_bt_with_config(cfg_idx, w.M, w.N, w.K, pA, ld[0], pBs[i % rotate], ld[1], pb, pC,
-                                             ld[2], epi, sh) if args.config is not None else \
-                lib.gemm_f16_bt(w.M, w.N, w.K, pA, ld[0], pBs[i % rotate], ld[1], pb, pC, ld[2], epi, sh)
-        else:
-            st = lib.gemm_f16_with_config(cfg_idx, w.M, w.N, w.K, pA, pBs[i % rotate], pb, pC, epi, sh) \
-                if args.config is not None else lib.gemm_f16(w.M, w.N, w.K, pA, pBs[i % rotate], pb, pC, epi, sh)
-        if st != 0:
-            raise g.GemmError(st)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # timed region: synchronised on both sides, HIP events on the launch stream
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    m = measure_gemm(g, torch, w, A, B, bias, args.steps, args.warmup, bt=bt, rotate=args.rotate,
+                     config=args.config)
+    if not m["finite"]:
+        print("bench.py: non-finite values in C for %s" % w.name, file=sys.stderr)
+        return 1
+    ms = m["ms"]
+    roof = roofline_of(m)
     tflops = w.flops / (ms * 1e-3) / 1e12
     gbs = w.algorithmic_bytes / (ms * 1e-3) / 1e9
-
-    # context: the vendor BLAS on the same tensors (torch.matmul, or F.linear for Bt; + bias + gelu eagerly if fused)
-    def torch_step(i):
-        c = torch.nn.functional.linear(dA, dBs[i % rotate]) if bt else torch.matmul(dA, dBs[i % rotate])
-        if w.epilogue == "bias":
-            c = c + db
-        elif w.epilogue == "bias_gelu":
-            c = torch.nn.functional.gelu(c + db)
-        return c
-    for i in range(5):
-        torch_step(i)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    n_t = max(10, min(args.steps, 100))
-    t0.record(stream)
-    for i in range(n_t):
-        torch_step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    torch_ms = t0.elapsed_time(t1) / n_t
-    il_ours, il_torch = interleaved_ms(torch, stream, step, torch_step, ms)
-
-    traffic = load_traffic(w.name + ("_bt" if bt else ""), cfg["name"])
-    if hbm_bound:
-        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": gbs / PEAK_HBM_GBS, "traffic": traffic}
-    else:
-        roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
-                "frac": tflops / PEAK_FP16_TFLOPS, "traffic": traffic}
-    roof["kernel"] = cfg["name"]
-    roof["algorithmic_flops_per_launch"] = w.flops
-    roof["algorithmic_bytes_per_launch"] = w.algorithmic_bytes
-    roof["avg_launch_us"] = ms * 1e3
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, A, B, bias)
+    del A, B, bias
+
+    head = context_line(m)
+    context = {
+        "regime": ("the %d timed launches follow %d warm-up launches (%.1f ms of work): the first milliseconds of "
+                   "load, before the power limiter has lowered the clock; context.sustained is the settled rate "
+                   "(>= %.0f ms of warm-up, then >= 25 ms of launches in ~1 ms chunks, median chunk)"
+                   % (args.steps, args.warmup, args.warmup * ms, m["sustained"]["warmup_ms"])),
+        "sustained": head["sustained"],
+        "algorithmic_GBps": round(gbs, 1),
+        "input_sha256": {w.name: digest},
+        "status": {w.name + ("_bt" if bt else ""): head["status"]},
+    }
+    if "gemm_f16_time_median_ms" in head:
+        context["gemm_f16_time_median_ms"] = head["gemm_f16_time_median_ms"]
+    context[("torch_linear_ms" if bt else "torch_matmul_ms")] = head.get("torch_ms")
+    if "torch_ms" in m:
+        context["torch_tflops"] = round(w.flops / (m["torch_ms"] * 1e-3) / 1e12, 3)
+        context["interleaved"] = head["interleaved"]
+    if not args.no_context and args.config is None:
+        # the other headline workloads on the same clock, each in its own try (a failure is recorded, not fatal)
+        context["workloads"] = {}
+        for name in CONTEXT_WORKLOADS:
+            if name == w.name:
+                continue
+            key = name + ("_bt" if bt else "")
+            try:
+                wc = workloads.WORKLOADS[name]
+                Ac, Bc, bc, dg = gemm_workload_inputs(wc)
+                context["input_sha256"][name] = dg
+                mc = measure_gemm(g, torch, wc, Ac, Bc, bc, args.steps, args.warmup, bt=bt)
+                del Ac, Bc, bc
+                line = context_line(mc)
+                context["workloads"][key] = line
+                context["status"][key] = line["status"]
+            except Exception as e:  # keep going, like the pages' section runner
+                context["status"][key] = "fail: %s" % str(e).splitlines()[0][:200]
 
     out = {
         "metric": "fp16 GEMM TFLOPS (4096\u00b3; fused bias+GELU MLP) + % of MI355X MFMA peak",
@@ -540,14 +687,10 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "epilogue": w.epilogue,
                    "b_layout": "Bt[N][K]" if bt else "B[K][N]",
-                   "inputs": "seeded numpy draws (%s), B copies rotated: %d" % (w.note, rotate)},
+                   "inputs": "seeded numpy draws (%s), B copies rotated: %d" % (w.note, m["rotate"])},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "context": {("torch_linear_ms" if bt else "torch_matmul_ms"): round(torch_ms, 6),
-                    "torch_tflops": round(w.flops / (torch_ms * 1e-3) / 1e12, 3),
-                    "algorithmic_GBps": round(gbs, 1),
-                    "interleaved": {"ours_ms": round(il_ours, 6), "torch_ms": round(il_torch, 6),
-                                    "torch_over_ours": round(il_torch / il_ours, 3)}},
+        "context": context,
     }
     print(json.dumps(out), flush=True)
     return 0
