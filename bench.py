@@ -39,6 +39,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -49,6 +50,7 @@ if ROOT not in sys.path:
 
 PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+WARMUP_MS = 5.0             # minimum back-to-back work before a timed region
 
 
 # Sources each kernel family is built from; a change to any of them voids that family's recorded traffic.
@@ -177,6 +179,172 @@ def hbm_calibration(g, torch) -> int:
     return 0
 
 
+class PowerSampler:
+    """Board power and shader clock of the GPU in use, sampled from its amdgpu hwmon files (power1_average or
+    power1_input in microwatts, freq1_input in Hz) by a host thread every `period_s`.  The card is the one whose
+    PCI address matches torch's device 0; failing that, every card is sampled and the one whose power rose the
+    most is reported.  Readings are None where the files cannot be read."""
+
+    def __init__(self, torch, period_s: float = 0.01):
+        import glob
+        import threading
+        self.period_s = period_s
+        self.cards = {}
+        for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+            hw = sorted(glob.glob(dev + "/hwmon/hwmon*"))
+            if not hw:
+                continue
+            pw = next((hw[0] + "/" + f for f in ("power1_average", "power1_input") if os.path.exists(hw[0] + "/" + f)),
+                      None)
+            fr = hw[0] + "/freq1_input" if os.path.exists(hw[0] + "/freq1_input") else None
+            if pw:
+                self.cards[os.path.basename(os.path.realpath(dev))] = (pw, fr)
+        self.match = None
+        try:
+            p = torch.cuda.get_device_properties(0)
+            bus = getattr(p, "pci_bus_id", None)
+            if bus is not None:
+                for addr in self.cards:
+                    if int(addr.split(":")[1], 16) == int(bus):
+                        self.match = addr
+        except Exception:
+            pass
+        self.samples = {a: [] for a in self.cards}
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _read(path):
+        try:
+            with open(path) as f:
+                return float(f.read().strip())
+        except (OSError, ValueError):
+            return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            for a, (pw, fr) in self.cards.items():
+                self.samples[a].append((self._read(pw), self._read(fr) if fr else None))
+            time.sleep(self.period_s)
+
+    def idle(self):
+        return {a: self._read(pw) for a, (pw, fr) in self.cards.items()}
+
+    def __enter__(self):
+        self._idle = self.idle()
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+
+    def summary(self) -> dict:
+        def med(v):
+            v = sorted(x for x in v if x is not None)
+            return v[len(v) // 2] if v else None
+        if not self.cards:
+            return {"card": None, "note": "no readable amdgpu hwmon power file"}
+        rise = {a: (med([p for p, _ in self.samples[a]]) or 0) - (self._idle.get(a) or 0) for a in self.cards}
+        card = self.match or max(rise, key=rise.get)
+        pw = med([p for p, _ in self.samples[card]])
+        fr = med([f for _, f in self.samples[card]])
+        return {"card": card, "matched_by": "pci bus" if self.match else "largest power rise",
+                "samples": len(self.samples[card]), "board_power_W": round(pw / 1e6, 1) if pw else None,
+                "idle_power_W": round(self._idle[card] / 1e6, 1) if self._idle.get(card) else None,
+                "sclk_GHz_hwmon": round(fr / 1e9, 3) if fr else None}
+
+
+def mfma_calibration(g, torch, seconds: float = 0.4) -> int:
+    """The practical MFMA ceiling under the board power limit: the register-only MFMA loop on all 256 CUs (two
+    waves per SIMD, 8 independent chains each) run back to back for `seconds`, for each MFMA shape; then the
+    shipped 4096^3 GEMM the same way.  Prints one JSON line per run: FLOP/s from HIP events (median launch),
+    the clock the loop ran at (s_memtime against the 100 MHz s_memrealtime), board power from hwmon, FLOP/J."""
+    import numpy as np
+    import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    wgs = 256
+    stamps = torch.zeros((wgs, 4), dtype=torch.int64, device=dev)
+    sink = torch.zeros(wgs * 512, dtype=torch.float32, device=dev)
+    lines = []
+    for shape in (16, 32):
+        def launch(iters):
+            st = g.mfma_calibration_raw(shape, iters, wgs, stamps.data_ptr(), sink.data_ptr(), sh)
+            if st != 0:
+                raise g.GemmError(st)
+        # size one launch at ~20 ms from a short probe
+        launch(2000)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        launch(2000)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        iters = max(1000, int(2000 * 20.0 / max(e0.elapsed_time(e1), 1e-3)))
+        n = max(5, int(seconds * 1e3 / 20.0))
+        evs = []
+        with PowerSampler(torch) as ps:
+            for _ in range(n):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                launch(iters)
+                b.record(stream)
+                evs.append((a, b))
+            torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in evs[1:])
+        t = ms[len(ms) // 2]
+        flops = g.mfma_calibration_flops(shape, iters, wgs)
+        st = stamps.cpu().numpy().astype(np.float64)
+        clk = np.median((st[:, 1] - st[:, 0]) / ((st[:, 3] - st[:, 2]) / 100e6)) / 1e9
+        pw = ps.summary()
+        tf = flops / (t * 1e-3) / 1e12
+        lines.append({"calibration": "mfma_f16_%dx%dx%d" % ((16, 16, 32) if shape == 16 else (32, 32, 16)),
+                      "workgroups": wgs, "waves_per_simd": 2, "iters": iters, "launches": n,
+                      "median_launch_ms": round(t, 3), "TFLOPs": round(tf, 1), "frac_of_spec": round(tf / PEAK_FP16_TFLOPS, 4),
+                      "sclk_GHz_memtime": round(float(clk), 3),
+                      "TFLOPs_at_2.4GHz_per_sclk": round(tf * 2.4 / float(clk), 1), "power": pw,
+                      "GFLOP_per_J": round(tf * 1e3 / pw["board_power_W"], 1) if pw.get("board_power_W") else None})
+    # the shipped 4096^3 GEMM, back to back for the same time
+    w = workloads.WORKLOADS["gemm_4096"]
+    A, B, _ = workloads.make_inputs(w)
+    dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+    dC = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    lib = g.load()
+    step = lambda: lib.gemm_f16(w.M, w.N, w.K, dA.data_ptr(), dB.data_ptr(), None, dC.data_ptr(), 0, sh)
+    for _ in range(50):
+        step()
+    torch.cuda.synchronize()
+    per = 10
+    chunks = []
+    with PowerSampler(torch) as ps:
+        t_end = time.perf_counter() + seconds
+        while time.perf_counter() < t_end:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(per):
+                step()
+            b.record(stream)
+            chunks.append((a, b))
+            if len(chunks) % 20 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) / per for a, b in chunks)
+    t = ms[len(ms) // 2]
+    tf = w.flops / (t * 1e-3) / 1e12
+    pw = ps.summary()
+    cfg = g.config_info(g.select_config_raw(w.M, w.N, w.K, dA.data_ptr(), dB.data_ptr(), None, dC.data_ptr(), 0))
+    lines.append({"calibration": "gemm_4096 (shipped kernel, back to back)", "kernel": cfg["name"],
+                  "launches": per * len(chunks), "median_launch_ms": round(t, 4), "TFLOPs": round(tf, 1),
+                  "frac_of_spec": round(tf / PEAK_FP16_TFLOPS, 4), "power": pw,
+                  "GFLOP_per_J": round(tf * 1e3 / pw["board_power_W"], 1) if pw.get("board_power_W") else None})
+    for l in lines:
+        print(json.dumps(l), flush=True)
+    return 0
+
+
 def cpu_baseline_softmax(w, X, target_s: float = 10.0):
     """Time the CPU oracle's row softmax on the first R rows (R grown as for the GEMM sample)."""
     import numpy as np
@@ -230,9 +398,7 @@ def bench_softmax(args, g, torch, w) -> int:
         if st != 0:
             raise g.GemmError(st)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    n_warm, _ = warm_up(torch, stream, step, args.warmup)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(args.steps):
@@ -277,7 +443,7 @@ def bench_softmax(args, g, torch, w) -> int:
                    "inputs": "seeded numpy draws (%s), X copies rotated: %d" % (w.note, rotate)},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "context": {"torch_softmax_ms": round(torch_ms, 6),
+        "context": {"warmup_launches": n_warm, "torch_softmax_ms": round(torch_ms, 6),
                     "torch_GBps": round(w.algorithmic_bytes / (torch_ms * 1e-3) / 1e9, 1),
                     "interleaved": {"ours_ms": round(il_ours, 6), "torch_ms": round(il_torch, 6),
                                     "torch_over_ours": round(il_torch / il_ours, 3)}},
@@ -338,9 +504,7 @@ def bench_attention(args, g, torch, w) -> int:
         if st != 0:
             raise g.GemmError(st)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    n_warm, _ = warm_up(torch, stream, lambda i: step(), args.warmup)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.steps):
@@ -394,13 +558,33 @@ def bench_attention(args, g, torch, w) -> int:
                    "inputs": "seeded numpy draws, Q, K, V ~ N(0, 1) (%s)" % w.note},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "context": {"torch_sdpa_ms": round(torch_ms, 6) if torch_ms else None, "torch_sdpa_backend": backend,
+        "context": {"warmup_launches": n_warm, "torch_sdpa_ms": round(torch_ms, 6) if torch_ms else None, "torch_sdpa_backend": backend,
                     "torch_tflops": round(w.flops / (torch_ms * 1e-3) / 1e12, 3) if torch_ms else None,
                     "interleaved": {"ours_ms": round(il[0], 6), "torch_ms": round(il[1], 6),
                                     "torch_over_ours": round(il[1] / il[0], 3)} if il else None},
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+def warm_up(torch, stream, step, warmup: int):
+    """Untimed launches before a timed region: the `warmup` requested, extended until >= WARMUP_MS of
+    back-to-back work has run, so that the timed launches see the clock the card settles at rather than its
+    ramp out of idle.  step(i) launches once.  Returns (launches run, their ms per launch estimate)."""
+    step(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(1, 4):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    one_ms = max(e0.elapsed_time(e1) / 3, 1e-3)
+    n_warm = max(warmup, int(math.ceil(WARMUP_MS / one_ms)))
+    for i in range(n_warm):
+        step(i)
+    torch.cuda.synchronize()
+    return 4 + n_warm, one_ms
 
 
 def sustained_ms(torch, stream, step, launch_ms: float, warm_ms: float = 5.0, total_ms: float = 25.0,
@@ -481,9 +665,7 @@ def measure_gemm(g, torch, w, A, B, bias, steps: int, warmup: int, bt: bool = Fa
             raise g.GemmError(st)
 
     t_start = time.perf_counter()
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
+    n_warm, one_ms = warm_up(torch, stream, step, warmup)
     warm_s = time.perf_counter() - t_start
     # timed region: synchronised on both sides, HIP events on the launch stream
     e0 = torch.cuda.Event(enable_timing=True)
@@ -495,6 +677,7 @@ def measure_gemm(g, torch, w, A, B, bias, steps: int, warmup: int, bt: bool = Fa
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     out = {"w": w, "bt": bt, "rotate": rotate, "hbm_bound": hbm_bound, "ms": ms, "cfg": cfg, "warm_s": warm_s,
+           "warmup_launches": n_warm, "warmup_ms": round(n_warm * one_ms, 2),
            "finite": bool(torch.isfinite(dC).all().item())}
     out["sustained"] = sustained_ms(torch, stream, step, ms)
     # the library's own timing entry point (median of event-bracketed launches); it takes one B, so only where
@@ -596,6 +779,10 @@ def main() -> int:
     ap.add_argument("--hbm-calibration", action="store_true",
                     help="run only the fp32 vector-add kernel on buffers of known size (the reference "
                          "point that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes)")
+    ap.add_argument("--mfma-calibration", action="store_true",
+                    help="run only the register-only MFMA loop (both MFMA shapes) and the shipped 4096^3 GEMM "
+                         "back to back, with board power and clock: the practical MFMA ceiling under the power "
+                         "limit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -614,6 +801,8 @@ def main() -> int:
     g.load()
     if args.hbm_calibration:
         return hbm_calibration(g, torch)
+    if args.mfma_calibration:
+        return mfma_calibration(g, torch)
     if args.workload in workloads.SOFTMAX_WORKLOADS:
         return bench_softmax(args, g, torch, workloads.SOFTMAX_WORKLOADS[args.workload])
     if args.workload in workloads.ATTENTION_WORKLOADS:
@@ -638,10 +827,11 @@ def main() -> int:
 
     head = context_line(m)
     context = {
-        "regime": ("the %d timed launches follow %d warm-up launches (%.1f ms of work): the first milliseconds of "
-                   "load, before the power limiter has lowered the clock; context.sustained is the settled rate "
-                   "(>= %.0f ms of warm-up, then >= 25 ms of launches in ~1 ms chunks, median chunk)"
-                   % (args.steps, args.warmup, args.warmup * ms, m["sustained"]["warmup_ms"])),
+        "regime": ("the %d timed launches follow %d untimed ones (the %d requested, extended to >= %.0f ms of "
+                   "back-to-back work, %.1f ms here) so the clock has left its ramp out of idle; "
+                   "context.sustained is the settled rate over >= 25 ms (median of ~1 ms chunks)"
+                   % (args.steps, m["warmup_launches"], args.warmup, WARMUP_MS, m["warmup_ms"])),
+        "warmup_launches": m["warmup_launches"],
         "sustained": head["sustained"],
         "algorithmic_GBps": round(gbs, 1),
         "input_sha256": {w.name: digest},

@@ -36,6 +36,7 @@ EXPORTS = [
     "gemm_f16_bt", "gemm_f16_bt_select_config", "gemm_f16_bt_with_config",
     "softmax_rows_f16", "softmax_rows_f16_path", "flash_attn_fwd_f16",
     "gemm_status_string", "gemm_f16_time",
+    "mfma_f16_calibration", "mfma_f16_calibration_flops",
 ]
 SOFTMAX_PATHS = {0: "none", 1: "wave", 2: "workgroup", 3: "online"}
 
@@ -82,6 +83,10 @@ def load():
     lib.gemm_status_string.restype = ctypes.c_char_p
     lib.gemm_f16_time.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, i32, vp, i32, ctypes.POINTER(ctypes.c_float)]
     lib.gemm_f16_time.restype = i32
+    lib.mfma_f16_calibration.argtypes = [i32, i64, i64, vp, vp, vp]
+    lib.mfma_f16_calibration.restype = i32
+    lib.mfma_f16_calibration_flops.argtypes = [i32, i64, i64]
+    lib.mfma_f16_calibration_flops.restype = i64
     lib.gemm_f16_num_configs.argtypes = []
     lib.gemm_f16_num_configs.restype = i32
     lib.gemm_f16_config_info.argtypes = [i32, ctypes.c_char_p, i32]
@@ -161,6 +166,15 @@ def gemm_f16_time_raw(M, N, K, A, B, bias, C, epilogue: int, iters: int, stream=
     out = ctypes.c_float(-1.0)
     st = int(load().gemm_f16_time(config, M, N, K, A, B, bias, C, epilogue, stream, iters, ctypes.byref(out)))
     return st, float(out.value)
+
+
+def mfma_calibration_raw(shape: int, iters: int, workgroups: int, stamps, sink, stream=0) -> int:
+    """Launch the register-only MFMA loop (include/calibration_f16.h); stamps and sink are device pointers."""
+    return int(load().mfma_f16_calibration(shape, iters, workgroups, stamps, sink, stream))
+
+
+def mfma_calibration_flops(shape: int, iters: int, workgroups: int) -> int:
+    return int(load().mfma_f16_calibration_flops(shape, iters, workgroups))
 
 
 def softmax_rows_raw(rows, cols, X, Y, stream=0) -> int:

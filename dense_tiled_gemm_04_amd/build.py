@@ -1,9 +1,10 @@
 """Build the gfx950 HIP library libgemm_f16.so in-tree with hipcc.
 
-Three translation units: csrc/gemm_f16.hip (every GEMM kernel instantiation and
+Four translation units: csrc/gemm_f16.hip (every GEMM kernel instantiation and
 the C ABI of include/gemm_f16.h), csrc/softmax.hip (the row softmax, C ABI in
 include/softmax_f16.h) and csrc/attention.hip (the attention forward pass, C ABI
-in include/attention_f16.h).  Flags: gfx950 only, -O3, no
+in include/attention_f16.h), csrc/calibration.hip (the MFMA throughput
+calibration, C ABI in include/calibration_f16.h).  Flags: gfx950 only, -O3, no
 fast-math, packed-fp32 VALU instructions disabled, a pragma-unroll threshold
 high enough for the fully unrolled MFMA schedules.
 
@@ -30,9 +31,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libgemm_f16.so")
 RESOURCES_PATH = os.path.join(BUILD_DIR, "kernel_resources.json")
-SOURCES = [os.path.join(CSRC, f) for f in ("gemm_f16.hip", "softmax.hip", "attention.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("gemm_f16.hip", "softmax.hip", "attention.hip", "calibration.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("common.h", "tile_pipe_kernel.h", "skinny_kernel.h")] + [
-    os.path.join(INCLUDE, "gemm_f16.h"), os.path.join(INCLUDE, "softmax_f16.h"), os.path.join(INCLUDE, "attention_f16.h")
+    os.path.join(INCLUDE, "gemm_f16.h"), os.path.join(INCLUDE, "softmax_f16.h"), os.path.join(INCLUDE, "attention_f16.h"),
+    os.path.join(INCLUDE, "calibration_f16.h"),
 ]
 
 

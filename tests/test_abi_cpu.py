@@ -232,3 +232,14 @@ def test_time_helper_validates_before_any_hip_call():
     assert t(-1, 4, 4, 4, FAKE + 1, FAKE, None, FAKE, 0, 5) == 7
     assert out.value == -7.0                                             # untouched on every error
     assert t(-1, 0, 4, 4, None, None, None, None, 0, 5) == 0 and out.value == 0.0   # empty: no launch
+
+
+def test_mfma_calibration_validates_before_any_hip_call():
+    lib = g.load()
+    assert lib.mfma_f16_calibration(8, 10, 1, FAKE, FAKE, None) == 6           # shape not 16 / 32
+    assert lib.mfma_f16_calibration(16, 0, 1, FAKE, FAKE, None) == 1           # iters < 1
+    assert lib.mfma_f16_calibration(16, 10, 0, FAKE, FAKE, None) == 1          # no workgroups
+    assert lib.mfma_f16_calibration(16, 10, 65537, FAKE, FAKE, None) == 1
+    assert lib.mfma_f16_calibration(32, 10, 1, None, FAKE, None) == 2
+    assert lib.mfma_f16_calibration(32, 10, 1, FAKE + 4, FAKE, None) == 7
+    assert g.mfma_calibration_flops(32, 3, 2) == 2 * 32 * 32 * 16 * 8 * 8 * 3 * 2

@@ -645,3 +645,24 @@ def test_mfma16_configs_agree_bitwise(lib):
     assert_parity(outs[names[0]], ref, names[0])
     for n in names[1:]:
         assert np.array_equal(outs[n].view(np.uint16), outs[names[0]].view(np.uint16)), (n, names[0])
+
+
+# ---------------------------------------------------------------------------
+# the MFMA throughput calibration kernel
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [16, 32])
+def test_mfma_calibration_runs_and_stamps(lib, shape):
+    import dense_tiled_gemm_04_amd as g
+    wgs = 8
+    stamps = torch.zeros((wgs, 4), dtype=torch.int64, device="cuda")
+    sink = torch.full((wgs * 512,), float("nan"), dtype=torch.float32, device="cuda")
+    assert g.mfma_calibration_raw(shape, 200, wgs, stamps.data_ptr(), sink.data_ptr()) == 0
+    torch.cuda.synchronize()
+    st = stamps.cpu().numpy()
+    assert np.all(st[:, 1] > st[:, 0]) and np.all(st[:, 3] > st[:, 2])
+    # the shader clock the loop saw lies between 0.5 and 3 GHz
+    clk = (st[:, 1] - st[:, 0]) / ((st[:, 3] - st[:, 2]) / 100e6)
+    assert np.all((clk > 0.5e9) & (clk < 3.0e9)), clk
+    assert bool(torch.isfinite(sink).all())
+    per_mfma = 2 * 16 * 16 * 32 if shape == 16 else 2 * 32 * 32 * 16
+    assert g.mfma_calibration_flops(shape, 200, wgs) == per_mfma * 8 * 8 * 200 * wgs
