@@ -359,6 +359,12 @@ def space() -> list:
     out.append(Tile(256, 256, 64, 2, 4, 2, 4, 4, 3, "dma", wpe=2, mf=16, spread=14 + 32))
     out.append(Tile(256, 256, 64, 2, 4, 2, 4, 4, 3, "dma", wpe=2, mf=16, spread=14 + 96, bt=1))
     out.append(Tile(256, 256, 64, 2, 4, 2, 4, 4, 3, "dma", wpe=2, mf=16, spread=30 + 32, bt=1))
+    # eight waves with A's ring one stage deeper than B's (3 A + 2 B buffers, exactly 160 KiB): the A copies of
+    # stage kt+3 go out during stage kt, so they have two stages to land
+    for bs, ds in ((4, 2), (4, 3), (8, 2), (8, 3)):
+        out.append(Tile(256, 256, 64, 2, 4, 2, 4, bs, ds, "dma", wpe=2, mf=16, spread=14 + 96 + 128))
+    for bs, ds in ((4, 3), (8, 2)):
+        out.append(Tile(256, 256, 64, 2, 4, 2, 4, bs, ds, "dma", wpe=2, mf=16, spread=30 + 96 + 128, bt=1))
     # the same large schedules with the copies issued as buffer loads (the vendor's copy form)
     for bs in (8, 16):
         out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, 2, "buf", mf=16, spread=14 + 96))
@@ -442,18 +448,19 @@ def build_sweep_lib(verbose: bool = True, configs: list | None = None) -> str:
     configs = space() if configs is None else configs
     sel = {}
     for cls in CLASSES:
-        sel[cls] = next(i for i, c in enumerate(configs) if class_of(c, cls))
+        # the sweep launches forced configurations only; a class without a member points at entry 0
+        sel[cls] = next((i for i, c in enumerate(configs) if class_of(c, cls)), 0)
     emit_table(configs, sel, SWEEP_TABLE, "Sweep space (generated by sweep.py --build); not the product table.")
-    cmd = libbuild.compile_cmd(SWEEP_LIB + ".tmp")
-    cmd.insert(1, "-DGEMM_F16_CONFIG_TABLE=\"%s\"" % SWEEP_TABLE)
     if verbose:
         print("%d configurations; compiling %s" % (len(configs), SWEEP_LIB), flush=True)
     t = time.time()
-    r = subprocess.run(cmd, cwd=PKG_DIR, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + r.stderr[-4000:])
-    os.replace(SWEEP_LIB + ".tmp", SWEEP_LIB)
+    # only the GEMM unit; scratch is allowed here (a spilling configuration is merely slow), and reported
+    rows = libbuild.build_library(SWEEP_LIB, [os.path.join(PKG_DIR, "csrc", "gemm_f16.hip")],
+                                  defines=["-DGEMM_F16_CONFIG_TABLE=\"%s\"" % SWEEP_TABLE], allow_scratch=True,
+                                  resources_path=os.path.join(PKG_DIR, "_build", "sweep_kernel_resources.json"))
     if verbose:
+        for r in libbuild.scratch_users(rows):
+            print("uses scratch (%s bytes/lane): %s" % (r.get("ScratchSize [bytes/lane]"), r["kernel"]), flush=True)
         print("built in %.0f s" % (time.time() - t), flush=True)
     return SWEEP_LIB
 
