@@ -103,33 +103,34 @@ __device__ __forceinline__ f16x4 lds_read_tr16_b64(const GK_LDS char* p) {
 // places "s_waitcnt vmcnt(0)" before it, which serialises the prefetch of
 // stage s+1 behind the compute of stage s.  Here the kernels order the copies
 // themselves (wait_vmcnt<> + barrier before a stage is read).  The LDS
-// destination of lane l is m0 + size*l; m0 is written right before each copy
-// and listed as clobbered, so the compiler keeps no value of its own in m0
-// across a copy.  The s_nop covers the one wait state that gfx9 parts need
-// between an SALU write of m0 and an LDS-DMA that reads it.
+// destination of lane l is m0 + size*l; the destination is an "{m0}" operand,
+// so the compiler itself writes m0 before each copy (often computing the
+// address straight into it) and knows what m0 holds afterwards.  The s_nop
+// covers the one wait state that gfx9 parts need between an SALU write of m0
+// and an LDS-DMA that reads it.
 __device__ __forceinline__ uint32_t lds_addr(const GK_LDS void* p) { return (uint32_t)(uintptr_t)p; }
 
 // 16 bytes per lane from sbase + voff (global, 64-bit scalar base + 32-bit lane offset).
 __device__ __forceinline__ void dma_global_16(const void* sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
-                 : "memory", "m0");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds)
+                 : "memory");
 }
 // Through a buffer resource: each dword that is not wholly below num_records
 // reads as 0.  16 bytes per lane.
 __device__ __forceinline__ void dma_buffer_16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "s"(lds)
-                 : "memory", "m0");
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds)
+                 : "memory");
 }
 // 16 bytes per lane, marked non-temporal: for data streamed exactly once (the
 // skinny path's B), so it does not displace reused lines in the caches.
 __device__ __forceinline__ void dma_buffer_16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(r), "s"(lds)
-                 : "memory", "m0");
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(r), "{m0}"(lds)
+                 : "memory");
 }
 // 4 bytes per lane.
 __device__ __forceinline__ void dma_buffer_4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "s"(lds)
-                 : "memory", "m0");
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds)
+                 : "memory");
 }
 
 __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
