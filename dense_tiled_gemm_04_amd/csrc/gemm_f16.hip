@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "gemm_f16.h"
+#include "pingpong_kernel.h"
 #include "skinny_kernel.h"
 #include "tile_pipe_kernel.h"
 
@@ -52,6 +53,13 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int G, int BT, int NT, int EPI>
+hipError_t launch_pingpong(const GemmArgs& a, hipStream_t s) {
+    dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(PP_WAVES * 64);
+    hipLaunchKernelGGL((gemm_pingpong_kernel<G, EPI, BT, NT>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
 // Tile config: block tile BM x BN x BK, WM x WN waves, ST LDS stages, tile
 // order group G, barrier slot BS, copy stride DS, loader, LDS-write slot CS
 // (register loader), waves per SIMD WPE, MFMA shape MF (32 or 16), spread
@@ -64,6 +72,18 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
             launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, BT, 0>,        \
                 launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, BT, 1>,    \
                 launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, BT, 2>     \
+        }                                                                                          \
+    }
+
+// Ping-pong config (gemm_pingpong_kernel): 256x256 tile, 8 waves in two groups that alternate between
+// MFMAs and loads, a ring of 4 slots of 32-deep k-slices, LDS-DMA copies; tile order group G, B transposed
+// BT, non-temporal C stores NT.  It reports itself as an LDS-DMA tile with BK = 32 and schedule flag 256.
+#define PINGPONG_CFG(G, BT, NT, NAME)                                                              \
+    Config {                                                                                       \
+        NAME, KIND_TILE, PP_BM, PP_BN, PP_BK, 2, 4, LOAD_DMA, G, PP_SLOTS, 0, 0, 0, 2, 16,             \
+            256 | 32 | ((NT) ? 64 : 0), BT, 0, PP_LDS_BYTES, PP_WAVES * 64,                        \
+        {                                                                                          \
+            launch_pingpong<G, BT, NT, 0>, launch_pingpong<G, BT, NT, 1>, launch_pingpong<G, BT, NT, 2> \
         }                                                                                          \
     }
 

@@ -53,6 +53,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 TABLE = os.path.join(CSRC, "config_table.inc")
 SWEEP_LIB = os.path.join(PKG_DIR, "libgemm_f16_sweep.so")
 SWEEP_TABLE = os.path.join(PKG_DIR, "_build", "sweep_space.inc")
+WARM_MS = 50.0   # back-to-back work before a configuration's timed chunks
 
 LDS_PER_CU = 160 * 1024
 REGS_PER_LANE = 512      # VGPR + AGPR per SIMD lane, shared by the waves resident on the SIMD
@@ -151,12 +152,43 @@ class Skinny:
         return "SKINNY_CFG(%d, %d, %d, %d, %d, \"%s\")" % (self.mb, self.stages, self.bt, self.krot, self.a16, self.name)
 
 
+@dataclasses.dataclass(frozen=True)
+class PingPong:
+    """The ping-pong schedule (csrc/pingpong_kernel.h): a 256x256 tile on 8 waves in two groups, one wave of
+    each per SIMD, taking turns between 32 back-to-back MFMAs and the LDS reads and copies of their next
+    k-step, over a ring of 4 slots of 32-deep k-slices (128 KiB); staged epilogue."""
+    group: int = 4
+    bt: int = 0
+    nt: int = 1          # non-temporal C stores
+
+    kind = "tile"
+    loader = "dma"
+    bm, bn, bk, wm, wn, stages, wpe, mf = 256, 256, 32, 2, 4, 4, 2, 16
+
+    @property
+    def spread(self) -> int:
+        return 256 | 32 | (64 if self.nt else 0)
+
+    @property
+    def name(self) -> str:
+        return "pp_256x256x32_w2x4_g%d" % self.group + ("_nt" if self.nt else "") + ("_bt" if self.bt else "")
+
+    @property
+    def lds_bytes(self) -> int:
+        return 4 * (256 * 32 * 2 + 32 * 256 * 2)
+
+    def macro(self) -> str:
+        return "PINGPONG_CFG(%d, %d, %d, \"%s\")" % (self.group, self.bt, self.nt, self.name)
+
+
 def pow2(x: int) -> bool:
     return x > 0 and (x & (x - 1)) == 0
 
 
 def valid(c) -> bool:
     """The kernels' static_asserts plus the LDS and register budgets."""
+    if isinstance(c, PingPong):   # one fixed shape, within budget by construction (static_asserts)
+        return c.group in (1, 4, 8) and c.lds_bytes <= LDS_PER_CU
     if isinstance(c, Skinny):
         b_ins = SK_BK * SK_BN * 2 // 16 // (SK_WAVES * 64)
         a_ins = 16 * c.mb * SK_BK * 2 // (16 if c.a16 else 4) // (SK_WAVES * 64)
@@ -365,6 +397,10 @@ def space() -> list:
         out.append(Tile(256, 256, 64, 2, 4, 2, 4, bs, ds, "dma", wpe=2, mf=16, spread=14 + 96 + 128))
     for bs, ds in ((4, 3), (8, 2)):
         out.append(Tile(256, 256, 64, 2, 4, 2, 4, bs, ds, "dma", wpe=2, mf=16, spread=30 + 96 + 128, bt=1))
+    # the ping-pong schedule (two wave groups alternating MFMAs and loads)
+    for bt in (0, 1):
+        for nt in (0, 1):
+            out.append(PingPong(4, bt, nt))
     # the same large schedules with the copies issued as buffer loads (the vendor's copy form)
     for bs in (8, 16):
         out.append(Tile(256, 256, 64, 2, 2, 2, 4, bs, 2, "buf", mf=16, spread=14 + 96))
@@ -586,8 +622,9 @@ def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str
         def time_config(i):
             """Sustained time per launch of config i, as the benchmark sees it: launches back to back (the
             benchmark puts no event between them), since the power limit sets the clock within milliseconds
-            and the gaps of per-launch events would let the card rest.  From a short idle: >= 5 ms of warm-up,
-            then >= 25 ms in chunks of ~1 ms between event pairs.  Returns the sorted per-launch chunk times
+            and the gaps of per-launch events would let the card rest.  From a short idle: >= WARM_MS of
+            warm-up (the controller boosts, throttles and settles within ~40 ms), then >= 25 ms in chunks of
+            ~1 ms between event pairs.  Returns the sorted per-launch chunk times
             (us) and leaves C written from the first copy of B, or None if the config cannot run the call."""
             def args(r=0):
                 return (i, w.M, w.N, w.K, dA.data_ptr(), dBs[r % len(dBs)].data_ptr(),
@@ -605,7 +642,7 @@ def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str
             torch.cuda.synchronize()
             t_one = max(e0.elapsed_time(e1) / 3, 1e-3)   # ms
             time.sleep(0.02)
-            for r in range(int(math.ceil(5.0 / t_one))):
+            for r in range(int(math.ceil(WARM_MS / t_one))):
                 call(*args(r + 1))
             per = max(1, int(round(1.0 / t_one)))        # launches per chunk
             evs = []
@@ -699,10 +736,9 @@ def select(results_path: str, table_path: str = TABLE, summary_path: str | None 
                "(%s). Do not edit by hand; rerun the sweep." % os.path.basename(results_path))
     if summary_path:
         lines = ["# Offline sweep of the tile and skinny kernels", "",
-                 "Per (configuration, workload) on one MI355X: launches back to back, as in bench.py; after >= 5 ms of "
-                 "warm-up, >= 25 ms in ~1 ms chunks between HIP events, median chunk time per launch (the clock has "
-                 "settled under the power limit by then; records of earlier runs timed each launch between its own "
-                 "events); the skinny",
+                 "Per (configuration, workload) on one MI355X: launches back to back, as in bench.py; after >= %.0f ms of "
+                 "warm-up (records of runs before the warm-up was raised from 5 ms: the clock was still recovering "
+                 "then), >= 25 ms in ~1 ms chunks between HIP events, median chunk time per launch; the skinny" % WARM_MS,
                  "workloads rotate 3 copies of B so the Infinity Cache cannot serve it;",
                  "outputs screened against a float32 PyTorch reference on sampled rows (parity proper is the",
                  "oracle tests). Command: `python -m dense_tiled_gemm_04_amd.sweep --run RESULTS` on the GPU, then",
@@ -727,7 +763,7 @@ def ablation(results_path: str, out_path: str) -> None:
     t = {(r["config"], r["workload"]): r for r in recs if r.get("ok")}
     by_name = {c.name: c for c in space()}
     lines = ["# Ablations: tile order (swizzle) and LDS stages", "",
-             "Back-to-back launches timed in ~1 ms chunks over >= 25 ms (after >= 5 ms of warm-up), median chunk, per cell on one "
+             "Back-to-back launches timed in ~1 ms chunks over >= 25 ms (after the warm-up of the record's run), median chunk, per cell on one "
              "MI355X, from the same sweep records as the",
              "configuration table (`python -m dense_tiled_gemm_04_amd.sweep --run RESULTS` on the GPU, then",
              "`--ablation RESULTS`).", "",

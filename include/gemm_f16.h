@@ -170,7 +170,9 @@ int gemm_f16_num_configs(void);
  * AGPRs, 8 copies issued right after the stage barrier, 16 the next k-step's
  * B reads front-loaded, 32 C staged through LDS and written with
  * row-contiguous 16-byte stores, 64 those stores non-temporal, 128 A given a
- * third LDS buffer so its copies run a stage ahead of B's; of the skinny
+ * third LDS buffer so its copies run a stage ahead of B's, 256 the ping-pong
+ * schedule, whose two wave groups alternate between MFMAs and loads over a
+ * ring of four 32-deep k-slices; of the skinny
  * kernel: 1 A copied with 16-byte LDS-DMA), b_transposed, k_rotate (skinny:
  * K order rotated per workgroup), lds_bytes, threads. */
 int gemm_f16_config_info(int idx, char* buf, int buflen);

@@ -99,10 +99,11 @@ def test_space_is_valid_and_unique():
 
 def _table_entries(path):
     src = open(path).read()
-    tiles = re.findall(r'TILE_CFG\(([^)]*)\)', src)
+    tiles = re.findall(r'(?<!PINGPONG_)TILE_CFG\(([^)]*)\)', src)
     skinny = re.findall(r'SKINNY_CFG\(([^)]*)\)', src)
+    pingpong = re.findall(r'PINGPONG_CFG\(([^)]*)\)', src)
     sel = dict(re.findall(r'#define (SEL_\w+) (\d+)', src))
-    return tiles, skinny, {k: int(v) for k, v in sel.items()}
+    return tiles + [("pp", x) for x in pingpong], skinny, {k: int(v) for k, v in sel.items()}
 
 
 def test_product_table_entries_are_in_budget():
@@ -110,6 +111,11 @@ def test_product_table_entries_are_in_budget():
     n = len(tiles) + len(skinny)
     assert set(sel) == set(sweep.CLASSES) and all(0 <= v < n for v in sel.values())
     for t in tiles:
+        if isinstance(t, tuple):  # a ping-pong entry: group, B transposed, non-temporal C, name
+            f = [x.strip() for x in t[1].split(",")]
+            c = sweep.PingPong(int(f[0]), int(f[1]), int(f[2]))
+            assert sweep.valid(c) and f[3].strip('"') == c.name
+            continue
         f = [x.strip() for x in t.split(",")]
         c = sweep.Tile(*map(int, f[:9]), f[9][len("LOAD_"):].lower(), int(f[10]), int(f[11]),
                        int(f[12]), int(f[13]), int(f[14]))
