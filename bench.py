@@ -17,7 +17,7 @@ Prints ONE JSON line:
   cpu_baseline = the CPU oracle (fp64, all host threads) on a bounded sample.
   context   = the vendor BLAS in the same process (sequential and interleaved),
               the settled rate under the power limiter (context.sustained:
-              >= 5 ms of warm-up, then >= 25 ms of launches in ~1 ms chunks,
+              >= 50 ms of warm-up, then >= 25 ms of launches in ~1 ms chunks,
               median chunk), the library's own event-median helper
               gemm_f16_time, the sha256 of every input, a status per workload,
               and (GEMM workloads, unless --no-context) the fused bias+GELU MLP
@@ -50,7 +50,9 @@ if ROOT not in sys.path:
 
 PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
-WARMUP_MS = 5.0             # minimum back-to-back work before a timed region
+# minimum back-to-back work before a timed region: after idle the power controller boosts the clock for ~2 ms,
+# throttles hard at ~3-8 ms and settles after 30-40 ms (bench.py --clock-series)
+WARMUP_MS = 50.0
 
 
 # Sources each kernel family is built from; a change to any of them voids that family's recorded traffic.
@@ -253,6 +255,57 @@ class PowerSampler:
                 "samples": len(self.samples[card]), "board_power_W": round(pw / 1e6, 1) if pw else None,
                 "idle_power_W": round(self._idle[card] / 1e6, 1) if self._idle.get(card) else None,
                 "sclk_GHz_hwmon": round(fr / 1e9, 3) if fr else None}
+
+
+def clock_series(g, torch, ms_total: float = 80.0) -> int:
+    """How the power controller sets the clock under sustained load: after 0.5 s idle, ms_total of back-to-back
+    launches of the 4096^3 GEMM and of the MLP up-projection in ~1 ms chunks between HIP events; prints one
+    JSON line per run with the time per launch of every chunk and the chunk's end time."""
+    import numpy as np
+    import workloads
+
+    lib = g.load()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    for name in ("gemm_4096", "mlp_up_8192x16384x4096"):
+        w = workloads.WORKLOADS[name]
+        A, B, bias = workloads.make_inputs(w)
+        dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        db = torch.from_numpy(bias).cuda() if bias is not None else None
+        dC = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+        epi = g.EPILOGUES[w.epilogue]
+
+        def step():
+            st = lib.gemm_f16(w.M, w.N, w.K, dA.data_ptr(), dB.data_ptr(), db.data_ptr() if db is not None else None,
+                              dC.data_ptr(), epi, sh)
+            if st != 0:
+                raise g.GemmError(st)
+        step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per = max(1, int(round(1.0 / max(e0.elapsed_time(e1), 1e-3))))
+        n = int(ms_total / max(per * e0.elapsed_time(e1), 1e-3)) + 1
+        time.sleep(0.5)
+        evs = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(per):
+                step()
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        us = [a.elapsed_time(b) / per * 1e3 for a, b in evs]
+        end_ms = np.cumsum([u * per / 1e3 for u in us])
+        print(json.dumps({"clock_series": name, "launches_per_chunk": per,
+                          "us_per_launch": [round(u, 1) for u in us], "chunk_end_ms": [round(float(t), 2) for t in end_ms]}),
+              flush=True)
+        del dA, dB, dC
+    return 0
 
 
 def mfma_calibration(g, torch, seconds: float = 0.4) -> int:
@@ -587,7 +640,7 @@ def warm_up(torch, stream, step, warmup: int):
     return 4 + n_warm, one_ms
 
 
-def sustained_ms(torch, stream, step, launch_ms: float, warm_ms: float = 5.0, total_ms: float = 25.0,
+def sustained_ms(torch, stream, step, launch_ms: float, warm_ms: float = WARMUP_MS, total_ms: float = 25.0,
                  chunk_ms: float = 1.0) -> dict:
     """The settled rate under the power limiter: >= warm_ms of untimed back-to-back launches, then >= total_ms of
     launches timed in chunks of ~chunk_ms, each chunk between its own pair of HIP events on the launch stream.
@@ -783,6 +836,9 @@ def main() -> int:
                     help="run only the register-only MFMA loop (both MFMA shapes) and the shipped 4096^3 GEMM "
                          "back to back, with board power and clock: the practical MFMA ceiling under the power "
                          "limit")
+    ap.add_argument("--clock-series", action="store_true",
+                    help="run only the 4096^3 GEMM and the MLP shape back to back for 80 ms each after idle, and print "
+                         "the time per launch of every ~1 ms chunk (how the power controller settles)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -803,6 +859,8 @@ def main() -> int:
         return hbm_calibration(g, torch)
     if args.mfma_calibration:
         return mfma_calibration(g, torch)
+    if args.clock_series:
+        return clock_series(g, torch)
     if args.workload in workloads.SOFTMAX_WORKLOADS:
         return bench_softmax(args, g, torch, workloads.SOFTMAX_WORKLOADS[args.workload])
     if args.workload in workloads.ATTENTION_WORKLOADS:
@@ -828,8 +886,9 @@ def main() -> int:
     head = context_line(m)
     context = {
         "regime": ("the %d timed launches follow %d untimed ones (the %d requested, extended to >= %.0f ms of "
-                   "back-to-back work, %.1f ms here) so the clock has left its ramp out of idle; "
-                   "context.sustained is the settled rate over >= 25 ms (median of ~1 ms chunks)"
+                   "back-to-back work, %.1f ms here): after idle the power controller boosts, throttles and settles "
+                   "within ~40 ms, so this is the settled rate; context.sustained is the same over >= 25 ms (median "
+                   "of ~1 ms chunks)"
                    % (args.steps, m["warmup_launches"], args.warmup, WARMUP_MS, m["warmup_ms"])),
         "warmup_launches": m["warmup_launches"],
         "sustained": head["sustained"],
