@@ -235,12 +235,13 @@ def valid(c) -> bool:
         if c.cslot + (ps - 1) * c.dstride >= d["ksteps"] * d["nmma"]:
             return False
     # registers per lane: accumulators, two fragment sets, staging (register loader), one copy offset per
-    # chunk (plus the k offset of each A chunk for the buffer loader) and ~56 of addressing and temporaries.  With one wave per SIMD the accumulators sit in the 256 AGPRs and the
+    # chunk (plus the k offset of each A chunk for the buffer loader) and ~48 of addressing and temporaries
+    # (the compiler's resource report of the eight-wave 256x256 kernels: 80-92 VGPRs beside 128 AGPRs).  With one wave per SIMD the accumulators sit in the 256 AGPRs and the
     # rest must fit the 256 VGPRs; with more waves all of it shares 512 / waves.
     acc = d["tm"] * d["tn"] * d["nacc"]
     frags = (1 if c.spread & 2 else 2) * d["tm"] * 4 + 2 * d["tn"] * 4
     stg = 4 * ps if c.loader == "reg" else 0
-    rest = frags + stg + ps + (d["a_ins"] if c.loader == "buf" else 0) + 56
+    rest = frags + stg + ps + (d["a_ins"] if c.loader == "buf" else 0) + 48
     if c.wpe == 1:
         return acc <= REGS_PER_LANE // 2 and rest <= REGS_PER_LANE // 2
     return acc + rest <= REGS_PER_LANE // c.wpe
@@ -397,6 +398,13 @@ def space() -> list:
         out.append(Tile(256, 256, 64, 2, 4, 2, 4, bs, ds, "dma", wpe=2, mf=16, spread=14 + 96 + 128))
     for bs, ds in ((4, 3), (8, 2)):
         out.append(Tile(256, 256, 64, 2, 4, 2, 4, bs, ds, "dma", wpe=2, mf=16, spread=30 + 96 + 128, bt=1))
+    # eight waves for the buffer loader (unaligned shapes): 256x192 tiles on 4x2 waves (64x96 per wave, 12-chunk
+    # epilogue rows) for the ragged class, 256x256 on 2x4 waves for the big unaligned class
+    for bs, ds in ((4, 3), (8, 2), (0, 3)):
+        out.append(Tile(256, 192, 64, 4, 2, 2, 4, bs, ds, "buf", wpe=2, mf=16, spread=14 + 32))
+        out.append(Tile(256, 192, 64, 4, 2, 2, 4, bs, ds, "buf", wpe=2, mf=16, spread=30 + 96, bt=1))
+    for bs, ds in ((4, 3), (8, 2)):
+        out.append(Tile(256, 256, 64, 2, 4, 2, 4, bs, ds, "buf", wpe=2, mf=16, spread=14 + 32))
     # the ping-pong schedule (two wave groups alternating MFMAs and loads)
     for bt in (0, 1):
         for nt in (0, 1):
@@ -700,6 +708,27 @@ def run(results_path: str, lib_path: str = SWEEP_LIB, iters: int = 20, only: str
     out.close()
 
 
+def scratch_configs(resources_path: str = os.path.join(PKG_DIR, "_build", "sweep_kernel_resources.json")) -> set:
+    """Names of the configurations whose kernels used scratch memory in the last sweep build (none if unknown)."""
+    import re
+
+    if not os.path.exists(resources_path) or not os.path.exists(SWEEP_TABLE):
+        return set()
+    rows = json.load(open(resources_path))
+    bad_sym = [r["kernel"] for r in rows if r.get("ScratchSize [bytes/lane]", 0) or r.get("VGPRs Spill", 0)]
+    out = set()
+    for c in space():
+        if c.kind != "tile" or isinstance(c, PingPong):
+            continue
+        args = [c.bm, c.bn, c.bk, c.wm, c.wn, c.stages, c.group]
+        tail = [c.bslot, c.dstride, {"dma": 0, "reg": 1, "buf": 2}[c.loader], c.cslot, c.wpe, c.mf, c.spread, c.bt]
+        for sym in bad_sym:
+            v = [int(x) for x in re.findall(r"Li(-?\d+)E", sym)]
+            if "gemm_tile_pipe_kernel" in sym and v[:7] == args and v[8:16] == tail:
+                out.add(c.name)
+    return out
+
+
 def select(results_path: str, table_path: str = TABLE, summary_path: str | None = None, note: str = "") -> dict:
     recs = [json.loads(l) for l in open(results_path) if l.strip()]
     # classes come from the current workload table, so a reclassification needs no new measurements
@@ -707,12 +736,13 @@ def select(results_path: str, table_path: str = TABLE, summary_path: str | None 
     for r in recs:
         r["classes"] = wl_classes.get(r["workload"], r["classes"])
     by_name = {c.name: c for c in space()}
+    spilled = scratch_configs()
     chosen, scores = {}, {}
     for cls in CLASSES:
         wls = sorted({r["workload"] for r in recs if cls in r["classes"]})
         best = None
         for name, c in by_name.items():
-            if not class_of(c, cls):
+            if not class_of(c, cls) or name in spilled:
                 continue
             ts = [r["median_us"] for r in recs if r["config"] == name and r["workload"] in wls]
             oks = [r["ok"] for r in recs if r["config"] == name and r["workload"] in wls]
