@@ -34,7 +34,7 @@ EXPORTS = [
     "gemm_f16_select_config", "gemm_f16_with_config", "vector_add_f32",
     "gemm_f16_ex", "gemm_f16_select_config_ex", "gemm_f16_with_config_ex",
     "gemm_f16_bt", "gemm_f16_bt_select_config", "gemm_f16_bt_with_config",
-    "softmax_rows_f16", "softmax_rows_f16_path", "flash_attn_fwd_f16",
+    "softmax_rows_f16", "softmax_rows_f16_path", "flash_attn_fwd_f16", "flash_attn_fwd_f16_kernel",
     "gemm_status_string", "gemm_f16_time",
     "mfma_f16_calibration", "mfma_f16_calibration_flops",
 ]
@@ -99,6 +99,8 @@ def load():
     lib.softmax_rows_f16_path.restype = i32
     lib.flash_attn_fwd_f16.argtypes = [i64, i64, i64, i64, i64, vp, vp, vp, vp, i32, ctypes.c_float, vp]
     lib.flash_attn_fwd_f16.restype = i32
+    lib.flash_attn_fwd_f16_kernel.argtypes = [i64, i64, i64, i64, i64, vp, vp, vp, vp, i32, ctypes.c_float, i32, vp]
+    lib.flash_attn_fwd_f16_kernel.restype = i32
     _lib = lib
     return lib
 
@@ -301,13 +303,21 @@ def softmax_f16(X, out=None):
     return out
 
 
-def flash_attn_raw(B, H, Nq, Nkv, D, Q, K, V, O, causal: bool, scale: float, stream=0) -> int:
-    return int(load().flash_attn_fwd_f16(B, H, Nq, Nkv, D, Q, K, V, O, 1 if causal else 0, float(scale), stream))
+# kernels of the attention forward pass (include/attention_f16.h)
+ATTN_KERNEL_AUTO, ATTN_KERNEL_BLOCK_SERIAL, ATTN_KERNEL_PIPELINED = 0, 1, 2
 
 
-def flash_attn(Q, K, V, causal: bool = False, scale: float | None = None, out=None):
+def flash_attn_raw(B, H, Nq, Nkv, D, Q, K, V, O, causal: bool, scale: float, stream=0, kernel=None) -> int:
+    if kernel is None:
+        return int(load().flash_attn_fwd_f16(B, H, Nq, Nkv, D, Q, K, V, O, 1 if causal else 0, float(scale), stream))
+    return int(load().flash_attn_fwd_f16_kernel(B, H, Nq, Nkv, D, Q, K, V, O, 1 if causal else 0, float(scale),
+                                                int(kernel), stream))
+
+
+def flash_attn(Q, K, V, causal: bool = False, scale: float | None = None, out=None, kernel=None):
     """Attention forward on contiguous float16 GPU tensors Q [B,H,Nq,D], K and V [B,H,Nkv,D] on the current
-    stream; D is 64 or 128, scale defaults to 1/sqrt(D), causal masks keys j > i.  Returns O [B,H,Nq,D]."""
+    stream; D is 64 or 128, scale defaults to 1/sqrt(D), causal masks keys j > i.  Returns O [B,H,Nq,D].
+    `kernel` (an ATTN_KERNEL_* value) forces one of the kernels; None is the default dispatch."""
     import math
     import torch
     for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
@@ -326,7 +336,7 @@ def flash_attn(Q, K, V, causal: bool = False, scale: float | None = None, out=No
             raise ValueError("out must have Q's shape")
     with torch.cuda.device(Q.device):
         st = flash_attn_raw(Bn, Hn, Nq, Nkv, D, Q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr(), causal,
-                            scale, _stream_handle())
+                            scale, _stream_handle(), kernel)
     if st != 0:
         raise GemmError(st)
     return out

@@ -310,6 +310,322 @@ flash_attn_fwd_kernel(FaArgs p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Software-pipelined forward kernel for D = 128.
+//
+// The block-serial kernel above runs, per 64-key block, the score MFMAs, then
+// the softmax on the vector ALU, then the PV MFMAs; each stage waits for the
+// one before, so a wave's matrix cores idle through its softmax.  A 32x32x16
+// MFMA occupies the matrix core for 32 cycles, during which the same wave can
+// issue independent vector instructions (about one exponential and two or
+// three FMAs) at almost no cost.  This kernel therefore interleaves the stages
+// of neighbouring blocks within each wave:
+//   phase A(j): the score MFMAs of block j+1    || exponentials of block j, keys 32..63
+//   phase B(j): the PV MFMAs of block j         || row maximum of block j+1 and its
+//                                                  exponentials of keys 0..31
+// Each phase is a fixed sequence of 16 slots fenced by scheduling barriers; a
+// slot holds one MFMA, the LDS reads of a later slot's operand, and a share of
+// the vector work.  Block j+1's first-half exponentials use the reference
+// maximum as it stands; if the block's maximum exceeds it by more than 2^8 (the
+// lazy-rescale test of the block-serial kernel), the reference is raised after
+// phase B, the accumulators and the running sum are rescaled, and those
+// exponentials are recomputed.  The result is the block-serial kernel's
+// arithmetic, evaluated in a different order of instructions.
+// K and V tiles are copied one block apart: after the barrier that opens
+// A(j), K(j+2) and V(j+1) are issued into the buffers that K(j) and V(j-1)
+// have left, so two buffers of each suffice.
+template <bool CAUSAL, bool PRESCALE>
+__global__ void __launch_bounds__(FA_NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+flash_attn_fwd_pipe_kernel(FaArgs p) {
+    constexpr int D = 128;
+    constexpr int CH = D / 8;
+    constexpr int TILE = FA_BN * D * 2;
+    constexpr int INS = FA_BN * CH / (FA_NW * 64);
+    constexpr int KS = D / 16;   // 8 k-steps of the score product
+    constexpr int DB = D / 32;   // 4 output column blocks
+    constexpr int PDK = 3;       // K fragment reads issued this many slots ahead
+    constexpr int PDV = 3;       // V fragment reads issued this many slots ahead
+    static_assert(INS * FA_NW * 64 == FA_BN * CH, "copy split");
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K[2] | V[2]
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int Nq = p.Nq, Nkv = p.Nkv;
+    const int lid = xcd_contiguous_id((int)blockIdx.x, (int)gridDim.x);
+    int qb = lid % p.q_blocks;
+    const int64_t bh = lid / p.q_blocks;
+    if (CAUSAL) qb = p.q_blocks - 1 - qb;  // longest rows first
+    const int q0 = qb * FA_BM;
+    const int row0 = q0 + 32 * wave_s;
+    const int i = row0 + (lane & 31);
+    const f16* Qp = p.Q + bh * (int64_t)Nq * D;
+    f16* Op = p.O + bh * (int64_t)Nq * D;
+
+    f16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        if (i < Nq) {
+            qf[ks] = *(const f16x8*)(Qp + (int64_t)i * D + 16 * ks + 8 * (lane >> 5));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qf[ks][e] = (f16)0.0f;
+        }
+    }
+
+    const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.K + bh * (int64_t)Nkv * D), (short)0, Nkv * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.V + bh * (int64_t)Nkv * D), (short)0, Nkv * D * 2, 0x00020000);
+    // Copy t of a tile moves key rows 16 t .. 16 t + 15 (4096 bytes further on than copy t - 1); the swizzle
+    // of a chunk depends on its row only through the row's low bits, which t does not change, so one
+    // offset per lane serves every copy.
+    uint32_t k_off0, v_off0;
+    {
+        const int jr = 4 * wave + (lane >> 4), pc = lane & 15;
+        k_off0 = (uint32_t)((jr * D + 8 * (pc ^ swz_k<D>(jr))) * 2);
+        v_off0 = (uint32_t)((jr * D + 8 * (pc ^ swz_v<D>(jr))) * 2);
+    }
+    const uint32_t lds0 = lds_addr((GK_LDS char*)smem) + wave_s * 64 * 16;
+    // Offsets derived from a base register are formed where they are used: an empty asm statement makes the
+    // base opaque there, so that the compiler does not hoist the derived values out of the loop and hold
+    // them in registers for its whole length.
+    auto opaque = [](auto v) {
+        asm volatile("" : "+v"(v));
+        return v;
+    };
+    auto issue_k = [&](int jb) {
+        const uint32_t kv = (uint32_t)jb * FA_BN * D * 2, ko = opaque(k_off0);
+#pragma unroll
+        for (int t = 0; t < INS; ++t)
+            dma_buffer_16(k_rsrc, ko + (kv + t * 4096u), lds0 + (jb & 1) * TILE + t * FA_NW * 64 * 16);
+    };
+    auto issue_v = [&](int jb) {
+        const uint32_t kv = (uint32_t)jb * FA_BN * D * 2, vo = opaque(v_off0);
+#pragma unroll
+        for (int t = 0; t < INS; ++t)
+            dma_buffer_16(v_rsrc, vo + (kv + t * 4096u), lds0 + (2 + (jb & 1)) * TILE + t * FA_NW * 64 * 16);
+    };
+
+    // LDS read offsets.  K fragment of score slot s (k-step s/2, 32-key half s%2): key row 32 (s%2) + l%32,
+    // 16-byte chunk (2 (s/2) + l/32) XOR (row % 16); the row's high half and the k-step enter as 8192 (s%2)
+    // and an XOR with 32 (s/2).  V^T fragment (column block db, key half h, 16-key step st) of the
+    // block-serial kernel: 2048 h + 4096 st + (vbase XOR 64 db).
+    const int kbase = ((lane & 31) * 256) | (((lane >> 5) ^ (lane & 15)) << 4);
+    int vbase;
+    {
+        const int g = lane >> 4, jq = (lane >> 2) & 3, q = lane & 3;
+        vbase = (4 * (g >> 1) + jq) * 256 + 64 * jq + 32 * (g & 1) + 16 * (q >> 1) + 8 * (q & 1);
+    }
+    auto k_rd = [&](int kb, int s) { return 8192 * (s & 1) + (kb ^ (32 * (s >> 1))); };
+    auto v_rd = [&](int vb, int h, int db, int st) { return 2048 * h + 4096 * st + (vb ^ (64 * db)); };
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+    const f32x16 zero16 = {};
+    float m_run, l_run = 0.0f;
+    const float c = PRESCALE ? 1.0f : p.scale_log2;
+    const f16x2 ones = {(f16)1.0f, (f16)1.0f};
+
+    // scores of two blocks in flight (sc[parity][32-key half]) and their fp16 probabilities
+    f32x16 sc[2][2];
+    f16x8 pf[2][2][2];
+
+    const int kv_blocks_all = (Nkv + FA_BN - 1) / FA_BN;
+    const int n_wg = CAUSAL ? min(kv_blocks_all, (q0 + FA_BM - 1) / FA_BN + 1) : kv_blocks_all;
+    const int n_w = CAUSAL ? min(kv_blocks_all, (row0 + 31) / FA_BN + 1) : kv_blocks_all;
+    // blocks [0, n_plain) need no mask for any row of this wave
+    int n_plain = min(Nkv / FA_BN, n_w);
+    if (CAUSAL) n_plain = min(n_plain, (row0 + 1) / FA_BN);
+
+    auto prepare = [&](f32x16 (&s)[2], int jb) {  // scale (non-positive scales) and mask one block's scores
+        if constexpr (PRESCALE) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[jj][r] *= p.scale_log2;
+        }
+        if (jb >= n_plain) {
+            const int kv0 = jb * FA_BN;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = kv0 + 32 * jj + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (j >= Nkv || (CAUSAL && j > i)) s[jj][r] = -INFINITY;
+                }
+        }
+    };
+    // partner lane l ^ 32 holds the other half of the row's keys
+    auto row_max = [&](float m) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    };
+    auto row_sum = [&](float v) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    };
+    // probabilities of scores 2k, 2k+1 of one 32-key half, rounded to fp16 in a pair; the row sum adds the
+    // same rounded values
+    // The pair and the running sum pass through an empty asm statement, which keeps their computation in the
+    // schedule slot where the pair is formed: the optimiser would otherwise sink this arithmetic to its
+    // first use (past the end of the phase) and undo the interleaving with the MFMAs.
+    auto exp_pair = [&](const f32x16& s, f16x8 (&pd)[2], int k, float m, float& l) {
+        const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * k], c, -m));
+        const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * k + 1], c, -m));
+        f16x2 h = __builtin_convertvector((f32x2){a, b}, f16x2);
+        l = __builtin_amdgcn_fdot2(h, ones, l, false);
+        asm volatile("" : "+v"(h), "+v"(l));
+        pd[k >> 2][2 * (k & 3)] = h[0];
+        pd[k >> 2][2 * (k & 3) + 1] = h[1];
+    };
+    auto max16 = [&](const f32x16& s, int h) {  // maximum of registers 8h .. 8h+7
+        float m = fmaxf(s[8 * h], s[8 * h + 1]);
+#pragma unroll
+        for (int r = 2; r < 8; ++r) m = fmaxf(m, s[8 * h + r]);
+        return m;
+    };
+
+    // ---- prologue: K(0), K(1), V(0) in LDS; block 0 scored, its reference maximum set, keys 0..31
+    issue_k(0);
+    if (n_wg > 1) issue_k(1);
+    issue_v(0);
+    wait_vmcnt0();
+    __syncthreads();
+    {
+        const GK_LDS char* Ks = (const GK_LDS char*)smem;
+        const int kb = opaque(kbase);
+#pragma unroll
+        for (int s = 0; s < 2 * KS; ++s) {
+            const f16x8 kf = *(const GK_LDS f16x8*)(Ks + k_rd(kb, s));
+            sc[0][s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[s >> 1], s < 2 ? zero16 : sc[0][s & 1], 0, 0, 0);
+        }
+        prepare(sc[0], 0);
+        const float mb = row_max(fmaxf(fmaxf(max16(sc[0][0], 0), max16(sc[0][0], 1)),
+                                       fmaxf(max16(sc[0][1], 0), max16(sc[0][1], 1))));
+        m_run = mb * c;  // the first block holds key 0, which every row may see: finite
+#pragma unroll
+        for (int k = 0; k < 8; ++k) exp_pair(sc[0][0], pf[0][0], k, m_run, l_run);
+    }
+
+    // phase A(j): score MFMAs of block j+1 (NEXT) || exponentials of block j, keys 32..63
+    auto phase_a = [&]<int PAR, bool NEXT>() {
+        constexpr int NX = PAR ^ 1;
+        const float mr = opaque(m_run);
+        if constexpr (NEXT) {
+            const GK_LDS char* Kn = (const GK_LDS char*)smem + NX * TILE;  // block j+1 has parity NX
+            f16x8 kf[2 * KS];
+            const int kb = opaque(kbase);
+#pragma unroll
+            for (int s = 0; s < PDK; ++s) kf[s] = *(const GK_LDS f16x8*)(Kn + k_rd(kb, s));
+#pragma unroll
+            for (int s = 0; s < 2 * KS; ++s) {
+                if (s + PDK < 2 * KS) kf[s + PDK] = *(const GK_LDS f16x8*)(Kn + k_rd(kb, s + PDK));
+                sc[NX][s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[s], qf[s >> 1], s < 2 ? zero16 : sc[NX][s & 1],
+                                                                        0, 0, 0);
+                if (s & 1) exp_pair(sc[PAR][1], pf[PAR][1], s >> 1, mr, l_run);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) exp_pair(sc[PAR][1], pf[PAR][1], k, mr, l_run);
+        }
+    };
+    // phase B(j): PV MFMAs of block j || (NEXT) row maximum of block j+1 and its exponentials of keys 0..31,
+    // formed with the reference maximum as it stands; returns block j+1's scaled row maximum
+    auto phase_b = [&]<int PAR, bool NEXT>(float& l_half) {
+        constexpr int NX = PAR ^ 1;
+        const GK_LDS char* Vs = (const GK_LDS char*)smem + (2 + PAR) * TILE;
+        const float mr = opaque(m_run);
+        f16x8 vf[16];
+        const int vb = opaque(vbase);
+        auto read_v = [&](int s) {
+            const int st = s >> 2, db = s & 3;
+            const f16x4 v0 = lds_read_tr16_b64(Vs + v_rd(vb, 0, db, st));
+            const f16x4 v1 = lds_read_tr16_b64(Vs + v_rd(vb, 1, db, st));
+            vf[s] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+#pragma unroll
+        for (int s = 0; s < PDV; ++s) read_v(s);
+        float mp[4], mc = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            if (s + PDV < 16) read_v(s + PDV);
+            const int st = s >> 2;
+            oacc[s & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[s], pf[PAR][st >> 1][st & 1], oacc[s & 3], 0, 0, 0);
+            if constexpr (NEXT) {
+                if (s < 4) {
+                    mp[s] = max16(sc[NX][s >> 1], s & 1);
+                    asm volatile("" : "+v"(mp[s]));
+                }
+                if (s == 4) {
+                    mc = row_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]))) * c;
+                    asm volatile("" : "+v"(mc));
+                }
+                if (s >= 6 && s < 14) exp_pair(sc[NX][0], pf[NX][0], s - 6, mr, l_half);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return mc;
+    };
+
+    // one pipelined step: PAR is the parity of block j (its scores are sc[PAR], probabilities pf[PAR])
+    auto step = [&]<int PAR>(int j) {
+        constexpr int NX = PAR ^ 1;
+        wait_vmcnt0();
+        __syncthreads();  // K(j+1) and V(j) in LDS for every wave; K(j) and V(j-1) free
+        if (j + 2 < n_wg) issue_k(j + 2);
+        if (j + 1 < n_wg) issue_v(j + 1);
+        if (j >= n_w) return;  // past this wave's last visible block (causal): copies and barriers only
+        if (j + 1 < n_w) {
+            phase_a.template operator()<PAR, true>();
+            prepare(sc[NX], j + 1);
+            float l_half = 0.0f;
+            const float mc = phase_b.template operator()<PAR, true>(l_half);
+            // The reference maximum moves only when some row's block maximum exceeds it by more than 2^8;
+            // block j+1's first-half probabilities were formed with the old one and are formed again.
+            if (__any(mc > m_run + kLazyLog2)) {
+                const float m_new = fmaxf(m_run, mc);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                l_half = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) exp_pair(sc[NX][0], pf[NX][0], k, m_run, l_half);
+            }
+            l_run += l_half;
+        } else {
+            phase_a.template operator()<PAR, false>();
+            float unused = 0.0f;
+            phase_b.template operator()<PAR, false>(unused);
+        }
+    };
+
+    for (int j = 0; j < n_wg; j += 2) {
+        step.template operator()<0>(j);
+        if (j + 1 < n_wg) step.template operator()<1>(j + 1);
+    }
+
+    const float inv = 1.0f / row_sum(l_run);
+    if (i < Nq) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                f16x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = (f16)(oacc[db][4 * r4 + e] * inv);
+                *(f16x4*)(Op + (int64_t)i * D + 32 * db + 8 * r4 + 4 * (lane >> 5)) = o;
+            }
+    }
+}
+
 template <int D, bool CAUSAL, bool PRESCALE>
 hipError_t launch(const FaArgs& a, int64_t BH, hipStream_t s) {
     hipLaunchKernelGGL((flash_attn_fwd_kernel<D, CAUSAL, PRESCALE>), dim3((unsigned)(BH * a.q_blocks)),
@@ -323,12 +639,33 @@ hipError_t launch_d(const FaArgs& a, int64_t BH, bool causal, bool prescale, hip
     return causal ? launch<D, true, false>(a, BH, s) : launch<D, false, false>(a, BH, s);
 }
 
+template <bool CAUSAL, bool PRESCALE>
+hipError_t launch_pipe(const FaArgs& a, int64_t BH, hipStream_t s) {
+    hipLaunchKernelGGL((flash_attn_fwd_pipe_kernel<CAUSAL, PRESCALE>), dim3((unsigned)(BH * a.q_blocks)),
+                       dim3(FA_NW * 64), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_pipe_d(const FaArgs& a, int64_t BH, bool causal, bool prescale, hipStream_t s) {
+    if (prescale) return causal ? launch_pipe<true, true>(a, BH, s) : launch_pipe<false, true>(a, BH, s);
+    return causal ? launch_pipe<true, false>(a, BH, s) : launch_pipe<false, false>(a, BH, s);
+}
+
 }  // namespace
 
 extern "C" {
 
 int flash_attn_fwd_f16(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, const void* Q, const void* K,
                        const void* V, void* O, int causal, float scale, void* stream) {
+    return flash_attn_fwd_f16_kernel(B, H, Nq, Nkv, D, Q, K, V, O, causal, scale, FLASH_ATTN_KERNEL_AUTO, stream);
+}
+
+int flash_attn_fwd_f16_kernel(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, const void* Q,
+                              const void* K, const void* V, void* O, int causal, float scale, int kernel,
+                              void* stream) {
+    if (kernel != FLASH_ATTN_KERNEL_AUTO && kernel != FLASH_ATTN_KERNEL_BLOCK_SERIAL &&
+        kernel != FLASH_ATTN_KERNEL_PIPELINED)
+        return GEMM_ERR_NO_CONFIG;
     if (B < 0 || H < 0 || Nq < 0 || Nkv < 0 || D < 0) return GEMM_ERR_INVALID_DIM;
     if (B == 0 || H == 0 || Nq == 0) return GEMM_OK;
     if (Nkv == 0) return GEMM_ERR_INVALID_DIM;  // a query with no key has no softmax
@@ -355,7 +692,12 @@ int flash_attn_fwd_f16(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
     // raw scores is the maximum of the scaled ones); otherwise scores are
     // scaled first
     const bool prescale = !(scale > 0.0f);
-    e = D == 128 ? launch_d<128>(a, B * H, causal != 0, prescale, s) : launch_d<64>(a, B * H, causal != 0, prescale, s);
+    if (kernel == FLASH_ATTN_KERNEL_PIPELINED && D != 128) return GEMM_ERR_UNSUPPORTED;
+    if (D == 128 && kernel != FLASH_ATTN_KERNEL_BLOCK_SERIAL)
+        e = launch_pipe_d(a, B * H, causal != 0, prescale, s);
+    else
+        e = D == 128 ? launch_d<128>(a, B * H, causal != 0, prescale, s)
+                     : launch_d<64>(a, B * H, causal != 0, prescale, s);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 

@@ -46,10 +46,35 @@ extern "C" {
 #endif
 
 /* O = attention(Q, K, V) as above on `stream`; scale is usually 1/sqrt(D).
- * Returns a gemm_status_t. */
+ * Returns a gemm_status_t.  Same as flash_attn_fwd_f16_kernel with
+ * FLASH_ATTN_KERNEL_AUTO. */
 int flash_attn_fwd_f16(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
                        const void* Q, const void* K, const void* V, void* O,
                        int causal, float scale, void* stream);
+
+/* Kernels of the forward pass.  Both form the same fp16 probabilities (the
+ * same lazily raised reference maximum, the same fp32 exponent arithmetic);
+ * the pipelined kernel adds a block's row sums in another order, so the two
+ * agree to fp32 rounding of the normaliser, not bit for bit.  They differ in
+ * instruction order:
+ *   BLOCK_SERIAL  per 64-key block: scores, softmax, PV product, in turn
+ *                 (D = 64 or 128)
+ *   PIPELINED     the scores of block j+1 and the PV product of block j run on
+ *                 the matrix cores while the same wave computes the softmax of
+ *                 its neighbouring blocks (D = 128 only)
+ *   AUTO          PIPELINED for D = 128, BLOCK_SERIAL for D = 64 */
+enum {
+    FLASH_ATTN_KERNEL_AUTO = 0,
+    FLASH_ATTN_KERNEL_BLOCK_SERIAL = 1,
+    FLASH_ATTN_KERNEL_PIPELINED = 2
+};
+
+/* flash_attn_fwd_f16 with the kernel chosen by the caller (for comparisons and
+ * tests).  Additional statuses: GEMM_ERR_NO_CONFIG for an unknown `kernel`,
+ * GEMM_ERR_UNSUPPORTED for PIPELINED with D != 128. */
+int flash_attn_fwd_f16_kernel(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                              const void* Q, const void* K, const void* V, void* O,
+                              int causal, float scale, int kernel, void* stream);
 
 #ifdef __cplusplus
 }

@@ -165,6 +165,17 @@ def test_attention_validation():
     assert fa(1, 1, 0, 0, 64, None, None, None, None, True, 0.1) == 0
 
 
+def test_attention_kernel_selector_validation():
+    fa = g.flash_attn_raw
+    # an unknown kernel is refused before anything else; the pipelined kernel exists for D = 128 only
+    assert fa(1, 1, 4, 4, 128, FAKE, FAKE, FAKE, FAKE, False, 0.1, kernel=7) == 5
+    assert fa(-1, 1, 4, 4, 128, FAKE, FAKE, FAKE, FAKE, False, 0.1, kernel=-1) == 5
+    assert fa(1, 1, 4, 4, 64, FAKE, FAKE, FAKE, FAKE, False, 0.1, kernel=g.ATTN_KERNEL_PIPELINED) == 6
+    assert fa(1, 1, 4, 4, 96, FAKE, FAKE, FAKE, FAKE, False, 0.1, kernel=g.ATTN_KERNEL_BLOCK_SERIAL) == 6
+    assert fa(1, 1, 4, 4, 128, None, FAKE, FAKE, FAKE, False, 0.1, kernel=g.ATTN_KERNEL_PIPELINED) == 2
+    assert fa(0, 1, 4, 4, 128, None, None, None, None, False, 0.1, kernel=g.ATTN_KERNEL_PIPELINED) == 0
+
+
 def test_strided_validation_and_dispatch():
     ex = g.gemm_f16_ex_raw
     assert ex(64, 64, 64, FAKE, 63, FAKE, 64, None, FAKE, 64, 0) == 1      # lda < K

@@ -25,10 +25,13 @@ def dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
-def run(lib, Q, K, V, causal, scale=None):
-    o = lib.flash_attn(dev(Q), dev(K), dev(V), causal=causal, scale=scale)
+def run(lib, Q, K, V, causal, scale=None, kernel=None):
+    o = lib.flash_attn(dev(Q), dev(K), dev(V), causal=causal, scale=scale, kernel=kernel)
     torch.cuda.synchronize()
     return o.cpu().numpy()
+
+
+KERNELS = {"block_serial": 1, "pipelined": 2}
 
 
 SHAPES = [  # B, H, Nq, Nkv
@@ -72,6 +75,46 @@ def test_constant_values_and_peaked_scores(lib):
         V2 = rng.standard_normal((1, 2, N, D)).astype(np.float16)
         ref = oracle.attention(Q, K, V2, causal=causal)
         assert_parity(run(lib, Q, K, V2, causal), ref, ("peaked", causal))
+
+
+@pytest.mark.parametrize("kernel", list(KERNELS))
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_both_kernels_d128(lib, shape, causal, kernel):
+    # D = 128 has two kernels (block-serial and software-pipelined); each is checked on its own
+    B, H, Nq, Nkv = shape
+    rng = np.random.default_rng(Nq * 11 + Nkv)
+    Q, K, V = (rng.standard_normal((B, H, n, 128)).astype(np.float16) for n in (Nq, Nkv, Nkv))
+    ref = oracle.attention(Q, K, V, causal=causal)
+    assert_parity(run(lib, Q, K, V, causal, kernel=KERNELS[kernel]), ref, (shape, causal, kernel))
+
+
+@pytest.mark.parametrize("kernel", list(KERNELS))
+@pytest.mark.parametrize("scale", [0.0, -0.05, 0.05, 1.0])
+def test_explicit_scales_d128(lib, scale, kernel):
+    # zero and negative scales take the path that scales the scores before the row maximum
+    Q, K, V = workloads.make_attention_inputs("attn_b1_h8_q777_kv1500_d128", B=1, H=2, Nq=200, Nkv=333)
+    for causal in (False, True):
+        ref = oracle.attention(Q, K, V, causal=causal, scale=scale)
+        assert_parity(run(lib, Q, K, V, causal, scale=scale, kernel=KERNELS[kernel]), ref, (scale, causal, kernel))
+
+
+@pytest.mark.parametrize("kernel", list(KERNELS))
+def test_rising_scores_move_the_reference_maximum(lib, kernel):
+    # Key rows grow in norm along the sequence, so a row's block maxima keep rising and the lazily raised
+    # reference maximum moves many times mid-sequence (each time a block maximum passes it by more than 2^8);
+    # in the pipelined kernel every such move recomputes the next block's first-half probabilities.
+    rng = np.random.default_rng(21)
+    N, D = 900, 128
+    Q = rng.standard_normal((1, 2, N, D))
+    K = rng.standard_normal((1, 2, N, D)) * (1.0 + np.arange(N) / 20.0)[None, None, :, None] / 4.0
+    V = rng.standard_normal((1, 2, N, D))
+    Q, K, V = (x.astype(np.float16) for x in (Q, K, V))
+    for causal in (False, True):
+        ref = oracle.attention(Q, K, V, causal=causal)
+        got = run(lib, Q, K, V, causal, kernel=KERNELS[kernel])
+        assert not np.isnan(got).any()
+        assert_parity(got, ref, ("rising", causal, kernel))
 
 
 def _slab_rows(w, max_slabs=8):
