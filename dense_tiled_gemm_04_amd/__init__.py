@@ -304,7 +304,7 @@ def softmax_f16(X, out=None):
 
 
 # kernels of the attention forward pass (include/attention_f16.h)
-ATTN_KERNEL_AUTO, ATTN_KERNEL_BLOCK_SERIAL, ATTN_KERNEL_PIPELINED, ATTN_KERNEL_PIPELINED_M16 = 0, 1, 2, 3
+ATTN_KERNEL_AUTO, ATTN_KERNEL_BLOCK_SERIAL, ATTN_KERNEL_PIPELINED = 0, 1, 2
 
 
 def flash_attn_raw(B, H, Nq, Nkv, D, Q, K, V, O, causal: bool, scale: float, stream=0, kernel=None) -> int:

@@ -642,362 +642,6 @@ flash_attn_fwd_pipe_kernel(FaArgs p) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// The pipelined forward kernel on 16x16x32 MFMAs (D = 128).
-//
-// Same schedule as flash_attn_fwd_pipe_kernel (phase A: scores of block j+1
-// || second-half exponentials of block j; phase B: PV product of block j ||
-// row maximum and first-half exponentials of block j+1), with the products on
-// v_mfma_f32_16x16x32_f16, which does the same work per cycle as the 32x32x16
-// form for less energy per FLOP; under the board's power limit the chip then
-// holds a higher clock.  Layout per wave (32 query rows = 2 blocks of 16):
-//  * S^T = K . Q^T in 16x16 tiles sc[qb][kb] (16 keys kb x 16 queries qb):
-//    lane l holds queries 16 qb + l % 16 and keys 16 kb + 4 (l / 16) + r, so a
-//    query row's 64 keys lie in the lanes l, l ^ 16, l ^ 32, l ^ 48, and the
-//    row maximum and sum take two lane swaps (v_permlane16/32_swap).
-//  * O^T += V^T . P^T per 32-key step st: the MFMA's k index 8 (l/16) + t is
-//    mapped to key 32 st + 4 (l/16) + t (t < 4) or 32 st + 16 + 4 (l/16) + t - 4
-//    (t >= 4), so P^T is two score tiles of the lane converted in place, and
-//    V^T is two transpose reads of 4 keys each.
-//  * V tiles are swizzled by 2 (row % 8) chunks, which spreads a half-wave's
-//    transpose read (8 rows x 32 bytes) over all 64 banks.
-template <bool CAUSAL, bool PRESCALE>
-__global__ void __launch_bounds__(FA_NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-flash_attn_fwd_pipe16_kernel(FaArgs p) {
-    constexpr int D = 128;
-    constexpr int CH = D / 8;
-    constexpr int TILE = FA_BN * D * 2;
-    constexpr int INS = FA_BN * CH / (FA_NW * 64);
-    constexpr int KS = D / 32;   // 4 k-steps of the score product
-    constexpr int KB = 4;        // 16-key tiles per 64-key block
-    constexpr int QB = 2;        // 16-row query tiles per wave
-    constexpr int DB = D / 16;   // 8 output column tiles
-    constexpr int PDK = 3;       // K fragments read this many reads ahead (one read serves 2 slots)
-    constexpr int PDV = 3;       // V fragments likewise
-    static_assert(INS * FA_NW * 64 == FA_BN * CH, "copy split");
-    __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K[2] | V[2]
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-    const int g = lane >> 4, c16 = lane & 15;
-    const int Nq = p.Nq, Nkv = p.Nkv;
-    const int lid = xcd_contiguous_id((int)blockIdx.x, (int)gridDim.x);
-    int qblk = lid % p.q_blocks;
-    const int64_t bh = lid / p.q_blocks;
-    if (CAUSAL) qblk = p.q_blocks - 1 - qblk;  // longest rows first
-    const int q0 = qblk * FA_BM;
-    const int row0 = q0 + 32 * wave_s;
-    const f16* Qp = p.Q + bh * (int64_t)Nq * D;
-    f16* Op = p.O + bh * (int64_t)Nq * D;
-
-    // Q^T fragments: lane l holds Q[row0 + 16 qb + l % 16][32 ks + 8 (l/16) .. +7]
-    f16x8 qf[QB][KS];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int i = row0 + 16 * qb + c16;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (i < Nq) {
-                qf[qb][ks] = *(const f16x8*)(Qp + (int64_t)i * D + 32 * ks + 8 * g);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qf[qb][ks][e] = (f16)0.0f;
-            }
-        }
-    }
-
-    const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.K + bh * (int64_t)Nkv * D), (short)0, Nkv * D * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.V + bh * (int64_t)Nkv * D), (short)0, Nkv * D * 2, 0x00020000);
-    // copy t of a tile moves key rows 16 t .. 16 t + 15; both swizzles depend on the row only through its low
-    // bits, which t does not change, so one offset per lane serves every copy
-    uint32_t k_off0, v_off0;
-    {
-        const int jr = 4 * wave + g, pc = lane & 15;
-        k_off0 = (uint32_t)((jr * D + 8 * (pc ^ swz_k<D>(jr))) * 2);
-        v_off0 = (uint32_t)((jr * D + 8 * (pc ^ (2 * (jr & 7)))) * 2);
-    }
-    const uint32_t lds0 = lds_addr((GK_LDS char*)smem) + wave_s * 64 * 16;
-    auto opaque = [](auto v) {
-        asm volatile("" : "+v"(v));
-        return v;
-    };
-    auto issue_k = [&](int jb) {
-        const uint32_t kv = (uint32_t)jb * FA_BN * D * 2, ko = opaque(k_off0);
-#pragma unroll
-        for (int t = 0; t < INS; ++t)
-            dma_buffer_16(k_rsrc, ko + (kv + t * 4096u), lds0 + (jb & 1) * TILE + t * FA_NW * 64 * 16);
-    };
-    auto issue_v = [&](int jb) {
-        const uint32_t kv = (uint32_t)jb * FA_BN * D * 2, vo = opaque(v_off0);
-#pragma unroll
-        for (int t = 0; t < INS; ++t)
-            dma_buffer_16(v_rsrc, vo + (kv + t * 4096u), lds0 + (2 + (jb & 1)) * TILE + t * FA_NW * 64 * 16);
-    };
-
-    // LDS read offsets.  K fragment (key tile kb, k-step ks): key row 16 kb + l % 16, chunk (4 ks + l/16) XOR
-    // (row % 16) = 4096 kb + (kbase XOR 64 ks).  V^T fragment (column tile db, 32-key step st, key half h):
-    // rows 32 st + 16 h + 4 (l/16) + (l % 16)/4, columns 16 db + 4 (l % 4) .. +3, chunks XOR 2 (row % 8)
-    // = 8192 st + 4096 h + (vbase XOR 32 db).
-    const int kbase = (c16 * 256) | ((g ^ c16) << 4);
-    int vbase;
-    {
-        const int rr = (4 * g + (c16 >> 2)) & 7;
-        vbase = (4 * g + (c16 >> 2)) * 256 + 32 * rr + 16 * ((c16 & 3) >> 1) + 8 * (c16 & 1);
-    }
-    auto k_rd = [&](int kb_, int m) { return 4096 * (m & 3) + (kb_ ^ (64 * (m >> 2))); };  // m = 4 ks + kb
-    auto v_rd = [&](int vb, int db, int st, int h) { return 8192 * st + 4096 * h + (vb ^ (32 * db)); };
-
-    f32x4 oacc[DB][QB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) oacc[db][qb][r] = 0.0f;
-    const f32x4 zero4 = {};
-    float m_run[QB], l_run[QB] = {0.0f, 0.0f};
-    const float c = PRESCALE ? 1.0f : p.scale_log2;
-    const f16x2 ones = {(f16)1.0f, (f16)1.0f};
-
-    // scores of two blocks in flight (sc[parity][query tile][key tile]) and their fp16 probabilities
-    // pf[parity][query tile][32-key step]
-    f32x4 sc[2][QB][KB];
-    f16x8 pf[2][QB][2];
-
-    const int kv_blocks_all = (Nkv + FA_BN - 1) / FA_BN;
-    const int n_wg = CAUSAL ? min(kv_blocks_all, (q0 + FA_BM - 1) / FA_BN + 1) : kv_blocks_all;
-    const int n_w = CAUSAL ? min(kv_blocks_all, (row0 + 31) / FA_BN + 1) : kv_blocks_all;
-    int n_plain = min(Nkv / FA_BN, n_w);
-    if (CAUSAL) n_plain = min(n_plain, (row0 + 1) / FA_BN);
-
-    auto prepare = [&](f32x4 (&s)[QB][KB], int jb) {
-        if constexpr (PRESCALE) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) s[qb][kb][r] *= p.scale_log2;
-        }
-        if (jb >= n_plain) {
-            const int kv0 = jb * FA_BN;
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const int i = row0 + 16 * qb + c16;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = kv0 + 16 * kb + 4 * g + r;
-                        if (j >= Nkv || (CAUSAL && j > i)) s[qb][kb][r] = -INFINITY;
-                    }
-            }
-        }
-    };
-    // a query row's keys lie in lanes l, l^16, l^32, l^48
-    auto row_max = [&](float m) {
-        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-        m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-        const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-        return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-    };
-    auto row_sum = [&](float v) {
-        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-        v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-        const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-        return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-    };
-    // probabilities of registers 2u, 2u+1 of score tile kb (query tile qb), rounded to fp16 as a pair into
-    // dword 2 (kb % 2) + u of the step-(kb / 2) operand; the pair and the running sum are pinned to the slot
-    // where they are formed (see the 32x32 kernel)
-    auto exp_pair = [&](const f32x4 (&s)[QB][KB], f16x8 (&pd)[QB][2], int qb, int kb, int u, float m, float& l) {
-        const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][2 * u], c, -m));
-        const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][2 * u + 1], c, -m));
-        f16x2 h = __builtin_convertvector((f32x2){a, b}, f16x2);
-        l = __builtin_amdgcn_fdot2(h, ones, l, false);
-        asm volatile("" : "+v"(h), "+v"(l));
-        pd[qb][kb >> 1][4 * (kb & 1) + 2 * u] = h[0];
-        pd[qb][kb >> 1][4 * (kb & 1) + 2 * u + 1] = h[1];
-    };
-    // pair index e (0..7) of a 32-key half hf: query tile e / 4, key tile 2 hf + (e / 2) % 2, pair e % 2
-    auto half_pair = [&](const f32x4 (&s)[QB][KB], f16x8 (&pd)[QB][2], int hf, int e, const float (&m)[QB],
-                         float (&l)[QB]) {
-        const int qb = e >> 2;
-        exp_pair(s, pd, qb, 2 * hf + ((e >> 1) & 1), e & 1, m[qb], l[qb]);
-    };
-    auto max4 = [&](const f32x4& v) { return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])); };
-
-    // ---- prologue: K(0), K(1), V(0) in LDS; block 0 scored, its reference maxima set, keys 0..31
-    issue_k(0);
-    if (n_wg > 1) issue_k(1);
-    issue_v(0);
-    wait_vmcnt0();
-    __syncthreads();
-    {
-        const GK_LDS char* Ks = (const GK_LDS char*)smem;
-        const int kb_ = opaque(kbase);
-#pragma unroll
-        for (int m = 0; m < KS * KB; ++m) {
-            const f16x8 kf = *(const GK_LDS f16x8*)(Ks + k_rd(kb_, m));
-            const int ks = m >> 2, kb = m & 3;
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-                sc[0][qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[qb][ks], ks == 0 ? zero4 : sc[0][qb][kb],
-                                                                        0, 0, 0);
-        }
-        prepare(sc[0], 0);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const float mb = row_max(fmaxf(fmaxf(max4(sc[0][qb][0]), max4(sc[0][qb][1])),
-                                           fmaxf(max4(sc[0][qb][2]), max4(sc[0][qb][3]))));
-            m_run[qb] = mb * c;  // the first block holds key 0, which every row may see: finite
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) half_pair(sc[0], pf[0], 0, e, m_run, l_run);
-    }
-
-    // phase A(j): score MFMAs of block j+1 (NEXT) || exponentials of block j, keys 32..63.  Slot s: key tile
-    // (s/2) % 4, k-step s/8, query tile s % 2; one K read per two slots.
-    auto phase_a = [&]<int PAR, bool NEXT>() {
-        constexpr int NX = PAR ^ 1;
-        float mr[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) mr[qb] = opaque(m_run[qb]);
-        if constexpr (NEXT) {
-            const GK_LDS char* Kn = (const GK_LDS char*)smem + NX * TILE;
-            f16x8 kf[KS * KB];
-            const int kb_ = opaque(kbase);
-#pragma unroll
-            for (int m = 0; m < PDK; ++m) kf[m] = *(const GK_LDS f16x8*)(Kn + k_rd(kb_, m));
-#pragma unroll
-            for (int s = 0; s < 2 * KS * KB; ++s) {
-                const int m = s >> 1, qb = s & 1, ks = m >> 2, kb = m & 3;
-                if (qb == 0 && m + PDK < KS * KB) kf[m + PDK] = *(const GK_LDS f16x8*)(Kn + k_rd(kb_, m + PDK));
-                sc[NX][qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], qf[qb][ks], ks == 0 ? zero4 : sc[NX][qb][kb],
-                                                                         0, 0, 0);
-                if ((s & 3) == 1) half_pair(sc[PAR], pf[PAR], 1, s >> 2, mr, l_run);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) half_pair(sc[PAR], pf[PAR], 1, e, mr, l_run);
-        }
-    };
-    // phase B(j): PV MFMAs of block j || (NEXT) row maxima of block j+1 and its exponentials of keys 0..31.
-    // Slot s: 32-key step s/16, column tile (s/2) % 8, query tile s % 2; one V^T fragment per two slots.
-    auto phase_b = [&]<int PAR, bool NEXT>(float (&mc)[QB], float (&l_half)[QB]) {
-        constexpr int NX = PAR ^ 1;
-        const GK_LDS char* Vs = (const GK_LDS char*)smem + (2 + PAR) * TILE;
-        float mr[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) mr[qb] = opaque(m_run[qb]);
-        f16x8 vf[16];
-        const int vb = opaque(vbase);
-        auto read_v = [&](int m) {  // m = 8 st + db
-            const int st = m >> 3, db = m & 7;
-            const f16x4 v0 = lds_read_tr16_b64(Vs + v_rd(vb, db, st, 0));
-            const f16x4 v1 = lds_read_tr16_b64(Vs + v_rd(vb, db, st, 1));
-            vf[m] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        };
-#pragma unroll
-        for (int m = 0; m < PDV; ++m) read_v(m);
-        float mp[QB][KB];
-#pragma unroll
-        for (int s = 0; s < 32; ++s) {
-            const int m = s >> 1, qb = s & 1, st = m >> 3, db = m & 7;
-            if (qb == 0 && m + PDV < 16) read_v(m + PDV);
-            oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[m], pf[PAR][qb][st], oacc[db][qb], 0, 0, 0);
-            if constexpr (NEXT) {
-                if (s < 8) {
-                    mp[s >> 2][s & 3] = max4(sc[NX][s >> 2][s & 3]);
-                    asm volatile("" : "+v"(mp[s >> 2][s & 3]));
-                }
-                if (s == 8 || s == 9) {
-                    const int q = s - 8;
-                    mc[q] = row_max(fmaxf(fmaxf(mp[q][0], mp[q][1]), fmaxf(mp[q][2], mp[q][3]))) * c;
-                    asm volatile("" : "+v"(mc[q]));
-                }
-                if (s >= 12 && s < 28 && (s & 1) == 0) half_pair(sc[NX], pf[NX], 0, (s - 12) >> 1, mr, l_half);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-
-    auto open_step = [&](int j) {
-        wait_vmcnt0();
-        __syncthreads();  // K(j+1) and V(j) in LDS for every wave; K(j) and V(j-1) free
-        if (j + 2 < n_wg) issue_k(j + 2);
-        if (j + 1 < n_wg) issue_v(j + 1);
-    };
-    auto step = [&]<int PAR, bool NEXT>(int j) {
-        constexpr int NX = PAR ^ 1;
-        open_step(j);
-        if constexpr (NEXT) {
-            phase_a.template operator()<PAR, true>();
-            prepare(sc[NX], j + 1);
-            float mc[QB], l_half[QB] = {0.0f, 0.0f};
-            phase_b.template operator()<PAR, true>(mc, l_half);
-            if (__any(mc[0] > m_run[0] + kLazyLog2 || mc[1] > m_run[1] + kLazyLog2)) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const float m_new = fmaxf(m_run[qb], mc[qb]);
-                    const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-                    m_run[qb] = m_new;
-                    l_run[qb] *= alpha;
-                    l_half[qb] = 0.0f;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) oacc[db][qb][r] *= alpha;
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) half_pair(sc[NX], pf[NX], 0, e, m_run, l_half);
-            }
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) l_run[qb] += l_half[qb];
-        } else {
-            phase_a.template operator()<PAR, false>();
-            float mc[QB], l_half[QB];
-            phase_b.template operator()<PAR, false>(mc, l_half);
-        }
-    };
-
-    // main loop of steps with a following block, a tail of one or two steps, then the workgroup's remaining
-    // barriers and copies (as in the 32x32 kernel)
-    int j = 0;
-    for (; j + 2 < n_w; j += 2) {
-        step.template operator()<0, true>(j);
-        step.template operator()<1, true>(j + 1);
-    }
-    if (j + 1 < n_w) {
-        step.template operator()<0, true>(j);
-        step.template operator()<1, false>(j + 1);
-        j += 2;
-    } else {
-        step.template operator()<0, false>(j);
-        j += 1;
-    }
-    for (; j < n_wg; ++j) open_step(j);
-
-    // lane l, register r of tile (db, qb) holds O[row0 + 16 qb + l % 16][16 db + 4 (l/16) + r]
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float inv = 1.0f / row_sum(l_run[qb]);
-        const int i = row0 + 16 * qb + c16;
-        if (i < Nq) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                f16x4 o;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = (f16)(oacc[db][qb][e] * inv);
-                *(f16x4*)(Op + (int64_t)i * D + 16 * db + 4 * g) = o;
-            }
-        }
-    }
-}
-
 template <int D, bool CAUSAL, bool PRESCALE>
 hipError_t launch(const FaArgs& a, int64_t BH, hipStream_t s) {
     hipLaunchKernelGGL((flash_attn_fwd_kernel<D, CAUSAL, PRESCALE>), dim3((unsigned)(BH * a.q_blocks)),
@@ -1023,18 +667,6 @@ hipError_t launch_pipe_d(const FaArgs& a, int64_t BH, bool causal, bool prescale
     return causal ? launch_pipe<true, false>(a, BH, s) : launch_pipe<false, false>(a, BH, s);
 }
 
-template <bool CAUSAL, bool PRESCALE>
-hipError_t launch_pipe16(const FaArgs& a, int64_t BH, hipStream_t s) {
-    hipLaunchKernelGGL((flash_attn_fwd_pipe16_kernel<CAUSAL, PRESCALE>), dim3((unsigned)(BH * a.q_blocks)),
-                       dim3(FA_NW * 64), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_pipe16_d(const FaArgs& a, int64_t BH, bool causal, bool prescale, hipStream_t s) {
-    if (prescale) return causal ? launch_pipe16<true, true>(a, BH, s) : launch_pipe16<false, true>(a, BH, s);
-    return causal ? launch_pipe16<true, false>(a, BH, s) : launch_pipe16<false, false>(a, BH, s);
-}
-
 }  // namespace
 
 extern "C" {
@@ -1048,7 +680,7 @@ int flash_attn_fwd_f16_kernel(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int
                               const void* K, const void* V, void* O, int causal, float scale, int kernel,
                               void* stream) {
     if (kernel != FLASH_ATTN_KERNEL_AUTO && kernel != FLASH_ATTN_KERNEL_BLOCK_SERIAL &&
-        kernel != FLASH_ATTN_KERNEL_PIPELINED && kernel != FLASH_ATTN_KERNEL_PIPELINED_M16)
+        kernel != FLASH_ATTN_KERNEL_PIPELINED)
         return GEMM_ERR_NO_CONFIG;
     if (B < 0 || H < 0 || Nq < 0 || Nkv < 0 || D < 0) return GEMM_ERR_INVALID_DIM;
     if (B == 0 || H == 0 || Nq == 0) return GEMM_OK;
@@ -1076,11 +708,8 @@ int flash_attn_fwd_f16_kernel(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int
     // raw scores is the maximum of the scaled ones); otherwise scores are
     // scaled first
     const bool prescale = !(scale > 0.0f);
-    if ((kernel == FLASH_ATTN_KERNEL_PIPELINED || kernel == FLASH_ATTN_KERNEL_PIPELINED_M16) && D != 128)
-        return GEMM_ERR_UNSUPPORTED;
-    if (D == 128 && kernel == FLASH_ATTN_KERNEL_PIPELINED_M16)
-        e = launch_pipe16_d(a, B * H, causal != 0, prescale, s);
-    else if (D == 128 && kernel != FLASH_ATTN_KERNEL_BLOCK_SERIAL)
+    if (kernel == FLASH_ATTN_KERNEL_PIPELINED && D != 128) return GEMM_ERR_UNSUPPORTED;
+    if (D == 128 && kernel != FLASH_ATTN_KERNEL_BLOCK_SERIAL)
         e = launch_pipe_d(a, B * H, causal != 0, prescale, s);
     else
         e = D == 128 ? launch_d<128>(a, B * H, causal != 0, prescale, s)

@@ -61,14 +61,12 @@ int flash_attn_fwd_f16(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
  *                 (D = 64 or 128)
  *   PIPELINED     the scores of block j+1 and the PV product of block j run on
  *                 the matrix cores while the same wave computes the softmax of
- *                 its neighbouring blocks (D = 128 only), on 32x32x16 MFMAs
- *   PIPELINED_M16 the same schedule on 16x16x32 MFMAs (D = 128 only)
+ *                 its neighbouring blocks (D = 128 only)
  *   AUTO          PIPELINED for D = 128, BLOCK_SERIAL for D = 64 */
 enum {
     FLASH_ATTN_KERNEL_AUTO = 0,
     FLASH_ATTN_KERNEL_BLOCK_SERIAL = 1,
-    FLASH_ATTN_KERNEL_PIPELINED = 2,
-    FLASH_ATTN_KERNEL_PIPELINED_M16 = 3
+    FLASH_ATTN_KERNEL_PIPELINED = 2
 };
 
 /* flash_attn_fwd_f16 with the kernel chosen by the caller (for comparisons and

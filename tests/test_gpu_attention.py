@@ -31,7 +31,7 @@ def run(lib, Q, K, V, causal, scale=None, kernel=None):
     return o.cpu().numpy()
 
 
-KERNELS = {"block_serial": 1, "pipelined": 2, "pipelined_m16": 3}
+KERNELS = {"block_serial": 1, "pipelined": 2}
 
 
 SHAPES = [  # B, H, Nq, Nkv
@@ -81,8 +81,7 @@ def test_constant_values_and_peaked_scores(lib):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SHAPES)
 def test_both_kernels_d128(lib, shape, causal, kernel):
-    # D = 128 has three kernels (block-serial, and software-pipelined on 32x32 or 16x16 MFMAs); each is
-    # checked on its own
+    # D = 128 has two kernels (block-serial and software-pipelined); each is checked on its own
     B, H, Nq, Nkv = shape
     rng = np.random.default_rng(Nq * 11 + Nkv)
     Q, K, V = (rng.standard_normal((B, H, n, 128)).astype(np.float16) for n in (Nq, Nkv, Nkv))
