@@ -536,6 +536,10 @@ def cpu_baseline_attention(w, Q, K, V, target_s: float = 10.0):
                       % (rows - 1, dt)}
 
 
+# kernels of the attention forward pass (flash_attn_fwd_f16_kernel); auto is the library's default dispatch
+ATTN_KERNELS = {"auto": 0, "block_serial": 1, "pipelined": 2}
+
+
 def bench_attention(args, g, torch, w) -> int:
     """Attention forward: Q, K, V resident in HBM, HIP events on the launch stream around `steps` launches."""
     import math
@@ -552,8 +556,11 @@ def bench_attention(args, g, torch, w) -> int:
     scale = 1.0 / math.sqrt(w.D)
     ptrs = (dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), dO.data_ptr())
 
+    kernel_id = ATTN_KERNELS[args.attn_kernel]
+    kernel_name = args.attn_kernel if args.attn_kernel != "auto" else ("pipelined" if w.D == 128 else "block_serial")
+
     def step():
-        st = lib.flash_attn_fwd_f16(w.B, w.H, w.Nq, w.Nkv, w.D, *ptrs, 1 if w.causal else 0, scale, sh)
+        st = lib.flash_attn_fwd_f16_kernel(w.B, w.H, w.Nq, w.Nkv, w.D, *ptrs, 1 if w.causal else 0, scale, kernel_id, sh)
         if st != 0:
             raise g.GemmError(st)
 
@@ -608,6 +615,7 @@ def bench_attention(args, g, torch, w) -> int:
         "dtype": "f16 in/out, f32 accumulate and softmax",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nkv": w.Nkv, "D": w.D, "causal": w.causal,
+                   "attention_kernel": kernel_name,
                    "inputs": "seeded numpy draws, Q, K, V ~ N(0, 1) (%s)" % w.note},
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -829,6 +837,8 @@ def main() -> int:
                     help="copies of B to rotate through (default: 3 for HBM-bound workloads, else 1)")
     ap.add_argument("--b-transposed", action="store_true",
                     help="GEMM workloads: B stored transposed, Bt[N][K], through gemm_f16_bt")
+    ap.add_argument("--attn-kernel", choices=sorted(ATTN_KERNELS), default="auto",
+                    help="attention workloads: force the block-serial or the pipelined kernel (D = 128)")
     ap.add_argument("--hbm-calibration", action="store_true",
                     help="run only the fp32 vector-add kernel on buffers of known size (the reference "
                          "point that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes)")
