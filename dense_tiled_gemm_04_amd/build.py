@@ -12,7 +12,10 @@ The units compile in parallel to objects, which are then linked.  Each compile
 asks for the compiler's per-kernel resource remarks (VGPRs, AGPRs, scratch,
 occupancy, LDS); they are written to _build/kernel_resources.json, and the
 build fails if any kernel of the shipped library uses scratch memory (a
-register spill would otherwise show up only as a slowdown).
+register spill would otherwise show up only as a slowdown).  Before a built
+library replaces the old one, its gfx950 code is disassembled and checked for
+wait-state hazards around the inline-asm copies and MFMAs, which the compiler
+does not guard (asm_check.py); a hazard fails the build.
 """
 from __future__ import annotations
 
@@ -24,6 +27,11 @@ import shutil
 import subprocess
 import sys
 
+try:
+    from . import asm_check
+except ImportError:  # run as a script from the package directory
+    import asm_check
+
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
@@ -32,7 +40,7 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libgemm_f16.so")
 RESOURCES_PATH = os.path.join(BUILD_DIR, "kernel_resources.json")
 SOURCES = [os.path.join(CSRC, f) for f in ("gemm_f16.hip", "softmax.hip", "attention.hip", "calibration.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("common.h", "tile_pipe_kernel.h", "skinny_kernel.h")] + [
+HEADERS = [os.path.join(CSRC, f) for f in ("common.h", "tile_pipe_kernel.h", "skinny_kernel.h", "pingpong_kernel.h")] + [
     os.path.join(INCLUDE, "gemm_f16.h"), os.path.join(INCLUDE, "softmax_f16.h"), os.path.join(INCLUDE, "attention_f16.h"),
     os.path.join(INCLUDE, "calibration_f16.h"),
 ]
@@ -128,6 +136,13 @@ def build_library(out: str, sources: list[str], defines: list[str] | None = None
         r = subprocess.run(cmd, cwd=PKG_DIR, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError("link failed:\n" + r.stderr[-4000:])
+        try:
+            n = asm_check.check_library(tmp)
+        except Exception:
+            os.remove(tmp)
+            raise
+        if verbose:
+            print("wait-state check: %d MFMA and vector-memory instructions, no hazard" % n, flush=True)
         os.replace(tmp, out)
     finally:
         for o in objs:

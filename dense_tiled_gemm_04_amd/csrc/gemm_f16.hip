@@ -75,9 +75,10 @@ hipError_t launch_pingpong(const GemmArgs& a, hipStream_t s) {
         }                                                                                          \
     }
 
-// Ping-pong config (gemm_pingpong_kernel): 256x256 tile, 8 waves in two groups that alternate between
-// MFMAs and loads, a ring of 4 slots of 32-deep k-slices, LDS-DMA copies; tile order group G, B transposed
-// BT, non-temporal C stores NT.  It reports itself as an LDS-DMA tile with BK = 32 and schedule flag 256.
+// Ping-pong config (gemm_pingpong_kernel): 256x256 tile, 8 waves in two groups that take turns between the
+// 64 MFMAs of a 64-deep stage and the LDS reads and copies of their next one, two stages in LDS, LDS-DMA
+// copies; tile order group G, B transposed BT, non-temporal C stores NT.  It reports itself as an LDS-DMA
+// tile with BK = 64 and schedule flag 256, and takes whole tiles only (M and N multiples of 256).
 #define PINGPONG_CFG(G, BT, NT, NAME)                                                              \
     Config {                                                                                       \
         NAME, KIND_TILE, PP_BM, PP_BN, PP_BK, 2, 4, LOAD_DMA, G, PP_SLOTS, 0, 0, 0, 2, 16,             \
@@ -160,9 +161,12 @@ bool supports(const Config& cfg, const Call& c) {
                                  : (c.K + SK_BK) * c.ldb * 2 < (int64_t)INT32_MAX;
         return vec_ok && c.M <= cfg.bm && b_fits && c.M * c.lda * 2 < (int64_t)INT32_MAX;
     }
-    if (cfg.loader == LOAD_DMA)
-        return vec_ok && c.K % cfg.bk == 0 && (int64_t)cfg.bm * c.lda * 2 < (int64_t)INT32_MAX &&
+    if (cfg.loader == LOAD_DMA) {
+        // the ping-pong kernel (schedule flag 256) takes whole 256x256 tiles only
+        const bool whole = !(cfg.spread & 256) || (c.M % cfg.bm == 0 && c.N % cfg.bn == 0);
+        return vec_ok && whole && c.K % cfg.bk == 0 && (int64_t)cfg.bm * c.lda * 2 < (int64_t)INT32_MAX &&
                (int64_t)(c.bt ? cfg.bn : cfg.bk) * c.ldb * 2 < (int64_t)INT32_MAX;
+    }
     if (cfg.loader == LOAD_BUF) {
         // 31-bit buffer sizes and offsets: all of A and B, and one stage's tiles.
         const int64_t lim = (int64_t)INT32_MAX - 64;

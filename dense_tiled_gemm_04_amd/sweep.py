@@ -155,15 +155,15 @@ class Skinny:
 @dataclasses.dataclass(frozen=True)
 class PingPong:
     """The ping-pong schedule (csrc/pingpong_kernel.h): a 256x256 tile on 8 waves in two groups, one wave of
-    each per SIMD, taking turns between 32 back-to-back MFMAs and the LDS reads and copies of their next
-    k-step, over a ring of 4 slots of 32-deep k-slices (128 KiB); staged epilogue."""
+    each per SIMD, taking turns between the 64 back-to-back MFMAs of a 64-deep stage and the LDS reads and
+    copies of their next one, two stages in LDS (128 KiB); staged epilogue; whole tiles only."""
     group: int = 4
     bt: int = 0
     nt: int = 1          # non-temporal C stores
 
     kind = "tile"
     loader = "dma"
-    bm, bn, bk, wm, wn, stages, wpe, mf = 256, 256, 32, 2, 4, 4, 2, 16
+    bm, bn, bk, wm, wn, stages, wpe, mf = 256, 256, 64, 2, 4, 2, 2, 16
 
     @property
     def spread(self) -> int:
@@ -171,11 +171,11 @@ class PingPong:
 
     @property
     def name(self) -> str:
-        return "pp_256x256x32_w2x4_g%d" % self.group + ("_nt" if self.nt else "") + ("_bt" if self.bt else "")
+        return "pp_256x256x64_w2x4_g%d" % self.group + ("_nt" if self.nt else "") + ("_bt" if self.bt else "")
 
     @property
     def lds_bytes(self) -> int:
-        return 4 * (256 * 32 * 2 + 32 * 256 * 2)
+        return 2 * (256 * 64 * 2 + 64 * 256 * 2)
 
     def macro(self) -> str:
         return "PINGPONG_CFG(%d, %d, %d, \"%s\")" % (self.group, self.bt, self.nt, self.name)

@@ -1,0 +1,112 @@
+"""The wait-state check of the library's machine code (dense_tiled_gemm_04_amd/asm_check.py): planted
+hazards in small assembly texts are found, their fixed forms pass, and the built library has none."""
+import os
+
+import pytest
+
+from dense_tiled_gemm_04_amd import asm_check
+
+HEAD = "_ZN2gk4testEv:\n"
+
+
+def rules(text):
+    return [h["rule"] for h in asm_check.hazards(HEAD + text)]
+
+
+def test_valu_sgpr_write_then_copy_is_flagged():
+    # the copy's scalar base written by readfirstlane one wait state before the load
+    asm = """
+        v_readfirstlane_b32 s38, v114
+        v_readfirstlane_b32 s39, v115
+        s_mov_b32 m0, s30
+        s_nop 0
+        global_load_lds_dwordx4 v106, s[38:39]
+        s_endpgm
+    """
+    assert rules(asm) == ["sgpr->vmem"]
+    assert asm_check.hazards(HEAD + asm)[0]["wait_states"] == 2  # s_mov + s_nop 0 after the s39 write
+
+
+def test_five_wait_states_or_a_salu_writer_pass():
+    ok_nops = """
+        v_readfirstlane_b32 s38, v114
+        v_readfirstlane_b32 s39, v115
+        s_nop 4
+        global_load_lds_dwordx4 v106, s[38:39]
+        s_endpgm
+    """
+    ok_salu = """
+        v_readfirstlane_b32 s8, v114
+        v_readfirstlane_b32 s9, v115
+        s_add_u32 s38, s8, s36
+        s_addc_u32 s39, s9, s37
+        global_load_lds_dwordx4 v106, s[38:39]
+        s_endpgm
+    """
+    buffer = """
+        v_readfirstlane_b32 s40, v1
+        s_nop 0
+        buffer_load_dwordx4 v2, s[40:43], 0 offen lds
+        s_endpgm
+    """
+    assert rules(ok_nops) == []
+    # s_add reads s8/s9, but the load reads s38/s39, last written by SALU
+    assert rules(ok_salu) == []
+    assert rules(buffer) == ["sgpr->vmem"]
+
+
+def test_hazard_across_a_loop_back_edge():
+    # the load at the loop head reads what the previous iteration's tail wrote
+    asm = """
+    .LBB0_1:
+        global_load_lds_dwordx4 v106, s[38:39]
+        s_add_u32 s2, s2, 1
+        s_cmp_lg_u32 s2, 8
+        v_readfirstlane_b32 s38, v7
+        s_cbranch_scc1 .LBB0_1
+        s_endpgm
+    """
+    assert rules(asm) == ["sgpr->vmem"]
+    # the fall-through predecessor alone would have shown nothing: the label has no instruction above it
+    asm_objdump = asm.replace(".LBB0_1:", "<L0>:").replace("s_cbranch_scc1 .LBB0_1", "s_cbranch_scc1 L0")
+    assert rules(asm_objdump) == ["sgpr->vmem"]
+
+
+def test_valu_write_then_mfma_source():
+    bad = """
+        v_mov_b32_e32 v12, v40
+        v_mfma_f32_16x16x32_f16 a[0:3], v[10:13], v[14:17], a[0:3]
+        s_endpgm
+    """
+    good = """
+        v_mov_b32_e32 v12, v40
+        s_nop 1
+        v_mfma_f32_16x16x32_f16 a[0:3], v[10:13], v[14:17], a[0:3]
+        s_endpgm
+    """
+    acc = """
+        v_accvgpr_write_b32 a2, 0
+        v_mfma_f32_16x16x32_f16 a[0:3], v[10:13], v[14:17], a[0:3]
+        s_endpgm
+    """
+    chained = """
+        v_mfma_f32_16x16x32_f16 a[0:3], v[10:13], v[14:17], a[0:3]
+        v_mfma_f32_16x16x32_f16 a[0:3], v[18:21], v[14:17], a[0:3]
+        s_endpgm
+    """
+    assert rules(bad) == ["valu->mfma"]
+    assert rules(good) == []
+    assert rules(acc) == ["valu->mfma"]
+    assert rules(chained) == []
+
+
+def test_built_library_has_no_hazard():
+    from dense_tiled_gemm_04_amd import build
+
+    if not os.path.exists(build.LIB_PATH):
+        pytest.skip("library not built")
+    try:
+        n = asm_check.check_library(build.LIB_PATH)
+    except FileNotFoundError as e:
+        pytest.skip("LLVM tools missing: %s" % e)
+    assert n > 1000  # the GEMM, attention and calibration kernels' MFMAs and copies were seen
