@@ -25,6 +25,9 @@ struct GemmArgs {
     int M, N, K;
     int lda, ldb, ldc;  // leading dimensions in elements (>= K, N, N)
     int tiles_m, tiles_n;
+    float* partial;     // split-K: fp32 partial sums [k_split][M][N] (workspace), else null
+    int k_split;        // split-K: number of K ranges
+    int k_chunk;        // split-K: K rows per range (a multiple of the stage depth)
 };
 
 // GELU in its erf form on an fp32 value:

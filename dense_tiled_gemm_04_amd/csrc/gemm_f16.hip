@@ -6,18 +6,20 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "gemm_f16.h"
 #include "pingpong_kernel.h"
 #include "skinny_kernel.h"
+#include "skinny_splitk_kernel.h"
 #include "tile_pipe_kernel.h"
 
 using namespace gk;
 
 namespace {
 
-enum Kind { KIND_TILE = 0, KIND_SKINNY = 1 };
+enum Kind { KIND_TILE = 0, KIND_SKINNY = 1, KIND_SPLITK = 2 };
 
 typedef hipError_t (*launch_fn)(const GemmArgs&, hipStream_t);
 
@@ -32,6 +34,7 @@ struct Config {
     int mfma, spread;                // MFMA shape (32: 32x32x16, 16: 16x16x32); schedule flags (skinny: 1 = 16-byte A copies)
     int bt;                          // 1: B given transposed (Bt[N][K])
     int krot;                        // skinny: K stages walked from stage (workgroup mod KT)
+    int ksplit;                      // split-K skinny: number of K ranges
     int lds_bytes;
     int threads;
     launch_fn launch[3];     // indexed by epilogue
@@ -66,7 +69,7 @@ hipError_t launch_pingpong(const GemmArgs& a, hipStream_t s) {
 // LDS reads SP, B transposed BT.
 #define TILE_CFG(BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, BT, NAME)             \
     Config {                                                                                       \
-        NAME, KIND_TILE, BM, BN, BK, WM, WN, LOADER, G, ST, BS, DS, CS, WPE, MF, SP, BT, 0,        \
+        NAME, KIND_TILE, BM, BN, BK, WM, WN, LOADER, G, ST, BS, DS, CS, WPE, MF, SP, BT, 0, 0,     \
             TilePipeCfg<BM, BN, BK, WM, WN, ST, MF, BT, ((SP) & 128) ? 1 : 0>::LDS_BYTES, WM * WN * 64, \
         {                                                                                          \
             launch_tile<BM, BN, BK, WM, WN, ST, G, BS, DS, LOADER, CS, WPE, MF, SP, BT, 0>,        \
@@ -82,7 +85,7 @@ hipError_t launch_pingpong(const GemmArgs& a, hipStream_t s) {
 #define PINGPONG_CFG(G, BT, NT, NAME)                                                              \
     Config {                                                                                       \
         NAME, KIND_TILE, PP_BM, PP_BN, PP_BK, 2, 4, LOAD_DMA, G, PP_SLOTS, 0, 0, 0, 2, 16,             \
-            256 | 32 | ((NT) ? 64 : 0), BT, 0, PP_LDS_BYTES, PP_WAVES * 64,                        \
+            256 | 32 | ((NT) ? 64 : 0), BT, 0, 0, PP_LDS_BYTES, PP_WAVES * 64,                     \
         {                                                                                          \
             launch_pingpong<G, BT, NT, 0>, launch_pingpong<G, BT, NT, 1>, launch_pingpong<G, BT, NT, 2> \
         }                                                                                          \
@@ -92,11 +95,32 @@ hipError_t launch_pingpong(const GemmArgs& a, hipStream_t s) {
 // 16-byte A copies A16.
 #define SKINNY_CFG(MB, ST, BT, KR, A16, NAME)                                                       \
     Config {                                                                                       \
-        NAME, KIND_SKINNY, 16 * MB, SK_BN, SK_BK, 1, SK_WAVES, -1, 1, ST, 0, 0, 0, 1, 16, A16, BT, KR, \
+        NAME, KIND_SKINNY, 16 * MB, SK_BN, SK_BK, 1, SK_WAVES, -1, 1, ST, 0, 0, 0, 1, 16, A16, BT, KR, 0, \
             ST * (16 * MB * SK_BK * 2 + SK_BK * SK_BN * 2), SK_WAVES * 64,                         \
         {                                                                                          \
             launch_skinny<MB, ST, BT, KR, A16, 0>, launch_skinny<MB, ST, BT, KR, A16, 1>,          \
                 launch_skinny<MB, ST, BT, KR, A16, 2>                                              \
+        }                                                                                          \
+    }
+
+template <int MB, int STAGES, int BK, int S, int EPI>
+hipError_t launch_splitk(const GemmArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((gemm_skinny_splitk_kernel<MB, STAGES, BK>), dim3((unsigned)(a.tiles_n * a.k_split)),
+                       dim3(SKS_WAVES * 64), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t quads = (int64_t)a.M * (a.N / 4);
+    hipLaunchKernelGGL((splitk_reduce_kernel<EPI, S>), dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// Split-K skinny config (B[K][N] only): 16*MB rows, ST LDS stages of BK k-rows, S K ranges.
+#define SPLITK_CFG(MB, ST, BK, S, NAME)                                                             \
+    Config {                                                                                       \
+        NAME, KIND_SPLITK, 16 * MB, SKS_BN, BK, 1, SKS_WAVES, -1, 1, ST, 0, 0, 0, 1, 16, 0, 0, 0, S, \
+            ST * (16 * MB * BK * 2 + BK * SKS_BN * 2), SKS_WAVES * 64,                            \
+        {                                                                                          \
+            launch_splitk<MB, ST, BK, S, 0>, launch_splitk<MB, ST, BK, S, 1>, launch_splitk<MB, ST, BK, S, 2> \
         }                                                                                          \
     }
 
@@ -161,6 +185,12 @@ bool supports(const Config& cfg, const Call& c) {
                                  : (c.K + SK_BK) * c.ldb * 2 < (int64_t)INT32_MAX;
         return vec_ok && c.M <= cfg.bm && b_fits && c.M * c.lda * 2 < (int64_t)INT32_MAX;
     }
+    if (cfg.kind == KIND_SPLITK) {
+        // 32-bit buffer offsets as for the skinny kernel (the last range's stage tail included); the fp32
+        // workspace (ranges x M x N) under 2 GiB
+        return vec_ok && c.K > 0 && c.M <= cfg.bm && (c.K + cfg.bk) * c.ldb * 2 < (int64_t)INT32_MAX &&
+               c.M * c.lda * 2 < (int64_t)INT32_MAX && (int64_t)cfg.ksplit * c.M * c.N * 4 < (int64_t)INT32_MAX;
+    }
     if (cfg.loader == LOAD_DMA) {
         // the ping-pong kernel (schedule flag 256) takes whole 256x256 tiles only
         const bool whole = !(cfg.spread & 256) || (c.M % cfg.bm == 0 && c.N % cfg.bn == 0);
@@ -211,8 +241,31 @@ int pick_default(const Call& c) {
     return big ? SEL_REG_BIG : SEL_REG_SMALL;
 }
 
+// Workspace of the split-K path: the fp32 partial sums.  One buffer per device, owned by the library, grown
+// (never shrunk) on demand and kept until the process ends.  Work on one stream runs in order, so calls on
+// the same stream reuse it freely; a call on another stream first waits, on the device, for the event
+// recorded after the previous call's reduce kernel.  The host side of a call holds a mutex, so calls from
+// several threads are ordered too.  Growing waits for that event on the host before the old buffer is freed.
+struct SplitkWorkspace {
+    std::mutex mu;
+    void* buf = nullptr;
+    size_t cap = 0;
+    hipEvent_t done = nullptr;
+    hipStream_t last = nullptr;
+    bool used = false;
+};
+
+SplitkWorkspace& splitk_workspace(int dev) {
+    static std::mutex mu;
+    static std::vector<SplitkWorkspace*> all;
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)all.size() <= dev) all.resize(dev + 1, nullptr);
+    if (!all[dev]) all[dev] = new SplitkWorkspace();  // lives until the process ends
+    return *all[dev];
+}
+
 int run(const Config& cfg, const Call& c, hipStream_t stream) {
-    GemmArgs a;
+    GemmArgs a = {};
     a.A = (const f16*)c.A;
     a.B = (const f16*)c.B;
     a.bias = (const f16*)c.bias;
@@ -223,6 +276,47 @@ int run(const Config& cfg, const Call& c, hipStream_t stream) {
     a.lda = (int)c.lda;
     a.ldb = (int)c.ldb;
     a.ldc = (int)c.ldc;
+    if (cfg.kind == KIND_SPLITK) {
+        // ranges of whole stages: K rows per range rounded up to the stage depth, and only non-empty ranges
+        const int64_t per = (c.K + cfg.ksplit - 1) / cfg.ksplit;
+        const int64_t chunk = (per + cfg.bk - 1) / cfg.bk * cfg.bk;
+        a.tiles_m = 1;
+        a.tiles_n = (int)((c.N + SKS_BN - 1) / SKS_BN);
+        a.k_chunk = (int)chunk;
+        a.k_split = (int)((c.K + chunk - 1) / chunk);
+        const size_t bytes = (size_t)a.k_split * c.M * c.N * sizeof(float);
+        int dev = 0;
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess) return GEMM_ERR_LAUNCH;
+        SplitkWorkspace& w = splitk_workspace(dev);
+        std::lock_guard<std::mutex> lock(w.mu);
+        if (!w.done && hipEventCreateWithFlags(&w.done, hipEventDisableTiming) != hipSuccess) {
+            w.done = nullptr;
+            return GEMM_ERR_LAUNCH;
+        }
+        if (w.cap < bytes) {
+            if (w.buf) {
+                if (w.used && hipEventSynchronize(w.done) != hipSuccess) return GEMM_ERR_LAUNCH;
+                (void)hipFree(w.buf);
+                w.buf = nullptr;
+                w.cap = 0;
+            }
+            const size_t want = (bytes + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);  // whole MiB
+            if (hipMalloc(&w.buf, want) != hipSuccess) {
+                w.buf = nullptr;
+                return GEMM_ERR_LAUNCH;
+            }
+            w.cap = want;
+        } else if (w.used && w.last != stream && hipStreamWaitEvent(stream, w.done, 0) != hipSuccess) {
+            return GEMM_ERR_LAUNCH;
+        }
+        a.partial = (float*)w.buf;
+        const hipError_t e = cfg.launch[c.epi](a, stream);
+        if (e != hipSuccess) return GEMM_ERR_LAUNCH;
+        if (hipEventRecord(w.done, stream) != hipSuccess) return GEMM_ERR_LAUNCH;
+        w.last = stream;
+        w.used = true;
+        return GEMM_OK;
+    }
     if (cfg.kind == KIND_SKINNY) {
         a.tiles_m = 1;
         a.tiles_n = (int)((c.N + SK_BN - 1) / SK_BN);
@@ -287,10 +381,11 @@ int gemm_f16_config_info(int idx, char* buf, int buflen) {
                      "\"waves_m\": %d, \"waves_n\": %d, \"loader\": \"%s\", \"group_m\": %d, \"stages\": %d, "
                      "\"bslot\": %d, \"dstride\": %d, \"cslot\": %d, \"waves_per_simd\": %d, "
                      "\"mfma\": %d, \"spread\": %d, \"b_transposed\": %d, \"k_rotate\": %d, \"lds_bytes\": %d, "
-                     "\"threads\": %d}",
-                     idx, c.name, c.kind == KIND_TILE ? "tile" : "skinny", c.bm, c.bn, c.bk, c.wm, c.wn,
-                     c.kind == KIND_TILE ? loaders[c.loader] : "lds_dma", c.group_m, c.stages, c.bslot,
-                     c.dstride, c.cslot, c.wpe, c.mfma, c.spread, c.bt, c.krot, c.lds_bytes, c.threads);
+                     "\"threads\": %d, \"k_split\": %d}",
+                     idx, c.name, c.kind == KIND_TILE ? "tile" : (c.kind == KIND_SKINNY ? "skinny" : "skinny_splitk"),
+                     c.bm, c.bn, c.bk, c.wm, c.wn, c.kind == KIND_TILE ? loaders[c.loader] : "lds_dma", c.group_m,
+                     c.stages, c.bslot, c.dstride, c.cslot, c.wpe, c.mfma, c.spread, c.bt, c.krot, c.lds_bytes,
+                     c.threads, c.ksplit);
     if (buf && buflen > 0) {
         strncpy(buf, tmp, (size_t)buflen - 1);
         buf[buflen - 1] = '\0';

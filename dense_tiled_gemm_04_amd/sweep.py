@@ -58,6 +58,7 @@ WARM_MS = 50.0   # back-to-back work before a configuration's timed chunks
 LDS_PER_CU = 160 * 1024
 REGS_PER_LANE = 512      # VGPR + AGPR per SIMD lane, shared by the waves resident on the SIMD
 SK_BN, SK_BK, SK_WAVES = 64, 128, 4   # skinny kernel constants (csrc/skinny_kernel.h)
+SKS_BN = 256                           # split-K skinny panel width (csrc/skinny_splitk_kernel.h)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -153,6 +154,32 @@ class Skinny:
 
 
 @dataclasses.dataclass(frozen=True)
+class SplitK:
+    """The split-K skinny path (csrc/skinny_splitk_kernel.h), B[K][N] only: 256-column panels over `splits`
+    contiguous K ranges (512-byte row segments of B), fp32 partial sums in a workspace, then a reduce kernel
+    that sums the ranges in order and applies the epilogue."""
+    mb: int
+    stages: int
+    bk: int = 32
+    splits: int = 4
+
+    kind = "splitk"
+    loader = "lds_dma"
+    bt = 0
+
+    @property
+    def name(self) -> str:
+        return "splitk_m%d_s%d_k%d_x%d" % (16 * self.mb, self.stages, self.bk, self.splits)
+
+    @property
+    def lds_bytes(self) -> int:
+        return self.stages * (16 * self.mb * self.bk * 2 + self.bk * SKS_BN * 2)
+
+    def macro(self) -> str:
+        return "SPLITK_CFG(%d, %d, %d, %d, \"%s\")" % (self.mb, self.stages, self.bk, self.splits, self.name)
+
+
+@dataclasses.dataclass(frozen=True)
 class PingPong:
     """The ping-pong schedule (csrc/pingpong_kernel.h): a 256x256 tile on 8 waves in two groups, one wave of
     each per SIMD, taking turns between the 64 back-to-back MFMAs of a 64-deep stage and the LDS reads and
@@ -189,6 +216,11 @@ def valid(c) -> bool:
     """The kernels' static_asserts plus the LDS and register budgets."""
     if isinstance(c, PingPong):   # one fixed shape, within budget by construction (static_asserts)
         return c.group in (1, 4, 8) and c.lds_bytes <= LDS_PER_CU
+    if isinstance(c, SplitK):
+        b_ins = c.bk * SKS_BN * 2 // 16 // (SK_WAVES * 64)
+        a_ins = 16 * c.mb * c.bk * 2 // 4 // (SK_WAVES * 64)
+        return (c.bk % 32 == 0 and c.stages >= 2 and c.splits >= 2 and (c.stages - 2) * (a_ins + b_ins) <= 63
+                and c.lds_bytes <= LDS_PER_CU)
     if isinstance(c, Skinny):
         b_ins = SK_BK * SK_BN * 2 // 16 // (SK_WAVES * 64)
         a_ins = 16 * c.mb * SK_BK * 2 // (16 if c.a16 else 4) // (SK_WAVES * 64)
@@ -428,6 +460,12 @@ def space() -> list:
             for st in sts:
                 for kr in (0, 1):
                     out.append(Skinny(mb, st, bt, kr, a16=1))
+    # split-K over 256-column panels (B[K][N]): four K ranges put 256 workgroups on N = 16384
+    for mb, sts in ((1, (4, 6, 8)), (2, (4, 6)), (4, (4,))):
+        for st in sts:
+            for bk in (32, 64):
+                for sp in (2, 4):
+                    out.append(SplitK(mb, st, bk, sp))
     return [c for c in out if valid(c)]
 
 
@@ -445,7 +483,7 @@ def class_of(c, cls: str) -> bool:
     register loader, which both run every call of the class."""
     if cls.startswith("SEL_SKINNY") or cls.startswith("SEL_BT_SKINNY"):
         bt = cls.startswith("SEL_BT_")
-        if c.kind == "skinny":
+        if c.kind in ("skinny", "splitk"):
             return bool(c.bt) == bt and 16 * c.mb >= int(cls.split("SKINNY")[1])
         return c.loader == "dma" and bool(c.bt) == bt
     if c.kind != "tile":

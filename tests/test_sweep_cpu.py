@@ -22,6 +22,13 @@ def test_budget_filter():
     assert not sweep.valid(sweep.Tile(256, 256, 64, 2, 2, 2, 4, 3, 2, "dma", wpe=2))
     # skinny: M <= 16 with 8 stages uses the whole 160 KiB; 9 would not fit
     assert sweep.valid(sweep.Skinny(1, 8)) and not sweep.valid(sweep.Skinny(1, 9))
+    # split-K skinny: stages of 32 k-rows x 256 columns (16 KiB) plus 1 KiB of A per 16 rows; 64 rows at
+    # BK = 64 and 4 stages is exactly 160 KiB, 5 stages is not; at least two K ranges; BK a multiple of 32
+    assert sweep.SplitK(4, 4, 64, 4).lds_bytes == 160 * 1024 and sweep.valid(sweep.SplitK(4, 4, 64, 4))
+    assert not sweep.valid(sweep.SplitK(4, 5, 64, 4))
+    assert not sweep.valid(sweep.SplitK(1, 4, 32, 1)) and not sweep.valid(sweep.SplitK(1, 4, 48, 4))
+    # at M = 16, BK = 32 a stage is 17 KiB: nine fit in the LDS, ten do not
+    assert sweep.valid(sweep.SplitK(1, 9, 32, 4)) and not sweep.valid(sweep.SplitK(1, 10, 32, 4))
 
 
 def test_eight_wave_budget_rules():
@@ -101,9 +108,11 @@ def _table_entries(path):
     src = open(path).read()
     tiles = re.findall(r'(?<!PINGPONG_)TILE_CFG\(([^)]*)\)', src)
     skinny = re.findall(r'SKINNY_CFG\(([^)]*)\)', src)
+    splitk = re.findall(r'SPLITK_CFG\(([^)]*)\)', src)
     pingpong = re.findall(r'PINGPONG_CFG\(([^)]*)\)', src)
     sel = dict(re.findall(r'#define (SEL_\w+) (\d+)', src))
-    return tiles + [("pp", x) for x in pingpong], skinny, {k: int(v) for k, v in sel.items()}
+    return tiles + [("pp", x) for x in pingpong], skinny + [("splitk", x) for x in splitk], \
+        {k: int(v) for k, v in sel.items()}
 
 
 def test_product_table_entries_are_in_budget():
@@ -122,6 +131,11 @@ def test_product_table_entries_are_in_budget():
         assert sweep.valid(c), c
         assert f[15].strip('"') == c.name
     for s in skinny:
+        if isinstance(s, tuple):  # a split-K entry: MB, stages, BK, ranges, name
+            f = [x.strip() for x in s[1].split(",")]
+            c = sweep.SplitK(*map(int, f[:4]))
+            assert sweep.valid(c) and f[4].strip('"') == c.name
+            continue
         f = [x.strip() for x in s.split(",")]
         c = sweep.Skinny(int(f[0]), int(f[1]), int(f[2]), int(f[3]), a16=int(f[4]))
         assert sweep.valid(c), c
