@@ -28,7 +28,15 @@ struct GemmArgs {
     float* partial;     // split-K: fp32 partial sums [k_split][M][N] (workspace), else null
     int k_split;        // split-K: number of K ranges
     int k_chunk;        // split-K: K rows per range (a multiple of the stage depth)
+    uint64_t* timeline; // timeline builds only (GK_TIMELINE): per-wave clock stamps, else null
 };
+
+// Timeline builds (compiled with -DGK_TIMELINE=1, never the shipped library): the tile kernel records, per
+// wave, the shader clock (s_memtime) and the 100 MHz real-time counter (s_memrealtime) at kernel entry, after
+// the prologue's barrier, after the K loop and after its C stores have completed.
+#ifndef GK_TIMELINE
+#define GK_TIMELINE 0
+#endif
 
 // GELU in its erf form on an fp32 value:
 //   gelu(x) = x * Phi(x),  Phi(x) = 0.5 * erfc(-x / sqrt 2)

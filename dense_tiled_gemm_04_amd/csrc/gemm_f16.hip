@@ -264,6 +264,10 @@ SplitkWorkspace& splitk_workspace(int dev) {
     return *all[dev];
 }
 
+#if GK_TIMELINE
+uint64_t* g_timeline = nullptr;  // stamp buffer of the tile kernels (timeline builds)
+#endif
+
 int run(const Config& cfg, const Call& c, hipStream_t stream) {
     GemmArgs a = {};
     a.A = (const f16*)c.A;
@@ -324,6 +328,9 @@ int run(const Config& cfg, const Call& c, hipStream_t stream) {
         a.tiles_m = (int)((c.M + cfg.bm - 1) / cfg.bm);
         a.tiles_n = (int)((c.N + cfg.bn - 1) / cfg.bn);
     }
+#if GK_TIMELINE
+    if (cfg.kind == KIND_TILE && !(cfg.spread & 256)) a.timeline = g_timeline;
+#endif
     hipError_t e = cfg.launch[c.epi](a, stream);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
@@ -352,6 +359,12 @@ __global__ void vector_add_f32_scalar_kernel(const float* __restrict__ A, const 
 }  // namespace
 
 extern "C" {
+
+#if GK_TIMELINE
+// Timeline builds only: the buffer (8 x uint64 per wave, indexed by workgroup and wave) that the tile kernels
+// write their clock stamps to; null turns the stamps off.
+void gemm_f16_timeline_buffer(void* p) { g_timeline = (uint64_t*)p; }
+#endif
 
 const char* gemm_f16_status_string(int status) {
     switch (status) {

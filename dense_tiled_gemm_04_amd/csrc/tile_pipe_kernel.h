@@ -151,6 +151,14 @@ template <int BM, int BN, int BK, int WM, int WN, int STAGES, int GROUP_M, int E
           int LOADER, int CSLOT, int WPE, int MF, int SPREAD, int BT>
 __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 gemm_tile_pipe_kernel(GemmArgs p) {
+    uint64_t tl[8] = {};  // timeline builds: shader clock at the 4 points, then the real-time counter
+    auto stamp = [&](int k) {
+        if constexpr (GK_TIMELINE) {
+            tl[k] = __builtin_amdgcn_s_memtime();
+            tl[4 + k] = __builtin_amdgcn_s_memrealtime();
+        }
+    };
+    stamp(0);
     using Cfg = TilePipeCfg<BM, BN, BK, WM, WN, STAGES, MF, BT, (SPREAD & 128) ? 1 : 0>;
     constexpr int KS = Cfg::KS;
     constexpr int NW = Cfg::NW, WTM = Cfg::WTM, WTN = Cfg::WTN, TM = Cfg::TM, TN = Cfg::TN;
@@ -494,6 +502,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         }
     }
     __syncthreads();
+    stamp(1);
     if (KT > 0) {
         if constexpr (INPLACE) {  // A[TM-1] is read at slot 0 of the k-step
 #pragma unroll
@@ -645,6 +654,7 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
         pin_order();
     }
+    stamp(2);
 
     // The epilogue's per-lane index math starts from a thread id that passes
     // through an empty asm here, after the K loop, so the compiler cannot
@@ -757,6 +767,15 @@ gemm_tile_pipe_kernel(GemmArgs p) {
                 for (int e = 0; e < 8; ++e)
                     if (n + e < N) dst[e] = v[e];
             }
+        }
+    }
+    if constexpr (GK_TIMELINE) {
+        wait_vmcnt0();  // the C stores have completed
+        stamp(3);
+        if (p.timeline != nullptr && (threadIdx.x & 63) == 0) {
+            uint64_t* o = p.timeline + ((size_t)blockIdx.x * (WM * WN) + (threadIdx.x >> 6)) * 8;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) o[k] = tl[k];
         }
     }
 }

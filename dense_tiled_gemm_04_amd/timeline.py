@@ -1,0 +1,217 @@
+"""Timeline of the tile GEMM kernel from clock stamps taken inside it.
+
+A diagnostic, not part of the product path.  `--build` compiles the GEMM unit
+with -DGK_TIMELINE=1 into _build/libgemm_f16_timeline.so (same kernels, same
+configuration table, plus per-wave stamps: shader clock `s_memtime` and the
+100 MHz `s_memrealtime` counter at kernel entry, after the prologue's barrier,
+after the K loop and after the C stores have completed).  `--run` (GPU) times
+the shipped library and the timeline build on the same inputs, checks that
+their outputs are bit-identical, and summarises one launch taken after >= 60 ms
+of back-to-back launches:
+  * per workgroup: prologue, K loop and epilogue durations (wave 0);
+  * the shader clock during the K loop (stamp cycles over stamp time), and the
+    loop's length in shader cycles;
+  * per XCD (workgroup w runs on XCD w mod 8): clock, loop time and when its
+    last workgroup ended.
+
+    python -m dense_tiled_gemm_04_amd.timeline --build
+    python -m dense_tiled_gemm_04_amd.timeline --run gpurun_out/timeline.json [--markdown out.md]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+TIMELINE_LIB = os.path.join(PKG_DIR, "_build", "libgemm_f16_timeline.so")
+RESOURCES = os.path.join(PKG_DIR, "_build", "timeline_kernel_resources.json")
+
+# (name, M, N, K, epilogue): the 4096^3 product and the MLP up-projection with bias + GELU
+WORKLOADS = (("gemm_4096", 4096, 4096, 4096, 0), ("mlp_up_8192x16384x4096", 8192, 16384, 4096, 2))
+
+
+def build(verbose: bool = True) -> str:
+    from dense_tiled_gemm_04_amd import build as libbuild
+
+    # the stamps' registers push a few register-loader kernels into scratch; those are never measured here
+    # (run() refuses a configuration whose kernel uses scratch in this build)
+    rows = libbuild.build_library(TIMELINE_LIB, [os.path.join(PKG_DIR, "csrc", "gemm_f16.hip")],
+                                  defines=["-DGK_TIMELINE=1"], allow_scratch=True, resources_path=RESOURCES,
+                                  verbose=verbose)
+    if verbose:
+        for r in libbuild.scratch_users(rows):
+            print("uses scratch in the timeline build: %s" % r["kernel"], flush=True)
+    return TIMELINE_LIB
+
+
+def _spilling_tile_kernels() -> list:
+    rows = json.load(open(RESOURCES)) if os.path.exists(RESOURCES) else []
+    return [r["kernel"] for r in rows if "gemm_tile_pipe_kernel" in r["kernel"] and
+            (int(r.get("ScratchSize [bytes/lane]", 0)) or int(r.get("VGPRs Spill", 0)))]
+
+
+def _pct(x, ps=(0, 10, 50, 90, 100)):
+    import numpy as np
+
+    return [round(float(np.percentile(x, p)), 3) for p in ps]
+
+
+def summarise(stamps, nwg: int, waves: int) -> dict:
+    """stamps: int64 [nwg, waves, 8] = shader clock at points 0-3, real-time counter (10 ns) at points 0-3."""
+    import numpy as np
+
+    t = stamps[:, :, 0:4].astype(np.float64)
+    r = stamps[:, :, 4:8].astype(np.float64) * 10.0   # ns
+    r0 = r[:, :, 0].min()
+    w0t, w0r = t[:, 0, :], r[:, 0, :]
+    loop_ns = w0r[:, 2] - w0r[:, 1]
+    loop_cyc = w0t[:, 2] - w0t[:, 1]
+    out = {
+        "span_us": round(float((r[:, :, 3].max() - r0) / 1e3), 2),
+        "start_us": _pct((r[:, :, 0].min(axis=1) - r0) / 1e3),
+        "prologue_us": _pct((w0r[:, 1] - w0r[:, 0]) / 1e3),
+        "loop_us": _pct(loop_ns / 1e3),
+        "loop_kcycles": _pct(loop_cyc / 1e3),
+        "loop_clock_GHz": _pct(loop_cyc / loop_ns),
+        "epilogue_us": _pct((w0r[:, 3] - w0r[:, 2]) / 1e3),
+        "epilogue_clock_GHz": _pct((w0t[:, 3] - w0t[:, 2]) / (w0r[:, 3] - w0r[:, 2])),
+        "end_us": _pct((r[:, :, 3].max(axis=1) - r0) / 1e3),
+        "percentiles": [0, 10, 50, 90, 100],
+        "per_xcd": [],
+    }
+    xcd = np.arange(nwg) % 8
+    for x in range(8):
+        m = xcd == x
+        if not m.any():
+            continue
+        out["per_xcd"].append({
+            "xcd": x, "workgroups": int(m.sum()),
+            "loop_clock_GHz": round(float(np.median(loop_cyc[m] / loop_ns[m])), 3),
+            "loop_us": round(float(np.median(loop_ns[m]) / 1e3), 2),
+            "last_end_us": round(float((r[m, :, 3].max() - r0) / 1e3), 2),
+        })
+    return out
+
+
+def run(out_path: str, markdown: str | None = None) -> dict:
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, ROOT)
+    from dense_tiled_gemm_04_amd import build as libbuild
+
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    libs = {"shipped": ctypes.CDLL(libbuild.LIB_PATH), "timeline": ctypes.CDLL(TIMELINE_LIB)}
+    for lib in libs.values():
+        lib.gemm_f16.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32, vp]
+        lib.gemm_f16.restype = i32
+        lib.gemm_f16_select_config.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32]
+        lib.gemm_f16_select_config.restype = i32
+        lib.gemm_f16_config_info.argtypes = [i32, ctypes.c_char_p, i32]
+    libs["timeline"].gemm_f16_timeline_buffer.argtypes = [vp]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    results = {}
+    for name, M, N, K, epi in WORKLOADS:
+        print("workload %s" % name, flush=True)
+        g = torch.Generator().manual_seed(1)
+        A = (torch.rand(M, K, generator=g) * 2 - 1).half().to(dev)
+        B = (torch.rand(K, N, generator=g) * 2 - 1).half().to(dev)
+        bias = (torch.randn(N, generator=g) * 0.1).half().to(dev)
+        C = {k: torch.empty(M, N, dtype=torch.float16, device=dev) for k in libs}
+        lib_t = libs["timeline"]
+        idx = lib_t.gemm_f16_select_config(M, N, K, A.data_ptr(), B.data_ptr(), bias.data_ptr() if epi else None,
+                                           C["timeline"].data_ptr(), epi)
+        buf = ctypes.create_string_buffer(1024)
+        lib_t.gemm_f16_config_info(idx, buf, 1024)
+        info = json.loads(buf.value.decode())
+        assert info["kind"] == "tile" and not info["spread"] & 256, info
+        tmpl = [info["bm"], info["bn"], info["bk"], info["waves_m"], info["waves_n"], info["stages"],
+                info["group_m"], epi, info["bslot"], info["dstride"], {"dma": 0, "reg": 1, "buf": 2}[info["loader"]],
+                info["cslot"], info["waves_per_simd"], info["mfma"], info["spread"], info["b_transposed"]]
+        sym = "gemm_tile_pipe_kernelI" + "".join("Li%dE" % v for v in tmpl)
+        assert not any(sym in k for k in _spilling_tile_kernels()), "the timeline build of %s spills" % info["name"]
+        waves = info["waves_m"] * info["waves_n"]
+        nwg = ((M + info["bm"] - 1) // info["bm"]) * ((N + info["bn"] - 1) // info["bn"])
+        stamps = torch.zeros(nwg * waves * 8, dtype=torch.int64, device=dev)
+        lib_t.gemm_f16_timeline_buffer(stamps.data_ptr())
+
+        def call(which):
+            st = libs[which].gemm_f16(M, N, K, A.data_ptr(), B.data_ptr(), bias.data_ptr() if epi else None,
+                                      C[which].data_ptr(), epi, stream.cuda_stream)
+            assert st == 0, st
+
+        def timed(which, n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                call(which)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n * 1e3   # us per launch
+
+        times = {k: [] for k in libs}
+        for _rep in range(3):
+            for which in libs:
+                one = timed(which, 3)
+                timed(which, max(1, int(60e3 / one)))             # >= 60 ms back to back
+                times[which].append(round(timed(which, max(20, int(25e3 / one))), 2))
+        # the stamps now hold the last launch of a back-to-back run
+        lib_t.gemm_f16_timeline_buffer(None)
+        s = stamps.cpu().numpy().reshape(nwg, waves, 8)
+        res = summarise(s, nwg, waves)
+        res.update({"config": info["name"], "us_per_launch": times,
+                    "outputs_identical": bool(torch.equal(C["shipped"], C["timeline"]))})
+        results[name] = res
+        print(json.dumps({name: {k: v for k, v in res.items() if k != "per_xcd"}}), flush=True)
+        for row in res["per_xcd"]:
+            print("   ", json.dumps(row), flush=True)
+    with open(out_path, "w") as f:
+        json.dump(results, f, indent=1)
+    if markdown:
+        write_markdown(results, markdown)
+    return results
+
+
+def write_markdown(results: dict, path: str) -> None:
+    lines = []
+    for name, r in results.items():
+        lines += ["### %s (`%s`)" % (name, r["config"]), "",
+                  "µs per launch (three rounds of ≥ 60 ms warm-up + ≥ 25 ms timed): shipped %s, timeline build %s; "
+                  "outputs bit-identical: %s." % (r["us_per_launch"]["shipped"], r["us_per_launch"]["timeline"],
+                                                 r["outputs_identical"]), "",
+                  "| quantity (percentiles over workgroups: 0/10/50/90/100) | values |", "|---|---|"]
+        for k in ("start_us", "prologue_us", "loop_us", "loop_kcycles", "loop_clock_GHz", "epilogue_us",
+                  "epilogue_clock_GHz", "end_us"):
+            lines.append("| %s | %s |" % (k, " / ".join("%g" % v for v in r[k])))
+        lines += ["| span of the launch (first entry to last C store) | %g µs |" % r["span_us"], "",
+                  "| XCD | workgroups | K-loop clock GHz | K loop µs (median) | last workgroup ends µs |",
+                  "|---:|---:|---:|---:|---:|"]
+        for x in r["per_xcd"]:
+            lines.append("| %d | %d | %.3f | %.2f | %.2f |" % (x["xcd"], x["workgroups"], x["loop_clock_GHz"],
+                                                              x["loop_us"], x["last_end_us"]))
+        lines.append("")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--build", action="store_true", help="compile the timeline build of the GEMM unit")
+    ap.add_argument("--run", metavar="OUT_JSON", help="measure on the GPU and write the summary")
+    ap.add_argument("--markdown", default=None, help="with --run: also write the tables as Markdown")
+    a = ap.parse_args()
+    if a.build:
+        print(build())
+    if a.run:
+        run(a.run, a.markdown)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
