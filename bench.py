@@ -57,7 +57,8 @@ WARMUP_MS = 50.0
 
 # Sources each kernel family is built from; a change to any of them voids that family's recorded traffic.
 KERNEL_SOURCES = {
-    "gemm": ["common.h", "tile_pipe_kernel.h", "skinny_kernel.h", "pingpong_kernel.h", "gemm_f16.hip", "config_table.inc"],
+    "gemm": ["common.h", "tile_pipe_kernel.h", "skinny_kernel.h", "skinny_splitk_kernel.h", "pingpong_kernel.h",
+             "gemm_f16.hip", "config_table.inc"],
     "softmax": ["common.h", "softmax.hip"],
     "attention": ["common.h", "attention.hip"],
 }
