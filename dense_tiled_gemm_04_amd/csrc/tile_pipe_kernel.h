@@ -503,6 +503,15 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     }
     __syncthreads();
     stamp(1);
+    if constexpr (GK_TIMELINE) {  // the first two stamps go out now, so none stays live across the K loop
+        if (p.timeline != nullptr && (threadIdx.x & 63) == 0) {
+            uint64_t* o = p.timeline + ((size_t)blockIdx.x * (WM * WN) + (threadIdx.x >> 6)) * 8;
+            o[0] = tl[0];
+            o[1] = tl[1];
+            o[4] = tl[4];
+            o[5] = tl[5];
+        }
+    }
     if (KT > 0) {
         if constexpr (INPLACE) {  // A[TM-1] is read at slot 0 of the k-step
 #pragma unroll
@@ -774,8 +783,10 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         stamp(3);
         if (p.timeline != nullptr && (threadIdx.x & 63) == 0) {
             uint64_t* o = p.timeline + ((size_t)blockIdx.x * (WM * WN) + (threadIdx.x >> 6)) * 8;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) o[k] = tl[k];
+            o[2] = tl[2];
+            o[3] = tl[3];
+            o[6] = tl[6];
+            o[7] = tl[7];
         }
     }
 }

@@ -29,8 +29,9 @@ ROOT = os.path.dirname(PKG_DIR)
 TIMELINE_LIB = os.path.join(PKG_DIR, "_build", "libgemm_f16_timeline.so")
 RESOURCES = os.path.join(PKG_DIR, "_build", "timeline_kernel_resources.json")
 
-# (name, M, N, K, epilogue): the 4096^3 product and the MLP up-projection with bias + GELU
-WORKLOADS = (("gemm_4096", 4096, 4096, 4096, 0), ("mlp_up_8192x16384x4096", 8192, 16384, 4096, 2))
+# (name, M, N, K, epilogue): the 4096^3 product, the MLP up-projection with bias + GELU, the ragged shape with bias
+WORKLOADS = (("gemm_4096", 4096, 4096, 4096, 0), ("mlp_up_8192x16384x4096", 8192, 16384, 4096, 2),
+             ("ragged_4095x3001x1000", 4095, 3001, 1000, 1))
 
 
 def build(verbose: bool = True) -> str:
@@ -96,7 +97,9 @@ def summarise(stamps, nwg: int, waves: int) -> dict:
     return out
 
 
-def run(out_path: str, markdown: str | None = None) -> dict:
+def run(out_path: str, markdown: str | None = None, extra: list | None = None) -> dict:
+    """Measure WORKLOADS with the default configurations, then `extra` runs: (name, M, N, K, epilogue,
+    configuration name or None), with B[K][N] as allocated (row stride N: aligned when N % 8 == 0)."""
     import ctypes
 
     import numpy as np
@@ -113,11 +116,19 @@ def run(out_path: str, markdown: str | None = None) -> dict:
         lib.gemm_f16_select_config.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32]
         lib.gemm_f16_select_config.restype = i32
         lib.gemm_f16_config_info.argtypes = [i32, ctypes.c_char_p, i32]
+        lib.gemm_f16_with_config.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, i32, vp]
+        lib.gemm_f16_with_config.restype = i32
     libs["timeline"].gemm_f16_timeline_buffer.argtypes = [vp]
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     results = {}
-    for name, M, N, K, epi in WORKLOADS:
+    names = []
+    for i in range(libs["timeline"].gemm_f16_num_configs()):
+        b = ctypes.create_string_buffer(1024)
+        libs["timeline"].gemm_f16_config_info(i, b, 1024)
+        names.append(json.loads(b.value.decode())["name"])
+    runs = [w + (None,) for w in WORKLOADS] + list(extra or [])
+    for name, M, N, K, epi, forced in runs:
         print("workload %s" % name, flush=True)
         g = torch.Generator().manual_seed(1)
         A = (torch.rand(M, K, generator=g) * 2 - 1).half().to(dev)
@@ -125,8 +136,11 @@ def run(out_path: str, markdown: str | None = None) -> dict:
         bias = (torch.randn(N, generator=g) * 0.1).half().to(dev)
         C = {k: torch.empty(M, N, dtype=torch.float16, device=dev) for k in libs}
         lib_t = libs["timeline"]
-        idx = lib_t.gemm_f16_select_config(M, N, K, A.data_ptr(), B.data_ptr(), bias.data_ptr() if epi else None,
-                                           C["timeline"].data_ptr(), epi)
+        if forced is None:
+            idx = lib_t.gemm_f16_select_config(M, N, K, A.data_ptr(), B.data_ptr(), bias.data_ptr() if epi else None,
+                                               C["timeline"].data_ptr(), epi)
+        else:
+            idx = names.index(forced)
         buf = ctypes.create_string_buffer(1024)
         lib_t.gemm_f16_config_info(idx, buf, 1024)
         info = json.loads(buf.value.decode())
@@ -142,8 +156,9 @@ def run(out_path: str, markdown: str | None = None) -> dict:
         lib_t.gemm_f16_timeline_buffer(stamps.data_ptr())
 
         def call(which):
-            st = libs[which].gemm_f16(M, N, K, A.data_ptr(), B.data_ptr(), bias.data_ptr() if epi else None,
-                                      C[which].data_ptr(), epi, stream.cuda_stream)
+            args = (M, N, K, A.data_ptr(), B.data_ptr(), bias.data_ptr() if epi else None, C[which].data_ptr(), epi,
+                    stream.cuda_stream)
+            st = libs[which].gemm_f16_with_config(idx, *args) if forced else libs[which].gemm_f16(*args)
             assert st == 0, st
 
         def timed(which, n):
@@ -205,11 +220,17 @@ def main() -> int:
     ap.add_argument("--build", action="store_true", help="compile the timeline build of the GEMM unit")
     ap.add_argument("--run", metavar="OUT_JSON", help="measure on the GPU and write the summary")
     ap.add_argument("--markdown", default=None, help="with --run: also write the tables as Markdown")
+    ap.add_argument("--extra", action="append", default=[], metavar="NAME:M:N:K:EPI:CONFIG",
+                    help="with --run: one more case with a forced configuration of the table (repeatable)")
     a = ap.parse_args()
     if a.build:
         print(build())
     if a.run:
-        run(a.run, a.markdown)
+        extra = []
+        for e in a.extra:
+            f = e.split(":")
+            extra.append((f[0], int(f[1]), int(f[2]), int(f[3]), int(f[4]), f[5]))
+        run(a.run, a.markdown, extra)
     return 0
 
 
