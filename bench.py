@@ -55,26 +55,15 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 WARMUP_MS = 50.0
 
 
-# Sources each kernel family is built from; a change to any of them voids that family's recorded traffic.
-KERNEL_SOURCES = {
-    "gemm": ["common.h", "tile_pipe_kernel.h", "skinny_kernel.h", "skinny_splitk_kernel.h", "pingpong_kernel.h",
-             "gemm_f16.hip", "config_table.inc"],
-    "softmax": ["common.h", "softmax.hip"],
-    "attention": ["common.h", "attention.hip"],
-}
-
-
 def kernel_family(workload: str) -> str:
     return "softmax" if workload.startswith("softmax") else "attention" if workload.startswith("attn") else "gemm"
 
 
 def kernel_source_digest(family: str = "gemm") -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "dense_tiled_gemm_04_amd", "csrc")
-    for f in sorted(KERNEL_SOURCES[family]):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
-    return h.hexdigest()
+    """Digest of a kernel family's sources (a change voids that family's recorded traffic)."""
+    from dense_tiled_gemm_04_amd import build as libbuild
+
+    return libbuild.source_digest(family)
 
 
 def interleaved_ms(torch, stream, ours, theirs, launch_ms: float, rounds: int = 6, chunk_ms: float = 2.0):
@@ -769,6 +758,8 @@ def measure_gemm(g, torch, w, A, B, bias, steps: int, warmup: int, bt: bool = Fa
            "warmup_launches": n_warm, "warmup_ms": round(n_warm * one_ms, 2),
            "finite": bool(torch.isfinite(dC).all().item())}
     out["sustained"] = sustained_ms(torch, stream, step, ms)
+    if not bt and not hbm_bound:
+        out["clock"] = timeline_clock(torch, w, pA, pBs[0], pb, pC, epi, stream, cfg)
     if hbm_bound and rotate > 1:
         # the same launches on one copy of B, which the Infinity Cache then partly serves: labelled, never `value`
         e0.record(stream)
@@ -810,6 +801,29 @@ def measure_gemm(g, torch, w, A, B, bias, steps: int, warmup: int, bt: bool = Fa
     return out
 
 
+def timeline_clock(torch, w, pA, pB, pb, pC, epi, stream, cfg) -> dict:
+    """The shader clock and MFMA share of the tile kernel's K loop, from clock stamps inside a timeline build of
+    the same kernel (dense_tiled_gemm_04_amd/timeline.py), one launch after 60 ms of back-to-back launches of it
+    on the same inputs; or a note saying why there is none.  The spec ceilings assume 2.4 GHz."""
+    try:
+        from dense_tiled_gemm_04_amd import timeline
+
+        ok, why = timeline.available()
+        if not ok:
+            return {"note": why}
+        r = timeline.measure(torch, w.M, w.N, w.K, epi, pA, pB, pb, pC, stream,
+                             config=timeline.config_index(cfg["name"]))
+        if "note" in r:
+            return {"note": r["note"]}
+        clk = r["loop_clock_GHz"]
+        return {"loop_GHz_median": clk[2], "loop_GHz_min": clk[0], "loop_GHz_max": clk[-1],
+                "per_xcd_loop_GHz": [x["loop_clock_GHz"] for x in r["per_xcd"]],
+                "loop_mfma_share": r["loop_mfma_share"], "launch_span_us": r["span_us"],
+                "source": "s_memtime against s_memrealtime stamps inside a GK_TIMELINE build of the same kernel"}
+    except Exception as e:  # a diagnostic: never fails the benchmark
+        return {"note": "timeline measurement failed: %s" % e}
+
+
 def roofline_of(m: dict) -> dict:
     w = m["w"]
     ms = m["ms"]
@@ -826,6 +840,8 @@ def roofline_of(m: dict) -> dict:
     roof["algorithmic_flops_per_launch"] = w.flops
     roof["algorithmic_bytes_per_launch"] = w.algorithmic_bytes
     roof["avg_launch_us"] = ms * 1e3
+    if "clock" in m:
+        roof["sclk"] = m["clock"]
     return roof
 
 

@@ -46,6 +46,27 @@ HEADERS = [os.path.join(CSRC, f) for f in ("common.h", "tile_pipe_kernel.h", "sk
 ]
 
 
+# Sources each kernel family is built from: a change to any of them voids what was measured on that family's
+# kernels (HBM traffic records, timeline builds).
+KERNEL_SOURCES = {
+    "gemm": ["common.h", "tile_pipe_kernel.h", "skinny_kernel.h", "skinny_splitk_kernel.h", "pingpong_kernel.h",
+             "gemm_f16.hip", "config_table.inc"],
+    "softmax": ["common.h", "softmax.hip"],
+    "attention": ["common.h", "attention.hip"],
+}
+
+
+def source_digest(family: str = "gemm") -> str:
+    """sha256 over the named sources of one kernel family (file names and contents, in name order)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(KERNEL_SOURCES[family]):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):

@@ -42,10 +42,117 @@ def build(verbose: bool = True) -> str:
     rows = libbuild.build_library(TIMELINE_LIB, [os.path.join(PKG_DIR, "csrc", "gemm_f16.hip")],
                                   defines=["-DGK_TIMELINE=1"], allow_scratch=True, resources_path=RESOURCES,
                                   verbose=verbose)
+    with open(TIMELINE_LIB + ".sha256", "w") as f:
+        f.write(libbuild.source_digest("gemm") + "\n")
     if verbose:
         for r in libbuild.scratch_users(rows):
             print("uses scratch in the timeline build: %s" % r["kernel"], flush=True)
     return TIMELINE_LIB
+
+
+def available() -> tuple:
+    """(True, None) when the timeline build exists and was built from the current GEMM sources, else
+    (False, reason)."""
+    from dense_tiled_gemm_04_amd import build as libbuild
+
+    if not os.path.exists(TIMELINE_LIB) or not os.path.exists(TIMELINE_LIB + ".sha256"):
+        return False, "no timeline build (python -m dense_tiled_gemm_04_amd.timeline --build)"
+    if open(TIMELINE_LIB + ".sha256").read().strip() != libbuild.source_digest("gemm"):
+        return False, "the timeline build is older than the GEMM sources"
+    return True, None
+
+
+_LIB = None
+
+
+def _load():
+    import ctypes
+
+    global _LIB
+    if _LIB is None:
+        i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        lib = ctypes.CDLL(TIMELINE_LIB)
+        lib.gemm_f16.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32, vp]
+        lib.gemm_f16.restype = i32
+        lib.gemm_f16_with_config.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, i32, vp]
+        lib.gemm_f16_with_config.restype = i32
+        lib.gemm_f16_select_config.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32]
+        lib.gemm_f16_select_config.restype = i32
+        lib.gemm_f16_config_info.argtypes = [i32, ctypes.c_char_p, i32]
+        lib.gemm_f16_timeline_buffer.argtypes = [vp]
+        _LIB = lib
+    return _LIB
+
+
+def _config(idx: int) -> dict:
+    import ctypes
+
+    b = ctypes.create_string_buffer(1024)
+    _load().gemm_f16_config_info(idx, b, 1024)
+    return json.loads(b.value.decode())
+
+
+def config_index(name: str) -> int:
+    lib = _load()
+    for i in range(lib.gemm_f16_num_configs()):
+        if _config(i)["name"] == name:
+            return i
+    raise KeyError(name)
+
+
+def measure(torch, M: int, N: int, K: int, epi: int, A: int, B: int, bias, C: int, stream, warm_ms: float = 60.0,
+            config: int | None = None) -> dict:
+    """Stamps of one launch of the timeline build of the tile kernel (B[K][N], device pointers A, B, bias, C),
+    taken after >= warm_ms of back-to-back launches of it on `stream`; the default configuration unless
+    `config` (an index of the table) is given.  Returns summarise() plus the configuration's name and the K
+    loop's MFMA share: MFMA cycles per SIMD (BM x BN x (K stages x BK) x 2 FLOP over 4 SIMDs at 1024 FLOP per
+    SIMD-cycle) over the loop's median shader cycles."""
+    lib = _load()
+    idx = config if config is not None else lib.gemm_f16_select_config(M, N, K, A, B, bias, C, epi)
+    info = _config(idx)
+    if info["kind"] != "tile" or info["spread"] & 256:
+        return {"config": info["name"], "note": "not a gemm_tile_pipe_kernel configuration: no stamps"}
+    tmpl = [info["bm"], info["bn"], info["bk"], info["waves_m"], info["waves_n"], info["stages"], info["group_m"],
+            epi, info["bslot"], info["dstride"], {"dma": 0, "reg": 1, "buf": 2}[info["loader"]], info["cslot"],
+            info["waves_per_simd"], info["mfma"], info["spread"], info["b_transposed"]]
+    sym = "gemm_tile_pipe_kernelI" + "".join("Li%dE" % v for v in tmpl)
+    if any(sym in k for k in _spilling_tile_kernels()):
+        return {"config": info["name"], "note": "this configuration spills in the timeline build: not measured"}
+    waves = info["waves_m"] * info["waves_n"]
+    nwg = ((M + info["bm"] - 1) // info["bm"]) * ((N + info["bn"] - 1) // info["bn"])
+    stamps = torch.zeros(nwg * waves * 8, dtype=torch.int64, device=torch.device("cuda:0"))
+    sh = stream.cuda_stream
+
+    def launch():
+        st = lib.gemm_f16_with_config(idx, M, N, K, A, B, bias, C, epi, sh)
+        if st != 0:
+            raise RuntimeError("timeline build: gemm_f16_with_config status %d" % st)
+
+    lib.gemm_f16_timeline_buffer(stamps.data_ptr())
+    try:
+        # the first launch of the timeline build also loads its code object: keep it out of the launch time
+        # that sizes the warm-up (a short warm-up would leave the stamped launch in the controller's early dip)
+        launch()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(3):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        one_ms = max(e0.elapsed_time(e1) / 3, 1e-3)
+        for _ in range(max(1, int(warm_ms / one_ms))):
+            launch()
+        torch.cuda.synchronize()
+    finally:
+        lib.gemm_f16_timeline_buffer(None)
+    s = stamps.cpu().numpy().reshape(nwg, waves, 8)
+    out = summarise(s, nwg, waves)
+    kt = (K + info["bk"] - 1) // info["bk"]
+    mfma_cycles = info["bm"] * info["bn"] * kt * info["bk"] * 2 / (4 * 1024)
+    out["config"] = info["name"]
+    out["loop_mfma_share"] = round(mfma_cycles / (out["loop_kcycles"][2] * 1e3), 3)
+    return out
 
 
 def _spilling_tile_kernels() -> list:
@@ -102,31 +209,21 @@ def run(out_path: str, markdown: str | None = None, extra: list | None = None) -
     configuration name or None), with B[K][N] as allocated (row stride N: aligned when N % 8 == 0)."""
     import ctypes
 
-    import numpy as np
     import torch
 
     sys.path.insert(0, ROOT)
     from dense_tiled_gemm_04_amd import build as libbuild
 
     i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
-    libs = {"shipped": ctypes.CDLL(libbuild.LIB_PATH), "timeline": ctypes.CDLL(TIMELINE_LIB)}
-    for lib in libs.values():
-        lib.gemm_f16.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32, vp]
-        lib.gemm_f16.restype = i32
-        lib.gemm_f16_select_config.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32]
-        lib.gemm_f16_select_config.restype = i32
-        lib.gemm_f16_config_info.argtypes = [i32, ctypes.c_char_p, i32]
-        lib.gemm_f16_with_config.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, i32, vp]
-        lib.gemm_f16_with_config.restype = i32
-    libs["timeline"].gemm_f16_timeline_buffer.argtypes = [vp]
+    shipped = ctypes.CDLL(libbuild.LIB_PATH)
+    shipped.gemm_f16.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32, vp]
+    shipped.gemm_f16.restype = i32
+    shipped.gemm_f16_with_config.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, i32, vp]
+    shipped.gemm_f16_with_config.restype = i32
+    lib_t = _load()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     results = {}
-    names = []
-    for i in range(libs["timeline"].gemm_f16_num_configs()):
-        b = ctypes.create_string_buffer(1024)
-        libs["timeline"].gemm_f16_config_info(i, b, 1024)
-        names.append(json.loads(b.value.decode())["name"])
     runs = [w + (None,) for w in WORKLOADS] + list(extra or [])
     for name, M, N, K, epi, forced in runs:
         print("workload %s" % name, flush=True)
@@ -134,31 +231,15 @@ def run(out_path: str, markdown: str | None = None, extra: list | None = None) -
         A = (torch.rand(M, K, generator=g) * 2 - 1).half().to(dev)
         B = (torch.rand(K, N, generator=g) * 2 - 1).half().to(dev)
         bias = (torch.randn(N, generator=g) * 0.1).half().to(dev)
-        C = {k: torch.empty(M, N, dtype=torch.float16, device=dev) for k in libs}
-        lib_t = libs["timeline"]
-        if forced is None:
-            idx = lib_t.gemm_f16_select_config(M, N, K, A.data_ptr(), B.data_ptr(), bias.data_ptr() if epi else None,
-                                               C["timeline"].data_ptr(), epi)
-        else:
-            idx = names.index(forced)
-        buf = ctypes.create_string_buffer(1024)
-        lib_t.gemm_f16_config_info(idx, buf, 1024)
-        info = json.loads(buf.value.decode())
-        assert info["kind"] == "tile" and not info["spread"] & 256, info
-        tmpl = [info["bm"], info["bn"], info["bk"], info["waves_m"], info["waves_n"], info["stages"],
-                info["group_m"], epi, info["bslot"], info["dstride"], {"dma": 0, "reg": 1, "buf": 2}[info["loader"]],
-                info["cslot"], info["waves_per_simd"], info["mfma"], info["spread"], info["b_transposed"]]
-        sym = "gemm_tile_pipe_kernelI" + "".join("Li%dE" % v for v in tmpl)
-        assert not any(sym in k for k in _spilling_tile_kernels()), "the timeline build of %s spills" % info["name"]
-        waves = info["waves_m"] * info["waves_n"]
-        nwg = ((M + info["bm"] - 1) // info["bm"]) * ((N + info["bn"] - 1) // info["bn"])
-        stamps = torch.zeros(nwg * waves * 8, dtype=torch.int64, device=dev)
-        lib_t.gemm_f16_timeline_buffer(stamps.data_ptr())
+        C = {k: torch.empty(M, N, dtype=torch.float16, device=dev) for k in ("shipped", "timeline")}
+        pb = bias.data_ptr() if epi else None
+        idx = config_index(forced) if forced else \
+            lib_t.gemm_f16_select_config(M, N, K, A.data_ptr(), B.data_ptr(), pb, C["timeline"].data_ptr(), epi)
 
         def call(which):
-            args = (M, N, K, A.data_ptr(), B.data_ptr(), bias.data_ptr() if epi else None, C[which].data_ptr(), epi,
-                    stream.cuda_stream)
-            st = libs[which].gemm_f16_with_config(idx, *args) if forced else libs[which].gemm_f16(*args)
+            L = shipped if which == "shipped" else lib_t
+            st = L.gemm_f16_with_config(idx, M, N, K, A.data_ptr(), B.data_ptr(), pb, C[which].data_ptr(), epi,
+                                        stream.cuda_stream)
             assert st == 0, st
 
         def timed(which, n):
@@ -170,21 +251,18 @@ def run(out_path: str, markdown: str | None = None, extra: list | None = None) -
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / n * 1e3   # us per launch
 
-        times = {k: [] for k in libs}
+        times = {"shipped": [], "timeline": []}
         for _rep in range(3):
-            for which in libs:
+            for which in times:
                 one = timed(which, 3)
                 timed(which, max(1, int(60e3 / one)))             # >= 60 ms back to back
                 times[which].append(round(timed(which, max(20, int(25e3 / one))), 2))
-        # the stamps now hold the last launch of a back-to-back run
-        lib_t.gemm_f16_timeline_buffer(None)
-        s = stamps.cpu().numpy().reshape(nwg, waves, 8)
-        res = summarise(s, nwg, waves)
-        res.update({"config": info["name"], "us_per_launch": times,
-                    "outputs_identical": bool(torch.equal(C["shipped"], C["timeline"]))})
+        res = measure(torch, M, N, K, epi, A.data_ptr(), B.data_ptr(), pb, C["timeline"].data_ptr(), stream,
+                      config=idx)
+        res.update({"us_per_launch": times, "outputs_identical": bool(torch.equal(C["shipped"], C["timeline"]))})
         results[name] = res
         print(json.dumps({name: {k: v for k, v in res.items() if k != "per_xcd"}}), flush=True)
-        for row in res["per_xcd"]:
+        for row in res.get("per_xcd", []):
             print("   ", json.dumps(row), flush=True)
     with open(out_path, "w") as f:
         json.dump(results, f, indent=1)
@@ -198,8 +276,9 @@ def write_markdown(results: dict, path: str) -> None:
     for name, r in results.items():
         lines += ["### %s (`%s`)" % (name, r["config"]), "",
                   "µs per launch (three rounds of ≥ 60 ms warm-up + ≥ 25 ms timed): shipped %s, timeline build %s; "
-                  "outputs bit-identical: %s." % (r["us_per_launch"]["shipped"], r["us_per_launch"]["timeline"],
-                                                 r["outputs_identical"]), "",
+                  "outputs bit-identical: %s. K loop MFMA share: %s." % (
+                      r["us_per_launch"]["shipped"], r["us_per_launch"]["timeline"], r["outputs_identical"],
+                      r.get("loop_mfma_share")), "",
                   "| quantity (percentiles over workgroups: 0/10/50/90/100) | values |", "|---|---|"]
         for k in ("start_us", "prologue_us", "loop_us", "loop_kcycles", "loop_clock_GHz", "epilogue_us",
                   "epilogue_clock_GHz", "end_us"):
