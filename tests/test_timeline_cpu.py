@@ -31,3 +31,19 @@ def test_summary_recovers_clock_loop_and_xcd_ends():
     # the slowest XCD (0, 1.6 GHz) ends last: 2 + 90 + 4 us
     assert abs(xs[0]["last_end_us"] - 96.0) < 0.02 and abs(out["span_us"] - 96.0) < 0.02
     assert xs[7]["last_end_us"] < xs[0]["last_end_us"]
+
+
+def test_stale_or_missing_timeline_build_is_reported_not_used(tmp_path, monkeypatch):
+    import bench
+
+    lib = tmp_path / "libgemm_f16_timeline.so"
+    monkeypatch.setattr(timeline, "TIMELINE_LIB", str(lib))
+    ok, why = timeline.available()
+    assert not ok and "no timeline build" in why
+    lib.write_bytes(b"")
+    (tmp_path / "libgemm_f16_timeline.so.sha256").write_text("0" * 64 + "\n")
+    ok, why = timeline.available()
+    assert not ok and "older than the GEMM sources" in why
+    # bench reports the reason instead of a clock, and never raises
+    r = bench.timeline_clock(None, None, 0, 0, None, 0, 0, None, {"name": "x"})
+    assert r == {"note": why}
