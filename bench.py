@@ -861,6 +861,8 @@ def context_line(m: dict) -> dict:
                          "frac": round(per(sus["ms"]) / peak, 4), "chunks": sus["chunks"],
                          "launches_per_chunk": sus["launches_per_chunk"]},
            "b_layout": "Bt[N][K]" if m["bt"] else "B[K][N]", "rotated_B_copies": m["rotate"]}
+    if "sclk" in roof:
+        out["sclk"] = roof["sclk"]
     if m.get("helper_median_ms") is not None:
         out["gemm_f16_time_median_ms"] = round(m["helper_median_ms"], 6)
     if "warm_unrotated_ms" in m:
