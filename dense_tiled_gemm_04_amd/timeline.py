@@ -15,7 +15,7 @@ of back-to-back launches:
     last workgroup ended.
 
     python -m dense_tiled_gemm_04_amd.timeline --build
-    python -m dense_tiled_gemm_04_amd.timeline --run gpurun_out/timeline.json [--markdown out.md]
+    python -m dense_tiled_gemm_04_amd.timeline --run timeline.json [--markdown timeline.md]
 """
 from __future__ import annotations
 
