@@ -145,17 +145,32 @@ def _tool(name: str) -> str:
     raise RuntimeError("%s not found (ROCm's LLVM tools are required for the wait-state check)" % name)
 
 
+BUNDLE_MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
+
+
 def disassemble_library(lib_path: str) -> str:
-    """The gfx950 disassembly of a HIP shared library built here (its .hip_fatbin offload bundle)."""
+    """The gfx950 disassembly of a HIP shared library built here: every offload bundle of its .hip_fatbin
+    section (one per translation unit linked into the library), concatenated."""
     with tempfile.TemporaryDirectory() as d:
-        fat, obj = os.path.join(d, "fatbin.bin"), os.path.join(d, "code.o")
+        fat = os.path.join(d, "fatbin.bin")
         subprocess.run([_tool("llvm-objcopy"), "--dump-section", ".hip_fatbin=" + fat, lib_path, os.devnull],
                        check=True, capture_output=True)
-        subprocess.run([_tool("clang-offload-bundler"), "--unbundle", "--type=o", "--input=" + fat,
-                        "--targets=" + TARGET, "--output=" + obj], check=True, capture_output=True)
-        r = subprocess.run([_tool("llvm-objdump"), "-d", "--symbolize-operands", "--no-show-raw-insn",
-                            "--no-leading-addr", "--mcpu=gfx950", obj], check=True, capture_output=True, text=True)
-        return r.stdout
+        data = open(fat, "rb").read()
+        starts = [m.start() for m in re.finditer(re.escape(BUNDLE_MAGIC), data)]
+        if not starts or starts[0] != 0:
+            raise RuntimeError("%s: .hip_fatbin does not start with an offload bundle" % lib_path)
+        out = []
+        for i, s in enumerate(starts):
+            part, obj = os.path.join(d, "bundle%d.bin" % i), os.path.join(d, "code%d.o" % i)
+            with open(part, "wb") as f:
+                f.write(data[s:starts[i + 1] if i + 1 < len(starts) else len(data)])
+            subprocess.run([_tool("clang-offload-bundler"), "--unbundle", "--type=o", "--input=" + part,
+                            "--targets=" + TARGET, "--output=" + obj], check=True, capture_output=True)
+            r = subprocess.run([_tool("llvm-objdump"), "-d", "--symbolize-operands", "--no-show-raw-insn",
+                                "--no-leading-addr", "--mcpu=gfx950", obj], check=True, capture_output=True,
+                               text=True)
+            out.append(r.stdout)
+        return "\n".join(out)
 
 
 def check_library(lib_path: str) -> int:

@@ -40,10 +40,6 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libgemm_f16.so")
 RESOURCES_PATH = os.path.join(BUILD_DIR, "kernel_resources.json")
 SOURCES = [os.path.join(CSRC, f) for f in ("gemm_f16.hip", "softmax.hip", "attention.hip", "calibration.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("common.h", "tile_pipe_kernel.h", "skinny_kernel.h", "pingpong_kernel.h")] + [
-    os.path.join(INCLUDE, "gemm_f16.h"), os.path.join(INCLUDE, "softmax_f16.h"), os.path.join(INCLUDE, "attention_f16.h"),
-    os.path.join(INCLUDE, "calibration_f16.h"),
-]
 
 
 # Sources each kernel family is built from: a change to any of them voids what was measured on that family's
