@@ -70,7 +70,12 @@ __device__ __forceinline__ float gelu_erf(float x) {
     const float e2 = __builtin_fmaf(a, a * (float)(-0.5 * GK_L2E), q);  // <= -1: log2 of erfc(z) / (2 t)
     const float half_erfc = t * __builtin_amdgcn_exp2f(e2);
     const float phi = x >= 0.0f ? 1.0f - half_erfc : half_erfc;
-    return x * phi;
+    // The product stays an fp32 multiply of its own (the empty asm hides it from instruction selection).
+    // Fused into the fp16 conversion it becomes v_fma_mix with a +0 addend, which turns an exact -0
+    // product (x = -0, or x below about -14.4 where Phi underflows) into +0.
+    float y = x * phi;
+    asm("" : "+v"(y));
+    return y;
 }
 #undef GK_L2E
 

@@ -230,6 +230,56 @@ def test_gelu_epilogue_every_finite_fp16(lib, M):
     assert np.array_equal(got[0].view(np.uint16), got[M - 1].view(np.uint16))
 
 
+@pytest.mark.parametrize("shape", [(16, 264, 64), (256, 520, 128), (72, 264, 8)])
+def test_epilogues_on_non_finite_sums(lib, shape):
+    # Rows whose fp32 sum is +inf, -inf, NaN (a NaN input; inf - inf) or past the fp16 range (+-131008), among
+    # finite rows, through every epilogue of every path able to run the shape.  Against the oracle: GELU(+inf)
+    # = +inf, GELU(-inf) = NaN (x Phi(x) is -inf * 0 there), NaN stays NaN, +131008 rounds to +inf and
+    # GELU(-131008) underflows to -0.  Non-NaN results of the special rows must match bit for bit (zeros of
+    # either sign), NaN positions exactly, and the finite rows keep the usual bar.
+    import dense_tiled_gemm_04_amd as g
+
+    M, N, K = shape
+    rng = np.random.default_rng(41)
+    A = rng.uniform(-1, 1, (M, K)).astype(np.float16)
+    B = rng.uniform(-1, 1, (K, N)).astype(np.float16)
+    B[0] = 1.0
+    if K > 1:
+        B[1] = 1.0
+    bias = workloads.random_f16(12, (N,), -3, 3)
+    rows = [0, 1, M // 2, M // 2 + 1, M - 2, M - 1]
+    A[rows[0], 0] = np.inf
+    A[rows[1], 0] = -np.inf
+    A[rows[2], 0] = np.nan
+    A[rows[3], 0], A[rows[3], 1] = np.inf, -np.inf
+    A[rows[4], 0], A[rows[4], 1] = 65504.0, 65504.0
+    A[rows[5], 0], A[rows[5], 1] = -65504.0, -65504.0
+    keep = np.setdiff1d(np.arange(M), rows)
+    Bt = np.ascontiguousarray(B.T)
+    for epi in ("none", "bias", "bias_gelu"):
+        b = None if epi == "none" else bias
+        ref = oracle.gemm(A, B, b, epi)
+        assert np.isnan(ref[rows[1]]).all() == (epi == "bias_gelu") and np.isnan(ref[rows[2:4]]).all()
+        calls = [(False, idx) for idx in configs_for(lib, M, N, K, epi) + [None]]
+        calls += [(True, c["idx"]) for c in lib.configs() if c["b_transposed"]] + [(True, None)]
+        for bt, idx in calls:
+            try:
+                out = g.gemm_f16(dev(A), dev(Bt) if bt else dev(B), None if b is None else dev(b), epi,
+                                 b_transposed=bt, config=idx)
+            except g.GemmError as e:
+                assert bt and idx is not None and e.status == 6, e  # a Bt config that does not take this shape
+                continue
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()
+            name = (epi, bt, "default" if idx is None else lib.config_info(idx)["name"])
+            assert_parity(got[keep], ref[keep], name)
+            gs, rs = got[rows], ref[rows]
+            assert np.array_equal(np.isnan(gs), np.isnan(rs)), name
+            fin = ~np.isnan(rs)
+            assert np.array_equal(gs[fin].astype(np.float64), rs[fin].astype(np.float64)), name
+            assert np.array_equal(np.signbit(gs[fin]), np.signbit(rs[fin])), name
+
+
 # ---------------------------------------------------------------------------
 # edges: canaries, misaligned views, degenerate sizes, determinism
 # ---------------------------------------------------------------------------
