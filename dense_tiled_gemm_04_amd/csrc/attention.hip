@@ -60,6 +60,7 @@ constexpr int FA_BN = 64;    // keys per block
 constexpr int FA_NW = 4;     // waves per workgroup
 constexpr float kLog2e = 1.44269504088896341f;
 constexpr float kLazyLog2 = 8.0f;  // rescale when a row maximum grows by more than 2^8
+constexpr float kLazySum = 256.0f;  // 2^kLazyLog2
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -321,16 +322,21 @@ flash_attn_fwd_kernel(FaArgs p) {
 // three FMAs) at almost no cost.  This kernel therefore interleaves the stages
 // of neighbouring blocks within each wave:
 //   phase A(j): the score MFMAs of block j+1    || exponentials of block j, keys 32..63
-//   phase B(j): the PV MFMAs of block j         || row maximum of block j+1 and its
-//                                                  exponentials of keys 0..31
+//   phase B(j): the PV MFMAs of block j         || exponentials of block j+1, keys 0..31
 // Each phase is a fixed sequence of 16 slots fenced by scheduling barriers; a
 // slot holds one MFMA, the LDS reads of a later slot's operand, and a share of
-// the vector work.  Block j+1's first-half exponentials use the reference
-// maximum as it stands; if the block's maximum exceeds it by more than 2^8 (the
-// lazy-rescale test of the block-serial kernel), the reference is raised after
-// phase B, the accumulators and the running sum are rescaled, and those
-// exponentials are recomputed.  The result is the block-serial kernel's
-// arithmetic, evaluated in a different order of instructions.
+// the vector work.  A block's exponentials use the reference maximum as it
+// stands.  The lazy-rescale test of the block-serial kernel (does the block's
+// maximum exceed the reference by more than 2^8?) is taken between phases A(j)
+// and B(j), once all of block j's probabilities exist, and without the block's
+// maximum: each probability is at most the sum of those a lane holds, so a lane
+// whose sum of the block's fp16 probabilities stays below 2^8 holds none above
+// 2^8.  Only when some lane's sum reaches 2^8 is the block's maximum formed; if
+// it exceeds the reference by more than 2^8, the reference is raised, the
+// accumulators and the running sum are rescaled and the block's probabilities
+// are formed again.  The rescale decisions are the block-serial kernel's (up to
+// a probability within a fraction of an fp16 ulp below 2^8), evaluated in a
+// different order of instructions.
 // K and V tiles are copied one block apart: after the barrier that opens
 // A(j), K(j+2) and V(j+1) are issued into the buffers that K(j) and V(j-1)
 // have left, so two buffers of each suffice.
@@ -425,7 +431,7 @@ flash_attn_fwd_pipe_kernel(FaArgs p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
     const f32x16 zero16 = {};
-    float m_run, l_run = 0.0f;
+    float m_run, l_run = 0.0f, l_first = 0.0f;
     const float c = PRESCALE ? 1.0f : p.scale_log2;
     const f16x2 ones = {(f16)1.0f, (f16)1.0f};
 
@@ -507,11 +513,11 @@ flash_attn_fwd_pipe_kernel(FaArgs p) {
                                        fmaxf(max16(sc[0][1], 0), max16(sc[0][1], 1))));
         m_run = mb * c;  // the first block holds key 0, which every row may see: finite
 #pragma unroll
-        for (int k = 0; k < 8; ++k) exp_pair(sc[0][0], pf[0][0], k, m_run, l_run);
+        for (int k = 0; k < 8; ++k) exp_pair(sc[0][0], pf[0][0], k, m_run, l_first);
     }
 
-    // phase A(j): score MFMAs of block j+1 (NEXT) || exponentials of block j, keys 32..63
-    auto phase_a = [&]<int PAR, bool NEXT>() {
+    // phase A(j): score MFMAs of block j+1 (NEXT) || exponentials of block j, keys 32..63, summed into l_b
+    auto phase_a = [&]<int PAR, bool NEXT>(float& l_b) {
         constexpr int NX = PAR ^ 1;
         const float mr = opaque(m_run);
         if constexpr (NEXT) {
@@ -525,16 +531,16 @@ flash_attn_fwd_pipe_kernel(FaArgs p) {
                 if (s + PDK < 2 * KS) kf[s + PDK] = *(const GK_LDS f16x8*)(Kn + k_rd(kb, s + PDK));
                 sc[NX][s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[s], qf[s >> 1], s < 2 ? zero16 : sc[NX][s & 1],
                                                                         0, 0, 0);
-                if (s & 1) exp_pair(sc[PAR][1], pf[PAR][1], s >> 1, mr, l_run);
+                if (s & 1) exp_pair(sc[PAR][1], pf[PAR][1], s >> 1, mr, l_b);
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) exp_pair(sc[PAR][1], pf[PAR][1], k, mr, l_run);
+            for (int k = 0; k < 8; ++k) exp_pair(sc[PAR][1], pf[PAR][1], k, mr, l_b);
         }
     };
-    // phase B(j): PV MFMAs of block j || (NEXT) row maximum of block j+1 and its exponentials of keys 0..31,
-    // formed with the reference maximum as it stands; returns block j+1's scaled row maximum
+    // phase B(j): PV MFMAs of block j || (NEXT) exponentials of block j+1, keys 0..31, formed with the reference
+    // maximum as it stands and summed into l_half
     auto phase_b = [&]<int PAR, bool NEXT>(float& l_half) {
         constexpr int NX = PAR ^ 1;
         const GK_LDS char* Vs = (const GK_LDS char*)smem + (2 + PAR) * TILE;
@@ -549,46 +555,25 @@ flash_attn_fwd_pipe_kernel(FaArgs p) {
         };
 #pragma unroll
         for (int s = 0; s < PDV; ++s) read_v(s);
-        float mp[4], mc = 0.0f;
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
             if (s + PDV < 16) read_v(s + PDV);
             const int st = s >> 2;
             oacc[s & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[s], pf[PAR][st >> 1][st & 1], oacc[s & 3], 0, 0, 0);
             if constexpr (NEXT) {
-                if (s < 4) {
-                    mp[s] = max16(sc[NX][s >> 1], s & 1);
-                    asm volatile("" : "+v"(mp[s]));
-                }
-                if (s == 4) {
-                    mc = row_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]))) * c;
-                    asm volatile("" : "+v"(mc));
-                }
-                if (s >= 6 && s < 14) exp_pair(sc[NX][0], pf[NX][0], s - 6, mr, l_half);
+                if (s & 1) exp_pair(sc[NX][0], pf[NX][0], s >> 1, mr, l_half);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        return mc;
     };
-
-    // Each step opens with the barrier of block j and the copies of K(j+2) and V(j+1).  NEXT: block j+1 is
-    // one of this wave's blocks (scored in phase A, its maximum and first half formed in phase B).
-    auto open_step = [&](int j) {
-        wait_vmcnt0();
-        __syncthreads();  // K(j+1) and V(j) in LDS for every wave; K(j) and V(j-1) free
-        if (j + 2 < n_wg) issue_k(j + 2);
-        if (j + 1 < n_wg) issue_v(j + 1);
-    };
-    auto step = [&]<int PAR, bool NEXT>(int j) {
-        constexpr int NX = PAR ^ 1;
-        open_step(j);
-        if constexpr (NEXT) {
-            phase_a.template operator()<PAR, true>();
-            prepare(sc[NX], j + 1);
-            float l_half = 0.0f;
-            const float mc = phase_b.template operator()<PAR, true>(l_half);
-            // The reference maximum moves only when some row's block maximum exceeds it by more than 2^8;
-            // block j+1's first-half probabilities were formed with the old one and are formed again.
+    // The lazy-rescale test of block j (scores in sc[PAR]), whose probabilities are all formed: l0 and l1 are the
+    // lane's sums of its first- and second-half probabilities.  A probability above 2^8 makes its lane's sum
+    // reach 2^8; only then is the block's maximum formed and compared with the reference.  The sums then join
+    // the running sum.
+    auto settle = [&]<int PAR>(float l0, float l1) {
+        if (__any(l0 + l1 >= kLazySum)) {
+            const float mc = row_max(fmaxf(fmaxf(max16(sc[PAR][0], 0), max16(sc[PAR][0], 1)),
+                                           fmaxf(max16(sc[PAR][1], 0), max16(sc[PAR][1], 1)))) * c;
             if (__any(mc > m_run + kLazyLog2)) {
                 const float m_new = fmaxf(m_run, mc);
                 const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -598,16 +583,35 @@ flash_attn_fwd_pipe_kernel(FaArgs p) {
                 for (int db = 0; db < DB; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-                l_half = 0.0f;
+                l0 = 0.0f;
+                l1 = 0.0f;
 #pragma unroll
-                for (int k = 0; k < 8; ++k) exp_pair(sc[NX][0], pf[NX][0], k, m_run, l_half);
+                for (int k = 0; k < 8; ++k) exp_pair(sc[PAR][0], pf[PAR][0], k, m_run, l0);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) exp_pair(sc[PAR][1], pf[PAR][1], k, m_run, l1);
             }
-            l_run += l_half;
-        } else {
-            phase_a.template operator()<PAR, false>();
-            float unused = 0.0f;
-            phase_b.template operator()<PAR, false>(unused);
         }
+        l_run += l0 + l1;
+    };
+
+    // Each step opens with the barrier of block j and the copies of K(j+2) and V(j+1).  NEXT: block j+1 is
+    // one of this wave's blocks (scored in phase A, its first half formed in phase B).  l_first carries the
+    // first-half sum of the block a step forms next.
+    auto open_step = [&](int j) {
+        wait_vmcnt0();
+        __syncthreads();  // K(j+1) and V(j) in LDS for every wave; K(j) and V(j-1) free
+        if (j + 2 < n_wg) issue_k(j + 2);
+        if (j + 1 < n_wg) issue_v(j + 1);
+    };
+    auto step = [&]<int PAR, bool NEXT>(int j) {
+        constexpr int NX = PAR ^ 1;
+        open_step(j);
+        float l_second = 0.0f;
+        phase_a.template operator()<PAR, NEXT>(l_second);
+        settle.template operator()<PAR>(l_first, l_second);
+        l_first = 0.0f;
+        if constexpr (NEXT) prepare(sc[NX], j + 1);
+        phase_b.template operator()<PAR, NEXT>(l_first);
     };
 
     // Blocks 0 .. n_w-1 are this wave's; the main loop runs only steps with a following block, so every
