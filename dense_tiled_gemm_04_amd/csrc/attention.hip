@@ -238,45 +238,60 @@ flash_attn_fwd_kernel(FaArgs p) {
                     if (j >= Nkv || (CAUSAL && j > i)) sc[jj][r] = -INFINITY;
                 }
         }
-        // block maximum of the row (unscaled; c > 0), then in the log2 domain
-        float mb = -INFINITY;
+        // row maximum of the block in the log2 domain (raw maxima; c > 0), the lane and its partner l ^ 32
+        auto block_max = [&]() {
+            float mb = -INFINITY;
 #pragma unroll
-        for (int jj = 0; jj < JB; ++jj)
+            for (int jj = 0; jj < JB; ++jj)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mb = fmaxf(mb, sc[jj][r]);
-        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-        const float mc = mb * c;
+                for (int r = 0; r < 16; ++r) mb = fmaxf(mb, sc[jj][r]);
+            return fmaxf(mb, __shfl_xor(mb, 32, 64)) * c;
+        };
+        // probabilities: exp2(s c - m) as one FMA and one v_exp_f32, rounded in
+        // pairs to fp16 (v_cvt_pk_f16_f32) for the P^T operand; the block's sum
+        // adds those same rounded pairs (v_dot2_f32_f16 with ones), so the
+        // weights applied to V sum to one
+        f16x8 pf[JB][2];
+        auto probabilities = [&](float& l) {
+#pragma unroll
+            for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[jj][2 * k], c, -m_run));
+                    const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[jj][2 * k + 1], c, -m_run));
+                    const f16x2 h = __builtin_convertvector((f32x2){a, b}, f16x2);
+                    l = __builtin_amdgcn_fdot2(h, ones, l, false);
+                    pf[jj][k >> 2][2 * (k & 3)] = h[0];
+                    pf[jj][k >> 2][2 * (k & 3) + 1] = h[1];
+                }
+        };
         // Lazy rescaling: the reference maximum moves only when some row's block
         // maximum exceeds it by more than 2^8, so probabilities stay below 256
         // (exact enough in fp16, far from overflow) and the accumulators are
-        // rescaled rarely.  The first block always sets it (m_run = -inf), and
-        // that block holds key 0, which every row may see.
-        if (__any(mc > m_run + kLazyLog2)) {
-            const float m_new = fmaxf(m_run, mc);
-            const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
+        // rescaled rarely.  The first block sets it from its own maximum (that
+        // block holds key 0, which every row may see, so it is finite).  Later
+        // blocks form their probabilities with the reference as it stands; each
+        // is at most the sum of the block's probabilities the lane holds, so the
+        // block's maximum is formed only when some lane's sum reaches 2^8.
+        if (jb == 0) m_run = block_max();
+        float l_blk = 0.0f;
+        probabilities(l_blk);
+        if (__any(l_blk >= kLazySum)) {
+            const float mc = block_max();
+            if (__any(mc > m_run + kLazyLog2)) {
+                const float m_new = fmaxf(m_run, mc);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+                for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        }
-        // probabilities: exp2(s c - m) as one FMA and one v_exp_f32, rounded in
-        // pairs to fp16 (v_cvt_pk_f16_f32) for the P^T operand; the row sum adds
-        // those same rounded pairs (v_dot2_f32_f16 with ones), so the weights
-        // applied to V sum to one
-        f16x8 pf[JB][2];
-#pragma unroll
-        for (int jj = 0; jj < JB; ++jj)
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[jj][2 * k], c, -m_run));
-                const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[jj][2 * k + 1], c, -m_run));
-                const f16x2 h = __builtin_convertvector((f32x2){a, b}, f16x2);
-                l_run = __builtin_amdgcn_fdot2(h, ones, l_run, false);
-                pf[jj][k >> 2][2 * (k & 3)] = h[0];
-                pf[jj][k >> 2][2 * (k & 3) + 1] = h[1];
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                l_blk = 0.0f;
+                probabilities(l_blk);
             }
+        }
+        l_run += l_blk;
         // O^T += V^T . P^T, 16 keys per step
 #pragma unroll
         for (int st = 0; st < FA_BN / 16; ++st) {
