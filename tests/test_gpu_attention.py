@@ -117,6 +117,34 @@ def test_rising_scores_move_the_reference_maximum(lib, kernel):
         assert_parity(got, ref, ("rising", causal, kernel))
 
 
+@pytest.mark.parametrize("kernel,D", [("block_serial", 64), ("block_serial", 128), ("pipelined", 128)])
+@pytest.mark.parametrize("key", [650, 700])
+def test_dominant_late_key_forces_rescale(lib, kernel, D, key):
+    # One key far into the sequence (block 10; key 650 in the first half of its 64-key block, 700 in the
+    # second) whose score passes the earlier keys' maximum by a log2 margin from about -1 to 58, depending on
+    # the row, D and beta: its probability against the stale reference would overflow fp16 unless the lazy
+    # rescale fires.
+    # The kernels take that decision from each lane's sum of the block's probabilities, not the block maximum,
+    # so a lane holding that one key must trigger it (rows past the threshold), and rows below the threshold
+    # must keep the old reference.
+    rng = np.random.default_rng(key + D)
+    N = 900
+    Q = rng.standard_normal((1, 2, N, D))
+    Q[..., 0] += 3.0                                     # every row leans on dimension 0
+    K = rng.standard_normal((1, 2, N, D)) * 0.25
+    V = rng.standard_normal((1, 2, N, D))
+    for beta in (20.0, 60.0):
+        Kb = K.copy()
+        Kb[:, :, key, :] = 0.0
+        Kb[:, :, key, 0] = beta
+        Q16, K16, V16 = (x.astype(np.float16) for x in (Q, Kb, V))
+        for causal in (False, True):
+            ref = oracle.attention(Q16, K16, V16, causal=causal)
+            got = run(lib, Q16, K16, V16, causal, kernel=KERNELS[kernel])
+            assert np.isfinite(got).all(), (kernel, D, key, beta, causal)
+            assert_parity(got, ref, ("dominant key", kernel, D, key, beta, causal))
+
+
 def _slab_rows(w, max_slabs=8):
     """Flat row indices of whole (batch, head) slabs: every slab when there are at most max_slabs of them,
     else the first, the last, the middle and seeded others, max_slabs in all."""
