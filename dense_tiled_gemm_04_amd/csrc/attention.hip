@@ -29,7 +29,10 @@
 //  * The softmax state is fp32 and in the log2 domain: each probability is one
 //    FMA (the scale folded in) and one v_exp_f32.  The reference maximum is
 //    raised lazily, only when a row's maximum grows by more than 2^8, so the
-//    accumulators are rarely rescaled and probabilities stay below 256.  The
+//    accumulators are rarely rescaled and probabilities stay below 256.  A
+//    block's probabilities are formed against the reference as it stands; the
+//    block's maximum is formed only when some lane's sum of them reaches 2^8
+//    (no probability can pass 2^8 while its lane's sum stays below).  The
 //    probabilities enter the PV product rounded to fp16 in pairs, and the row
 //    sum adds those same rounded values (v_dot2 with ones), so each output row
 //    is an exact convex combination of value rows up to fp32 rounding.
