@@ -1,0 +1,86 @@
+"""HIP graph capture of the library's entry points (torch.cuda.CUDAGraph on the ROCm build).
+
+The shipped kernels allocate nothing and issue no memset, and every call is plain kernel launches on the
+caller's stream, so a captured sequence of calls replays as recorded.  The graph below holds the GEMM on three
+paths (tile kernel with bias + GELU, skinny kernel, B given transposed), the row softmax and both attention
+kernels.  Before each replay the inputs are rewritten in place with new seeded values, the same calls run
+eagerly and the outputs are poisoned with NaN; the replay must then reproduce the eager outputs bit for bit
+(every kernel here is deterministic), several times in a row, with eager work and synchronisations between.
+"""
+import numpy as np
+import pytest
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def test_graph_replays_match_eager(lib):
+    import dense_tiled_gemm_04_amd as g
+
+    f16 = dict(dtype=torch.float16, device="cuda")
+    gemms = [  # M, N, K, epilogue, B given transposed
+        (300, 520, 256, "bias_gelu", False),
+        (16, 1032, 384, "bias", False),
+        (257, 136, 192, "none", True),
+    ]
+    ops = []
+    for M, N, K, epi, bt in gemms:
+        A = torch.empty((M, K), **f16)
+        B = torch.empty((N, K) if bt else (K, N), **f16)
+        bias = torch.empty((N,), **f16)
+        C = torch.empty((M, N), **f16)
+        ops.append(("gemm", (A, B, bias), C, (epi, bt)))
+    X = torch.empty((37, 3001), **f16)
+    ops.append(("softmax", (X,), torch.empty_like(X), None))
+    for Bn, H, N, D in ((1, 2, 200, 64), (1, 2, 300, 128)):
+        Q, K, V = (torch.empty((Bn, H, N, D), **f16) for _ in range(3))
+        ops.append(("attention", (Q, K, V), torch.empty_like(Q), None))
+
+    def fill(seed):
+        for i, (_, ins, _, _) in enumerate(ops):
+            for j, t in enumerate(ins):
+                t.copy_(torch.from_numpy(workloads.random_f16(1000 * seed + 10 * i + j, tuple(t.shape))))
+
+    def calls():
+        for kind, ins, out, extra in ops:
+            if kind == "gemm":
+                A, B, bias = ins
+                epi, bt = extra
+                g.gemm_f16(A, B, None if epi == "none" else bias, epi, out=out, b_transposed=bt)
+            elif kind == "softmax":
+                g.softmax_f16(ins[0], out=out)
+            else:
+                g.flash_attn(*ins, causal=True, out=out)
+
+    fill(0)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    torch.cuda.synchronize()
+
+    outs = [o for _, _, o, _ in ops]
+    for rep in range(4):
+        fill(rep + 1)
+        torch.cuda.synchronize()
+        calls()
+        torch.cuda.synchronize()
+        eager = [o.clone() for o in outs]
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for (kind, _, _, extra), e, o in zip(ops, eager, outs):
+            assert not torch.isnan(o).any() or torch.isnan(e).any(), (rep, kind, extra)
+            assert torch.equal(e.view(torch.int16), o.view(torch.int16)), (rep, kind, extra)
