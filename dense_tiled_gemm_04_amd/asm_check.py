@@ -19,6 +19,9 @@ back-edges too) until the required count is reached.
 
 `check_library(path)` raises if the library's gfx950 code has any hazard;
 `hazards(text)` scans assembly text (compiler `-S` output or llvm-objdump).
+`instruction_markers(text)` counts, per kernel, the matrix-core, LDS-DMA copy,
+LDS read/write, barrier and exponential instructions, so that tests can check
+that each kernel was built the way its design says.
 """
 from __future__ import annotations
 
@@ -133,6 +136,35 @@ def hazards(text: str) -> list:
     for name, body in _functions(text):
         out += _scan_function(name, body)
     return out
+
+
+MARKERS = ("v_mfma_f32_16x16x32_f16", "v_mfma_f32_32x32x16_f16", "global_load_lds_dwordx4", "buffer_load_lds",
+           "ds_read_b64_tr_b16", "ds_read_b128", "ds_write_b128", "s_barrier", "v_exp_f32")
+
+
+def instruction_markers(text: str) -> dict:
+    """Per kernel, how often each of MARKERS occurs: the matrix-core, asynchronous-copy (LDS-DMA), LDS read and
+    write, barrier and exponential instructions by which one can tell that a kernel was built the intended way.
+    `buffer_load_lds` counts buffer loads that write LDS (the `lds` modifier)."""
+    out = {}
+    for name, body in _functions(text):
+        c = dict.fromkeys(MARKERS, 0)
+        for op, args in body:
+            if op == "LABEL":
+                continue
+            if op.startswith("buffer_load") and "lds" in args:
+                c["buffer_load_lds"] += 1
+                continue
+            for m in MARKERS:
+                if op == m or op.startswith(m + "_"):
+                    c[m] += 1
+        out[name] = c
+    return out
+
+
+def template_ints(name: str) -> list:
+    """The integer and bool template arguments of an Itanium-mangled kernel name, in order."""
+    return [int(v) for v in re.findall(r"L[ib](-?\d+)E", name)]
 
 
 def _tool(name: str) -> str:

@@ -1,5 +1,6 @@
-"""The wait-state check of the library's machine code (dense_tiled_gemm_04_amd/asm_check.py): planted
-hazards in small assembly texts are found, their fixed forms pass, and the built library has none."""
+"""The checks of the library's machine code (dense_tiled_gemm_04_amd/asm_check.py): planted wait-state hazards
+in small assembly texts are found, their fixed forms pass, the built library has none, and every kernel of the
+built library uses the instructions its design names."""
 import os
 
 import pytest
@@ -126,3 +127,50 @@ def test_disassembly_covers_every_unit():
     for unit_kernel in ("gemm_tile_pipe_kernel", "gemm_skinny_kernel", "flash_attn_fwd_pipe_kernel",
                         "softmax_reg_kernel", "vector_add_f32_kernel"):
         assert any(unit_kernel in n for n in names), unit_kernel
+
+
+def test_kernels_use_the_intended_instructions():
+    # The pages read the generated code for tensor-core operations, asynchronous copies and barriers.  Here every
+    # kernel of the built library is checked for the gfx950 instructions of its design, decoded from its
+    # template arguments: the MFMA shape, the copy form of its loader (LDS-DMA from global or buffer
+    # addresses, or register staging written with ds_write_b128), LDS transpose reads exactly when B is
+    # row-major, a barrier, and exponentials exactly in the GELU instantiations.
+    from dense_tiled_gemm_04_amd import build
+
+    if not os.path.exists(build.LIB_PATH):
+        pytest.skip("library not built")
+    try:
+        text = asm_check.disassemble_library(build.LIB_PATH)
+    except FileNotFoundError as e:
+        pytest.skip("LLVM tools missing: %s" % e)
+    seen = dict.fromkeys(("tile", "skinny", "attention", "softmax"), 0)
+    for name, m in asm_check.instruction_markers(text).items():
+        a = asm_check.template_ints(name)
+        if "gemm_tile_pipe_kernel" in name:
+            # BM BN BK WM WN STAGES GROUP_M EPI BSLOT DSTRIDE LOADER CSLOT WPE MF SPREAD BT
+            seen["tile"] += 1
+            epi, loader, mf, bt = a[7], a[10], a[13], a[15]
+            assert m["v_mfma_f32_%s_f16" % ("16x16x32" if mf == 16 else "32x32x16")] > 0, name
+            copy = {0: "global_load_lds_dwordx4", 1: "ds_write_b128", 2: "buffer_load_lds"}[loader]
+            assert m[copy] > 0, name
+            if loader != 1:
+                assert m["ds_write_b128"] == 0, name          # the LDS-DMA loaders stage nothing through VGPRs
+            assert (m["ds_read_b64_tr_b16"] > 0) == (bt == 0), name
+            assert m["s_barrier"] > 0, name
+            assert (m["v_exp_f32"] > 0) == (epi == 2), name
+        elif "gemm_skinny_kernel" in name:
+            # MB STAGES EPI BT KROT A16
+            seen["skinny"] += 1
+            epi, bt = a[2], a[3]
+            assert m["v_mfma_f32_16x16x32_f16"] > 0 and m["buffer_load_lds"] > 0, name
+            assert (m["ds_read_b64_tr_b16"] > 0) == (bt == 0), name
+            assert (m["v_exp_f32"] > 0) == (epi == 2), name
+        elif "flash_attn_fwd" in name:
+            seen["attention"] += 1
+            assert m["v_mfma_f32_32x32x16_f16"] > 0 and m["buffer_load_lds"] > 0, name
+            assert m["ds_read_b64_tr_b16"] > 0 and m["v_exp_f32"] > 0 and m["s_barrier"] > 0, name
+        elif "softmax" in name:
+            seen["softmax"] += 1
+            assert m["v_mfma_f32_16x16x32_f16"] == m["v_mfma_f32_32x32x16_f16"] == 0, name
+            assert m["v_exp_f32"] > 0, name
+    assert all(seen.values()), seen
