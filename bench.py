@@ -883,6 +883,147 @@ def context_line(m: dict) -> dict:
 CONTEXT_WORKLOADS = ["mlp_up_8192x16384x4096", "skinny_16x16384x8192"]
 
 
+def report(g, torch) -> int:
+    """The pages' report utility (latency, throughput and error per kernel) as one table over every workload:
+    ours and the torch comparator each timed after >= 50 ms of back-to-back launches (median of ~1 ms chunks),
+    the rate against the MI355X peak, and the relative Frobenius error of our output against a float32
+    reference computed with torch on the GPU (a sanity check like the pages' `check`; parity against the oracle
+    is the test suite's).  Prints a Markdown table, then one JSON line with the same rows."""
+    import numpy as np
+    import torch.nn.functional as F
+
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    lib = g.load()
+
+    def ok(st):
+        if st != 0:
+            raise g.GemmError(st)
+
+    def settled(step):
+        step(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(1, 4):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return sustained_ms(torch, stream, step, max(e0.elapsed_time(e1) / 3, 1e-3))["ms"]
+
+    def rel_fro(got, ref):
+        d = got.float() - ref
+        return float(torch.linalg.vector_norm(d) / torch.linalg.vector_norm(ref))
+
+    rows = []
+
+    def row(name, path, ms, torch_ms, err, flops=None, nbytes=None, comparator=""):
+        if flops is not None:
+            rate, unit = flops / (ms * 1e-3) / 1e12, "TFLOP/s"
+            frac = rate / PEAK_FP16_TFLOPS
+        else:
+            rate, unit = nbytes / (ms * 1e-3) / 1e9, "GB/s"
+            frac = rate / PEAK_HBM_GBS
+        rows.append({"workload": name, "path": path, "ours_us": round(ms * 1e3, 2), "rate": round(rate, 1),
+                     "unit": unit, "frac_of_peak": round(frac, 4), "torch": comparator,
+                     "torch_us": round(torch_ms * 1e3, 2), "torch_over_ours": round(torch_ms / ms, 3),
+                     "rel_fro_vs_fp32": float("%.3g" % err)})
+        print("report: %s %s done" % (name, path), file=sys.stderr, flush=True)
+
+    for wname, w in workloads.WORKLOADS.items():
+        A, B, bias = workloads.make_inputs(w)
+        hbm = w.flops / w.algorithmic_bytes < 100.0
+        rot = 3 if hbm else 1
+        dA = torch.from_numpy(A).to(dev)
+        db = torch.from_numpy(bias).to(dev) if bias is not None else None
+        for bt in ((False, True) if wname in ("gemm_4096", "mlp_up_8192x16384x4096") else (False,)):
+            dBs = [torch.from_numpy(np.ascontiguousarray(B.T) if bt else B).to(dev) for _ in range(rot)]
+            out = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+            pBs = [t.data_ptr() for t in dBs]
+            pA, pC, pb, epi = dA.data_ptr(), out.data_ptr(), db.data_ptr() if db is not None else None, \
+                g.EPILOGUES[w.epilogue]
+
+            def ours(i):  # the C ABI directly, as in the bench lines (the torch binding adds host time per call)
+                ok(lib.gemm_f16_bt(w.M, w.N, w.K, pA, w.K, pBs[i % rot], w.K, pb, pC, w.N, epi, sh) if bt else
+                   lib.gemm_f16(w.M, w.N, w.K, pA, pBs[i % rot], pb, pC, epi, sh))
+
+            ms = settled(ours)
+
+            def vendor(i):
+                y = F.linear(dA, dBs[i % rot]) if bt else torch.matmul(dA, dBs[i % rot])
+                if w.epilogue != "none":
+                    y = y + db
+                if w.epilogue == "bias_gelu":
+                    y = F.gelu(y)
+                return y
+
+            tms = settled(vendor)
+            g.gemm_f16(dA, dBs[0], db, w.epilogue, out=out, b_transposed=bt)
+            ref = dA.float() @ (dBs[0].float().t() if bt else dBs[0].float())
+            if w.epilogue != "none":
+                ref += db.float()
+            if w.epilogue == "bias_gelu":
+                ref = F.gelu(ref)
+            err = rel_fro(out, ref)
+            del ref
+            cfg = g.config_info(g.select_config(dA, dBs[0], db, w.epilogue, out=out, b_transposed=bt))["name"]
+            row(wname + (" (Bt)" if bt else ""), cfg, ms, tms, err,
+                flops=None if hbm else w.flops, nbytes=w.algorithmic_bytes if hbm else None,
+                comparator=("F.linear" if bt else "matmul") + {"none": "", "bias": " + add",
+                                                                "bias_gelu": " + add + gelu"}[w.epilogue])
+            del dBs, out
+        del dA, db, A, B, bias
+    for wname, w in workloads.SOFTMAX_WORKLOADS.items():
+        X = workloads.make_softmax_input(w)
+        rot = 3 if X.nbytes >= (64 << 20) else 1
+        dXs = [torch.from_numpy(X).to(dev) for _ in range(rot)]
+        out = torch.empty_like(dXs[0])
+        pXs, pY = [t.data_ptr() for t in dXs], out.data_ptr()
+        ms = settled(lambda i: ok(g.softmax_rows_raw(w.rows, w.cols, pXs[i % rot], pY, sh)))
+        tms = settled(lambda i: torch.softmax(dXs[i % rot], dim=-1))
+        g.softmax_f16(dXs[0], out=out)
+        err = rel_fro(out, torch.softmax(dXs[0].float(), dim=-1))
+        row(wname, "softmax " + g.softmax_path(*X.shape), ms, tms, err, nbytes=w.algorithmic_bytes,
+            comparator="torch.softmax")
+        del dXs, out, X
+    for wname, w in workloads.ATTENTION_WORKLOADS.items():
+        Q, K, V = (torch.from_numpy(x).to(dev) for x in workloads.make_attention_inputs(w))
+        out = torch.empty_like(Q)
+        ptrs = (Q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr())
+        ms = settled(lambda i: ok(g.flash_attn_raw(w.B, w.H, w.Nq, w.Nkv, w.D, *ptrs, w.causal,
+                                                   1.0 / math.sqrt(w.D), sh)))
+        tms = settled(lambda i: F.scaled_dot_product_attention(Q, K, V, is_causal=w.causal))
+        g.flash_attn(Q, K, V, causal=w.causal, out=out)
+        # float32 reference, one (batch, head) slab at a time; the transposed operand is made contiguous
+        err_num = err_den = 0.0
+        for b in range(w.B):
+            for h in range(w.H):
+                q, k, v = Q[b, h].float(), K[b, h].float(), V[b, h].float()
+                sc = (q @ k.t().contiguous()) / math.sqrt(w.D)
+                if w.causal:
+                    sc = sc.masked_fill(torch.ones_like(sc, dtype=torch.bool).triu(1), float("-inf"))
+                ref = torch.softmax(sc, dim=-1) @ v
+                err_num += float(torch.linalg.vector_norm(out[b, h].float() - ref) ** 2)
+                err_den += float(torch.linalg.vector_norm(ref) ** 2)
+        row(wname, "flash_attn_fwd", ms, tms, math.sqrt(err_num / err_den), flops=w.flops,
+            comparator="F.scaled_dot_product_attention")
+        del Q, K, V, out
+
+    print("| workload | path | ours, us | rate | of peak | torch comparator | torch, us | torch / ours | "
+          "rel. Frobenius vs fp32 |")
+    print("|---|---|---:|---:|---:|---|---:|---:|---:|")
+    for r in rows:
+        print("| %s | `%s` | %.2f | %.1f %s | %.3f | %s | %.2f | %.2f | %.2e |" % (
+            r["workload"], r["path"], r["ours_us"], r["rate"], r["unit"], r["frac_of_peak"], r["torch"],
+            r["torch_us"], r["torch_over_ours"], r["rel_fro_vs_fp32"]))
+    print(json.dumps({"report": rows}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -906,6 +1047,9 @@ def main() -> int:
                     help="run only the register-only MFMA loop (both MFMA shapes) and the shipped 4096^3 GEMM "
                          "back to back, with board power and clock: the practical MFMA ceiling under the power "
                          "limit")
+    ap.add_argument("--report", action="store_true",
+                    help="run every workload, ours beside the torch comparator, and print one table of latency, "
+                         "rate, fraction of peak and error against a float32 reference (then the rows as JSON)")
     ap.add_argument("--clock-series", action="store_true",
                     help="run only the 4096^3 GEMM and the MLP shape back to back for 80 ms each after idle, and print "
                          "the time per launch of every ~1 ms chunk (how the power controller settles)")
@@ -931,6 +1075,8 @@ def main() -> int:
         return mfma_calibration(g, torch)
     if args.clock_series:
         return clock_series(g, torch)
+    if args.report:
+        return report(g, torch)
     if args.workload in workloads.SOFTMAX_WORKLOADS:
         return bench_softmax(args, g, torch, workloads.SOFTMAX_WORKLOADS[args.workload])
     if args.workload in workloads.ATTENTION_WORKLOADS:
