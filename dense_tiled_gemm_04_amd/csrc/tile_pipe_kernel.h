@@ -749,7 +749,11 @@ gemm_tile_pipe_kernel(GemmArgs p) {
         }
     }
     if constexpr (LDS_EPI) {
-        __syncthreads();  // the sub-tile's LDS writes precede its reads by other lanes
+        // Each wave reads back only the region it wrote (its own sub-tile), so no workgroup barrier is
+        // needed: once this wave's LDS writes have completed, its lanes read what other lanes of the same
+        // wave wrote.  The memory clobber keeps the compiler from moving the reads above the wait.  A wave
+        // then stores C while other waves of the workgroup still form theirs.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         // 16-byte stores need 16-byte-aligned rows of C (always so with LOAD_DMA)
         const bool c_al = LOADER == LOAD_DMA || ((((uintptr_t)p.C) & 15) == 0 && (ldc & 7) == 0);
         static_assert((WTM * RCH) % 64 == 0, "whole store instructions per sub-tile");
