@@ -352,9 +352,8 @@ flash_attn_fwd_kernel(FaArgs p) {
 // 2^8.  Only when some lane's sum reaches 2^8 is the block's maximum formed; if
 // it exceeds the reference by more than 2^8, the reference is raised, the
 // accumulators and the running sum are rescaled and the block's probabilities
-// are formed again.  The rescale decisions are the block-serial kernel's (up to
-// a probability within a fraction of an fp16 ulp below 2^8), evaluated in a
-// different order of instructions.
+// are formed again.  The block-serial kernel takes the same test on the same
+// probabilities; the two differ in the order of instructions and of the sums.
 // K and V tiles are copied one block apart: after the barrier that opens
 // A(j), K(j+2) and V(j+1) are issued into the buffers that K(j) and V(j-1)
 // have left, so two buffers of each suffice.
