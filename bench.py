@@ -1056,7 +1056,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the GEMM runs on a single MI355X and this build has no "
+        print("bench.py measures one GPU only: the GEMM runs on a single MI355X and the library has no "
               "multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
         return 2
 

@@ -38,7 +38,7 @@ def build(verbose: bool = True) -> str:
     from dense_tiled_gemm_04_amd import build as libbuild
 
     # the stamps' registers push a few register-loader kernels into scratch; those are never measured here
-    # (run() refuses a configuration whose kernel uses scratch in this build)
+    # (run() refuses a configuration whose kernel uses scratch in the timeline build)
     rows = libbuild.build_library(TIMELINE_LIB, [os.path.join(PKG_DIR, "csrc", "gemm_f16.hip")],
                                   defines=["-DGK_TIMELINE=1"], allow_scratch=True, resources_path=RESOURCES,
                                   verbose=verbose)
