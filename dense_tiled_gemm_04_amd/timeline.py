@@ -8,7 +8,9 @@ after the K loop and after the C stores have completed).  `--run` (GPU) times
 the shipped library and the timeline build on the same inputs, checks that
 their outputs are bit-identical, and summarises one launch taken after >= 60 ms
 of back-to-back launches:
-  * per workgroup: prologue, K loop and epilogue durations (wave 0);
+  * per workgroup: prologue and K loop durations (wave 0), and the epilogue from
+    the end of wave 0's K loop to the completion of the last wave's C stores
+    (waves store their parts of C independently), with wave 0's own beside it;
   * the shader clock during the K loop (stamp cycles over stamp time), and the
     loop's length in shader cycles;
   * per XCD (workgroup w runs on XCD w mod 8): clock, loop time and when its
@@ -184,7 +186,8 @@ def summarise(stamps, nwg: int, waves: int) -> dict:
         "loop_us": _pct(loop_ns / 1e3),
         "loop_kcycles": _pct(loop_cyc / 1e3),
         "loop_clock_GHz": _pct(loop_cyc / loop_ns),
-        "epilogue_us": _pct((w0r[:, 3] - w0r[:, 2]) / 1e3),
+        "epilogue_us": _pct((r[:, :, 3].max(axis=1) - w0r[:, 2]) / 1e3),
+        "epilogue_wave0_us": _pct((w0r[:, 3] - w0r[:, 2]) / 1e3),
         "epilogue_clock_GHz": _pct((w0t[:, 3] - w0t[:, 2]) / (w0r[:, 3] - w0r[:, 2])),
         "end_us": _pct((r[:, :, 3].max(axis=1) - r0) / 1e3),
         "percentiles": [0, 10, 50, 90, 100],
@@ -281,7 +284,7 @@ def write_markdown(results: dict, path: str) -> None:
                       r.get("loop_mfma_share")), "",
                   "| quantity (percentiles over workgroups: 0/10/50/90/100) | values |", "|---|---|"]
         for k in ("start_us", "prologue_us", "loop_us", "loop_kcycles", "loop_clock_GHz", "epilogue_us",
-                  "epilogue_clock_GHz", "end_us"):
+                  "epilogue_wave0_us", "epilogue_clock_GHz", "end_us"):
             lines.append("| %s | %s |" % (k, " / ".join("%g" % v for v in r[k])))
         lines += ["| span of the launch (first entry to last C store) | %g µs |" % r["span_us"], "",
                   "| XCD | workgroups | K-loop clock GHz | K loop µs (median) | last workgroup ends µs |",

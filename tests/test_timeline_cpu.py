@@ -21,7 +21,10 @@ def _stamps(nwg=16, waves=8):
 
 def test_summary_recovers_clock_loop_and_xcd_ends():
     s = _stamps()
+    s[3, 5, 7] += 150  # wave 5 of workgroup 3 completes its C stores 1.5 us after wave 0
     out = timeline.summarise(s, 16, 8)
+    # the workgroup's epilogue runs to its last wave's stores; wave 0's own stays 4 us
+    assert abs(out["epilogue_us"][-1] - 5.5) < 0.02 and abs(out["epilogue_wave0_us"][-1] - 4.0) < 0.02
     assert out["loop_kcycles"][2] == 144.0
     assert abs(out["loop_clock_GHz"][0] - 1.6) < 2e-3 and abs(out["loop_clock_GHz"][-1] - 1.74) < 2e-3
     assert abs(out["prologue_us"][2] - 2.0) < 0.02 and abs(out["epilogue_us"][2] - 4.0) < 0.02
