@@ -685,10 +685,12 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     // LDS_EPI (SPREAD bit 5): the stage buffers are free once the last stage
     // has been read, and the whole fp16 C tile fits in them.  Each wave writes
     // its sub-tile there in the MFMA layout (8 bytes per lane, rows of WTN
-    // columns whose 16-byte chunks are XOR-swizzled by row), then reads it
-    // back row-contiguous and writes C with 16-byte stores: one store
-    // instruction covers 64 consecutive 16-byte chunks of the sub-tile's rows
-    // (RCH = WTN/8 chunks per row) instead of MF rows x 8 bytes x 4 lanes.
+    // columns whose 16-byte chunks are XOR-swizzled by row), one MFMA row
+    // block at a time, and reads each block back row-contiguous and writes it
+    // to C with 16-byte stores before it forms the next: one store instruction
+    // covers 64 consecutive 16-byte chunks of the sub-tile's rows (RCH = WTN/8
+    // chunks per row) instead of MF rows x 8 bytes x 4 lanes, and the stores
+    // of a block go out while the wave forms the next ones.
     // NT_C (SPREAD bit 6): those stores are marked non-temporal (C is not
     // read again by this kernel).
     constexpr int NQ = NACC / 4;  // column quads per lane and block
@@ -705,35 +707,96 @@ gemm_tile_pipe_kernel(GemmArgs p) {
     // of r, which keeps a chunk inside its aligned group of 4 and so inside the row.
     auto c_swz = [&](int r) { return RCH_P2 ? (r & ((RCH < 16 ? RCH : 16) - 1)) : ((r >> 2) & 3); };
     GK_LDS char* const c_lds = a_lds + wave_e * (WTM * WTN * 2);  // this wave's sub-tile [WTM][WTN] fp16
-    if constexpr (LDS_EPI) __syncthreads();  // every wave has finished reading the last stage
+    // C in row blocks: for each MFMA row block mi, the epilogue of its accumulators, then (LDS_EPI) its rows
+    // staged through LDS and stored at once, so that a wave's C stores go out while it still forms the next
+    // row blocks (rows of block mi are complete once every column block of it is written).
+    auto col_of = [&](int ni, int r4) {  // column of the lane's quad in the sub-tile
+        return ni * MF + (MF == 32 ? 8 * r4 + 4 * (lane_e >> 5) : 4 * (lane_e >> 4));
+    };
+    auto bias_quad = [&](int n, float (&bv)[4]) {
 #pragma unroll
-    for (int ni = 0; ni < TN; ++ni) {
+        for (int e = 0; e < 4; ++e) bv[e] = 0.0f;
+        if constexpr (EPI != EPI_NONE) {
+            if (n + 4 <= N) {
+                const f16x4 b4 = *(const f16x4_u*)(p.bias + n);
 #pragma unroll
-        for (int r4 = 0; r4 < NQ; ++r4) {
-            const int nc = ni * MF + (MF == 32 ? 8 * r4 + 4 * (lane_e >> 5) : 4 * (lane_e >> 4));  // column in the sub-tile
-            const int n = n0 + wn_e * WTN + nc;
-            const bool quad = n + 4 <= N;
-            float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (EPI != EPI_NONE) {
-                if (quad) {
-                    const f16x4 b4 = *(const f16x4_u*)(p.bias + n);
+                for (int e = 0; e < 4; ++e) bv[e] = (float)b4[e];
+            } else if (LOADER != LOAD_DMA) {  // LOAD_DMA: N % 8 == 0, the quad is wholly past N
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) bv[e] = (float)b4[e];
-                } else if (LOADER != LOAD_DMA) {  // LOAD_DMA: N % 8 == 0, the quad is wholly past N
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) bv[e] = (float)p.bias[n + e];
+            }
+        }
+    };
+    if constexpr (LDS_EPI) {
+        __syncthreads();  // every wave has finished reading the last stage
+        // 16-byte stores need 16-byte-aligned rows of C (always so with LOAD_DMA)
+        const bool c_al = LOADER == LOAD_DMA || ((((uintptr_t)p.C) & 15) == 0 && (ldc & 7) == 0);
+        constexpr int ITB = MF * RCH / 64;  // store instructions per row block
+        static_assert((MF * RCH) % 64 == 0, "whole store instructions per row block");
+        float bvs[TN][NQ][4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < N) bv[e] = (float)p.bias[n + e];
+        for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+            for (int r4 = 0; r4 < NQ; ++r4) bias_quad(n0 + wn_e * WTN + col_of(ni, r4), bvs[ni][r4]);
+#pragma unroll
+        for (int mi = 0; mi < TM; ++mi) {
+            const int rr = mi * MF + (lane_e % MF);  // row in the sub-tile
+#pragma unroll
+            for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+                for (int r4 = 0; r4 < NQ; ++r4) {
+                    const int nc = col_of(ni, r4);
+                    f16x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = (f16)apply_epilogue<EPI>(acc[mi][ni][4 * r4 + e], bvs[ni][r4][e]);
+                    *(GK_LDS f16x4*)(c_lds + rr * WTN * 2 + (((nc >> 3) ^ c_swz(rr)) << 4) + ((nc & 7) << 1)) = o;
+                }
+            // Each wave reads back only the region it wrote (its own sub-tile): once this wave's LDS writes
+            // have completed, its lanes read what other lanes of the same wave wrote.  The memory clobber keeps
+            // the compiler from moving the reads above the wait.
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int j = 0; j < ITB; ++j) {
+                const int lc = (mi * ITB + j) * 64 + lane_e;  // chunk of the sub-tile, row-major
+                const int rc = lc / RCH, c = lc % RCH;
+                const f16x8 v = *(const GK_LDS f16x8*)(c_lds + rc * WTN * 2 + ((c ^ c_swz(rc)) << 4));
+                const int m = m0 + wm_e * WTM + rc, n = n0 + wn_e * WTN + 8 * c;
+                if (m >= M || n >= N) continue;
+                f16* dst = p.C + (size_t)m * ldc + n;
+                if (n + 8 <= N) {
+                    if (c_al) {
+                        if constexpr (NT_C) {
+                            __builtin_nontemporal_store(v, (f16x8*)dst);
+                        } else {
+                            *(f16x8*)dst = v;
+                        }
+                    } else {
+                        *(f16x8_u*)dst = v;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < N) dst[e] = v[e];
                 }
             }
+        }
+    } else {
 #pragma unroll
-            for (int mi = 0; mi < TM; ++mi) {
-                const int rr = mi * MF + (lane_e % MF);  // row in the sub-tile
-                f16x4 o;
+        for (int ni = 0; ni < TN; ++ni) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = (f16)apply_epilogue<EPI>(acc[mi][ni][4 * r4 + e], bv[e]);
-                if constexpr (LDS_EPI) {
-                    *(GK_LDS f16x4*)(c_lds + rr * WTN * 2 + (((nc >> 3) ^ c_swz(rr)) << 4) + ((nc & 7) << 1)) = o;
-                } else {
+            for (int r4 = 0; r4 < NQ; ++r4) {
+                const int nc = col_of(ni, r4);
+                const int n = n0 + wn_e * WTN + nc;
+                const bool quad = n + 4 <= N;
+                float bv[4];
+                bias_quad(n, bv);
+#pragma unroll
+                for (int mi = 0; mi < TM; ++mi) {
+                    const int rr = mi * MF + (lane_e % MF);  // row in the sub-tile
+                    f16x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = (f16)apply_epilogue<EPI>(acc[mi][ni][4 * r4 + e], bv[e]);
                     const int m = m0 + wm_e * WTM + rr;
                     if (m >= M || n >= N) continue;
                     f16* dst = p.C + (size_t)m * ldc + n;
@@ -745,40 +808,6 @@ gemm_tile_pipe_kernel(GemmArgs p) {
                             if (n + e < N) dst[e] = o[e];
                     }
                 }
-            }
-        }
-    }
-    if constexpr (LDS_EPI) {
-        // Each wave reads back only the region it wrote (its own sub-tile), so no workgroup barrier is
-        // needed: once this wave's LDS writes have completed, its lanes read what other lanes of the same
-        // wave wrote.  The memory clobber keeps the compiler from moving the reads above the wait.  A wave
-        // then stores C while other waves of the workgroup still form theirs.
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        // 16-byte stores need 16-byte-aligned rows of C (always so with LOAD_DMA)
-        const bool c_al = LOADER == LOAD_DMA || ((((uintptr_t)p.C) & 15) == 0 && (ldc & 7) == 0);
-        static_assert((WTM * RCH) % 64 == 0, "whole store instructions per sub-tile");
-#pragma unroll
-        for (int it = 0; it < WTM * RCH / 64; ++it) {
-            const int lc = it * 64 + lane_e;             // chunk of the sub-tile, row-major
-            const int rr = lc / RCH, c = lc % RCH;
-            const f16x8 v = *(const GK_LDS f16x8*)(c_lds + rr * WTN * 2 + ((c ^ c_swz(rr)) << 4));
-            const int m = m0 + wm_e * WTM + rr, n = n0 + wn_e * WTN + 8 * c;
-            if (m >= M || n >= N) continue;
-            f16* dst = p.C + (size_t)m * ldc + n;
-            if (n + 8 <= N) {
-                if (c_al) {
-                    if constexpr (NT_C) {
-                        __builtin_nontemporal_store(v, (f16x8*)dst);
-                    } else {
-                        *(f16x8*)dst = v;
-                    }
-                } else {
-                    *(f16x8_u*)dst = v;
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (n + e < N) dst[e] = v[e];
             }
         }
     }
