@@ -466,6 +466,13 @@ def space() -> list:
             for bk in (32, 64):
                 for sp in (2, 4):
                     out.append(SplitK(mb, st, bk, sp))
+    # two workgroups per CU: 256x128 and 128x256 tiles at BK = 32 on four waves (128x64 or 64x128 per wave,
+    # 32x32 MFMAs, 48 or 72 KiB of LDS each), so that one workgroup's epilogue can run beside the other's K loop
+    for bm, bn in ((256, 128), (128, 256)):
+        for st in (2, 3):
+            for fl in (96, 4 + 96, 14 + 96):
+                for bs, ds in ((1, 1), (3, 2), (4, 2)):
+                    out.append(Tile(bm, bn, 32, 2, 2, st, 4, bs, ds, "dma", wpe=2, spread=fl))
     return [c for c in out if valid(c)]
 
 
