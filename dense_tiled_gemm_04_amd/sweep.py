@@ -466,6 +466,13 @@ def space() -> list:
             for bk in (32, 64):
                 for sp in (2, 4):
                     out.append(SplitK(mb, st, bk, sp))
+    # eight-wave 256x256 tiles on 32x32x16 MFMAs (half the operand register reads per FLOP of 16x16x32)
+    for bt in (0, 1):
+        for fl in (0, 4, 6):
+            for bs, ds in ((2, 2), (4, 2), (4, 3)):
+                out.append(Tile(256, 256, 64, 2, 4, 2, 4, bs, ds, "dma", wpe=2, spread=fl + 96, bt=bt))
+        for bs, ds in ((2, 2), (4, 2), (4, 3)):
+            out.append(Tile(256, 256, 64, 4, 2, 2, 4, bs, ds, "dma", wpe=2, spread=6 + 96, bt=bt))
     # two workgroups per CU: 256x128 and 128x256 tiles at BK = 32 on four waves (128x64 or 64x128 per wave,
     # 32x32 MFMAs, 48 or 72 KiB of LDS each), so that one workgroup's epilogue can run beside the other's K loop
     for bm, bn in ((256, 128), (128, 256)):
