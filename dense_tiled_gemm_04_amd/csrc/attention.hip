@@ -330,7 +330,7 @@ flash_attn_fwd_kernel(FaArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Software-pipelined forward kernel for D = 128.
+// Software-pipelined forward kernel for D = 128 and 64.
 //
 // The block-serial kernel above runs, per 64-key block, the score MFMAs, then
 // the softmax on the vector ALU, then the PV MFMAs; each stage waits for the
@@ -341,9 +341,10 @@ flash_attn_fwd_kernel(FaArgs p) {
 // of neighbouring blocks within each wave:
 //   phase A(j): the score MFMAs of block j+1    || exponentials of block j, keys 32..63
 //   phase B(j): the PV MFMAs of block j         || exponentials of block j+1, keys 0..31
-// Each phase is a fixed sequence of 16 slots fenced by scheduling barriers; a
-// slot holds one MFMA, the LDS reads of a later slot's operand, and a share of
-// the vector work.  A block's exponentials use the reference maximum as it
+// Each phase is a fixed sequence of 16 slots (8 at D = 64) fenced by
+// scheduling barriers; a slot holds one MFMA, the LDS reads of a later slot's
+// operand, and a share of the vector work (at D = 64 an exponential pair in
+// every slot, at D = 128 in every other one).  A block's exponentials use the reference maximum as it
 // stands.  The lazy-rescale test of the block-serial kernel (does the block's
 // maximum exceed the reference by more than 2^8?) is taken between phases A(j)
 // and B(j), once all of block j's probabilities exist, and without the block's
@@ -357,15 +358,18 @@ flash_attn_fwd_kernel(FaArgs p) {
 // K and V tiles are copied one block apart: after the barrier that opens
 // A(j), K(j+2) and V(j+1) are issued into the buffers that K(j) and V(j-1)
 // have left, so two buffers of each suffice.
-template <bool CAUSAL, bool PRESCALE>
+template <int D, bool CAUSAL, bool PRESCALE>
 __global__ void __launch_bounds__(FA_NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 flash_attn_fwd_pipe_kernel(FaArgs p) {
-    constexpr int D = 128;
+    static_assert(D == 64 || D == 128, "head dimension");
     constexpr int CH = D / 8;
     constexpr int TILE = FA_BN * D * 2;
     constexpr int INS = FA_BN * CH / (FA_NW * 64);
-    constexpr int KS = D / 16;   // 8 k-steps of the score product
-    constexpr int DB = D / 32;   // 4 output column blocks
+    constexpr int KS = D / 16;   // k-steps of the score product (8 or 4)
+    constexpr int DB = D / 32;   // output column blocks (4 or 2)
+    constexpr int NSA = 2 * KS;  // MFMA slots of phase A (score MFMAs, two 32-key halves)
+    constexpr int NSB = 4 * DB;  // MFMA slots of phase B (PV MFMAs, four 16-key steps)
+    constexpr int EA = NSA / 8, EB = NSB / 8;  // slots per exponential pair (8 pairs per phase)
     constexpr int PDK = 3;       // K fragment reads issued this many slots ahead
     constexpr int PDV = 3;       // V fragment reads issued this many slots ahead
     static_assert(INS * FA_NW * 64 == FA_BN * CH, "copy split");
@@ -399,12 +403,12 @@ flash_attn_fwd_pipe_kernel(FaArgs p) {
         (void*)(p.K + bh * (int64_t)Nkv * D), (short)0, Nkv * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.V + bh * (int64_t)Nkv * D), (short)0, Nkv * D * 2, 0x00020000);
-    // Copy t of a tile moves key rows 16 t .. 16 t + 15 (4096 bytes further on than copy t - 1); the swizzle
-    // of a chunk depends on its row only through the row's low bits, which t does not change, so one
+    // Copy t of a tile moves the 4096 bytes after copy t - 1 (16 key rows at D = 128, 32 at D = 64); the
+    // swizzle of a chunk depends on its row only through the row's low bits, which t does not change, so one
     // offset per lane serves every copy.
     uint32_t k_off0, v_off0;
     {
-        const int jr = 4 * wave + (lane >> 4), pc = lane & 15;
+        const int jr = (wave * 64 + lane) / CH, pc = (wave * 64 + lane) % CH;
         k_off0 = (uint32_t)((jr * D + 8 * (pc ^ swz_k<D>(jr))) * 2);
         v_off0 = (uint32_t)((jr * D + 8 * (pc ^ swz_v<D>(jr))) * 2);
     }
@@ -430,17 +434,19 @@ flash_attn_fwd_pipe_kernel(FaArgs p) {
     };
 
     // LDS read offsets.  K fragment of score slot s (k-step s/2, 32-key half s%2): key row 32 (s%2) + l%32,
-    // 16-byte chunk (2 (s/2) + l/32) XOR (row % 16); the row's high half and the k-step enter as 8192 (s%2)
-    // and an XOR with 32 (s/2).  V^T fragment (column block db, key half h, 16-key step st) of the
-    // block-serial kernel: 2048 h + 4096 st + (vbase XOR 64 db).
-    const int kbase = ((lane & 31) * 256) | (((lane >> 5) ^ (lane & 15)) << 4);
+    // 16-byte chunk (2 (s/2) + l/32) XOR swz_k(row); the swizzle depends on the row only through l%32, so the
+    // row's high half and the k-step enter as 64 D (s%2) bytes and an XOR with 32 (s/2).  V^T fragment
+    // (column block db, 8-key half h, 16-key step st) of the block-serial kernel: key row 4 (g/2) + 8 h + jq
+    // + 16 st, columns 32 db + 16 (g%2) + 4 q; the swizzle depends on the row only through jq, so
+    // 16 D h + 32 D st + (vbase XOR 64 db).
+    const int kbase = ((lane & 31) * 2 * D) | (((lane >> 5) ^ swz_k<D>(lane & 31)) << 4);
     int vbase;
     {
         const int g = lane >> 4, jq = (lane >> 2) & 3, q = lane & 3;
-        vbase = (4 * (g >> 1) + jq) * 256 + 64 * jq + 32 * (g & 1) + 16 * (q >> 1) + 8 * (q & 1);
+        vbase = (4 * (g >> 1) + jq) * 2 * D + 16 * swz_v<D>(jq) + 32 * (g & 1) + 16 * (q >> 1) + 8 * (q & 1);
     }
-    auto k_rd = [&](int kb, int s) { return 8192 * (s & 1) + (kb ^ (32 * (s >> 1))); };
-    auto v_rd = [&](int vb, int h, int db, int st) { return 2048 * h + 4096 * st + (vb ^ (64 * db)); };
+    auto k_rd = [&](int kb, int s) { return 64 * D * (s & 1) + (kb ^ (32 * (s >> 1))); };
+    auto v_rd = [&](int vb, int h, int db, int st) { return 16 * D * h + 32 * D * st + (vb ^ (64 * db)); };
 
     f32x16 oacc[DB];
 #pragma unroll
@@ -533,22 +539,23 @@ flash_attn_fwd_pipe_kernel(FaArgs p) {
         for (int k = 0; k < 8; ++k) exp_pair(sc[0][0], pf[0][0], k, m_run, l_first);
     }
 
+    // The 8 exponential pairs of a phase go one per EA (EB) slots, on the last slot of each group.
     // phase A(j): score MFMAs of block j+1 (NEXT) || exponentials of block j, keys 32..63, summed into l_b
     auto phase_a = [&]<int PAR, bool NEXT>(float& l_b) {
         constexpr int NX = PAR ^ 1;
         const float mr = opaque(m_run);
         if constexpr (NEXT) {
             const GK_LDS char* Kn = (const GK_LDS char*)smem + NX * TILE;  // block j+1 has parity NX
-            f16x8 kf[2 * KS];
+            f16x8 kf[NSA];
             const int kb = opaque(kbase);
 #pragma unroll
             for (int s = 0; s < PDK; ++s) kf[s] = *(const GK_LDS f16x8*)(Kn + k_rd(kb, s));
 #pragma unroll
-            for (int s = 0; s < 2 * KS; ++s) {
-                if (s + PDK < 2 * KS) kf[s + PDK] = *(const GK_LDS f16x8*)(Kn + k_rd(kb, s + PDK));
+            for (int s = 0; s < NSA; ++s) {
+                if (s + PDK < NSA) kf[s + PDK] = *(const GK_LDS f16x8*)(Kn + k_rd(kb, s + PDK));
                 sc[NX][s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[s], qf[s >> 1], s < 2 ? zero16 : sc[NX][s & 1],
                                                                         0, 0, 0);
-                if (s & 1) exp_pair(sc[PAR][1], pf[PAR][1], s >> 1, mr, l_b);
+                if (s % EA == EA - 1) exp_pair(sc[PAR][1], pf[PAR][1], s / EA, mr, l_b);
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
@@ -562,10 +569,10 @@ flash_attn_fwd_pipe_kernel(FaArgs p) {
         constexpr int NX = PAR ^ 1;
         const GK_LDS char* Vs = (const GK_LDS char*)smem + (2 + PAR) * TILE;
         const float mr = opaque(m_run);
-        f16x8 vf[16];
+        f16x8 vf[NSB];
         const int vb = opaque(vbase);
         auto read_v = [&](int s) {
-            const int st = s >> 2, db = s & 3;
+            const int st = s / DB, db = s % DB;
             const f16x4 v0 = lds_read_tr16_b64(Vs + v_rd(vb, 0, db, st));
             const f16x4 v1 = lds_read_tr16_b64(Vs + v_rd(vb, 1, db, st));
             vf[s] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -573,12 +580,12 @@ flash_attn_fwd_pipe_kernel(FaArgs p) {
 #pragma unroll
         for (int s = 0; s < PDV; ++s) read_v(s);
 #pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            if (s + PDV < 16) read_v(s + PDV);
-            const int st = s >> 2;
-            oacc[s & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[s], pf[PAR][st >> 1][st & 1], oacc[s & 3], 0, 0, 0);
+        for (int s = 0; s < NSB; ++s) {
+            if (s + PDV < NSB) read_v(s + PDV);
+            const int st = s / DB;
+            oacc[s % DB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[s], pf[PAR][st >> 1][st & 1], oacc[s % DB], 0, 0, 0);
             if constexpr (NEXT) {
-                if (s & 1) exp_pair(sc[NX][0], pf[NX][0], s >> 1, mr, l_half);
+                if (s % EB == EB - 1) exp_pair(sc[NX][0], pf[NX][0], s / EB, mr, l_half);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -676,16 +683,17 @@ hipError_t launch_d(const FaArgs& a, int64_t BH, bool causal, bool prescale, hip
     return causal ? launch<D, true, false>(a, BH, s) : launch<D, false, false>(a, BH, s);
 }
 
-template <bool CAUSAL, bool PRESCALE>
+template <int D, bool CAUSAL, bool PRESCALE>
 hipError_t launch_pipe(const FaArgs& a, int64_t BH, hipStream_t s) {
-    hipLaunchKernelGGL((flash_attn_fwd_pipe_kernel<CAUSAL, PRESCALE>), dim3((unsigned)(BH * a.q_blocks)),
+    hipLaunchKernelGGL((flash_attn_fwd_pipe_kernel<D, CAUSAL, PRESCALE>), dim3((unsigned)(BH * a.q_blocks)),
                        dim3(FA_NW * 64), 0, s, a);
     return hipGetLastError();
 }
 
+template <int D>
 hipError_t launch_pipe_d(const FaArgs& a, int64_t BH, bool causal, bool prescale, hipStream_t s) {
-    if (prescale) return causal ? launch_pipe<true, true>(a, BH, s) : launch_pipe<false, true>(a, BH, s);
-    return causal ? launch_pipe<true, false>(a, BH, s) : launch_pipe<false, false>(a, BH, s);
+    if (prescale) return causal ? launch_pipe<D, true, true>(a, BH, s) : launch_pipe<D, false, true>(a, BH, s);
+    return causal ? launch_pipe<D, true, false>(a, BH, s) : launch_pipe<D, false, false>(a, BH, s);
 }
 
 }  // namespace
@@ -729,9 +737,9 @@ int flash_attn_fwd_f16_kernel(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int
     // raw scores is the maximum of the scaled ones); otherwise scores are
     // scaled first
     const bool prescale = !(scale > 0.0f);
-    if (kernel == FLASH_ATTN_KERNEL_PIPELINED && D != 128) return GEMM_ERR_UNSUPPORTED;
-    if (D == 128 && kernel != FLASH_ATTN_KERNEL_BLOCK_SERIAL)
-        e = launch_pipe_d(a, B * H, causal != 0, prescale, s);
+    if (kernel != FLASH_ATTN_KERNEL_BLOCK_SERIAL)
+        e = D == 128 ? launch_pipe_d<128>(a, B * H, causal != 0, prescale, s)
+                     : launch_pipe_d<64>(a, B * H, causal != 0, prescale, s);
     else
         e = D == 128 ? launch_d<128>(a, B * H, causal != 0, prescale, s)
                      : launch_d<64>(a, B * H, causal != 0, prescale, s);

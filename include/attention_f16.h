@@ -61,8 +61,8 @@ int flash_attn_fwd_f16(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
  *                 (D = 64 or 128)
  *   PIPELINED     the scores of block j+1 and the PV product of block j run on
  *                 the matrix cores while the same wave computes the softmax of
- *                 its neighbouring blocks (D = 128 only)
- *   AUTO          PIPELINED for D = 128, BLOCK_SERIAL for D = 64 */
+ *                 its neighbouring blocks (D = 64 or 128)
+ *   AUTO          PIPELINED */
 enum {
     FLASH_ATTN_KERNEL_AUTO = 0,
     FLASH_ATTN_KERNEL_BLOCK_SERIAL = 1,
@@ -70,8 +70,7 @@ enum {
 };
 
 /* flash_attn_fwd_f16 with the kernel chosen by the caller (for comparisons and
- * tests).  Additional statuses: GEMM_ERR_NO_CONFIG for an unknown `kernel`,
- * GEMM_ERR_UNSUPPORTED for PIPELINED with D != 128. */
+ * tests).  Additional status: GEMM_ERR_NO_CONFIG for an unknown `kernel`. */
 int flash_attn_fwd_f16_kernel(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
                               const void* Q, const void* K, const void* V, void* O,
                               int causal, float scale, int kernel, void* stream);

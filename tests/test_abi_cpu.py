@@ -170,7 +170,7 @@ def test_attention_kernel_selector_validation():
     # an unknown kernel is refused before anything else; the pipelined kernel exists for D = 128 only
     assert fa(1, 1, 4, 4, 128, FAKE, FAKE, FAKE, FAKE, False, 0.1, kernel=7) == 5
     assert fa(-1, 1, 4, 4, 128, FAKE, FAKE, FAKE, FAKE, False, 0.1, kernel=-1) == 5
-    assert fa(1, 1, 4, 4, 64, FAKE, FAKE, FAKE, FAKE, False, 0.1, kernel=g.ATTN_KERNEL_PIPELINED) == 6
+    assert fa(1, 1, 4, 4, 96, FAKE, FAKE, FAKE, FAKE, False, 0.1, kernel=g.ATTN_KERNEL_PIPELINED) == 6
     assert fa(1, 1, 4, 4, 128, FAKE, FAKE, FAKE, FAKE, False, 0.1, kernel=3) == 5
     assert fa(1, 1, 4, 4, 96, FAKE, FAKE, FAKE, FAKE, False, 0.1, kernel=g.ATTN_KERNEL_BLOCK_SERIAL) == 6
     assert fa(1, 1, 4, 4, 128, None, FAKE, FAKE, FAKE, False, 0.1, kernel=g.ATTN_KERNEL_PIPELINED) == 2

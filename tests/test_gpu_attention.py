@@ -77,35 +77,38 @@ def test_constant_values_and_peaked_scores(lib):
         assert_parity(run(lib, Q, K, V2, causal), ref, ("peaked", causal))
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("kernel", list(KERNELS))
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SHAPES)
-def test_both_kernels_d128(lib, shape, causal, kernel):
-    # D = 128 has two kernels (block-serial and software-pipelined); each is checked on its own
+def test_both_kernels(lib, shape, causal, kernel, D):
+    # Both kernels (block-serial and software-pipelined) at both head dimensions, each checked on its own
     B, H, Nq, Nkv = shape
-    rng = np.random.default_rng(Nq * 11 + Nkv)
-    Q, K, V = (rng.standard_normal((B, H, n, 128)).astype(np.float16) for n in (Nq, Nkv, Nkv))
+    rng = np.random.default_rng(Nq * 11 + Nkv + D)
+    Q, K, V = (rng.standard_normal((B, H, n, D)).astype(np.float16) for n in (Nq, Nkv, Nkv))
     ref = oracle.attention(Q, K, V, causal=causal)
     assert_parity(run(lib, Q, K, V, causal, kernel=KERNELS[kernel]), ref, (shape, causal, kernel))
 
 
 @pytest.mark.parametrize("kernel", list(KERNELS))
 @pytest.mark.parametrize("scale", [0.0, -0.05, 0.05, 1.0])
-def test_explicit_scales_d128(lib, scale, kernel):
-    # zero and negative scales take the path that scales the scores before the row maximum
-    Q, K, V = workloads.make_attention_inputs("attn_b1_h8_q777_kv1500_d128", B=1, H=2, Nq=200, Nkv=333)
+@pytest.mark.parametrize("wname", ["attn_b1_h8_q777_kv1500_d128", "attn_b2_h16_n1000_d64_causal"])
+def test_explicit_scales_by_kernel(lib, scale, kernel, wname):
+    # zero and negative scales take the path that scales the scores before the row maximum (D = 128 and 64)
+    Q, K, V = workloads.make_attention_inputs(wname, B=1, H=2, Nq=200, Nkv=333)
     for causal in (False, True):
         ref = oracle.attention(Q, K, V, causal=causal, scale=scale)
         assert_parity(run(lib, Q, K, V, causal, scale=scale, kernel=KERNELS[kernel]), ref, (scale, causal, kernel))
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("kernel", list(KERNELS))
-def test_rising_scores_move_the_reference_maximum(lib, kernel):
+def test_rising_scores_move_the_reference_maximum(lib, kernel, D):
     # Key rows grow in norm along the sequence, so a row's block maxima keep rising and the lazily raised
     # reference maximum moves many times mid-sequence (each time a block maximum passes it by more than 2^8);
     # in the pipelined kernel every such move recomputes the next block's first-half probabilities.
     rng = np.random.default_rng(21)
-    N, D = 900, 128
+    N = 900
     Q = rng.standard_normal((1, 2, N, D))
     K = rng.standard_normal((1, 2, N, D)) * (1.0 + np.arange(N) / 20.0)[None, None, :, None] / 4.0
     V = rng.standard_normal((1, 2, N, D))
@@ -117,7 +120,8 @@ def test_rising_scores_move_the_reference_maximum(lib, kernel):
         assert_parity(got, ref, ("rising", causal, kernel))
 
 
-@pytest.mark.parametrize("kernel,D", [("block_serial", 64), ("block_serial", 128), ("pipelined", 128)])
+@pytest.mark.parametrize("kernel,D", [("block_serial", 64), ("block_serial", 128), ("pipelined", 64),
+                                      ("pipelined", 128)])
 @pytest.mark.parametrize("key", [650, 700])
 def test_dominant_late_key_forces_rescale(lib, kernel, D, key):
     # One key far into the sequence (block 10; key 650 in the first half of its 64-key block, 700 in the
