@@ -3,7 +3,7 @@
 The shipped kernels allocate nothing and issue no memset, and every call is plain kernel launches on the
 caller's stream, so a captured sequence of calls replays as recorded.  The graph below holds the GEMM on three
 paths (tile kernel with bias + GELU, skinny kernel, B given transposed), the row softmax and both attention
-kernels.  Before each replay the inputs are rewritten in place with new seeded values, the same calls run
+kernels (block-serial forced at D = 64, the default pipelined one at D = 128).  Before each replay the inputs are rewritten in place with new seeded values, the same calls run
 eagerly and the outputs are poisoned with NaN; the replay must then reproduce the eager outputs bit for bit
 (every kernel here is deterministic), several times in a row, with eager work and synchronisations between.
 """
@@ -35,9 +35,9 @@ def test_graph_replays_match_eager(lib):
         ops.append(("gemm", (A, B, bias), C, (epi, bt)))
     X = torch.empty((37, 3001), **f16)
     ops.append(("softmax", (X,), torch.empty_like(X), None))
-    for Bn, H, N, D in ((1, 2, 200, 64), (1, 2, 300, 128)):
+    for Bn, H, N, D, kernel in ((1, 2, 200, 64, g.ATTN_KERNEL_BLOCK_SERIAL), (1, 2, 300, 128, None)):
         Q, K, V = (torch.empty((Bn, H, N, D), **f16) for _ in range(3))
-        ops.append(("attention", (Q, K, V), torch.empty_like(Q), None))
+        ops.append(("attention", (Q, K, V), torch.empty_like(Q), kernel))
 
     def fill(seed):
         for i, (_, ins, _, _) in enumerate(ops):
@@ -53,7 +53,7 @@ def test_graph_replays_match_eager(lib):
             elif kind == "softmax":
                 g.softmax_f16(ins[0], out=out)
             else:
-                g.flash_attn(*ins, causal=True, out=out)
+                g.flash_attn(*ins, causal=True, out=out, kernel=extra)
 
     fill(0)
     torch.cuda.synchronize()
