@@ -336,28 +336,28 @@ flash_attn_fwd_kernel(FaArgs p) {
 // the softmax on the vector ALU, then the PV MFMAs; each stage waits for the
 // one before, so a wave's matrix cores idle through its softmax.  A 32x32x16
 // MFMA occupies the matrix core for 32 cycles, during which the same wave can
-// issue independent vector instructions (about one exponential and two or
-// three FMAs) at almost no cost.  This kernel therefore interleaves the stages
-// of neighbouring blocks within each wave:
+// issue independent vector instructions (about one exponential and two or three
+// FMAs) at almost no cost.  This kernel therefore interleaves the stages of
+// neighbouring blocks within each wave:
 //   phase A(j): the score MFMAs of block j+1    || exponentials of block j, keys 32..63
 //   phase B(j): the PV MFMAs of block j         || exponentials of block j+1, keys 0..31
-// Each phase is a fixed sequence of 16 slots (8 at D = 64) fenced by
-// scheduling barriers; a slot holds one MFMA, the LDS reads of a later slot's
-// operand, and a share of the vector work (at D = 64 an exponential pair in
-// every slot, at D = 128 in every other one).  A block's exponentials use the reference maximum as it
-// stands.  The lazy-rescale test of the block-serial kernel (does the block's
-// maximum exceed the reference by more than 2^8?) is taken between phases A(j)
-// and B(j), once all of block j's probabilities exist, and without the block's
-// maximum: each probability is at most the sum of those a lane holds, so a lane
-// whose sum of the block's fp16 probabilities stays below 2^8 holds none above
-// 2^8.  Only when some lane's sum reaches 2^8 is the block's maximum formed; if
-// it exceeds the reference by more than 2^8, the reference is raised, the
-// accumulators and the running sum are rescaled and the block's probabilities
-// are formed again.  The block-serial kernel takes the same test on the same
-// probabilities; the two differ in the order of instructions and of the sums.
-// K and V tiles are copied one block apart: after the barrier that opens
-// A(j), K(j+2) and V(j+1) are issued into the buffers that K(j) and V(j-1)
-// have left, so two buffers of each suffice.
+// Each phase is a fixed sequence of 16 slots (8 at D = 64) fenced by scheduling
+// barriers; a slot holds one MFMA, the LDS reads of a later slot's operand, and
+// a share of the vector work (at D = 64 an exponential pair in every slot,
+// at D = 128 in every other one).  A block's exponentials use the reference
+// maximum as it stands.  The lazy-rescale test of the block-serial kernel (does the
+// block's maximum exceed the reference by more than 2^8?) is taken between
+// phases A(j) and B(j), once all of block j's probabilities exist, and without
+// the block's maximum: each probability is at most the sum of those a lane
+// holds, so a lane whose sum of the block's fp16 probabilities stays below 2^8
+// holds none above 2^8.  Only when some lane's sum reaches 2^8 is the block's
+// maximum formed; if it exceeds the reference by more than 2^8, the reference
+// is raised, the accumulators and the running sum are rescaled and the block's
+// probabilities are formed again.  The block-serial kernel takes the same test
+// on the same probabilities; the two differ in the order of instructions and of
+// the sums.  K and V tiles are copied one block apart: after the barrier that
+// opens A(j), K(j+2) and V(j+1) are issued into the buffers that K(j) and
+// V(j-1) have left, so two buffers of each suffice.
 template <int D, bool CAUSAL, bool PRESCALE>
 __global__ void __launch_bounds__(FA_NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 flash_attn_fwd_pipe_kernel(FaArgs p) {
