@@ -199,3 +199,16 @@ def test_determinism(lib):
     b = g.flash_attn(Q, K, V, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", list(workloads.ATTENTION_WORKLOADS))
+def test_block_serial_kernel_whole_slabs(lib, name):
+    # The block-serial kernel, no longer the default at either head dimension, forced on the full-size
+    # workloads: whole (batch, head) slabs against the oracle (2 slabs of each 4096-token workload, 8 otherwise).
+    w = workloads.ATTENTION_WORKLOADS[name]
+    Q, K, V = workloads.make_attention_inputs(w)
+    got = run(lib, Q, K, V, w.causal, kernel=KERNELS["block_serial"]).reshape(-1, w.D)
+    slabs, rows = _slab_rows(w, max_slabs=2 if w.Nq >= 4096 else 8)
+    ref = oracle.attention_rows(Q, K, V, rows, causal=w.causal)
+    assert_parity(got[rows], ref, (name, slabs))
+    assert not np.isnan(got).any()
